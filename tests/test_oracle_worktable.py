@@ -1,0 +1,43 @@
+"""Pins for the work-table checker: it accepts hand-made valid tables and
+rejects each kind of invalid one."""
+import numpy as np
+import pytest
+
+from oracle import worktable as wt
+
+CAPS = np.array([[64, 16], [0, 48]])
+ACTIVE = np.array([True, True])
+
+
+def _valid():
+    # heads (0,0): 64 tokens, (0,1): 16, (1,0): 0, (1,1): 48; two workers of 4 pages
+    rows = [(0, 0, 32, 0), (0, 32, 64, 0), (1, 0, 16, 0), (3, 0, 16, 0), (3, 16, 48, 0)]
+    # worker 0: rows 0,1 (4 pages); worker 1: rows 2..4 (1 + 1 + 2 pages)
+    return np.array(rows), np.array([0, 2, 5]), np.array([0, 2, 3, 3, 5])
+
+
+def test_accepts_valid():
+    rows, ws, hrs = _valid()
+    loads = wt.check(rows, ws, hrs, CAPS, ACTIVE)
+    assert loads == [4, 4]
+
+
+@pytest.mark.parametrize("mutate", ["gap", "overlap", "unaligned", "short", "foreign", "unbalanced"])
+def test_rejects_invalid(mutate):
+    rows, ws, hrs = _valid()
+    rows = rows.copy()
+    if mutate == "gap":
+        rows[1, 1] = 48
+    elif mutate == "overlap":
+        rows[1, 1] = 16
+    elif mutate == "unaligned":
+        rows[0, 2] = 33
+        rows[1, 1] = 33
+    elif mutate == "short":
+        rows[4, 2] = 40
+    elif mutate == "foreign":
+        rows[2, 0] = 2
+    elif mutate == "unbalanced":
+        ws = np.array([0, 0, 5])
+    with pytest.raises(AssertionError):
+        wt.check(rows, ws, hrs, CAPS, ACTIVE)
