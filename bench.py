@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark: non-uniform paged decode attention on one MI355X.
+
+One step is one decode step of the Qwen2.5-32B-shaped multi-turn layer
+(64 sessions, 40 query / 8 KV heads, head_dim 128, contexts uniform in
+[8192, 65536], per-KV-head keep ratios ~ Beta(0.5, 2), 4 head groups, 16-token
+pages): kv_append of one token per (session, KV head), the frame commit, and
+attn_decode_nonuniform (split-K partial attention + log-sum-exp merge).
+Inputs are synthetic (seeded) and resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is the step's algorithmic bytes per second
+(GB/s); `roofline` is the split-K partial-attention kernel (the dominant
+kernel) timed with HIP events on its own stream; `cpu_baseline` is the fp64
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def kv_bytes(lengths, D=128):
+    return int(np.asarray(lengths, dtype=np.int64).sum()) * 2 * D * 2
+
+
+def algorithmic_bytes(lengths, caps, B, Hq, Hkv, ng, D=128, page=16, gqa_rows=True):
+    """Bytes the decode attention must move: retained K+V, q, out, the page
+    table entries it walks and the lengths."""
+    L = np.asarray(lengths, dtype=np.int64)
+    kv = int(L.sum()) * 2 * D * 2
+    q = B * Hq * D * 2
+    out = B * Hq * D * 4
+    gh = Hkv // ng
+    pages = 0
+    for g in range(ng):
+        pages += int(np.ceil(np.asarray(caps)[:, g * gh:(g + 1) * gh].max(axis=1) / page).sum())
+    return kv + q + out + pages * 4 + B * Hkv * 4
+
+
+class Setup:
+    """Pools, context and step buffers for one workload on the GPU."""
+
+    def __init__(self, w, headroom_steps, num_workers=0, plan_mode=0, uniform_splits=0):
+        import torch
+        import non_uniform_paged_amd as nup
+        import workloads as W
+
+        self.w = w
+        pad = 16 * int(math.ceil((headroom_steps + 1) / 16))
+        self.caps = (w.lengths + pad).astype(np.int32)
+        self.lengths0 = w.lengths.astype(np.int32)
+        B, H, Hq, D, ng = w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, w.num_groups
+        gh = H // ng
+        max_pages = int(math.ceil(self.caps.max() / 16))
+        need = 0
+        for g in range(ng):
+            need += int(np.ceil(self.caps[:, g * gh:(g + 1) * gh].max(axis=1) / 16).sum())
+        num_pages = max(w.num_pages, need)
+        self.kpool = torch.empty((num_pages, gh, 16, D), dtype=torch.bfloat16, device="cuda")
+        self.vpool = torch.empty_like(self.kpool)
+        W.fill_normal_bf16_torch(self.kpool, "k")
+        W.fill_normal_bf16_torch(self.vpool, "v")
+        cfg = dict(num_kv_heads=H, num_q_heads=Hq, head_dim=D, num_groups=ng, max_batch=B,
+                   num_pages=num_pages, max_pages=max_pages, num_workers=num_workers,
+                   plan_mode=plan_mode, uniform_splits=uniform_splits)
+        self.desc = torch.empty(nup.desc_bytes(**cfg), dtype=torch.uint8, device="cuda")
+        self.ctx = nup.Context(**cfg, k_pool=self.kpool, v_pool=self.vpool, desc=self.desc,
+                               free_list_init=w.free_list_init)
+        nup.kv_alloc_groups(self.ctx, np.arange(B), self.caps, self.lengths0)
+        nup.nup_commit(self.ctx)
+        self.q = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+        W.fill_normal_bf16_torch(self.q, "q")
+        self.k_new = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+        self.v_new = torch.empty_like(self.k_new)
+        W.fill_normal_bf16_torch(self.k_new, "k", 77)
+        W.fill_normal_bf16_torch(self.v_new, "v", 77)
+        self.out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(nup.workspace_bytes(self.ctx), dtype=torch.uint8, device="cuda")
+        self.scale = 1.0 / math.sqrt(D)
+        self.num_pages = num_pages
+        self.steps_done = 0
+
+    def step(self, append=True):
+        import non_uniform_paged_amd as nup
+        if append:
+            nup.kv_append(self.ctx, self.k_new, self.v_new)
+            self.steps_done += 1
+        nup.nup_commit(self.ctx)
+        nup.attn_decode_nonuniform(self.ctx, self.q, self.out, self.lse, self.scale, self.ws)
+
+    def free(self):
+        import torch
+        del self.ctx
+        del self.kpool, self.vpool, self.desc, self.ws
+        torch.cuda.empty_cache()
+
+
+def time_steps(setup, steps, warmup, append=True):
+    """Returns (ms per step, partial-kernel ms per launch, mean lengths)."""
+    import torch
+    import non_uniform_paged_amd as nup
+    for _ in range(warmup):
+        setup.step(append)
+    torch.cuda.synchronize()
+    nup.kernel_time(setup.ctx, reset=True)
+    nup.set_timing(setup.ctx, True)
+    L_before = setup.lengths0 + setup.steps_done
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        setup.step(append)
+    e1.record()
+    torch.cuda.synchronize()
+    nup.set_timing(setup.ctx, False)
+    ms = e0.elapsed_time(e1) / steps
+    kms, n = nup.kernel_time(setup.ctx, reset=True)
+    L_after = setup.lengths0 + setup.steps_done
+    # lengths seen by the attention of each timed step: L_before+1 .. L_after
+    mean_L = (L_before + L_after + (1 if append else 0)) / 2.0 if append else L_before
+    return ms, kms / max(n, 1), mean_L
+
+
+def traffic_from_profiles(kernel_src_sha):
+    p = os.path.join(ROOT, "profiles", "traffic_partial_attn_qwen25_32b.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+    except Exception:
+        return None
+    if t.get("kernels_hip_sha256") != kernel_src_sha:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(setup, budget_s=15.0):
+    """The fp64 oracle on the first n sessions of the same workload, n chosen so
+    that the run takes roughly budget_s seconds of CPU time."""
+    import torch
+    import oracle
+    from oracle import pager as pg
+    w = setup.w
+    spec = pg.PagerSpec(w.num_kv_heads, w.num_groups, w.batch, setup.num_pages,
+                        int(math.ceil(setup.caps.max() / 16)), 16, w.free_list_init)
+    assert spec.alloc(np.arange(w.batch), setup.caps, setup.lengths0) == pg.OK
+    threads = os.cpu_count() or 1
+
+    def run(seqs):
+        sub = spec.page_table[:, seqs, :]
+        used = np.unique(sub[sub >= 0])
+        remap = np.full(spec.num_pages, -1, np.int64)
+        remap[used] = np.arange(len(used))
+        pt = np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(np.int32)
+        idx = torch.from_numpy(used.astype(np.int64)).cuda()
+        pk = setup.kpool.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+        pv = setup.vpool.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+        q = setup.q.view(torch.int16).cpu().numpy().view(np.uint16)[seqs]
+        L = spec.lengths[seqs]
+        t0 = time.perf_counter()
+        oracle.decode(q, pk, pv, pt, L, spec.group_of_head, spec.slot_of_head, setup.scale,
+                      num_threads=threads)
+        dt = time.perf_counter() - t0
+        b = algorithmic_bytes(L, setup.caps[seqs], len(seqs), w.num_q_heads, w.num_kv_heads,
+                              w.num_groups)
+        return dt, b
+
+    dt, b = run([0])
+    n = int(max(1, min(w.batch, math.floor(budget_s / max(dt, 1e-3)))))
+    if n > 1:
+        dt, b = run(list(range(n)))
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.batch} sessions of the same batch (all their KV heads), "
+                      f"one decode step, fp64 C oracle with OpenMP; {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-controls", action="store_true")
+    ap.add_argument("--workers", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the path shards by sequence "
+                                   "or head group with no exchange, but no multi-GPU run is provided",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import non_uniform_paged_amd as nup  # noqa: F401  (fails loudly when not built)
+    import workloads as W
+
+    src = open(os.path.join(ROOT, "non_uniform_paged_amd", "csrc", "kernels.hip"), "rb").read()
+    sha = hashlib.sha256(src).hexdigest()
+
+    w = W.qwen25_32b()
+    headroom = args.warmup + args.steps + 8
+    st = Setup(w, headroom, num_workers=args.workers)
+    ms, kms, mean_L = time_steps(st, args.steps, args.warmup)
+    B, Hq, H, D, ng = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_groups
+    step_bytes = algorithmic_bytes(mean_L, st.caps, B, Hq, H, ng) + B * H * D * 2 * 2 * 2
+    kern_bytes = algorithmic_bytes(mean_L, st.caps, B, Hq, H, ng) - B * Hq * D * 4
+    value = step_bytes / (ms * 1e-3) / 1e9
+    achieved = kern_bytes / (kms * 1e-3) / 1e9
+    extra = {"kv_bytes_per_step": kv_bytes(mean_L), "partial_kernel_ms": round(kms, 4),
+             "pct_of_peak_step": round(100 * value / PEAK_HBM_GBS, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(st)
+    st.free()
+    del st
+
+    if not args.no_controls:
+        # Uniform-budget control on the same contexts (keep 50% of every head):
+        # the gate compares the non-uniform kernel's bytes/s with this one's.
+        for tag, ctl in (("uniform50", "uniform50"), ("uniform_mean", "uniform_mean")):
+            wc = W.qwen25_32b(control=ctl)
+            sc = Setup(wc, headroom, num_workers=args.workers)
+            cms, ckms, cL = time_steps(sc, max(10, args.steps // 2), args.warmup)
+            cb = algorithmic_bytes(cL, sc.caps, B, Hq, H, ng) - B * Hq * D * 4
+            extra[f"control_{tag}_kernel_GBs"] = round(cb / (ckms * 1e-3) / 1e9, 1)
+            extra[f"control_{tag}_kernel_ms"] = round(ckms, 4)
+            sc.free()
+            del sc
+        extra["nonuniform_over_uniform50"] = round(achieved / extra["control_uniform50_kernel_GBs"], 4)
+
+    traffic = traffic_from_profiles(sha)
+    line = {
+        "metric": "decode-attn achieved HBM GB/s (% of peak) + tokens/s/step, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s_per_step": round(B / (ms * 1e-3), 1),
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Qwen2.5-32B-shaped multi-turn decode layer: 64 sessions, 40 q / 8 KV "
+                               "heads, head_dim 128, contexts U[8192,65536], keep ratio Beta(0.5,2) "
+                               "per KV head, 4 head groups, 16-token pages",
+                   "kv_dtype": "bf16", "batch": B, "kv_bytes": kv_bytes(mean_L),
+                   "step": "kv_append + nup_commit + attn_decode_nonuniform (partial + merge)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": "partial_attn_kernel<128,5,false>"},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,259 @@
+/*
+ * nupaged.h -- C ABI of libnupaged.so: non-uniform paged decode attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path: single-token decode attention over a paged bf16 KV cache whose
+ * KV heads each keep a different, fixed number of tokens; heads are
+ * clustered into groups that each own a page table; a split-K work table is
+ * computed ahead of time from the budgets; scattered pages or top-K entries
+ * can be gathered into contiguous staging.
+ *   - Tangram (Unlocking Non-Uniform KV Cache): fixed per-head budgets,
+ *     Head Group Page (Fig 8), ahead-of-time load balancing (Fig 4c, Fig 5,
+ *     Fig 13).
+ *   - KV-RM (Regularizing KV-Cache Movement): block pager with Reserve /
+ *     Trim edits, one committed descriptor per decode step through a
+ *     shadow-to-active swap, descriptor merging into few large transfers
+ *     (Fig 2, Fig 3).
+ *   - KVDrive (multi-tier KV cache): attention over selected critical
+ *     entries (Fig 1).
+ *
+ * Conventions
+ *   Status.   Every call returns an nup_status; no exception crosses the ABI.
+ *             nup_last_error() gives the message of the last failure on a
+ *             context.  Host-state mutators are all-or-nothing: on error the
+ *             pager state is unchanged.
+ *   Memory.   The caller owns every device buffer: the K and V pools, the
+ *             descriptor arena, q, out, lse, staging and workspace.  The
+ *             library never allocates device memory.  It owns its host state
+ *             and two pinned host staging buffers (hipHostMalloc) used to
+ *             upload the descriptor.
+ *   Streams.  `stream` is a hipStream_t passed as void*.  Every launch and
+ *             copy is asynchronous on that stream.  All calls on one context
+ *             must be ordered on one stream (the active descriptor is shared
+ *             state on the device).  Device-side faults surface at the
+ *             caller's next synchronisation; NUP_E_HIP reports launch-time
+ *             failures only.  Data errors found by kernels (bad top-K
+ *             indices) are latched in the arena and read by
+ *             nup_device_errors().
+ *   Threads.  A context is not thread-safe; use one context per thread.
+ *   Layouts.  bf16 values are passed as raw 16-bit words.
+ *     K/V pool:    bf16 [num_pages][heads_per_group][page_size][head_dim]
+ *                  (one pool for K, one for V; a page holds page_size tokens
+ *                  of every head of one group, each head's rows contiguous)
+ *     q:           bf16 [max_batch][num_q_heads][head_dim]
+ *     out:         fp32 [max_batch][num_q_heads][head_dim]
+ *     lse:         fp32 [max_batch][num_q_heads], natural log; may be NULL
+ *     GQA:         query head r reads KV head r / (num_q_heads/num_kv_heads)
+ *     page table:  int32 [num_groups][max_batch][max_pages], -1 padded
+ *   Inactive sequence slots (never allocated, or freed) produce out = 0 and
+ *   lse = -inf.
+ */
+#ifndef NUPAGED_H
+#define NUPAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t nup_status;
+enum {
+    NUP_OK = 0,
+    NUP_E_ARG = 1,      /* bad argument or unsupported shape */
+    NUP_E_NOPAGES = 2,  /* not enough free pages for a Reserve */
+    NUP_E_CAPACITY = 3, /* append past a head's fixed budget */
+    NUP_E_STATE = 4,    /* slot busy / not active, or uncommitted edits */
+    NUP_E_HIP = 5,      /* a HIP call failed at launch or copy time */
+    NUP_E_INDEX = 6     /* a top-K index is out of range, unsorted or repeated */
+};
+
+/* Split-K planning policy. */
+enum {
+    /* Tangram's ahead-of-time balance: the pages of all heads, concatenated,
+     * are cut into num_workers equal contiguous shares (rows split at head
+     * boundaries); every worker is resident for the whole launch. */
+    NUP_PLAN_BALANCED = 0,
+    /* The uniform split Tangram measures against (Fig 4c): every head is cut
+     * into the same number of chunks regardless of its length, one chunk
+     * per worker, scheduled by the hardware. */
+    NUP_PLAN_UNIFORM = 1
+};
+
+typedef struct nup_ctx nup_ctx;
+
+typedef struct nup_config {
+    int32_t num_kv_heads;   /* H_kv */
+    int32_t num_q_heads;    /* H_q, a multiple of H_kv; H_q/H_kv in {1,2,4,5,8} */
+    int32_t head_dim;       /* D: 64 or 128 */
+    int32_t page_size;      /* P: must be 16 */
+    int32_t num_groups;     /* n_g, divides H_kv; heads per group G_h = H_kv / n_g */
+    int32_t max_batch;      /* B_max: sequence slots in the fixed-shape descriptor */
+    int32_t num_pages;      /* physical pages in each pool */
+    int32_t max_pages;      /* logical pages per (slot, group): page-table row length */
+    int32_t num_workers;    /* split-K workers (waves); 0 = chosen from the device */
+    int32_t plan_mode;      /* NUP_PLAN_BALANCED or NUP_PLAN_UNIFORM */
+    int32_t uniform_splits; /* chunks per head for NUP_PLAN_UNIFORM (0 = 8) */
+    int32_t reserved0;
+    void *k_pool;           /* device, bf16 pool for K (caller-owned) */
+    void *v_pool;           /* device, bf16 pool for V (caller-owned) */
+    void *desc;             /* device, descriptor arena of nup_desc_bytes() bytes,
+                               256-byte aligned (caller-owned) */
+    const int32_t *free_list_init; /* host, [num_pages] permutation giving the
+                               initial free-list order, or NULL for 0..N-1; copied */
+} nup_config;
+
+/* Bytes of the device descriptor arena a configuration needs (active
+ * descriptor, page tables, error word).  Host only; no device call. */
+nup_status nup_desc_bytes(const nup_config *cfg, size_t *bytes);
+
+/* Create a context over caller-owned pools and arena.  The arena is not
+ * touched until the first nup_commit().  cfg->k_pool / v_pool / desc may be
+ * NULL for host-only use (pager, planner and coalescer queries); device
+ * calls on such a context fail with NUP_E_STATE.  Errors: NUP_E_ARG. */
+nup_status nup_create(const nup_config *cfg, nup_ctx **out);
+void nup_destroy(nup_ctx *ctx);
+const char *nup_last_error(const nup_ctx *ctx);
+
+/*
+ * kv_alloc_groups -- Reserve (KV-RM, Fig 3) for n sequence slots under fixed
+ * per-head budgets (Tangram, abstract: a static footprint per head).
+ *   slots [n]           slot ids in [0, B_max), distinct, currently inactive
+ *   cap   [n][H_kv]     capacity in tokens per (slot, KV head): the head's
+ *                       fixed budget plus any decode headroom; <= max_pages*P
+ *   len   [n][H_kv]     tokens already present (0..cap), or NULL for 0
+ *   group_of_head_out [H_kv] or NULL: receives each head's group
+ * On the first successful call the heads are grouped (Tangram, Fig 8):
+ * ordered by the sum of their capacities over this call's slots (ties by
+ * head index) and cut into n_g equal groups; the grouping is fixed after
+ * that.  Each (slot, group) receives ceil(max cap over the group / P) pages,
+ * popped from the front of the FIFO free list in (slot, group, logical page)
+ * order.  The shadow descriptor and the split-K plan are updated; nothing
+ * reaches the device before nup_commit().
+ * Errors: NUP_E_ARG, NUP_E_STATE (slot active), NUP_E_NOPAGES. */
+nup_status kv_alloc_groups(nup_ctx *ctx, int32_t n, const int32_t *slots,
+                           const int32_t *cap, const int32_t *len,
+                           int32_t *group_of_head_out);
+
+/* kv_free_seqs -- Trim (KV-RM, Fig 3; EOS absorbed by the pager): return the
+ * slots' pages to the back of the free list in (group, logical page) order
+ * and mark the slots inactive.  Errors: NUP_E_ARG, NUP_E_STATE (not active). */
+nup_status kv_free_seqs(nup_ctx *ctx, int32_t n, const int32_t *slots);
+
+/* nup_commit -- seal the step (KV-RM, Fig 3: one Frame commit through a
+ * shadow-to-active descriptor swap).  One host-to-device copy of the packed
+ * shadow (activity, lengths, and when they changed: the split-K plan, the
+ * trains and page-table row patches) into the arena, then, if rows changed,
+ * one small kernel that applies the patches.  Kernels enqueued earlier on
+ * the stream see the previous descriptor.  Errors: NUP_E_STATE, NUP_E_HIP. */
+nup_status nup_commit(nup_ctx *ctx, void *stream);
+
+/*
+ * kv_append -- the decode step's write: for every active (slot, KV head),
+ * store the new token's K and V rows at logical position L (page table
+ * entry L / P of the head's group, row L % P of the head's slot) and
+ * advance L by one, on the device and in the shadow.
+ *   k_new, v_new   device bf16 [B_max][H_kv][D]; rows of inactive slots ignored
+ * Requires a committed descriptor (NUP_E_STATE if edits are pending).
+ * NUP_E_CAPACITY, checked on the host before launch, if any active head
+ * has L == cap (a fixed budget is never exceeded; nothing is written). */
+nup_status kv_append(nup_ctx *ctx, const void *k_new, const void *v_new, void *stream);
+
+/*
+ * kv_gather_compact -- copy cache rows into contiguous staging (KV-RM,
+ * Fig 2: coalesced transfers feeding the attention kernel; KVDrive, Fig 1:
+ * fetch of critical entries).  Bit-exact copies of K and V rows.
+ *   mode 0 (trains): for every active (s, h), rows 0..L-1 go to
+ *        k_out/v_out rows row_off[s*H_kv + h] .. + L - 1.  The copy walks the
+ *        committed trains (maximal runs of physically consecutive pages).
+ *        row_off: device int64 [B_max*H_kv]; idx ignored.
+ *   mode 1 (indices): staging[s][h][k] = row of logical position
+ *        idx[s][h][k], k < K; idx: device int32 [B_max][H_kv][K],
+ *        ascending, distinct, 0 <= idx < L.  k_out/v_out: bf16
+ *        [B_max][H_kv][K][D].  A violating index is not read: its staging
+ *        row is zero-filled and NUP_E_INDEX is latched for nup_device_errors().
+ *   phys_out: optional device int32 receiving each copied row's physical
+ *        row id (page * G_h * P + slot * P + t % P), laid out like the
+ *        staging rows; NULL to skip.
+ * Rows of inactive slots are not written.  Errors: NUP_E_ARG, NUP_E_STATE, NUP_E_HIP. */
+nup_status kv_gather_compact(nup_ctx *ctx, int32_t mode, const int32_t *idx, int32_t K,
+                             void *k_out, void *v_out, const int64_t *row_off,
+                             int32_t *phys_out, void *stream);
+
+/* Workspace bytes attn_decode_nonuniform / attn_decode_topk need for split-K
+ * partial results at this configuration (K = top-K count, 0 for the paged
+ * call).  Host only. */
+nup_status nup_workspace_bytes(const nup_ctx *ctx, int32_t K, size_t *bytes);
+
+/*
+ * attn_decode_nonuniform -- decode attention of one query token per active
+ * slot over each KV head's own retained length, read through its group's
+ * page table (Tangram, abstract and Fig 8), split ahead of time by the
+ * committed work table (Tangram, Fig 13) and merged by log-sum-exp
+ * (the split-K decoding scheme Tangram builds on).
+ *   q        device bf16 [B_max][H_q][D]
+ *   out      device fp32 [B_max][H_q][D];  lse device fp32 [B_max][H_q] or NULL
+ *   scale    softmax scale (1/sqrt(D) is the usual choice)
+ *   workspace device, >= nup_workspace_bytes(ctx, 0) bytes, 256-byte aligned
+ * Uses the active descriptor: the state of the last nup_commit() plus the
+ * appends since.  Errors: NUP_E_ARG, NUP_E_STATE, NUP_E_HIP. */
+nup_status attn_decode_nonuniform(nup_ctx *ctx, const void *q, float *out, float *lse,
+                                  float scale, void *workspace, size_t ws_bytes,
+                                  void *stream);
+
+/*
+ * attn_decode_topk -- decode attention over K gathered entries per active
+ * (slot, KV head) held contiguously (KVDrive, Fig 1: sparse attention over
+ * critical entries), e.g. the output of kv_gather_compact mode 1.
+ *   k_stage, v_stage  device bf16 [B_max][H_kv][K][D]
+ *   out / lse / scale / workspace as for attn_decode_nonuniform, with
+ *   workspace >= nup_workspace_bytes(ctx, K).
+ * Activity comes from the active descriptor.  Errors: NUP_E_ARG, NUP_E_STATE, NUP_E_HIP. */
+nup_status attn_decode_topk(nup_ctx *ctx, const void *q, const void *k_stage,
+                            const void *v_stage, int32_t K, float *out, float *lse,
+                            float scale, void *workspace, size_t ws_bytes, void *stream);
+
+/* ---- host-side queries (no device call; for tests and reports) ---------- */
+
+/* Shadow page table int32 [n_g][B_max][max_pages]. */
+nup_status nup_get_page_table(const nup_ctx *ctx, int32_t *out);
+/* Shadow lengths int32 [B_max][H_kv] (0 for inactive slots). */
+nup_status nup_get_lengths(const nup_ctx *ctx, int32_t *out);
+/* group_of_head / slot_of_head int32 [H_kv] each (-1 before the first Reserve). */
+nup_status nup_get_groups(const nup_ctx *ctx, int32_t *group_of_head, int32_t *slot_of_head);
+/* Free list front to back: int32 [num_pages] capacity, count in *n. */
+nup_status nup_get_free_list(const nup_ctx *ctx, int32_t *out, int32_t *n);
+/* Trains of the shadow page tables: int32 [max_runs][5] rows of
+ * (slot, group, first physical page, pages, first logical page) in (slot,
+ * group, logical page) order; count in *n (NUP_E_ARG if max_runs is short). */
+nup_status nup_get_runs(const nup_ctx *ctx, int32_t *out, int32_t max_runs, int32_t *n);
+/* Split-K plan of the shadow: counts first (any pointer may be NULL).
+ *   rows           int32 [n_rows][4] = (slot*H_kv + head, t0, t1, 0)
+ *   worker_start   int32 [n_workers + 1]
+ *   head_row_start int32 [B_max*H_kv + 1] */
+nup_status nup_get_plan(const nup_ctx *ctx, int32_t *n_rows, int32_t *n_workers,
+                        int32_t *rows, int32_t *worker_start, int32_t *head_row_start);
+
+/* ---- measurement helpers ------------------------------------------------ */
+
+/* When enabled, the library brackets each split-K partial-attention launch
+ * with HIP events on the caller's stream; nup_kernel_time() returns the
+ * summed milliseconds and launch count since the last reset (synchronises
+ * on the recorded events). */
+nup_status nup_set_timing(nup_ctx *ctx, int32_t enable);
+nup_status nup_kernel_time(nup_ctx *ctx, double *partial_ms, int32_t *launches, int32_t reset);
+
+/* Read and clear the latched device error word (synchronises the stream).
+ * *code receives NUP_OK or NUP_E_INDEX. */
+nup_status nup_device_errors(nup_ctx *ctx, void *stream, int32_t *code);
+
+/* Plain streaming copy of `bytes` (a multiple of 16) from src to dst with
+ * 16-byte loads and stores: the calibration kernel for HBM counters and the
+ * achievable-bandwidth ceiling.  Errors: NUP_E_ARG, NUP_E_HIP. */
+nup_status nup_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NUPAGED_H */

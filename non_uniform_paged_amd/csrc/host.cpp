@@ -1,0 +1,909 @@
+// Host control plane and C ABI of libnupaged.so.
+//
+//  * Head grouping and the head-group block pager (Tangram, Fig 8 Head Group
+//    Page; KV-RM, Fig 3 Reserve / Trim): a FIFO free list of physical pages,
+//    one dense int32 page table per (group, sequence slot).
+//  * Ahead-of-time split-K plan (Tangram, Fig 4c / Fig 13): computed from the
+//    reserved capacities whenever the batch composition changes, never per
+//    decode step.
+//  * Trains (KV-RM, Fig 3 descriptor merging): maximal runs of physically
+//    consecutive pages per (slot, group).
+//  * Frame commit (KV-RM, Fig 3 shadow-to-active swap): the host shadow is
+//    packed into a pinned buffer and reaches the device in one copy; page
+//    table rows that changed travel as patches applied by one small kernel.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <numeric>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/nupaged.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Byte sizes of the packed descriptor sections, all int32 words.
+struct Sizes {
+    size_t fixed;        // active[B] lengths[B*H] goh[H] soh[H] head_of_gslot[H]
+    size_t plan_max;     // worker_start[W+1] head_row_start[B*H+1] rows[R][4]
+    size_t runs_max;     // runs[N][4] run_prefix[N+1]
+    size_t patches_max;  // hdr[ng*B][4] data[ng*B*max_pages]
+    size_t inbox;        // fixed + plan_max + runs_max + patches_max (aligned)
+    size_t pt;           // page table bytes
+    size_t total;        // inbox + pt + error word
+    int max_rows;
+    int max_workers;
+};
+
+int default_workers_hostonly() { return 2048; }
+
+bool valid_gqa(int g) { return g == 1 || g == 2 || g == 4 || g == 5 || g == 8; }
+
+nup_status validate(const nup_config *c, std::string *why) {
+    auto bad = [&](const char *m) { if (why) *why = m; return NUP_E_ARG; };
+    if (!c) return bad("config is NULL");
+    if (c->num_kv_heads <= 0 || c->num_q_heads <= 0) return bad("head counts must be positive");
+    if (c->num_q_heads % c->num_kv_heads) return bad("num_q_heads must be a multiple of num_kv_heads");
+    if (!valid_gqa(c->num_q_heads / c->num_kv_heads)) return bad("num_q_heads/num_kv_heads must be 1, 2, 4, 5 or 8");
+    if (c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 64 or 128");
+    if (c->page_size != nup::kPage) return bad("page_size must be 16");
+    if (c->num_groups <= 0 || c->num_kv_heads % c->num_groups) return bad("num_groups must divide num_kv_heads");
+    if (c->max_batch <= 0 || c->num_pages <= 0 || c->max_pages <= 0) return bad("max_batch, num_pages, max_pages must be positive");
+    if ((long long)c->num_pages * (c->num_kv_heads / c->num_groups) * nup::kPage > 0x7fffffffLL)
+        return bad("pool too large for 32-bit row ids");
+    if ((long long)c->max_pages * nup::kPage > 0x7fffffffLL) return bad("max_pages too large");
+    if (c->num_workers < 0) return bad("num_workers must be >= 0");
+    if (c->plan_mode != NUP_PLAN_BALANCED && c->plan_mode != NUP_PLAN_UNIFORM) return bad("unknown plan_mode");
+    if (c->uniform_splits < 0) return bad("uniform_splits must be >= 0");
+    return NUP_OK;
+}
+
+Sizes compute_sizes(const nup_config &c, int workers) {
+    Sizes z{};
+    const size_t B = c.max_batch, H = c.num_kv_heads, ng = c.num_groups;
+    const int splits = c.uniform_splits > 0 ? c.uniform_splits : 8;
+    if (c.plan_mode == NUP_PLAN_UNIFORM) {
+        z.max_rows = (int)(B * H * splits);
+        z.max_workers = z.max_rows;
+    } else {
+        z.max_rows = workers + (int)(B * H);
+        z.max_workers = workers;
+    }
+    z.fixed = align_up(4 * (B + B * H + 3 * H));
+    z.plan_max = align_up(4 * ((size_t)z.max_workers + 1)) + align_up(4 * (B * H + 1)) +
+                 align_up(16 * (size_t)z.max_rows);
+    z.runs_max = align_up(16 * (size_t)c.num_pages) + align_up(4 * ((size_t)c.num_pages + 1));
+    z.patches_max = align_up(16 * ng * B) + align_up(4 * ng * B * (size_t)c.max_pages);
+    z.inbox = z.fixed + z.plan_max + z.runs_max + z.patches_max;
+    z.pt = align_up(4 * ng * B * (size_t)c.max_pages);
+    z.total = z.inbox + z.pt + kAlign;
+    return z;
+}
+
+}  // namespace
+
+struct nup_ctx {
+    nup_config cfg{};
+    int H = 0, Hq = 0, D = 0, P = 0, ng = 0, gh = 0, B = 0, num_pages = 0, max_pages = 0, gqa = 0;
+    int workers = 0;      // balanced-plan worker count
+    Sizes sz{};
+    std::string err;
+    bool has_device = false;
+
+    // pager shadow
+    std::deque<int32_t> free_list;
+    std::vector<int32_t> pt;       // [ng][B][max_pages]
+    std::vector<int32_t> npages;   // [ng][B]
+    std::vector<int32_t> len, cap; // [B][H]
+    std::vector<int32_t> active;   // [B]
+    std::vector<int32_t> goh, soh, head_of_gslot;
+    bool grouped = false;
+
+    // edits since the last commit
+    std::vector<int32_t> dirty_count;  // [ng*B]: page-table entries to send, 0 = clean
+    bool plan_dirty = true;
+    bool pending = true;               // no commit yet, or edits since
+
+    // plan (shadow)
+    std::vector<int32_t> rows;         // [n][4]
+    std::vector<int32_t> worker_start; // [W+1]
+    std::vector<int32_t> head_row_start; // [B*H+1]
+
+    // active descriptor on the device (offsets into the inbox, in bytes)
+    bool committed = false;
+    size_t off_ws = 0, off_hrs = 0, off_rows = 0, off_runs = 0, off_runpre = 0;
+    int dev_workers = 0, dev_rows = 0, dev_runs = 0, dev_run_pages = 0;
+
+    // device pointers
+    char *desc = nullptr;
+    uint16_t *kpool = nullptr, *vpool = nullptr;
+
+    // pinned staging for commits
+    char *pinned[2] = {nullptr, nullptr};
+    hipEvent_t pinned_ev[2] = {nullptr, nullptr};
+    bool pinned_used[2] = {false, false};
+    int pinned_next = 0;
+
+    // timing
+    bool timing = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> tev;
+    double acc_ms = 0.0;
+    int launches = 0;
+
+    int32_t *inbox_i32(size_t off) { return reinterpret_cast<int32_t *>(desc + off); }
+    int32_t *d_active() { return inbox_i32(0); }
+    int32_t *d_len() { return inbox_i32(4 * (size_t)B); }
+    int32_t *d_goh() { return inbox_i32(4 * ((size_t)B + (size_t)B * H)); }
+    int32_t *d_soh() { return d_goh() + H; }
+    int32_t *d_hog() { return d_goh() + 2 * H; }
+    int32_t *d_pt() { return reinterpret_cast<int32_t *>(desc + sz.inbox); }
+    int32_t *d_err() { return reinterpret_cast<int32_t *>(desc + sz.inbox + sz.pt); }
+};
+
+namespace {
+
+nup_status fail(nup_ctx *c, nup_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->err = buf;
+    return st;
+}
+
+nup_status hip_fail(nup_ctx *c, hipError_t e, const char *what) {
+    return fail(c, NUP_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- grouping (Tangram, Fig 8) --------------------------------------------
+void group_heads(nup_ctx *c, int n, const int32_t *cap) {
+    std::vector<long long> key(c->H, 0);
+    for (int i = 0; i < n; ++i)
+        for (int h = 0; h < c->H; ++h) key[h] += cap[(size_t)i * c->H + h];
+    std::vector<int> order(c->H);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return key[a] < key[b]; });
+    for (int rank = 0; rank < c->H; ++rank) {
+        const int h = order[rank];
+        c->goh[h] = rank / c->gh;
+        c->soh[h] = rank % c->gh;
+        c->head_of_gslot[rank] = h;
+    }
+    c->grouped = true;
+}
+
+// ---- ahead-of-time split-K plan -------------------------------------------
+void plan_balanced(nup_ctx *c) {
+    const int B = c->B, H = c->H, P = c->P, W = c->workers;
+    std::vector<long long> base((size_t)B * H + 1, 0);  // first page of each head
+    for (int sh = 0; sh < B * H; ++sh) {
+        const int s = sh / H;
+        const long long pages = c->active[s] ? (c->cap[sh] + P - 1) / P : 0;
+        base[sh + 1] = base[sh] + pages;
+    }
+    const long long T = base[(size_t)B * H];
+    c->rows.clear();
+    c->worker_start.assign(W + 1, 0);
+    std::vector<int32_t> per_head((size_t)B * H, 0);
+    int sh = 0;
+    for (int w = 0; w < W; ++w) {
+        c->worker_start[w] = (int)(c->rows.size() / 4);
+        const long long lo = T * w / W, hi = T * (w + 1) / W;
+        long long p = lo;
+        while (p < hi) {
+            while (base[sh + 1] <= p) ++sh;  // head holding page p
+            const long long end = std::min(hi, base[sh + 1]);
+            const long long t0 = (p - base[sh]) * P;
+            const long long t1 = std::min<long long>((end - base[sh]) * P, c->cap[sh]);
+            c->rows.insert(c->rows.end(), {sh, (int32_t)t0, (int32_t)t1, 0});
+            per_head[sh]++;
+            p = end;
+        }
+    }
+    c->worker_start[W] = (int)(c->rows.size() / 4);
+    c->head_row_start.assign((size_t)B * H + 1, 0);
+    for (int i = 0; i < B * H; ++i) c->head_row_start[i + 1] = c->head_row_start[i] + per_head[i];
+}
+
+void plan_uniform(nup_ctx *c) {
+    const int B = c->B, H = c->H, P = c->P;
+    const int S = c->cfg.uniform_splits > 0 ? c->cfg.uniform_splits : 8;
+    c->rows.clear();
+    c->head_row_start.assign((size_t)B * H + 1, 0);
+    for (int sh = 0; sh < B * H; ++sh) {
+        const int s = sh / H;
+        const int cap = c->active[s] ? c->cap[sh] : 0;
+        int nr = 0;
+        if (cap > 0) {
+            const long long chunk = (long long)P * ((((long long)cap + S - 1) / S + P - 1) / P);
+            for (long long t0 = 0; t0 < cap; t0 += chunk) {
+                c->rows.insert(c->rows.end(), {sh, (int32_t)t0, (int32_t)std::min<long long>(t0 + chunk, cap), 0});
+                ++nr;
+            }
+        }
+        c->head_row_start[sh + 1] = c->head_row_start[sh] + nr;
+    }
+    const int n = (int)(c->rows.size() / 4);
+    c->worker_start.resize(n + 1);
+    std::iota(c->worker_start.begin(), c->worker_start.end(), 0);
+}
+
+void replan(nup_ctx *c) {
+    if (c->cfg.plan_mode == NUP_PLAN_UNIFORM) plan_uniform(c); else plan_balanced(c);
+}
+
+// ---- trains (KV-RM, Fig 3) --------------------------------------------------
+// Appends (slot, group, first physical page, pages, first logical page).
+void build_runs(const nup_ctx *c, std::vector<int32_t> &out) {
+    out.clear();
+    for (int s = 0; s < c->B; ++s) {
+        if (!c->active[s]) continue;
+        for (int g = 0; g < c->ng; ++g) {
+            const int32_t *row = &c->pt[((size_t)g * c->B + s) * c->max_pages];
+            const int n = c->npages[(size_t)g * c->B + s];
+            int i = 0;
+            while (i < n) {
+                const int start = i;
+                while (i + 1 < n && row[i + 1] == row[i] + 1) ++i;
+                out.insert(out.end(), {s, g, row[start], i - start + 1, start});
+                ++i;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+nup_status nup_desc_bytes(const nup_config *cfg, size_t *bytes) {
+    if (!bytes) return NUP_E_ARG;
+    if (validate(cfg, nullptr) != NUP_OK) return NUP_E_ARG;
+    int workers = cfg->num_workers > 0 ? cfg->num_workers : 0;
+    if (workers == 0) {
+        // largest default the library may pick: every CU at the highest occupancy
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+            workers = prop.multiProcessorCount * 32;
+        else
+            workers = default_workers_hostonly();
+    }
+    *bytes = compute_sizes(*cfg, workers).total;
+    return NUP_OK;
+}
+
+nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
+    if (!out) return NUP_E_ARG;
+    *out = nullptr;
+    std::string why;
+    if (validate(cfg, &why) != NUP_OK) {
+        fprintf(stderr, "nup_create: %s\n", why.c_str());
+        return NUP_E_ARG;
+    }
+    nup_ctx *c = new (std::nothrow) nup_ctx();
+    if (!c) return NUP_E_ARG;
+    c->cfg = *cfg;
+    c->H = cfg->num_kv_heads;
+    c->Hq = cfg->num_q_heads;
+    c->D = cfg->head_dim;
+    c->P = cfg->page_size;
+    c->ng = cfg->num_groups;
+    c->gh = c->H / c->ng;
+    c->B = cfg->max_batch;
+    c->num_pages = cfg->num_pages;
+    c->max_pages = cfg->max_pages;
+    c->gqa = c->Hq / c->H;
+    c->has_device = cfg->k_pool && cfg->v_pool && cfg->desc;
+    c->kpool = static_cast<uint16_t *>(cfg->k_pool);
+    c->vpool = static_cast<uint16_t *>(cfg->v_pool);
+    c->desc = static_cast<char *>(cfg->desc);
+    if (c->has_device && (reinterpret_cast<uintptr_t>(c->desc) % kAlign)) {
+        delete c;
+        fprintf(stderr, "nup_create: descriptor arena must be 256-byte aligned\n");
+        return NUP_E_ARG;
+    }
+    if (cfg->num_workers > 0) {
+        c->workers = cfg->num_workers;
+    } else if (!c->has_device) {
+        c->workers = default_workers_hostonly();
+    } else {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            delete c;
+            fprintf(stderr, "nup_create: no HIP device for a device context\n");
+            return NUP_E_HIP;
+        }
+        const int nb = nup::partial_blocks_per_cu(c->D, c->gqa, false);
+        c->workers = prop.multiProcessorCount * std::max(1, nb) * nup::kWavesPerBlock;
+    }
+    c->sz = compute_sizes(c->cfg, c->workers);
+    if (cfg->free_list_init) {
+        std::vector<char> seen(c->num_pages, 0);
+        for (int i = 0; i < c->num_pages; ++i) {
+            const int32_t p = cfg->free_list_init[i];
+            if (p < 0 || p >= c->num_pages || seen[p]) {
+                delete c;
+                fprintf(stderr, "nup_create: free_list_init is not a permutation\n");
+                return NUP_E_ARG;
+            }
+            seen[p] = 1;
+            c->free_list.push_back(p);
+        }
+    } else {
+        for (int i = 0; i < c->num_pages; ++i) c->free_list.push_back(i);
+    }
+    c->pt.assign((size_t)c->ng * c->B * c->max_pages, -1);
+    c->npages.assign((size_t)c->ng * c->B, 0);
+    c->len.assign((size_t)c->B * c->H, 0);
+    c->cap.assign((size_t)c->B * c->H, 0);
+    c->active.assign(c->B, 0);
+    c->goh.assign(c->H, -1);
+    c->soh.assign(c->H, -1);
+    c->head_of_gslot.assign(c->H, -1);
+    c->dirty_count.assign((size_t)c->ng * c->B, 0);
+    replan(c);
+    *out = c;
+    return NUP_OK;
+}
+
+void nup_destroy(nup_ctx *c) {
+    if (!c) return;
+    for (int i = 0; i < 2; ++i) {
+        if (c->pinned_ev[i]) {
+            (void)hipEventSynchronize(c->pinned_ev[i]);
+            (void)hipEventDestroy(c->pinned_ev[i]);
+        }
+        if (c->pinned[i]) (void)hipHostFree(c->pinned[i]);
+    }
+    for (auto &e : c->tev) {
+        (void)hipEventDestroy(e.first);
+        (void)hipEventDestroy(e.second);
+    }
+    delete c;
+}
+
+const char *nup_last_error(const nup_ctx *c) { return c ? c->err.c_str() : "null context"; }
+
+nup_status kv_alloc_groups(nup_ctx *c, int32_t n, const int32_t *slots, const int32_t *cap,
+                           const int32_t *len, int32_t *group_of_head_out) {
+    if (!c) return NUP_E_ARG;
+    if (n < 0) return fail(c, NUP_E_ARG, "n < 0");
+    if (n == 0) {
+        if (group_of_head_out && c->grouped) std::copy(c->goh.begin(), c->goh.end(), group_of_head_out);
+        return NUP_OK;
+    }
+    if (!slots || !cap) return fail(c, NUP_E_ARG, "slots and cap are required");
+    std::vector<char> seen(c->B, 0);
+    for (int i = 0; i < n; ++i) {
+        const int s = slots[i];
+        if (s < 0 || s >= c->B) return fail(c, NUP_E_ARG, "slot %d out of range", s);
+        if (seen[s]) return fail(c, NUP_E_ARG, "slot %d repeated", s);
+        seen[s] = 1;
+        for (int h = 0; h < c->H; ++h) {
+            const long long cp = cap[(size_t)i * c->H + h];
+            const long long ln = len ? len[(size_t)i * c->H + h] : 0;
+            if (cp < 0 || cp > (long long)c->max_pages * c->P)
+                return fail(c, NUP_E_ARG, "cap %lld of slot %d head %d outside [0, %lld]", cp, s, h,
+                            (long long)c->max_pages * c->P);
+            if (ln < 0 || ln > cp) return fail(c, NUP_E_ARG, "len %lld of slot %d head %d outside [0, cap]", ln, s, h);
+        }
+    }
+    for (int i = 0; i < n; ++i)
+        if (c->active[slots[i]]) return fail(c, NUP_E_STATE, "slot %d is already active", slots[i]);
+
+    // grouping of this call (fixed only once the call succeeds)
+    std::vector<int32_t> goh = c->goh;
+    if (!c->grouped) {
+        nup_ctx tmp;  // reuse group_heads on a scratch context
+        tmp.H = c->H;
+        tmp.gh = c->gh;
+        tmp.goh.assign(c->H, 0);
+        tmp.soh.assign(c->H, 0);
+        tmp.head_of_gslot.assign(c->H, 0);
+        group_heads(&tmp, n, cap);
+        goh = tmp.goh;
+    }
+    std::vector<int32_t> need((size_t)n * c->ng, 0);
+    long long total = 0;
+    for (int i = 0; i < n; ++i)
+        for (int h = 0; h < c->H; ++h) {
+            int32_t &x = need[(size_t)i * c->ng + goh[h]];
+            x = std::max<int32_t>(x, (cap[(size_t)i * c->H + h] + c->P - 1) / c->P);
+        }
+    for (int32_t x : need) total += x;
+    if (total > (long long)c->free_list.size())
+        return fail(c, NUP_E_NOPAGES, "need %lld pages, %zu free", total, c->free_list.size());
+
+    if (!c->grouped) group_heads(c, n, cap);
+    for (int i = 0; i < n; ++i) {
+        const int s = slots[i];
+        for (int g = 0; g < c->ng; ++g) {
+            const int np = need[(size_t)i * c->ng + g];
+            int32_t *row = &c->pt[((size_t)g * c->B + s) * c->max_pages];
+            for (int j = 0; j < np; ++j) {
+                row[j] = c->free_list.front();
+                c->free_list.pop_front();
+            }
+            const size_t ri = (size_t)g * c->B + s;
+            c->dirty_count[ri] = std::max(c->dirty_count[ri], np);
+            c->npages[ri] = np;
+        }
+        for (int h = 0; h < c->H; ++h) {
+            c->cap[(size_t)s * c->H + h] = cap[(size_t)i * c->H + h];
+            c->len[(size_t)s * c->H + h] = len ? len[(size_t)i * c->H + h] : 0;
+        }
+        c->active[s] = 1;
+    }
+    replan(c);
+    c->plan_dirty = true;
+    c->pending = true;
+    if (group_of_head_out) std::copy(c->goh.begin(), c->goh.end(), group_of_head_out);
+    return NUP_OK;
+}
+
+nup_status kv_free_seqs(nup_ctx *c, int32_t n, const int32_t *slots) {
+    if (!c) return NUP_E_ARG;
+    if (n < 0 || (n > 0 && !slots)) return fail(c, NUP_E_ARG, "bad slot list");
+    std::vector<char> seen(c->B, 0);
+    for (int i = 0; i < n; ++i) {
+        const int s = slots[i];
+        if (s < 0 || s >= c->B) return fail(c, NUP_E_ARG, "slot %d out of range", s);
+        if (seen[s]) return fail(c, NUP_E_ARG, "slot %d repeated", s);
+        seen[s] = 1;
+    }
+    for (int i = 0; i < n; ++i)
+        if (!c->active[slots[i]]) return fail(c, NUP_E_STATE, "slot %d is not active", slots[i]);
+    if (n == 0) return NUP_OK;
+    for (int i = 0; i < n; ++i) {
+        const int s = slots[i];
+        for (int g = 0; g < c->ng; ++g) {
+            const size_t ri = (size_t)g * c->B + s;
+            int32_t *row = &c->pt[ri * c->max_pages];
+            for (int j = 0; j < c->npages[ri]; ++j) {
+                c->free_list.push_back(row[j]);
+                row[j] = -1;
+            }
+            c->dirty_count[ri] = std::max(c->dirty_count[ri], c->npages[ri]);
+            c->npages[ri] = 0;
+        }
+        for (int h = 0; h < c->H; ++h) {
+            c->cap[(size_t)s * c->H + h] = 0;
+            c->len[(size_t)s * c->H + h] = 0;
+        }
+        c->active[s] = 0;
+    }
+    replan(c);
+    c->plan_dirty = true;
+    c->pending = true;
+    return NUP_OK;
+}
+
+nup_status nup_commit(nup_ctx *c, void *stream) {
+    if (!c) return NUP_E_ARG;
+    if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int i = c->pinned_next;
+    if (!c->pinned[i]) {
+        hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&c->pinned[i]), c->sz.inbox, hipHostMallocDefault);
+        if (e != hipSuccess) return hip_fail(c, e, "hipHostMalloc");
+        e = hipEventCreateWithFlags(&c->pinned_ev[i], hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(c, e, "hipEventCreate");
+    }
+    if (c->pinned_used[i]) {
+        hipError_t e = hipEventSynchronize(c->pinned_ev[i]);
+        if (e != hipSuccess) return hip_fail(c, e, "hipEventSynchronize");
+    }
+    char *blob = c->pinned[i];
+    int32_t *w = reinterpret_cast<int32_t *>(blob);
+    const size_t B = c->B, H = c->H;
+    for (size_t s = 0; s < B; ++s) w[s] = c->active[s];
+    for (size_t k = 0; k < B * H; ++k) w[B + k] = c->active[k / H] ? c->len[k] : 0;
+    std::copy(c->goh.begin(), c->goh.end(), w + B + B * H);
+    std::copy(c->soh.begin(), c->soh.end(), w + B + B * H + H);
+    std::copy(c->head_of_gslot.begin(), c->head_of_gslot.end(), w + B + B * H + 2 * H);
+    size_t used = c->sz.fixed;
+    int n_patches = 0;
+    size_t off_hdr = 0, off_data = 0;
+    if (c->plan_dirty || !c->committed) {
+        // plan
+        const int nw = (int)c->worker_start.size() - 1;
+        const int nr = (int)(c->rows.size() / 4);
+        size_t off = used;
+        c->off_ws = off;
+        std::memcpy(blob + off, c->worker_start.data(), 4 * c->worker_start.size());
+        off = align_up(off + 4 * c->worker_start.size());
+        c->off_hrs = off;
+        std::memcpy(blob + off, c->head_row_start.data(), 4 * c->head_row_start.size());
+        off = align_up(off + 4 * c->head_row_start.size());
+        c->off_rows = off;
+        if (nr) std::memcpy(blob + off, c->rows.data(), 16 * (size_t)nr);
+        off = align_up(off + 16 * (size_t)nr);
+        // trains
+        std::vector<int32_t> runs5;
+        build_runs(c, runs5);
+        const int nruns = (int)(runs5.size() / 5);
+        c->off_runs = off;
+        int32_t *rw = reinterpret_cast<int32_t *>(blob + off);
+        for (int r = 0; r < nruns; ++r) {
+            rw[r * 4 + 0] = runs5[r * 5 + 0] * c->ng + runs5[r * 5 + 1];
+            rw[r * 4 + 1] = runs5[r * 5 + 2];
+            rw[r * 4 + 2] = runs5[r * 5 + 3];
+            rw[r * 4 + 3] = runs5[r * 5 + 4];
+        }
+        off = align_up(off + 16 * (size_t)nruns);
+        c->off_runpre = off;
+        int32_t *pre = reinterpret_cast<int32_t *>(blob + off);
+        pre[0] = 0;
+        for (int r = 0; r < nruns; ++r) pre[r + 1] = pre[r] + runs5[r * 5 + 3];
+        off = align_up(off + 4 * ((size_t)nruns + 1));
+        // page-table patches
+        off_hdr = off;
+        int32_t *hdr = reinterpret_cast<int32_t *>(blob + off);
+        for (size_t ri = 0; ri < c->dirty_count.size(); ++ri)
+            if (c->dirty_count[ri] > 0) ++n_patches;
+        off = align_up(off + 16 * (size_t)n_patches);
+        off_data = off;
+        int32_t *data = reinterpret_cast<int32_t *>(blob + off);
+        size_t dpos = 0;
+        int p = 0;
+        for (size_t ri = 0; ri < c->dirty_count.size(); ++ri) {
+            const int cnt = c->dirty_count[ri];
+            if (cnt <= 0) continue;
+            hdr[p * 4 + 0] = (int32_t)ri;
+            hdr[p * 4 + 1] = cnt;
+            hdr[p * 4 + 2] = (int32_t)dpos;
+            hdr[p * 4 + 3] = 0;
+            std::memcpy(data + dpos, &c->pt[ri * c->max_pages], 4 * (size_t)cnt);
+            dpos += cnt;
+            ++p;
+        }
+        used = off + 4 * dpos;
+        c->dev_workers = nw;
+        c->dev_rows = nr;
+        c->dev_runs = nruns;
+        c->dev_run_pages = pre[nruns];
+    }
+    hipError_t e;
+    if (!c->committed) {  // the latched device error word starts clear
+        e = hipMemsetAsync(c->d_err(), 0, 4, st);
+        if (e != hipSuccess) return hip_fail(c, e, "hipMemsetAsync (error word)");
+    }
+    e = hipMemcpyAsync(c->desc, blob, used, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync (commit)");
+    if (n_patches > 0) {
+        e = nup::launch_apply_patches(c->d_pt(), reinterpret_cast<const int32_t *>(c->desc + off_hdr),
+                                      reinterpret_cast<const int32_t *>(c->desc + off_data), n_patches,
+                                      c->max_pages, st);
+        if (e != hipSuccess) return hip_fail(c, e, "apply_patches launch");
+    }
+    e = hipEventRecord(c->pinned_ev[i], st);
+    if (e != hipSuccess) return hip_fail(c, e, "hipEventRecord");
+    c->pinned_used[i] = true;
+    c->pinned_next = 1 - i;
+    std::fill(c->dirty_count.begin(), c->dirty_count.end(), 0);
+    c->plan_dirty = false;
+    c->pending = false;
+    c->committed = true;
+    return NUP_OK;
+}
+
+nup_status kv_append(nup_ctx *c, const void *k_new, const void *v_new, void *stream) {
+    if (!c) return NUP_E_ARG;
+    if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
+    if (!k_new || !v_new) return fail(c, NUP_E_ARG, "k_new and v_new are required");
+    if (!c->committed || c->pending) return fail(c, NUP_E_STATE, "edits pending: nup_commit first");
+    for (int s = 0; s < c->B; ++s) {
+        if (!c->active[s]) continue;
+        for (int h = 0; h < c->H; ++h) {
+            const size_t k = (size_t)s * c->H + h;
+            if (c->len[k] >= c->cap[k])
+                return fail(c, NUP_E_CAPACITY, "slot %d head %d is at its budget (%d tokens)", s, h, c->cap[k]);
+        }
+    }
+    nup::AppendArgs a{};
+    a.k_pool = c->kpool;
+    a.v_pool = c->vpool;
+    a.k_new = static_cast<const uint16_t *>(k_new);
+    a.v_new = static_cast<const uint16_t *>(v_new);
+    a.page_table = c->d_pt();
+    a.active = c->d_active();
+    a.group_of_head = c->d_goh();
+    a.slot_of_head = c->d_soh();
+    a.lengths = c->d_len();
+    a.bmax = c->B;
+    a.hkv = c->H;
+    a.gh = c->gh;
+    a.max_pages = c->max_pages;
+    hipError_t e = nup::launch_append(a, c->D, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "append launch");
+    for (int s = 0; s < c->B; ++s)
+        if (c->active[s])
+            for (int h = 0; h < c->H; ++h) c->len[(size_t)s * c->H + h]++;
+    return NUP_OK;
+}
+
+nup_status kv_gather_compact(nup_ctx *c, int32_t mode, const int32_t *idx, int32_t K, void *k_out,
+                             void *v_out, const int64_t *row_off, int32_t *phys_out, void *stream) {
+    if (!c) return NUP_E_ARG;
+    if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
+    if (!c->committed) return fail(c, NUP_E_STATE, "no committed descriptor");
+    if (!k_out || !v_out) return fail(c, NUP_E_ARG, "k_out and v_out are required");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (mode == 1) {
+        if (!idx || K <= 0) return fail(c, NUP_E_ARG, "index mode needs idx and K > 0");
+        nup::GatherIndexArgs a{};
+        a.k_pool = c->kpool;
+        a.v_pool = c->vpool;
+        a.page_table = c->d_pt();
+        a.active = c->d_active();
+        a.lengths = c->d_len();
+        a.group_of_head = c->d_goh();
+        a.slot_of_head = c->d_soh();
+        a.idx = idx;
+        a.k_out = static_cast<uint16_t *>(k_out);
+        a.v_out = static_cast<uint16_t *>(v_out);
+        a.phys_out = phys_out;
+        a.err = c->d_err();
+        a.bmax = c->B;
+        a.hkv = c->H;
+        a.gh = c->gh;
+        a.max_pages = c->max_pages;
+        a.k = K;
+        e = nup::launch_gather_index(a, c->D, st);
+    } else if (mode == 0) {
+        if (!row_off) return fail(c, NUP_E_ARG, "train mode needs row_off");
+        nup::GatherRunsArgs a{};
+        a.k_pool = c->kpool;
+        a.v_pool = c->vpool;
+        a.runs = c->inbox_i32(c->off_runs);
+        a.run_prefix = c->inbox_i32(c->off_runpre);
+        a.active = c->d_active();
+        a.lengths = c->d_len();
+        a.head_of_gslot = c->d_hog();
+        a.row_off = row_off;
+        a.k_out = static_cast<uint16_t *>(k_out);
+        a.v_out = static_cast<uint16_t *>(v_out);
+        a.phys_out = phys_out;
+        a.n_runs = c->dev_runs;
+        a.ng = c->ng;
+        a.gh = c->gh;
+        a.hkv = c->H;
+        e = nup::launch_gather_runs(a, c->D, c->dev_run_pages, st);
+    } else {
+        return fail(c, NUP_E_ARG, "mode must be 0 (trains) or 1 (indices)");
+    }
+    if (e != hipSuccess) return hip_fail(c, e, "gather launch");
+    return NUP_OK;
+}
+
+static void topk_split(const nup_ctx *c, int K, int *splits, int *chunk) {
+    const int heads = c->B * c->H;
+    const int pages = (K + nup::kPage - 1) / nup::kPage;
+    int S = std::max(1, (c->workers + heads - 1) / heads);
+    S = std::min(S, pages);
+    int ch = nup::kPage * ((pages + S - 1) / S);
+    S = (K + ch - 1) / ch;
+    *splits = S;
+    *chunk = ch;
+}
+
+nup_status nup_workspace_bytes(const nup_ctx *c, int32_t K, size_t *bytes) {
+    if (!c || !bytes || K < 0) return NUP_E_ARG;
+    long long rows;
+    if (K > 0) {
+        int S, ch;
+        topk_split(c, K, &S, &ch);
+        rows = (long long)c->B * c->H * S;
+    } else {
+        rows = c->sz.max_rows;
+    }
+    *bytes = align_up((size_t)rows * c->gqa * c->D * 4) + align_up((size_t)rows * c->gqa * 2 * 4);
+    return NUP_OK;
+}
+
+static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse, float scale, void *ws,
+                              size_t ws_bytes, void *stream, bool topk, const void *ks, const void *vs, int K) {
+    if (!c) return NUP_E_ARG;
+    if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
+    if (!c->committed) return fail(c, NUP_E_STATE, "no committed descriptor");
+    if (!q || !out || !ws) return fail(c, NUP_E_ARG, "q, out and workspace are required");
+    if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(c, NUP_E_ARG, "scale must be positive and finite");
+    size_t need = 0;
+    nup_workspace_bytes(c, topk ? K : 0, &need);
+    if (ws_bytes < need) return fail(c, NUP_E_ARG, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    nup::PartialArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.active = c->d_active();
+    a.lengths = c->d_len();
+    a.group_of_head = c->d_goh();
+    a.slot_of_head = c->d_soh();
+    a.bmax = c->B;
+    a.hkv = c->H;
+    a.gh = c->gh;
+    a.max_pages = c->max_pages;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    int rows_max;
+    int splits = 0;
+    if (topk) {
+        int ch;
+        topk_split(c, K, &splits, &ch);
+        a.kbase = static_cast<const uint16_t *>(ks);
+        a.vbase = static_cast<const uint16_t *>(vs);
+        a.topk_k = K;
+        a.topk_splits = splits;
+        a.topk_chunk = ch;
+        a.n_workers = c->B * c->H * splits;
+        rows_max = a.n_workers;
+    } else {
+        a.kbase = c->kpool;
+        a.vbase = c->vpool;
+        a.page_table = c->d_pt();
+        a.rows = c->inbox_i32(c->off_rows);
+        a.worker_start = c->inbox_i32(c->off_ws);
+        a.n_workers = c->dev_workers;
+        rows_max = c->sz.max_rows;
+    }
+    float *wso = static_cast<float *>(ws);
+    float *wsml = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                            align_up((size_t)rows_max * c->gqa * c->D * 4));
+    a.ws_o = wso;
+    a.ws_ml = wsml;
+    hipError_t e;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (c->timing) {
+        if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess)
+            return hip_fail(c, e, "hipEventCreate");
+        if ((e = hipEventRecord(e0, st)) != hipSuccess) return hip_fail(c, e, "hipEventRecord");
+    }
+    e = nup::launch_partial(a, c->D, c->gqa, topk, st);
+    if (e != hipSuccess) return hip_fail(c, e, "partial attention launch");
+    if (c->timing) {
+        if ((e = hipEventRecord(e1, st)) != hipSuccess) return hip_fail(c, e, "hipEventRecord");
+        c->tev.emplace_back(e0, e1);
+    }
+    nup::MergeArgs m{};
+    m.ws_o = wso;
+    m.ws_ml = wsml;
+    m.head_row_start = topk ? nullptr : c->inbox_i32(c->off_hrs);
+    m.uniform_splits = splits;
+    m.out = out;
+    m.lse = lse;
+    m.hkv = c->H;
+    e = nup::launch_merge(m, c->D, c->gqa, c->B * c->H, st);
+    if (e != hipSuccess) return hip_fail(c, e, "merge launch");
+    return NUP_OK;
+}
+
+nup_status attn_decode_nonuniform(nup_ctx *c, const void *q, float *out, float *lse, float scale,
+                                  void *workspace, size_t ws_bytes, void *stream) {
+    return attn_common(c, q, out, lse, scale, workspace, ws_bytes, stream, false, nullptr, nullptr, 0);
+}
+
+nup_status attn_decode_topk(nup_ctx *c, const void *q, const void *k_stage, const void *v_stage, int32_t K,
+                            float *out, float *lse, float scale, void *workspace, size_t ws_bytes,
+                            void *stream) {
+    if (!c) return NUP_E_ARG;
+    if (K <= 0 || !k_stage || !v_stage) return fail(c, NUP_E_ARG, "top-K needs K > 0 and staging buffers");
+    return attn_common(c, q, out, lse, scale, workspace, ws_bytes, stream, true, k_stage, v_stage, K);
+}
+
+nup_status nup_get_page_table(const nup_ctx *c, int32_t *out) {
+    if (!c || !out) return NUP_E_ARG;
+    std::copy(c->pt.begin(), c->pt.end(), out);
+    return NUP_OK;
+}
+
+nup_status nup_get_lengths(const nup_ctx *c, int32_t *out) {
+    if (!c || !out) return NUP_E_ARG;
+    for (size_t k = 0; k < c->len.size(); ++k) out[k] = c->active[k / c->H] ? c->len[k] : 0;
+    return NUP_OK;
+}
+
+nup_status nup_get_groups(const nup_ctx *c, int32_t *goh, int32_t *soh) {
+    if (!c) return NUP_E_ARG;
+    if (goh) std::copy(c->goh.begin(), c->goh.end(), goh);
+    if (soh) std::copy(c->soh.begin(), c->soh.end(), soh);
+    return NUP_OK;
+}
+
+nup_status nup_get_free_list(const nup_ctx *c, int32_t *out, int32_t *n) {
+    if (!c || !n) return NUP_E_ARG;
+    *n = (int32_t)c->free_list.size();
+    if (out) std::copy(c->free_list.begin(), c->free_list.end(), out);
+    return NUP_OK;
+}
+
+nup_status nup_get_runs(const nup_ctx *c, int32_t *out, int32_t max_runs, int32_t *n) {
+    if (!c || !n) return NUP_E_ARG;
+    std::vector<int32_t> runs;
+    build_runs(c, runs);
+    *n = (int32_t)(runs.size() / 5);
+    if (!out) return NUP_OK;
+    if (*n > max_runs) return NUP_E_ARG;
+    std::copy(runs.begin(), runs.end(), out);
+    return NUP_OK;
+}
+
+nup_status nup_get_plan(const nup_ctx *c, int32_t *n_rows, int32_t *n_workers, int32_t *rows,
+                        int32_t *worker_start, int32_t *head_row_start) {
+    if (!c) return NUP_E_ARG;
+    if (n_rows) *n_rows = (int32_t)(c->rows.size() / 4);
+    if (n_workers) *n_workers = (int32_t)c->worker_start.size() - 1;
+    if (rows) std::copy(c->rows.begin(), c->rows.end(), rows);
+    if (worker_start) std::copy(c->worker_start.begin(), c->worker_start.end(), worker_start);
+    if (head_row_start) std::copy(c->head_row_start.begin(), c->head_row_start.end(), head_row_start);
+    return NUP_OK;
+}
+
+nup_status nup_set_timing(nup_ctx *c, int32_t enable) {
+    if (!c) return NUP_E_ARG;
+    c->timing = enable != 0;
+    return NUP_OK;
+}
+
+nup_status nup_kernel_time(nup_ctx *c, double *partial_ms, int32_t *launches, int32_t reset) {
+    if (!c) return NUP_E_ARG;
+    for (auto &ev : c->tev) {
+        hipError_t e = hipEventSynchronize(ev.second);
+        if (e != hipSuccess) return hip_fail(c, e, "hipEventSynchronize");
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, ev.first, ev.second);
+        if (e != hipSuccess) return hip_fail(c, e, "hipEventElapsedTime");
+        c->acc_ms += ms;
+        c->launches++;
+        (void)hipEventDestroy(ev.first);
+        (void)hipEventDestroy(ev.second);
+    }
+    c->tev.clear();
+    if (partial_ms) *partial_ms = c->acc_ms;
+    if (launches) *launches = c->launches;
+    if (reset) {
+        c->acc_ms = 0.0;
+        c->launches = 0;
+    }
+    return NUP_OK;
+}
+
+nup_status nup_device_errors(nup_ctx *c, void *stream, int32_t *code) {
+    if (!c || !code) return NUP_E_ARG;
+    if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t h = 0;
+    hipError_t e = hipMemcpyAsync(&h, c->d_err(), 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(c, e, "read device error word");
+    const int32_t zero = 0;
+    e = hipMemcpyAsync(c->d_err(), &zero, 4, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(c, e, "clear device error word");
+    *code = h ? NUP_E_INDEX : NUP_OK;
+    return NUP_OK;
+}
+
+nup_status nup_probe_copy(const void *src, void *dst, size_t bytes, void *stream) {
+    if (!src || !dst || bytes % 16) return NUP_E_ARG;
+    hipError_t e = nup::launch_probe_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NUP_OK : NUP_E_HIP;
+}
+
+}  // extern "C"

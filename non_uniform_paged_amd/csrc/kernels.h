@@ -1,0 +1,85 @@
+// Internal interface between the host control plane (host.cpp) and the
+// gfx950 kernels (kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nup {
+
+constexpr int kPage = 16;           // tokens per page
+constexpr int kWavesPerBlock = 4;   // split-K workers per 256-thread workgroup
+
+// Split-K partial attention.  One wave is one worker.  In table mode a
+// worker walks rows[worker_start[w] .. worker_start[w+1]) of (head, t0, t1);
+// in top-K mode worker w takes chunk w % splits of head w / splits of a
+// contiguous staging buffer holding topk_k rows per head.
+struct PartialArgs {
+    const uint16_t *q;          // bf16 [Bmax][Hq][D]
+    const uint16_t *kbase;      // K pool [pages][Gh][16][D] or staging [Bmax*Hkv][K][D]
+    const uint16_t *vbase;
+    const int32_t *page_table;  // [ng][Bmax][max_pages] (paged)
+    const int32_t *active;      // [Bmax]
+    const int32_t *lengths;     // [Bmax*Hkv] (paged)
+    const int32_t *group_of_head;
+    const int32_t *slot_of_head;
+    const int32_t *rows;        // [n][4] (sh, t0, t1, 0) (paged)
+    const int32_t *worker_start;// [W+1] (paged)
+    float *ws_o;                // [rows][gqa][D]
+    float *ws_ml;               // [rows][gqa][2]  (max in log2 units, sum)
+    int32_t bmax, hkv, gh, max_pages, n_workers;
+    int32_t topk_k, topk_splits, topk_chunk;
+    float scale_log2;           // softmax scale * log2(e)
+};
+
+struct MergeArgs {
+    const float *ws_o;
+    const float *ws_ml;
+    const int32_t *head_row_start; // [Bmax*Hkv+1] (table mode) or NULL
+    int32_t uniform_splits;        // rows of head sh are sh*splits.. (when table NULL)
+    float *out;                    // fp32 [Bmax][Hq][D]
+    float *lse;                    // fp32 [Bmax][Hq] or NULL
+    int32_t hkv;
+};
+
+struct AppendArgs {
+    uint16_t *k_pool, *v_pool;
+    const uint16_t *k_new, *v_new; // [Bmax][Hkv][D]
+    const int32_t *page_table, *active, *group_of_head, *slot_of_head;
+    int32_t *lengths;
+    int32_t bmax, hkv, gh, max_pages;
+};
+
+struct GatherIndexArgs {
+    const uint16_t *k_pool, *v_pool;
+    const int32_t *page_table, *active, *lengths, *group_of_head, *slot_of_head;
+    const int32_t *idx;            // [Bmax*Hkv][K]
+    uint16_t *k_out, *v_out;       // [Bmax*Hkv][K][D]
+    int32_t *phys_out;             // [Bmax*Hkv][K] or NULL
+    int32_t *err;                  // latched error word
+    int32_t bmax, hkv, gh, max_pages, k;
+};
+
+struct GatherRunsArgs {
+    const uint16_t *k_pool, *v_pool;
+    const int32_t *runs;           // [n_runs][4] (slot*ng+g, phys, pages, logical)
+    const int32_t *run_prefix;     // [n_runs+1] page prefix sums
+    const int32_t *active, *lengths, *head_of_gslot;
+    const int64_t *row_off;        // [Bmax*Hkv]
+    uint16_t *k_out, *v_out;       // packed rows of D
+    int32_t *phys_out;             // packed like the rows, or NULL
+    int32_t n_runs, ng, gh, hkv;
+};
+
+bool supported_shape(int head_dim, int gqa);
+int partial_blocks_per_cu(int head_dim, int gqa, bool topk);
+
+hipError_t launch_partial(const PartialArgs &a, int head_dim, int gqa, bool topk, hipStream_t st);
+hipError_t launch_merge(const MergeArgs &a, int head_dim, int gqa, int n_heads, hipStream_t st);
+hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t st);
+hipError_t launch_gather_index(const GatherIndexArgs &a, int head_dim, hipStream_t st);
+hipError_t launch_gather_runs(const GatherRunsArgs &a, int head_dim, int total_pages, hipStream_t st);
+hipError_t launch_apply_patches(int32_t *page_table, const int32_t *hdr, const int32_t *data,
+                                int n_patches, int max_pages, hipStream_t st);
+hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t st);
+
+}  // namespace nup

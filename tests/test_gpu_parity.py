@@ -1,0 +1,430 @@
+"""GPU parity: every kernel of the path against the oracle, through the C ABI.
+
+Attention: max-abs <= 1e-2 and rel-L2 <= 5e-3 against the fp64 oracle (and
+rel-L2 <= 1e-4 as a bug detector).  Page tables, appended rows, gathered
+rows and their physical row ids: bit-exact.
+"""
+import gc
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import non_uniform_paged_amd as nup
+import oracle
+import workloads as W
+from oracle import pager as pg
+from tests.gpu_common import (DEV, Case, assert_attention_close, sub_oracle, u16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _cleanup():
+    yield
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _ragged(seed, B, H, maxL, p_zero=0.1, p_one=0.1):
+    rs = np.random.default_rng(seed)
+    L = rs.integers(2, maxL + 1, size=(B, H))
+    L[rs.random((B, H)) < p_zero] = 0
+    L[rs.random((B, H)) < p_one] = 1
+    caps = L + rs.integers(0, 40, size=(B, H))
+    return L.astype(np.int32), caps.astype(np.int32)
+
+
+def test_tiny_config():
+    w = W.tiny()
+    c = Case(H=4, Hq=4, D=64, ng=2, B=2, num_pages=64, max_pages=16,
+             free_list_init=w.free_list_init)
+    c.alloc([0, 1], w.caps, w.lengths)
+    c.commit()
+    out, lse = c.attend()
+    ref, ref_lse = c.oracle()
+    assert_attention_close(out, lse, ref, ref_lse, "tiny")
+
+
+@pytest.mark.parametrize("D,gqa,H,ng,workers,seed", [
+    (64, 1, 4, 2, 5, 1), (64, 2, 4, 1, 64, 2), (128, 4, 8, 4, 13, 3), (128, 5, 8, 4, 31, 4),
+    (128, 8, 4, 2, 9, 5), (128, 5, 8, 2, 2048, 6), (128, 4, 8, 1, 1, 7), (64, 5, 8, 8, 17, 8)])
+def test_ragged_shapes(D, gqa, H, ng, workers, seed):
+    B = 5
+    L, caps = _ragged(seed, B, H, 300)
+    max_pages = int(math.ceil(caps.max() / 16)) + 1
+    rs = np.random.default_rng(seed + 100)
+    num_pages = B * ng * max_pages + 7
+    c = Case(H=H, Hq=H * gqa, D=D, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages,
+             free_list_init=rs.permutation(num_pages), num_workers=workers, salt=seed)
+    c.alloc([4, 0, 2, 3], caps[:4], L[:4])      # slot 1 stays inactive
+    c.commit()
+    out, lse = c.attend()
+    ref, ref_lse = c.oracle()
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+    assert_attention_close(out, lse, ref, ref_lse, f"D{D} gqa{gqa} ng{ng} W{workers}")
+
+
+def test_long_skewed_head():
+    """One head at the 131072-token clip among short ones: split over many
+    workers, merged exactly."""
+    H, gqa, D, B = 8, 4, 128, 2
+    L = np.full((B, H), 48, np.int32)
+    L[1, 3] = 131072
+    L[0, 0] = 5
+    caps = L.copy()
+    max_pages = 131072 // 16
+    num_pages = 2 * 2 * max_pages
+    c = Case(H=H, Hq=H * gqa, D=D, ng=2, B=B, num_pages=num_pages, max_pages=max_pages,
+             num_workers=512, salt=9)
+    c.alloc([0, 1], caps, L)
+    c.commit()
+    out, lse = c.attend()
+    ref, ref_lse = c.oracle()
+    assert_attention_close(out, lse, ref, ref_lse, "long head")
+
+
+def test_length_one_returns_v_bit_exact():
+    H, gqa, D, B = 8, 5, 128, 3
+    L = np.ones((B, H), np.int32)
+    c = Case(H=H, Hq=H * gqa, D=D, ng=4, B=B, num_pages=64, max_pages=2, num_workers=11, salt=10)
+    c.alloc([0, 1, 2], L + 16, L)
+    c.commit()
+    out, _ = c.attend()
+    vp = u16(c.vpool)
+    for s in range(B):
+        for r in range(H * gqa):
+            h = r // gqa
+            page = c.spec.page_table[c.spec.group_of_head[h], s, 0]
+            v0 = W.bf16_bits_to_f64(vp[page, c.spec.slot_of_head[h], 0])
+            assert np.array_equal(out[s, r], v0)
+
+
+def test_page_permutation_bit_identical():
+    H, gqa, D, B = 8, 4, 128, 4
+    L, caps = _ragged(11, B, H, 500, p_zero=0, p_one=0)
+    max_pages = int(math.ceil(caps.max() / 16))
+    num_pages = B * 2 * max_pages + 3
+    a = Case(H=H, Hq=H * gqa, D=D, ng=2, B=B, num_pages=num_pages, max_pages=max_pages,
+             num_workers=37, salt=11)
+    b = Case(H=H, Hq=H * gqa, D=D, ng=2, B=B, num_pages=num_pages, max_pages=max_pages,
+             num_workers=37, salt=11,
+             free_list_init=np.random.default_rng(5).permutation(num_pages))
+    for x in (a, b):
+        x.alloc(list(range(B)), caps, L)
+        x.commit()
+    pa = torch.from_numpy(a.spec.page_table[a.spec.page_table >= 0].astype(np.int64)).to(DEV)
+    pb = torch.from_numpy(b.spec.page_table[b.spec.page_table >= 0].astype(np.int64)).to(DEV)
+    b.kpool[pb] = a.kpool[pa]
+    b.vpool[pb] = a.vpool[pa]
+    oa, la = a.attend()
+    ob, lb = b.attend()
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_split_invariance():
+    H, gqa, D, B = 8, 5, 128, 3
+    L, caps = _ragged(12, B, H, 900, p_zero=0)
+    max_pages = int(math.ceil(caps.max() / 16))
+    outs = []
+    for workers in (1, 3, 64, 2048):
+        c = Case(H=H, Hq=H * gqa, D=D, ng=4, B=B, num_pages=B * 4 * max_pages,
+                 max_pages=max_pages, num_workers=workers, salt=12)
+        c.alloc(list(range(B)), caps, L)
+        c.commit()
+        out, lse = c.attend()
+        ref, ref_lse = c.oracle()
+        assert_attention_close(out, lse, ref, ref_lse, f"W={workers}")
+        outs.append(out)
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 1e-5
+
+
+def test_uniform_plan_mode():
+    H, gqa, D, B = 8, 4, 128, 4
+    L, caps = _ragged(13, B, H, 700)
+    max_pages = int(math.ceil(caps.max() / 16))
+    c = Case(H=H, Hq=H * gqa, D=D, ng=4, B=B, num_pages=B * 4 * max_pages, max_pages=max_pages,
+             plan_mode=nup.PLAN_UNIFORM, uniform_splits=3, salt=13)
+    c.alloc(list(range(B)), caps, L)
+    c.commit()
+    out, lse = c.attend()
+    ref, ref_lse = c.oracle()
+    assert_attention_close(out, lse, ref, ref_lse, "uniform plan")
+
+
+def test_append_then_decode():
+    """Decode steps: append one token per active head, commit, attend.  The
+    pool after the appends equals the oracle's placement bit-exactly."""
+    H, gqa, D, B = 8, 4, 128, 3
+    L, _ = _ragged(14, B, H, 60, p_zero=0.2, p_one=0.2)
+    caps = L + 12
+    max_pages = int(math.ceil(caps.max() / 16))
+    num_pages = B * 2 * max_pages + 5
+    c = Case(H=H, Hq=H * gqa, D=D, ng=2, B=B, num_pages=num_pages, max_pages=max_pages,
+             free_list_init=np.random.default_rng(3).permutation(num_pages), num_workers=19,
+             salt=14)
+    c.alloc([0, 2], caps[[0, 2]], L[[0, 2]])   # slot 1 inactive
+    c.commit()
+    kp = u16(c.kpool).copy()
+    vp = u16(c.vpool).copy()
+    flat_k = kp.reshape(-1, D)
+    flat_v = vp.reshape(-1, D)
+    for step in range(10):
+        kn = W.normal_bf16("k", (B, H, D), 1000 + step)
+        vn = W.normal_bf16("v", (B, H, D), 1000 + step)
+        nup.kv_append(c.ctx, torch.from_numpy(kn.view(np.int16)).to(DEV),
+                      torch.from_numpy(vn.view(np.int16)).to(DEV))
+        st, pos = c.spec.append_positions()
+        assert st == pg.OK
+        for s in range(B):
+            if not c.spec.active[s]:
+                continue
+            for h in range(H):
+                row = c.spec.physical_row(s, h, int(pos[s, h]))
+                flat_k[row] = kn[s, h]
+                flat_v[row] = vn[s, h]
+        c.commit()
+        assert np.array_equal(nup.get_lengths(c.ctx), c.spec.lengths)
+    out, lse = c.attend()
+    assert np.array_equal(u16(c.kpool), kp) and np.array_equal(u16(c.vpool), vp)
+    ref, ref_lse = oracle.decode(u16(c.q), kp, vp, c.spec.page_table, c.spec.lengths,
+                                 c.spec.group_of_head, c.spec.slot_of_head, c.scale)
+    assert_attention_close(out, lse, ref, ref_lse, "after appends")
+
+
+def test_append_errors():
+    H, D, B = 4, 64, 2
+    c = Case(H=H, Hq=H, D=D, ng=1, B=B, num_pages=8, max_pages=2, salt=15)
+    c.alloc([0], np.array([[20, 20, 20, 20]]), np.array([[3, 20, 0, 1]]))
+    kn = torch.zeros((B, H, D), dtype=torch.bfloat16, device=DEV)
+    # edits pending: commit first
+    assert nup.kv_append(c.ctx, kn, kn, raise_on_error=False) == nup.NUP_E_STATE
+    c.commit()
+    # head 1 is at its budget: nothing is written, nothing advances
+    assert nup.kv_append(c.ctx, kn, kn, raise_on_error=False) == nup.NUP_E_CAPACITY
+    assert nup.get_lengths(c.ctx)[0].tolist() == [3, 20, 0, 1]
+    out, lse = c.attend()
+    ref, ref_lse = c.oracle()
+    assert_attention_close(out, lse, ref, ref_lse, "after refused append")
+
+
+def test_shadow_edits_invisible_until_commit():
+    H, gqa, D, B = 8, 4, 128, 4
+    L, caps = _ragged(16, B, H, 200, p_zero=0)
+    max_pages = int(math.ceil(caps.max() / 16))
+    c = Case(H=H, Hq=H * gqa, D=D, ng=2, B=B, num_pages=B * 2 * max_pages, max_pages=max_pages,
+             num_workers=23, salt=16)
+    c.alloc([0, 1, 2], caps[:3], L[:3])
+    c.commit()
+    ref, ref_lse = c.oracle()
+    # edit the shadow without committing: the kernels keep the committed frame
+    c.free([1])
+    c.alloc([3], caps[3:], L[3:])
+    out, lse = c.attend()
+    assert_attention_close(out, lse, ref, ref_lse, "pre-commit view")
+    c.commit()
+    out, lse = c.attend()
+    ref2, ref_lse2 = c.oracle()
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+    assert_attention_close(out, lse, ref2, ref_lse2, "post-commit view")
+
+
+def _gather_case(seed, B=3, H=8, gqa=4, D=128, ng=1, maxL=700):
+    rs = np.random.default_rng(seed)
+    L = rs.integers(300, maxL, size=(B, H)).astype(np.int32)
+    caps = L + 16
+    max_pages = int(math.ceil(caps.max() / 16))
+    num_pages = B * ng * max_pages + 9
+    c = Case(H=H, Hq=H * gqa, D=D, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages,
+             free_list_init=rs.permutation(num_pages), num_workers=29, salt=seed)
+    return c, L, caps
+
+
+def test_gather_index_and_topk_attention():
+    c, L, caps = _gather_case(17)
+    B, H, D, K = c.B, c.H, c.D, 96
+    c.alloc([0, 2], caps[[0, 2]], L[[0, 2]])   # slot 1 inactive
+    c.commit()
+    lens = np.where(c.spec.active[:, None], c.spec.lengths, 300)
+    idx = W.topk_indices(lens, K, salt=17)
+    d_idx = torch.from_numpy(idx).to(DEV)
+    ks = torch.full((B, H, K, D), 7, dtype=torch.int16, device=DEV)
+    vs = torch.full_like(ks, 7)
+    phys = torch.full((B, H, K), -7, dtype=torch.int32, device=DEV)
+    nup.kv_gather_compact(c.ctx, 1, ks, vs, idx=d_idx, K=K, phys_out=phys)
+    torch.cuda.synchronize()
+    assert nup.device_errors(c.ctx) == nup.NUP_OK
+    sk, sv, sphys = pg.gather_index(c.spec, u16(c.kpool), u16(c.vpool), idx)
+    gk = ks.cpu().numpy().view(np.uint16)
+    gv = vs.cpu().numpy().view(np.uint16)
+    gp = phys.cpu().numpy()
+    for s in (0, 2):
+        assert np.array_equal(gk[s], sk[s]) and np.array_equal(gv[s], sv[s])
+        assert np.array_equal(gp[s], sphys[s])
+    assert (gk[1] == 7).all() and (gp[1] == -7).all()     # inactive rows untouched
+    ws = torch.empty(nup.workspace_bytes(c.ctx, K), dtype=torch.uint8, device=DEV)
+    nup.attn_decode_topk(c.ctx, c.q, ks.view(torch.bfloat16), vs.view(torch.bfloat16), K,
+                         c.out, c.lse, c.scale, ws)
+    torch.cuda.synchronize()
+    out = c.out.cpu().numpy().astype(np.float64)
+    lse = c.lse.cpu().numpy().astype(np.float64)
+    ref, ref_lse = c.oracle(tokens=idx)
+    assert_attention_close(out, lse, ref, ref_lse, "top-K")
+
+
+@pytest.mark.parametrize("K", [1, 16, 37])
+def test_topk_ragged_k(K):
+    c, L, caps = _gather_case(18 + K, B=2, gqa=5, ng=2)
+    c.alloc([0, 1], caps, L)
+    c.commit()
+    idx = W.topk_indices(c.spec.lengths, max(K, 2), salt=18)[..., :K].copy()
+    idx.sort(axis=-1)
+    ks = torch.zeros((c.B, c.H, K, c.D), dtype=torch.int16, device=DEV)
+    vs = torch.zeros_like(ks)
+    nup.kv_gather_compact(c.ctx, 1, ks, vs, idx=torch.from_numpy(idx).to(DEV), K=K)
+    ws = torch.empty(nup.workspace_bytes(c.ctx, K), dtype=torch.uint8, device=DEV)
+    nup.attn_decode_topk(c.ctx, c.q, ks.view(torch.bfloat16), vs.view(torch.bfloat16), K,
+                         c.out, c.lse, c.scale, ws)
+    torch.cuda.synchronize()
+    assert nup.device_errors(c.ctx) == nup.NUP_OK
+    ref, ref_lse = c.oracle(tokens=idx)
+    assert_attention_close(c.out.cpu().numpy().astype(np.float64),
+                           c.lse.cpu().numpy().astype(np.float64), ref, ref_lse, f"K={K}")
+
+
+def test_gather_index_rejects_bad_indices():
+    c, L, caps = _gather_case(19, B=2, H=4, gqa=1, D=64)
+    c.alloc([0, 1], caps, L)
+    c.commit()
+    K = 8
+    idx = np.tile(np.arange(K, dtype=np.int32) * 3, (2, 4, 1))
+    idx[0, 1, 5] = idx[0, 1, 4]          # repeated
+    idx[1, 2, 7] = L[1, 2]               # past the retained length
+    idx[1, 3, 0] = -1                    # negative
+    ks = torch.full((2, 4, K, 64), 9, dtype=torch.int16, device=DEV)
+    vs = torch.full_like(ks, 9)
+    nup.kv_gather_compact(c.ctx, 1, ks, vs, idx=torch.from_numpy(idx).to(DEV), K=K)
+    assert nup.device_errors(c.ctx) == nup.NUP_E_INDEX
+    assert nup.device_errors(c.ctx) == nup.NUP_OK        # latched word was cleared
+    gk = ks.cpu().numpy().view(np.uint16)
+    for (s, h, k) in ((0, 1, 5), (1, 2, 7), (1, 3, 0)):
+        assert (gk[s, h, k] == 0).all()
+    good = idx.copy()
+    good[0, 1, 5] = good[0, 1, 4] + 1
+    good[1, 2, 7] = 0
+    good[1, 3, 0] = 0
+    sk, _, _ = pg.gather_index(c.spec, u16(c.kpool), u16(c.vpool), np.clip(good, 0, None))
+    assert np.array_equal(gk[0, 0], sk[0, 0]) and np.array_equal(gk[1, 1], sk[1, 1])
+
+
+def test_gather_trains_bit_exact():
+    c, L, caps = _gather_case(20, B=4, H=8, ng=2)
+    c.alloc([0, 1, 3], caps[[0, 1, 3]], L[[0, 1, 3]])
+    c.free([1])
+    c.alloc([2], caps[[2]], L[[2]])      # reuses freed pages: trains break up
+    c.commit()
+    lens = c.spec.lengths.astype(np.int64)
+    row_off = np.concatenate([[0], np.cumsum(lens.reshape(-1))[:-1]]).astype(np.int64)
+    total = int(lens.sum())
+    ks = torch.zeros((total, c.D), dtype=torch.int16, device=DEV)
+    vs = torch.zeros_like(ks)
+    phys = torch.full((total,), -1, dtype=torch.int32, device=DEV)
+    nup.kv_gather_compact(c.ctx, 0, ks, vs, row_off=torch.from_numpy(row_off).to(DEV),
+                          phys_out=phys)
+    torch.cuda.synchronize()
+    want = pg.gather_pages(c.spec, u16(c.kpool), u16(c.vpool), row_off)
+    gk = ks.cpu().numpy().view(np.uint16)
+    gv = vs.cpu().numpy().view(np.uint16)
+    gp = phys.cpu().numpy()
+    H = c.H
+    for (s, h), (kr, vr, rows) in want.items():
+        o = row_off[s * H + h]
+        n = len(kr)
+        assert np.array_equal(gk[o:o + n], kr) and np.array_equal(gv[o:o + n], vr)
+        assert np.array_equal(gp[o:o + n], rows)
+    runs = nup.get_runs(c.ctx)
+    assert [tuple(r) for r in runs.tolist()] == pg.coalesce(c.spec.page_table, c.spec.n_pages,
+                                                             c.spec.active)
+
+
+# ---- full-size configurations, checked on sampled sequences -----------------
+
+def _full_case(w, num_workers=0, max_pages=None):
+    max_pages = max_pages or int(math.ceil(w.caps.max() / 16))
+    return Case(H=w.num_kv_heads, Hq=w.num_q_heads, D=w.head_dim, ng=w.num_groups, B=w.batch,
+                num_pages=w.num_pages, max_pages=max_pages, free_list_init=w.free_list_init,
+                num_workers=num_workers)
+
+
+@pytest.mark.parametrize("name", ["qwen3_4b", "qwen25_32b", "qwen25_32b_uniform50"])
+def test_full_size_sampled(name):
+    if name == "qwen25_32b_uniform50":
+        w = W.qwen25_32b(control="uniform50")
+    else:
+        w = W.CONFIGS[name]()
+    c = _full_case(w)
+    c.alloc(list(range(w.batch)), w.caps, w.lengths)
+    c.commit()
+    out, lse = c.attend()
+    seqs = [0, 1, w.batch // 2, w.batch - 1]
+    ref, ref_lse = sub_oracle(c.spec, c.q, c.kpool, c.vpool, seqs, c.scale)
+    assert_attention_close(out[seqs], lse[seqs], ref, ref_lse, name)
+    assert np.isfinite(out).all()
+
+
+def test_full_size_llama_topk():
+    w = W.llama3_8b_topk()
+    c = _full_case(w)
+    c.alloc(list(range(w.batch)), w.caps, w.lengths)
+    c.commit()
+    K = w.topk
+    idx = W.topk_indices(w.lengths, K)
+    ks = torch.empty((w.batch, 8, K, 128), dtype=torch.bfloat16, device=DEV)
+    vs = torch.empty_like(ks)
+    phys = torch.empty((w.batch, 8, K), dtype=torch.int32, device=DEV)
+    nup.kv_gather_compact(c.ctx, 1, ks, vs, idx=torch.from_numpy(idx).to(DEV), K=K, phys_out=phys)
+    ws = torch.empty(nup.workspace_bytes(c.ctx, K), dtype=torch.uint8, device=DEV)
+    nup.attn_decode_topk(c.ctx, c.q, ks, vs, K, c.out, c.lse, c.scale, ws)
+    torch.cuda.synchronize()
+    assert nup.device_errors(c.ctx) == nup.NUP_OK
+    seqs = [0, 5]
+    gp = phys.cpu().numpy()
+    flat_k = c.kpool.view(-1, 128)
+    for s in seqs:
+        for h in range(8):
+            want = np.array([c.spec.physical_row(s, h, int(t)) for t in idx[s, h]], np.int64)
+            assert np.array_equal(gp[s, h], want)
+            rows = flat_k.index_select(0, torch.from_numpy(want).to(DEV))
+            assert torch.equal(rows.view(torch.int16), ks[s, h].view(torch.int16))
+    ref, ref_lse = sub_oracle(c.spec, c.q, c.kpool, c.vpool, seqs, c.scale, tokens=idx)
+    out = c.out.cpu().numpy().astype(np.float64)
+    lse = c.lse.cpu().numpy().astype(np.float64)
+    assert_attention_close(out[seqs], lse[seqs], ref, ref_lse, "llama top-K")
+
+
+def test_full_size_mixed_churn():
+    w = W.mixed_churn()
+    c = _full_case(w, max_pages=int(math.ceil((131072 + 16) / 16)))
+    drv = W.ChurnDriver(w.batch)
+    c.alloc(list(range(w.batch)), w.caps, w.lengths)
+    c.commit()
+    freed = np.zeros(0, np.int32)
+    for step in range(6):
+        if len(freed):
+            L = drv.refill_lengths(len(freed))
+            Ls = np.repeat(L[:, None], 8, axis=1)
+            assert c.alloc(freed, Ls + 16, Ls) == pg.OK
+        active = np.nonzero(c.spec.active)[0]
+        freed = drv.eos(active)
+        c.free(freed)
+        c.commit()
+    out, lse = c.attend()
+    act = np.nonzero(c.spec.active)[0]
+    seqs = [int(act[0]), int(act[len(act) // 2]), int(act[-1])]
+    ref, ref_lse = sub_oracle(c.spec, c.q, c.kpool, c.vpool, seqs, c.scale)
+    assert_attention_close(out[seqs], lse[seqs], ref, ref_lse, "mixed churn")
+    for s in freed:
+        assert np.all(out[s] == 0) and np.all(np.isneginf(lse[s]))
