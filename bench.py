@@ -196,6 +196,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-controls", action="store_true")
     ap.add_argument("--workers", type=int, default=0)
+    ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
+                    help="only run the plain streaming copy kernel over BYTES (counter "
+                         "calibration and achievable-bandwidth ceiling), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the path shards by sequence "
@@ -206,6 +209,26 @@ def main():
     import torch
     import non_uniform_paged_amd as nup  # noqa: F401  (fails loudly when not built)
     import workloads as W
+
+    if args.probe_copy:
+        n = args.probe_copy // 16 * 16
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(2):
+            nup.probe_copy(a, b, n)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            nup.probe_copy(a, b, n)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        print(json.dumps({"probe_copy_bytes": n, "ms": round(ms, 4),
+                          "read_plus_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
 
     src = open(os.path.join(ROOT, "non_uniform_paged_amd", "csrc", "kernels.hip"), "rb").read()
     sha = hashlib.sha256(src).hexdigest()
@@ -241,6 +264,23 @@ def main():
             sc.free()
             del sc
         extra["nonuniform_over_uniform50"] = round(achieved / extra["control_uniform50_kernel_GBs"], 4)
+
+    # achievable streaming-read ceiling on this device (4 GiB, beyond the caches)
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nup.probe_read(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        nup.probe_read(buf, nbytes, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    extra["read_ceiling_GBs"] = round(5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    extra["partial_over_read_ceiling"] = round(achieved / extra["read_ceiling_GBs"], 4)
+    del buf
 
     traffic = traffic_from_profiles(sha)
     line = {

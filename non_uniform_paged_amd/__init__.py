@@ -72,6 +72,7 @@ _sigs = {
     "nup_kernel_time": [_P, _P, _P, _I],
     "nup_device_errors": [_P, _P, _P],
     "nup_probe_copy": [_P, _P, _S, _P],
+    "nup_probe_read": [_P, _S, _P, _P],
 }
 for _name, _args in _sigs.items():
     _f = getattr(_lib, _name)
@@ -285,6 +286,12 @@ def device_errors(ctx: Context, stream=None) -> int:
     code = ctypes.c_int32()
     ctx.check(_lib.nup_device_errors(ctx.handle, _stream(stream), ctypes.byref(code)))
     return code.value
+
+
+def probe_read(src, nbytes: int, sink, stream=None):
+    st = _lib.nup_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(stream))
+    if st != NUP_OK:
+        raise NupError(st, "nup_probe_read failed")
 
 
 def probe_copy(src, dst, nbytes: int, stream=None):

@@ -906,4 +906,11 @@ nup_status nup_probe_copy(const void *src, void *dst, size_t bytes, void *stream
     return e == hipSuccess ? NUP_OK : NUP_E_HIP;
 }
 
+nup_status nup_probe_read(const void *src, size_t bytes, void *sink, void *stream) {
+    if (!src || !sink || bytes % 16) return NUP_E_ARG;
+    hipError_t e = nup::launch_probe_read(src, bytes, static_cast<uint32_t *>(sink),
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NUP_OK : NUP_E_HIP;
+}
+
 }  // extern "C"

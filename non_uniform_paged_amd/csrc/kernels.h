@@ -39,6 +39,7 @@ struct MergeArgs {
     float *out;                    // fp32 [Bmax][Hq][D]
     float *lse;                    // fp32 [Bmax][Hq] or NULL
     int32_t hkv;
+    int32_t n_pairs;               // (slot, query head) pairs; set by the launcher
 };
 
 struct AppendArgs {
@@ -81,5 +82,6 @@ hipError_t launch_gather_runs(const GatherRunsArgs &a, int head_dim, int total_p
 hipError_t launch_apply_patches(int32_t *page_table, const int32_t *hdr, const int32_t *data,
                                 int n_patches, int max_pages, hipStream_t st);
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t st);
+hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
 
 }  // namespace nup

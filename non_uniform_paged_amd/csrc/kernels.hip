@@ -6,12 +6,11 @@
 // rows are one contiguous 4 KB block at head_dim 128.
 //
 // Decode attention is bound by HBM bandwidth: every cached byte is read
-// once and feeds GQA multiply-adds, far below the matrix-core ridge.  The
-// partial kernel therefore keeps the arithmetic on the vector ALU in fp32
-// (q.k with the packed bf16 dot2 instruction, whose products are exact and
-// whose sum is kept in fp32), and spends its effort on keeping enough
-// 16-byte loads in flight: each wave streams a page (K and V) ahead of the
-// one it computes.
+// once and feeds only GQA multiply-adds.  The partial kernel puts q.k on the
+// matrix core (a 16-token x 16-column tile whose bf16 products are exact in
+// the fp32 accumulator), keeps softmax and P.V in fp32 on the vector ALU, and
+// spends its registers on keeping 16-byte loads in flight: each wave streams
+// a page (K and V) ahead of the one it computes.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -21,7 +20,6 @@
 namespace nup {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -30,159 +28,111 @@ constexpr float kLn2 = 0.6931471805599453f;
 // skips almost all rescaling of the accumulators.
 constexpr float kRescaleSlack = 8.0f;
 
+// Pages a wave keeps in its register ring (the page being computed plus
+// kDepth-1 in flight).
+#ifndef NUP_PREFETCH
+#define NUP_PREFETCH 2
+#endif
+constexpr int kDepth = NUP_PREFETCH;
+// Minimum waves per SIMD the partial kernel is compiled for.
+#ifndef NUP_WAVES_PER_EU
+#define NUP_WAVES_PER_EU 2
+#endif
+
+// Wave-uniform read of descriptor data (plan rows, lengths, page tables):
+// through the constant address space, so it becomes a scalar load and
+// everything derived from it (page addresses) stays in scalar registers.
+// The descriptor is never written while an attention kernel runs.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T *p) {
+    return *(const __attribute__((address_space(4))) T *)(p);
+}
+
+// 2^x on the transcendental unit (v_exp_f32).  Arguments here are at most
+// kRescaleSlack; results that underflow to zero or a denormal are harmless.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte streaming load with the nontemporal hint: K/V rows are read
+// exactly once per step, and on gfx950 the hint lifts streaming reads by
+// about a tenth (measured on the HBM read probe).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
-// row_ror:8.
-constexpr int kQuadSwap1 = 0xB1;
-constexpr int kQuadSwap2 = 0x4E;
-constexpr int kHalfMirror = 0x141;
-constexpr int kRowRor8 = 0x128;
-
-// Sum over the 8 lanes of an aligned group (lanes 8k .. 8k+7).
-__device__ __forceinline__ float sum8(float x) {
-    x += dpp<kQuadSwap1>(x);
-    x += dpp<kQuadSwap2>(x);
-    x += dpp<kHalfMirror>(x);
-    return x;
-}
-
-// Across the 8 groups that share a lane position inside their group
-// (lanes e, e+8, ..., e+56).
-__device__ __forceinline__ float max_groups(float x) {
-    x = fmaxf(x, dpp<kRowRor8>(x));
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
-}
-__device__ __forceinline__ float sum_groups(float x) {
-    x += dpp<kRowRor8>(x);
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
-}
 
 // ---------------------------------------------------------------------------
 // Split-K partial attention.
 //
-// Lane layout inside a wave (64 lanes): lane = 8*tq + e.  For a 16-token
-// page the lane owns tokens tq and tq+8 and, of each, the 16-byte pieces
-// e and e+8 of the row (dims 8e..8e+7 and 64+8e..64+8e+7 at head_dim 128).
-// Eight consecutive lanes thus read 128 contiguous bytes of one row, and a
-// wave-wide load instruction covers eight rows: every load is a full
-// 16-byte, fully coalesced access.  q.k is finished with three DPP adds
-// across the 8 lanes of a token; the softmax state and the output
-// accumulator are kept per lane (per token subset) and combined once per
-// row at the end.
+// One wave is one worker of the ahead-of-time plan; it walks its rows
+// (head, token range) page by page.  For a 16-token page of one head:
+//
+//   scores  S^T[16 tokens][16] = K_page[16][D] . Q^T[D][16] on the matrix
+//           core (v_mfma_f32_16x16x32_bf16, D/32 steps).  The GQA query rows
+//           of the head fill columns 0..GQA-1 of Q^T, the rest is zero.  The
+//           bf16 products are exact and accumulate in fp32.
+//           A operand: lane l holds token l%16 and the 16-byte pieces
+//           4j + l/16 of its row (step j), i.e. 64 contiguous bytes of each
+//           row per load instruction.  Lane l of the result holds query row
+//           l%16 for tokens 4(l/16) .. 4(l/16)+3.
+//   softmax fp32, online, per query row; the running maximum of a row is
+//           shared by the whole wave, so the output accumulators of all
+//           lanes use one scale and combine by plain sums.
+//   P.V     fp32 on the vector ALU.  Lane (tg, e) holds tokens
+//           tg*TPL .. tg*TPL+TPL-1 and dims 8e .. 8e+7 of V (a wave-wide load
+//           covers 64/LPR full rows).  The softmax weights reach these lanes
+//           through a 512-byte LDS tile per wave.
 // ---------------------------------------------------------------------------
-template <int D, int GQA, bool TOPK>
-struct Partial {
-    static constexpr int NH = D / 64;  // 16-byte pieces per token per lane
-
-    float o[GQA][NH * 8];
-    float m[GQA], l[GQA];
-
-    // qs: this wave's q rows in LDS, bf16 [GQA][D]; read one row at a time
-    // so that q occupies no registers across the page loop.
-    __device__ __forceinline__ void compute(const uint4 (&k)[2][NH], const uint4 (&v)[2][NH],
-                                            const uint4 *qs, int e, bool valid0, bool valid1,
-                                            float scale_log2) {
-        float sc[2][GQA];
-#pragma unroll
-        for (int r = 0; r < GQA; ++r) {
-            uint4 qv[NH];
-#pragma unroll
-            for (int hh = 0; hh < NH; ++hh) qv[hh] = qs[r * (D / 8) + e + 8 * hh];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                float acc = 0.f;
-#pragma unroll
-                for (int hh = 0; hh < NH; ++hh) {
-                    acc = dot2(qv[hh].x, k[i][hh].x, acc);
-                    acc = dot2(qv[hh].y, k[i][hh].y, acc);
-                    acc = dot2(qv[hh].z, k[i][hh].z, acc);
-                    acc = dot2(qv[hh].w, k[i][hh].w, acc);
-                }
-                sc[i][r] = acc;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < GQA; ++r) sc[i][r] = sum8(sc[i][r]) * scale_log2;
-
-#pragma unroll
-        for (int r = 0; r < GQA; ++r) {
-            const float s0 = valid0 ? sc[0][r] : -INFINITY;
-            const float s1 = valid1 ? sc[1][r] : -INFINITY;
-            const float mx = fmaxf(s0, s1);
-            if (mx > m[r] + kRescaleSlack) {
-                const float a = exp2f(m[r] - mx);
-                m[r] = mx;
-                l[r] *= a;
-#pragma unroll
-                for (int d = 0; d < NH * 8; ++d) o[r][d] *= a;
-            }
-            const float p0 = valid0 ? exp2f(s0 - m[r]) : 0.f;
-            const float p1 = valid1 ? exp2f(s1 - m[r]) : 0.f;
-            l[r] += p0 + p1;
-#pragma unroll
-            for (int hh = 0; hh < NH; ++hh) {
-                const uint32_t w0[4] = {v[0][hh].x, v[0][hh].y, v[0][hh].z, v[0][hh].w};
-                const uint32_t w1[4] = {v[1][hh].x, v[1][hh].y, v[1][hh].z, v[1][hh].w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    float *od = &o[r][hh * 8 + 2 * c];
-                    od[0] = fmaf(p1, bf16lo(w1[c]), fmaf(p0, bf16lo(w0[c]), od[0]));
-                    od[1] = fmaf(p1, bf16hi(w1[c]), fmaf(p0, bf16hi(w0[c]), od[1]));
-                }
-            }
-        }
-    }
-};
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D, int GQA, bool TOPK>
-__global__ __launch_bounds__(256) void partial_attn_kernel(PartialArgs a) {
-    using W = Partial<D, GQA, TOPK>;
-    constexpr int NH = W::NH;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NUP_WAVES_PER_EU, 8)))
+void partial_attn_kernel(PartialArgs a) {
+    constexpr int NJ = D / 32;     // MFMA steps over the head dim
+    constexpr int LPR = D / 8;     // lanes per V row (16-byte pieces)
+    constexpr int TPL = LPR / 4;   // tokens per lane for V
+    constexpr int NTG = 64 / LPR;  // token groups in a wave for V
+    static_assert(GQA <= 8, "query rows per KV head");
+
+    __shared__ float4 p_lds[kWavesPerBlock][8][4];   // [row][16 tokens]
+    __shared__ float alpha_lds[kWavesPerBlock][8];
+
     const int lane = threadIdx.x & 63;
-    const int w = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = blockIdx.x * kWavesPerBlock + wid;
     if (w >= a.n_workers) return;
-    const int tq = lane >> 3, e = lane & 7;
+    float *pl = reinterpret_cast<float *>(p_lds[wid]);
+    float *al = alpha_lds[wid];
+
+    // MFMA-side coordinates
+    const int qn = lane & 15;       // query row (column of S^T)
+    const int qg = lane >> 4;       // token quad of the result, piece group of A/B
+    // V-side coordinates
+    const int tg = lane / LPR, ve = lane % LPR;
 
     int rb, re;
     if (TOPK) {
         rb = w;
         re = w + 1;
     } else {
-        rb = a.worker_start[w];
-        re = a.worker_start[w + 1];
+        rb = ld_uniform(a.worker_start + w);
+        re = ld_uniform(a.worker_start + w + 1);
     }
-    __shared__ uint4 q_lds[kWavesPerBlock][GQA * D / 8];
-    uint4 *qs = q_lds[threadIdx.x >> 6];
-    W st;
     for (int row = rb; row < re; ++row) {
         int sh, t0, t1;
         if (TOPK) {
             sh = row / a.topk_splits;
             t0 = (row - sh * a.topk_splits) * a.topk_chunk;
-            const int L = a.active[sh / a.hkv] ? a.topk_k : 0;
+            const int L = ld_uniform(a.active + sh / a.hkv) ? a.topk_k : 0;
             t1 = min(t0 + a.topk_chunk, L);
         } else {
-            sh = a.rows[row * 4 + 0];
-            t0 = a.rows[row * 4 + 1];
-            t1 = min(a.rows[row * 4 + 2], a.lengths[sh]);
+            sh = ld_uniform(a.rows + row * 4 + 0);
+            t0 = ld_uniform(a.rows + row * 4 + 1);
+            t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + sh));
         }
         const int s = sh / a.hkv, h = sh - s * a.hkv;
         float *ml = a.ws_ml + (size_t)row * GQA * 2;
@@ -193,104 +143,168 @@ __global__ __launch_bounds__(256) void partial_attn_kernel(PartialArgs a) {
             }
             continue;
         }
-        // q rows of this KV head -> this wave's LDS slot (the wave's own
-        // in-order LDS queue orders these writes before the reads below)
-        const uint4 *qh = reinterpret_cast<const uint4 *>(
-            a.q + ((size_t)s * a.hkv * GQA + (size_t)h * GQA) * D);
-        __builtin_amdgcn_wave_barrier();
-        for (int c = lane; c < GQA * D / 8; c += 64) qs[c] = qh[c];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // Q^T operand: column qn holds query row qn of this KV head (zero past GQA)
+        uint4 qv[NJ];
+        {
+            const uint4 *qh = reinterpret_cast<const uint4 *>(
+                a.q + ((size_t)s * a.hkv * GQA + (size_t)h * GQA + (qn < GQA ? qn : 0)) * D);
 #pragma unroll
-        for (int r = 0; r < GQA; ++r) {
-            st.m[r] = -INFINITY;
-            st.l[r] = 0.f;
-#pragma unroll
-            for (int d = 0; d < NH * 8; ++d) st.o[r][d] = 0.f;
+            for (int j = 0; j < NJ; ++j) {
+                qv[j] = qh[4 * j + qg];
+                if (qn >= GQA) qv[j] = make_uint4(0, 0, 0, 0);
+            }
         }
+        float m_run = -INFINITY;   // running max of row qn (log2 units), wave-consistent
+        float l_run = 0.f;         // this lane's share of the row's sum
+        float o[GQA][8];
+#pragma unroll
+        for (int r = 0; r < GQA; ++r)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) o[r][c] = 0.f;
 
         const int32_t *ptrow = nullptr;
         size_t slot_off = 0;
         if (!TOPK) {
-            ptrow = a.page_table +
-                    ((size_t)a.group_of_head[h] * a.bmax + s) * (size_t)a.max_pages;
-            slot_off = (size_t)a.slot_of_head[h] * kPage * D;
+            ptrow = a.page_table + ((size_t)ld_uniform(a.group_of_head + h) * a.bmax + s) * (size_t)a.max_pages;
+            slot_off = (size_t)ld_uniform(a.slot_of_head + h) * kPage * D;
         }
         const size_t head_base = TOPK ? (size_t)sh * a.topk_k * D : 0;
         const int p0 = t0 / kPage, p1 = (t1 - 1) / kPage;  // inclusive page range
 
         auto page_base = [&](int pi) -> size_t {
             if (TOPK) return head_base + (size_t)pi * kPage * D;
-            return (size_t)ptrow[pi] * a.gh * kPage * D + slot_off;
+            return (size_t)ld_uniform(ptrow + pi) * a.gh * kPage * D + slot_off;
         };
-        auto load = [&](int pi, size_t base, uint4 (&k)[2][NH], uint4 (&v)[2][NH]) {
+        // Lane offsets (in 16-byte pieces) inside a head's 16-row block; rows
+        // past the end of the range are clamped to the last valid row.  The
+        // block base is wave-uniform, so loads take a scalar base and a
+        // 32-bit lane offset.
+        auto load = [&](int pi, size_t base, uint4 (&k)[NJ], uint4 (&v)[TPL]) {
+            const int last = t1 - 1 - pi * kPage;
+            const uint4 *kp = reinterpret_cast<const uint4 *>(a.kbase + base);
+            const uint4 *vp = reinterpret_cast<const uint4 *>(a.vbase + base);
+            const uint32_t koff = (uint32_t)min(qn, last) * (D / 8) + qg;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                int j = tq + 8 * i;
-                j = min(pi * kPage + j, t1 - 1) - pi * kPage;  // clamp past the end
-                const size_t off = base + (size_t)j * D;
-                const uint4 *kp = reinterpret_cast<const uint4 *>(a.kbase + off);
-                const uint4 *vp = reinterpret_cast<const uint4 *>(a.vbase + off);
+            for (int j = 0; j < NJ; ++j) k[j] = ld_stream(kp + koff + 4 * j);
 #pragma unroll
-                for (int hh = 0; hh < NH; ++hh) {
-                    k[i][hh] = kp[e + 8 * hh];
-                    v[i][hh] = vp[e + 8 * hh];
-                }
+            for (int i = 0; i < TPL; ++i) {
+                const uint32_t voff = (uint32_t)min(tg * TPL + i, last) * (D / 8) + ve;
+                v[i] = ld_stream(vp + voff);
             }
         };
+        auto compute = [&](int pi, const uint4 (&k)[NJ], const uint4 (&v)[TPL]) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k[j]),
+                                                              __builtin_bit_cast(bf16x8_t, qv[j]),
+                                                              acc, 0, 0, 0);
+            const int tbase = pi * kPage + 4 * qg;
+            float sc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] = (tbase + i < t1) ? acc[i] * a.scale_log2 : -INFINITY;
+            float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // raise a row's maximum only when it grows by more than the slack;
+            // the decision is made for the whole wave at once
+            const bool need = (qn < GQA) && (mx > m_run + kRescaleSlack);
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                const float alpha = need ? fast_exp2(m_run - mx) : 1.f;
+                if (need) {
+                    m_run = mx;
+                    l_run *= alpha;
+                }
+                if (lane < GQA) al[lane] = alpha;
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int r = 0; r < GQA; ++r) {
+                    const float ar = al[r];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) o[r][c] *= ar;
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+            float pr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[i] = (sc[i] == -INFINITY) ? 0.f : fast_exp2(sc[i] - m_run);
+            l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            if (qn < GQA) reinterpret_cast<float4 *>(pl)[qn * 4 + qg] = make_float4(pr[0], pr[1], pr[2], pr[3]);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int r = 0; r < GQA; ++r) {
+                float pv[TPL];
+                if (TPL == 4) {
+                    const float4 x = reinterpret_cast<const float4 *>(pl)[r * 4 + tg];
+                    pv[0] = x.x; pv[1] = x.y; pv[2 % TPL] = x.z; pv[3 % TPL] = x.w;
+                } else {
+                    const float2 x = reinterpret_cast<const float2 *>(pl)[r * 8 + tg];
+                    pv[0] = x.x; pv[1 % TPL] = x.y;
+                }
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    const uint32_t wv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        o[r][2 * c] = fmaf(pv[i], bf16lo(wv[c]), o[r][2 * c]);
+                        o[r][2 * c + 1] = fmaf(pv[i], bf16hi(wv[c]), o[r][2 * c + 1]);
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        };
 
-        uint4 kA[2][NH], vA[2][NH], kB[2][NH], vB[2][NH];
-        size_t baseB = 0;
+        // Two page buffers: page p+1 is in flight while page p is computed.
+        uint4 kA[NJ], vA[TPL], kB[NJ], vB[TPL];
         load(p0, page_base(p0), kA, vA);
-        if (p0 + 1 <= p1) baseB = page_base(p0 + 1);
-        for (int pi = p0; pi <= p1; pi += 2) {
-            const bool hasB = pi + 1 <= p1;
-            if (hasB) load(pi + 1, baseB, kB, vB);
-            size_t baseA = 0;
-            if (pi + 2 <= p1) baseA = page_base(pi + 2);
-            st.compute(kA, vA, qs, e, pi * kPage + tq < t1, pi * kPage + tq + 8 < t1, a.scale_log2);
-            if (!hasB) break;
-            if (pi + 2 <= p1) load(pi + 2, baseA, kA, vA);
-            if (pi + 3 <= p1) baseB = page_base(pi + 3);
-            st.compute(kB, vB, qs, e, (pi + 1) * kPage + tq < t1, (pi + 1) * kPage + tq + 8 < t1,
-                       a.scale_log2);
+        for (int p = p0; p <= p1; p += 2) {
+            if (p + 1 <= p1) load(p + 1, page_base(p + 1), kB, vB);
+            compute(p, kA, vA);
+            if (p + 1 > p1) break;
+            if (p + 2 <= p1) load(p + 2, page_base(p + 2), kA, vA);
+            compute(p + 1, kB, vB);
         }
 
-        // Combine the eight token groups of the wave.
+        // Combine: the row sums over the four token quads, the outputs over
+        // the token groups of V.
+        float lt = l_run;
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
         float *wo = a.ws_o + (size_t)row * GQA * D;
 #pragma unroll
         for (int r = 0; r < GQA; ++r) {
-            const float mm = max_groups(st.m[r]);
-            const float f = (st.m[r] == -INFINITY) ? 0.f : exp2f(st.m[r] - mm);
-            const float lt = sum_groups(st.l[r] * f);
-            float ot[NH * 8];
 #pragma unroll
-            for (int d = 0; d < NH * 8; ++d) ot[d] = sum_groups(st.o[r][d] * f);
-            if (tq == r) {
+            for (int c = 0; c < 8; ++c) {
+                float x = o[r][c];
 #pragma unroll
-                for (int hh = 0; hh < NH; ++hh) {
-                    float4 *dst = reinterpret_cast<float4 *>(wo + (size_t)r * D + 8 * e + 64 * hh);
-                    dst[0] = make_float4(ot[hh * 8 + 0], ot[hh * 8 + 1], ot[hh * 8 + 2], ot[hh * 8 + 3]);
-                    dst[1] = make_float4(ot[hh * 8 + 4], ot[hh * 8 + 5], ot[hh * 8 + 6], ot[hh * 8 + 7]);
-                }
-                if (e == 0) {
-                    ml[r * 2 + 0] = mm;
-                    ml[r * 2 + 1] = lt;
-                }
+                for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
+                o[r][c] = x;
             }
+            if (tg == r % NTG) {
+                float4 *dst = reinterpret_cast<float4 *>(wo + (size_t)r * D + 8 * ve);
+                dst[0] = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
+                dst[1] = make_float4(o[r][4], o[r][5], o[r][6], o[r][7]);
+            }
+        }
+        if (lane < GQA) {
+            ml[lane * 2 + 0] = m_run;
+            ml[lane * 2 + 1] = lt;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of split-K partials: one 64-lane block per (slot, KV head).
+// Log-sum-exp merge of split-K partials: one wave per (slot, query head),
+// four per block.  The partial rows of a head are independent loads, so the
+// loop is unrolled to keep several in flight.
 // ---------------------------------------------------------------------------
 template <int D, int GQA>
-__global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     constexpr int NJ = D / 64;
-    const int sh = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wv = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wv >= a.n_pairs) return;
+    const int sh = wv / GQA, r = wv - sh * GQA;
     const int s = sh / a.hkv, h = sh - s * a.hkv;
     int rb, re;
     if (a.head_row_start) {
@@ -300,31 +314,32 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
         rb = sh * a.uniform_splits;
         re = rb + a.uniform_splits;
     }
-    const int hq = a.hkv * GQA;
+    float M = -INFINITY;
+    for (int i = rb; i < re; ++i) M = fmaxf(M, a.ws_ml[((size_t)i * GQA + r) * 2]);
+    float L = 0.f, acc[NJ];
 #pragma unroll
-    for (int r = 0; r < GQA; ++r) {
-        float M = -INFINITY;
-        for (int i = rb; i < re; ++i) M = fmaxf(M, a.ws_ml[((size_t)i * GQA + r) * 2]);
-        float L = 0.f, acc[NJ];
+    for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 4
+        for (int i = rb; i < re; ++i) {
+            const float mi = a.ws_ml[((size_t)i * GQA + r) * 2];
+            const float li = a.ws_ml[((size_t)i * GQA + r) * 2 + 1];
+            const float wgt = (mi == -INFINITY) ? 0.f : exp2f(mi - M);
+            L = fmaf(wgt, li, L);
+            const float *oi = a.ws_o + ((size_t)i * GQA + r) * D;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
-        if (M != -INFINITY) {
-            for (int i = rb; i < re; ++i) {
-                const float mi = a.ws_ml[((size_t)i * GQA + r) * 2];
-                if (mi == -INFINITY) continue;
-                const float wgt = exp2f(mi - M);
-                L = fmaf(wgt, a.ws_ml[((size_t)i * GQA + r) * 2 + 1], L);
-                const float *oi = a.ws_o + ((size_t)i * GQA + r) * D;
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[j] = fmaf(wgt, oi[lane + 64 * j], acc[j]);
+            for (int j = 0; j < NJ; ++j) {
+                // rows with no tokens carry no o; skip their (unwritten) values
+                const float ov = (mi == -INFINITY) ? 0.f : oi[lane + 64 * j];
+                acc[j] = fmaf(wgt, ov, acc[j]);
             }
         }
-        const size_t qr = (size_t)s * hq + (size_t)h * GQA + r;
-        const float inv = (M != -INFINITY) ? 1.0f / L : 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) a.out[qr * D + lane + 64 * j] = acc[j] * inv;
-        if (a.lse && lane == 0) a.lse[qr] = (M != -INFINITY) ? (M + log2f(L)) * kLn2 : -INFINITY;
     }
+    const size_t qr = (size_t)s * a.hkv * GQA + (size_t)h * GQA + r;
+    const float inv = (M != -INFINITY) ? 1.0f / L : 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) a.out[qr * D + lane + 64 * j] = acc[j] * inv;
+    if (a.lse && lane == 0) a.lse[qr] = (M != -INFINITY) ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -385,7 +400,7 @@ __global__ __launch_bounds__(256) void gather_index_kernel(GatherIndexArgs a) {
     }
     const int pid = a.page_table[((size_t)a.group_of_head[h] * a.bmax + s) * a.max_pages + t / kPage];
     const size_t rowid = ((size_t)pid * a.gh + a.slot_of_head[h]) * kPage + t % kPage;
-    *dst = reinterpret_cast<const uint4 *>((isv ? a.v_pool : a.k_pool) + rowid * D)[c];
+    *dst = ld_stream(reinterpret_cast<const uint4 *>((isv ? a.v_pool : a.k_pool) + rowid * D) + c);
     if (a.phys_out && sub == 0) a.phys_out[gr] = (int32_t)rowid;
 }
 
@@ -421,7 +436,7 @@ __global__ __launch_bounds__(256) void gather_runs_kernel(GatherRunsArgs a) {
         const int t = lp * kPage + row;
         if (t >= a.lengths[sh]) continue;
         const size_t rowid = ((size_t)pid * a.gh + j) * kPage + row;
-        const uint4 v = reinterpret_cast<const uint4 *>((isv ? a.v_pool : a.k_pool) + rowid * D)[piece];
+        const uint4 v = ld_stream(reinterpret_cast<const uint4 *>((isv ? a.v_pool : a.k_pool) + rowid * D) + piece);
         const long long dr = a.row_off[sh] + t;
         reinterpret_cast<uint4 *>((isv ? a.v_out : a.k_out) + (size_t)dr * D)[piece] = v;
         if (a.phys_out && !isv && piece == 0) a.phys_out[dr] = (int32_t)rowid;
@@ -435,9 +450,36 @@ __global__ __launch_bounds__(256) void apply_patches_kernel(int32_t *pt, const i
     for (int i = threadIdx.x; i < count; i += 256) pt[(size_t)row * max_pages + i] = data[off + i];
 }
 
+// Streaming probes: each thread moves four 16-byte pieces per iteration.
 __global__ __launch_bounds__(256) void probe_copy_kernel(const uint4 *src, uint4 *dst, size_t n) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const uint4 a0 = src[i], a1 = src[i + stride], a2 = src[i + 2 * stride], a3 = src[i + 3 * stride];
+        dst[i] = a0;
+        dst[i + stride] = a1;
+        dst[i + 2 * stride] = a2;
+        dst[i + 3 * stride] = a3;
+    }
+    for (; i < n; i += stride) dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(256) void probe_read_kernel(const uint4 *src, uint32_t *sink, size_t n) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t x = 0;
+    for (; i + 7 * stride < n; i += 8 * stride) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = ld_stream(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n; i += stride) {
+        const uint4 v = ld_stream(src + i);
+        x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (x == 0x9e3779b9u) sink[0] = x;  // keeps the loads; practically never stores
 }
 
 template <int D, int GQA, bool TOPK>
@@ -506,7 +548,9 @@ hipError_t launch_merge(const MergeArgs &a, int head_dim, int gqa, int n_heads, 
     if (!fn) return hipErrorInvalidValue;
     if (n_heads <= 0) return hipSuccess;
     MergeArgs copy = a;
-    return launch_raw(fn, dim3(n_heads), dim3(64), &copy, sizeof(copy), st);
+    copy.n_pairs = n_heads * gqa;
+    const unsigned blocks = (unsigned)((copy.n_pairs + kWavesPerBlock - 1) / kWavesPerBlock);
+    return launch_raw(fn, dim3(blocks), dim3(256), &copy, sizeof(copy), st);
 }
 
 hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t st) {
@@ -550,9 +594,19 @@ hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream
     const size_t n = bytes / 16;
     if (n == 0) return hipSuccess;
     size_t blocks = (n + 255) / 256;
-    if (blocks > 256 * 64) blocks = 256 * 64;
+    if (blocks > 256 * 32) blocks = 256 * 32;
     hipLaunchKernelGGL(probe_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
                        static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st) {
+    const size_t n = bytes / 16;
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 256 * 128) blocks = 256 * 128;
+    hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const uint4 *>(src), sink, n);
     return hipGetLastError();
 }
 
