@@ -158,7 +158,9 @@ def cpu_baseline(setup, budget_s=15.0):
     spec = pg.PagerSpec(w.num_kv_heads, w.num_groups, w.batch, setup.num_pages,
                         int(math.ceil(setup.caps.max() / 16)), 16, w.free_list_init)
     assert spec.alloc(np.arange(w.batch), setup.caps, setup.lengths0) == pg.OK
-    threads = os.cpu_count() or 1
+    # the threads the oracle actually runs on: the OpenMP setting of this host
+    # (the GPU hosts pin it to the CPU share of one GPU), else the affinity mask
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
 
     def run(seqs):
         sub = spec.page_table[:, seqs, :]
@@ -183,9 +185,15 @@ def cpu_baseline(setup, budget_s=15.0):
     n = int(max(1, min(w.batch, math.floor(budget_s / max(dt, 1e-3)))))
     if n > 1:
         dt, b = run(list(range(n)))
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    reps, total_t, total_b = 1, dt, b
+    while total_t < budget_s * 0.6 and reps < 50:   # whole batch is quick: repeat it
+        dt, b = run(list(range(n)))
+        reps, total_t, total_b = reps + 1, total_t + dt, total_b + b
+    return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
             "sample": f"first {n} of {w.batch} sessions of the same batch (all their KV heads), "
-                      f"one decode step, fp64 C oracle with OpenMP; {dt:.1f} s wall"}
+                      f"one decode step of attention, x{reps} runs, {total_t:.1f} s wall; fp64 C "
+                      f"oracle with OpenMP"}
 
 
 def main():

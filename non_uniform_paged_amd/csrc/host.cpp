@@ -42,6 +42,7 @@ struct Sizes {
     size_t patches_max;  // hdr[ng*B][4] data[ng*B*max_pages]
     size_t inbox;        // fixed + plan_max + runs_max + patches_max (aligned)
     size_t pt;           // page table bytes
+    size_t err;          // error word (padded)
     size_t total;        // inbox + pt + error word
     int max_rows;
     int max_workers;
@@ -78,7 +79,7 @@ Sizes compute_sizes(const nup_config &c, int workers) {
         z.max_rows = (int)(B * H * splits);
         z.max_workers = z.max_rows;
     } else {
-        z.max_rows = workers + (int)(B * H);
+        z.max_rows = workers + 2 * (int)(B * H);
         z.max_workers = workers;
     }
     z.fixed = align_up(4 * (B + B * H + 3 * H));
@@ -88,7 +89,8 @@ Sizes compute_sizes(const nup_config &c, int workers) {
     z.patches_max = align_up(16 * ng * B) + align_up(4 * ng * B * (size_t)c.max_pages);
     z.inbox = z.fixed + z.plan_max + z.runs_max + z.patches_max;
     z.pt = align_up(4 * ng * B * (size_t)c.max_pages);
-    z.total = z.inbox + z.pt + kAlign;
+    z.err = kAlign;
+    z.total = z.inbox + z.pt + z.err;
     return z;
 }
 
@@ -186,38 +188,61 @@ void group_heads(nup_ctx *c, int n, const int32_t *cap) {
 }
 
 // ---- ahead-of-time split-K plan -------------------------------------------
+// Balanced plan: the pages of all active heads, concatenated in (slot, head)
+// order, are cut into `workers` equal contiguous shares; a share is split
+// into rows at head boundaries.  A head with no pages gets one empty row on
+// the worker at its position, so that its (zero) output is written too.
+// Rows come out sorted by head and, within that, by worker.
 void plan_balanced(nup_ctx *c) {
     const int B = c->B, H = c->H, P = c->P, W = c->workers;
-    std::vector<long long> base((size_t)B * H + 1, 0);  // first page of each head
-    for (int sh = 0; sh < B * H; ++sh) {
-        const int s = sh / H;
-        const long long pages = c->active[s] ? (c->cap[sh] + P - 1) / P : 0;
+    const int NH = B * H;
+    std::vector<long long> base((size_t)NH + 1, 0);  // first page of each head
+    for (int sh = 0; sh < NH; ++sh) {
+        const long long pages = c->active[sh / H] ? (c->cap[sh] + P - 1) / P : 0;
         base[sh + 1] = base[sh] + pages;
     }
-    const long long T = base[(size_t)B * H];
+    const long long T = base[NH];
+    auto share_lo = [&](long long w) { return T * w / W; };
+    auto worker_of = [&](long long p) {  // the worker whose share holds page p
+        long long w = T > 0 ? p * W / T : 0;
+        while (w + 1 < W && share_lo(w + 1) <= p) ++w;
+        while (w > 0 && share_lo(w) > p) --w;
+        return (int)w;
+    };
+    std::vector<int32_t> owner;
     c->rows.clear();
-    c->worker_start.assign(W + 1, 0);
-    std::vector<int32_t> per_head((size_t)B * H, 0);
-    int sh = 0;
-    for (int w = 0; w < W; ++w) {
-        c->worker_start[w] = (int)(c->rows.size() / 4);
-        const long long lo = T * w / W, hi = T * (w + 1) / W;
-        long long p = lo;
-        while (p < hi) {
-            while (base[sh + 1] <= p) ++sh;  // head holding page p
-            const long long end = std::min(hi, base[sh + 1]);
+    c->head_row_start.assign((size_t)NH + 1, 0);
+    for (int sh = 0; sh < NH; ++sh) {
+        c->head_row_start[sh] = (int32_t)(c->rows.size() / 4);
+        if (base[sh + 1] == base[sh]) {
+            const int w = T > 0 ? worker_of(std::min(base[sh], T - 1)) : (int)((long long)sh * W / NH);
+            c->rows.insert(c->rows.end(), {sh, 0, 0, 0});
+            owner.push_back(w);
+            continue;
+        }
+        long long p = base[sh];
+        while (p < base[sh + 1]) {
+            const int w = worker_of(p);
+            const long long end = std::min(base[sh + 1], share_lo(w + 1));
             const long long t0 = (p - base[sh]) * P;
             const long long t1 = std::min<long long>((end - base[sh]) * P, c->cap[sh]);
             c->rows.insert(c->rows.end(), {sh, (int32_t)t0, (int32_t)t1, 0});
-            per_head[sh]++;
+            owner.push_back(w);
             p = end;
         }
     }
-    c->worker_start[W] = (int)(c->rows.size() / 4);
-    c->head_row_start.assign((size_t)B * H + 1, 0);
-    for (int i = 0; i < B * H; ++i) c->head_row_start[i + 1] = c->head_row_start[i] + per_head[i];
+    c->head_row_start[NH] = (int32_t)(c->rows.size() / 4);
+    c->worker_start.assign(W + 1, 0);
+    size_t r = 0;
+    for (int w = 0; w <= W; ++w) {
+        while (r < owner.size() && owner[r] < w) ++r;
+        c->worker_start[w] = (int32_t)r;
+    }
+    c->worker_start[W] = (int32_t)owner.size();
 }
 
+// The uniform split (the control): every head is cut into the same number of
+// page-aligned chunks regardless of its length, one chunk per worker.
 void plan_uniform(nup_ctx *c) {
     const int B = c->B, H = c->H, P = c->P;
     const int S = c->cfg.uniform_splits > 0 ? c->cfg.uniform_splits : 8;
@@ -233,6 +258,9 @@ void plan_uniform(nup_ctx *c) {
                 c->rows.insert(c->rows.end(), {sh, (int32_t)t0, (int32_t)std::min<long long>(t0 + chunk, cap), 0});
                 ++nr;
             }
+        } else {
+            c->rows.insert(c->rows.end(), {sh, 0, 0, 0});
+            nr = 1;
         }
         c->head_row_start[sh + 1] = c->head_row_start[sh] + nr;
     }
@@ -500,6 +528,10 @@ nup_status nup_commit(nup_ctx *c, void *stream) {
     if (!c) return NUP_E_ARG;
     if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // Nothing edited since the last commit: the device already holds this
+    // frame (appends advance the device lengths themselves), so the commit
+    // sends nothing.
+    if (c->committed && !c->pending) return NUP_OK;
     const int i = c->pinned_next;
     if (!c->pinned[i]) {
         hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&c->pinned[i]), c->sz.inbox, hipHostMallocDefault);
@@ -583,8 +615,8 @@ nup_status nup_commit(nup_ctx *c, void *stream) {
     }
     hipError_t e;
     if (!c->committed) {  // the latched device error word starts clear
-        e = hipMemsetAsync(c->d_err(), 0, 4, st);
-        if (e != hipSuccess) return hip_fail(c, e, "hipMemsetAsync (error word)");
+        e = nup::launch_fill(c->d_err(), 1, 0, st);
+        if (e != hipSuccess) return hip_fail(c, e, "clear device error word");
     }
     e = hipMemcpyAsync(c->desc, blob, used, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync (commit)");
@@ -768,6 +800,9 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
                                             align_up((size_t)rows_max * c->gqa * c->D * 4));
     a.ws_o = wso;
     a.ws_ml = wsml;
+    a.out = out;
+    a.lse = lse;
+    a.head_row_start = topk ? nullptr : c->inbox_i32(c->off_hrs);
     hipError_t e;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (c->timing) {
@@ -784,7 +819,7 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
     nup::MergeArgs m{};
     m.ws_o = wso;
     m.ws_ml = wsml;
-    m.head_row_start = topk ? nullptr : c->inbox_i32(c->off_hrs);
+    m.head_row_start = a.head_row_start;
     m.uniform_splits = splits;
     m.out = out;
     m.lse = lse;

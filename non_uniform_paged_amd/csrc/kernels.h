@@ -9,10 +9,12 @@ namespace nup {
 constexpr int kPage = 16;           // tokens per page
 constexpr int kWavesPerBlock = 4;   // split-K workers per 256-thread workgroup
 
-// Split-K partial attention.  One wave is one worker.  In table mode a
+// Split-K decode attention.  One wave is one worker.  In table mode a
 // worker walks rows[worker_start[w] .. worker_start[w+1]) of (head, t0, t1);
 // in top-K mode worker w takes chunk w % splits of head w / splits of a
-// contiguous staging buffer holding topk_k rows per head.
+// contiguous staging buffer holding topk_k rows per head.  A head covered by
+// one row is written to out directly; otherwise each row leaves a partial
+// (o, m, l) for the merge kernel.
 struct PartialArgs {
     const uint16_t *q;          // bf16 [Bmax][Hq][D]
     const uint16_t *kbase;      // K pool [pages][Gh][16][D] or staging [Bmax*Hkv][K][D]
@@ -24,8 +26,11 @@ struct PartialArgs {
     const int32_t *slot_of_head;
     const int32_t *rows;        // [n][4] (sh, t0, t1, 0) (paged)
     const int32_t *worker_start;// [W+1] (paged)
+    const int32_t *head_row_start; // [Bmax*Hkv+1] (paged); top-K rows of head sh are sh*splits..
     float *ws_o;                // [rows][gqa][D]
     float *ws_ml;               // [rows][gqa][2]  (max in log2 units, sum)
+    float *out;                 // fp32 [Bmax][Hq][D]
+    float *lse;                 // fp32 [Bmax][Hq] or NULL
     int32_t bmax, hkv, gh, max_pages, n_workers;
     int32_t topk_k, topk_splits, topk_chunk;
     float scale_log2;           // softmax scale * log2(e)
@@ -79,6 +84,7 @@ hipError_t launch_merge(const MergeArgs &a, int head_dim, int gqa, int n_heads, 
 hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t st);
 hipError_t launch_gather_index(const GatherIndexArgs &a, int head_dim, hipStream_t st);
 hipError_t launch_gather_runs(const GatherRunsArgs &a, int head_dim, int total_pages, hipStream_t st);
+hipError_t launch_fill(int32_t *p, int n, int32_t value, hipStream_t st);
 hipError_t launch_apply_patches(int32_t *page_table, const int32_t *hdr, const int32_t *data,
                                 int n_patches, int max_pages, hipStream_t st);
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t st);

@@ -89,6 +89,20 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// Write the final output of one KV head's query rows: out = o / l (o given per
+// lane as acc[r][j] for dims lane + 64 j), lse in natural log.  With o == NULL
+// (no tokens) writes zeros and lse = -inf.
+template <int D, int GQA>
+__device__ __forceinline__ void write_final(const PartialArgs &a, size_t qh0, int lane, float, float,
+                                            const float (*acc)[D / 64]) {
+    constexpr int NJ = D / 64;
+#pragma unroll
+    for (int r = 0; r < GQA; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) a.out[(qh0 + r) * D + lane + 64 * j] = acc ? acc[r][j] : 0.f;
+    if (!acc && a.lse && lane < GQA) a.lse[qh0 + lane] = -INFINITY;
+}
+
 template <int D, int GQA, bool TOPK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NUP_WAVES_PER_EU, 8)))
 void partial_attn_kernel(PartialArgs a) {
@@ -98,8 +112,10 @@ void partial_attn_kernel(PartialArgs a) {
     constexpr int NTG = 64 / LPR;  // token groups in a wave for V
     static_assert(GQA <= 8, "query rows per KV head");
 
-    __shared__ float4 p_lds[kWavesPerBlock][8][4];   // [row][16 tokens]
-    __shared__ float alpha_lds[kWavesPerBlock][8];
+    // softmax weights [row][16 tokens], rows padded to 20 floats so that the
+    // writes of the five-plus rows land in distinct LDS banks
+    __shared__ float4 p_lds[kWavesPerBlock][8][5];
+    __shared__ float alpha_lds[kWavesPerBlock][16];   // rescale factors; final 1/l, lse
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -136,10 +152,23 @@ void partial_attn_kernel(PartialArgs a) {
         }
         const int s = sh / a.hkv, h = sh - s * a.hkv;
         float *ml = a.ws_ml + (size_t)row * GQA * 2;
+        int hr0, nrows;   // the rows of this head
+        if (TOPK) {
+            hr0 = sh * a.topk_splits;
+            nrows = a.topk_splits;
+        } else {
+            hr0 = ld_uniform(a.head_row_start + sh);
+            nrows = ld_uniform(a.head_row_start + sh + 1) - hr0;
+        }
+        const size_t qh0 = (size_t)s * a.hkv * GQA + (size_t)h * GQA;   // first query head
         if (t0 >= t1) {
-            if (lane < GQA) {
-                ml[lane * 2 + 0] = -INFINITY;
-                ml[lane * 2 + 1] = 0.f;
+            if (nrows == 1) {
+                write_final<D, GQA>(a, qh0, lane, 0.f, -INFINITY, nullptr);
+            } else {
+                if (lane < GQA) {
+                    ml[lane * 2 + 0] = -INFINITY;
+                    ml[lane * 2 + 1] = 0.f;
+                }
             }
             continue;
         }
@@ -229,16 +258,16 @@ void partial_attn_kernel(PartialArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) pr[i] = (sc[i] == -INFINITY) ? 0.f : fast_exp2(sc[i] - m_run);
             l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-            if (qn < GQA) reinterpret_cast<float4 *>(pl)[qn * 4 + qg] = make_float4(pr[0], pr[1], pr[2], pr[3]);
+            if (qn < GQA) reinterpret_cast<float4 *>(pl)[qn * 5 + qg] = make_float4(pr[0], pr[1], pr[2], pr[3]);
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int r = 0; r < GQA; ++r) {
                 float pv[TPL];
                 if (TPL == 4) {
-                    const float4 x = reinterpret_cast<const float4 *>(pl)[r * 4 + tg];
+                    const float4 x = reinterpret_cast<const float4 *>(pl)[r * 5 + tg];
                     pv[0] = x.x; pv[1] = x.y; pv[2 % TPL] = x.z; pv[3 % TPL] = x.w;
                 } else {
-                    const float2 x = reinterpret_cast<const float2 *>(pl)[r * 8 + tg];
+                    const float2 x = reinterpret_cast<const float2 *>(pl)[r * 10 + tg];
                     pv[0] = x.x; pv[1 % TPL] = x.y;
                 }
 #pragma unroll
@@ -270,9 +299,8 @@ void partial_attn_kernel(PartialArgs a) {
         float lt = l_run;
         lt += __shfl_xor(lt, 16);
         lt += __shfl_xor(lt, 32);
-        float *wo = a.ws_o + (size_t)row * GQA * D;
 #pragma unroll
-        for (int r = 0; r < GQA; ++r) {
+        for (int r = 0; r < GQA; ++r)
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 float x = o[r][c];
@@ -280,6 +308,29 @@ void partial_attn_kernel(PartialArgs a) {
                 for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
                 o[r][c] = x;
             }
+        if (nrows == 1) {
+            // the head is this row: normalise and write the output
+            if (lane < GQA) {
+                al[lane] = 1.0f / lt;
+                al[8 + lane] = (m_run + log2f(lt)) * kLn2;
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int r = 0; r < GQA; ++r) {
+                if (tg == r % NTG) {
+                    const float inv = al[r];
+                    float4 *dst = reinterpret_cast<float4 *>(a.out + (qh0 + r) * D + 8 * ve);
+                    dst[0] = make_float4(o[r][0] * inv, o[r][1] * inv, o[r][2] * inv, o[r][3] * inv);
+                    dst[1] = make_float4(o[r][4] * inv, o[r][5] * inv, o[r][6] * inv, o[r][7] * inv);
+                }
+            }
+            if (a.lse && lane < GQA) a.lse[qh0 + lane] = al[8 + lane];
+            __builtin_amdgcn_wave_barrier();
+            continue;
+        }
+        float *wo = a.ws_o + (size_t)row * GQA * D;
+#pragma unroll
+        for (int r = 0; r < GQA; ++r) {
             if (tg == r % NTG) {
                 float4 *dst = reinterpret_cast<float4 *>(wo + (size_t)r * D + 8 * ve);
                 dst[0] = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
@@ -295,7 +346,7 @@ void partial_attn_kernel(PartialArgs a) {
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of split-K partials: one wave per (slot, query head),
-// four per block.  The partial rows of a head are independent loads, so the
+// four per block, for heads split over several rows.  The partial rows of a head are independent loads, so the
 // loop is unrolled to keep several in flight.
 // ---------------------------------------------------------------------------
 template <int D, int GQA>
@@ -314,6 +365,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         rb = sh * a.uniform_splits;
         re = rb + a.uniform_splits;
     }
+    if (re - rb <= 1) return;   // a head of one row was written by the partial kernel
     float M = -INFINITY;
     for (int i = rb; i < re; ++i) M = fmaxf(M, a.ws_ml[((size_t)i * GQA + r) * 2]);
     float L = 0.f, acc[NJ];
@@ -441,6 +493,11 @@ __global__ __launch_bounds__(256) void gather_runs_kernel(GatherRunsArgs a) {
         reinterpret_cast<uint4 *>((isv ? a.v_out : a.k_out) + (size_t)dr * D)[piece] = v;
         if (a.phys_out && !isv && piece == 0) a.phys_out[dr] = (int32_t)rowid;
     }
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(int32_t *p, int n, int32_t value) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = value;
 }
 
 __global__ __launch_bounds__(256) void apply_patches_kernel(int32_t *pt, const int32_t *hdr,
@@ -581,6 +638,12 @@ hipError_t launch_gather_runs(const GatherRunsArgs &a, int head_dim, int total_p
     if (head_dim == 64) return launch_raw((void *)&gather_runs_kernel<64>, dim3(total_pages), dim3(256), &copy, sizeof(copy), st);
     if (head_dim == 128) return launch_raw((void *)&gather_runs_kernel<128>, dim3(total_pages), dim3(256), &copy, sizeof(copy), st);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill(int32_t *p, int n, int32_t value, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, value);
+    return hipGetLastError();
 }
 
 hipError_t launch_apply_patches(int32_t *page_table, const int32_t *hdr, const int32_t *data,

@@ -7,6 +7,9 @@ the table is judged by properties rather than bit-exactly:
 
   * coverage: for every active (s, h), the rows of that head tile
     [0, cap[s][h]) exactly once, in order, and are contiguous in the table;
+    a head with no capacity (inactive sequence, or a zero budget) is covered
+    by exactly one empty row (t0 = t1 = 0), whose worker writes that head's
+    zero output;
   * granularity: every row starts on a page boundary;
   * head index: head_row_start[s*Hkv + h] .. head_row_start[s*Hkv + h + 1]
     lists exactly that head's rows;
@@ -42,7 +45,8 @@ def check(rows, worker_start, head_row_start, caps, active, page=16,
         lo, hi = int(head_row_start[sh]), int(head_row_start[sh + 1])
         cap = int(caps[s, h]) if active[s] else 0
         if cap == 0:
-            assert lo == hi, f"head {sh} has rows but no capacity"
+            assert hi - lo == 1, f"head {sh} without capacity needs one empty row"
+            assert tuple(rows[lo, :3]) == (sh, 0, 0), f"head {sh}: row {rows[lo]}"
             continue
         t = 0
         for i in range(lo, hi):

@@ -428,3 +428,29 @@ def test_full_size_mixed_churn():
     assert_attention_close(out[seqs], lse[seqs], ref, ref_lse, "mixed churn")
     for s in freed:
         assert np.all(out[s] == 0) and np.all(np.isneginf(lse[s]))
+
+
+def test_repeated_launches_bit_identical():
+    """Split-K arrival counters return to zero after every launch: repeated
+    launches, interleaved paged and top-K calls, give identical results."""
+    c, L, caps = _gather_case(21, B=3, H=8, gqa=5, ng=4)
+    c.alloc([0, 1, 2], caps, L)
+    c.commit()
+    K = 64
+    idx = W.topk_indices(c.spec.lengths, K, salt=21)
+    ks = torch.zeros((c.B, c.H, K, c.D), dtype=torch.int16, device=DEV)
+    vs = torch.zeros_like(ks)
+    nup.kv_gather_compact(c.ctx, 1, ks, vs, idx=torch.from_numpy(idx).to(DEV), K=K)
+    ws_k = torch.empty(nup.workspace_bytes(c.ctx, K), dtype=torch.uint8, device=DEV)
+    first = None
+    for it in range(4):
+        out, lse = c.attend()
+        if first is None:
+            first = (out, lse)
+            ref, ref_lse = c.oracle()
+            assert_attention_close(out, lse, ref, ref_lse, "repeat")
+        else:
+            assert np.array_equal(out, first[0]) and np.array_equal(lse, first[1]), f"launch {it}"
+        nup.attn_decode_topk(c.ctx, c.q, ks.view(torch.bfloat16), vs.view(torch.bfloat16), K,
+                             c.out, c.lse, c.scale, ws_k)
+    torch.cuda.synchronize()

@@ -10,10 +10,11 @@ ACTIVE = np.array([True, True])
 
 
 def _valid():
-    # heads (0,0): 64 tokens, (0,1): 16, (1,0): 0, (1,1): 48; two workers of 4 pages
-    rows = [(0, 0, 32, 0), (0, 32, 64, 0), (1, 0, 16, 0), (3, 0, 16, 0), (3, 16, 48, 0)]
-    # worker 0: rows 0,1 (4 pages); worker 1: rows 2..4 (1 + 1 + 2 pages)
-    return np.array(rows), np.array([0, 2, 5]), np.array([0, 2, 3, 3, 5])
+    # heads (0,0): 64 tokens, (0,1): 16, (1,0): 0 (one empty row), (1,1): 48;
+    # two workers of 4 pages
+    rows = [(0, 0, 32, 0), (0, 32, 64, 0), (1, 0, 16, 0), (2, 0, 0, 0), (3, 0, 16, 0), (3, 16, 48, 0)]
+    # worker 0: rows 0,1 (4 pages); worker 1: rows 2..5 (1 + 0 + 1 + 2 pages)
+    return np.array(rows), np.array([0, 2, 6]), np.array([0, 2, 3, 4, 6])
 
 
 def test_accepts_valid():
@@ -22,7 +23,8 @@ def test_accepts_valid():
     assert loads == [4, 4]
 
 
-@pytest.mark.parametrize("mutate", ["gap", "overlap", "unaligned", "short", "foreign", "unbalanced"])
+@pytest.mark.parametrize("mutate", ["gap", "overlap", "unaligned", "short", "foreign", "unbalanced",
+                                    "empty_head_uncovered"])
 def test_rejects_invalid(mutate):
     rows, ws, hrs = _valid()
     rows = rows.copy()
@@ -34,10 +36,14 @@ def test_rejects_invalid(mutate):
         rows[0, 2] = 33
         rows[1, 1] = 33
     elif mutate == "short":
-        rows[4, 2] = 40
+        rows[5, 2] = 40
     elif mutate == "foreign":
         rows[2, 0] = 2
     elif mutate == "unbalanced":
-        ws = np.array([0, 0, 5])
+        ws = np.array([0, 0, 6])
+    elif mutate == "empty_head_uncovered":
+        rows = np.delete(rows, 3, axis=0)
+        ws = np.array([0, 2, 5])
+        hrs = np.array([0, 2, 3, 3, 5])
     with pytest.raises(AssertionError):
         wt.check(rows, ws, hrs, CAPS, ACTIVE)
