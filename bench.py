@@ -52,22 +52,29 @@ def algorithmic_bytes(lengths, caps, B, Hq, Hkv, ng, D=128, page=16, gqa_rows=Tr
 class Setup:
     """Pools, context and step buffers for one workload on the GPU."""
 
-    def __init__(self, w, headroom_steps, num_workers=0, plan_mode=0, uniform_splits=0):
+    def __init__(self, w, headroom_steps, num_workers=0, plan_mode=0, uniform_splits=0,
+                 max_pages=None):
         import torch
         import non_uniform_paged_amd as nup
         import workloads as W
 
         self.w = w
-        pad = 16 * int(math.ceil((headroom_steps + 1) / 16))
+        # decode headroom: room for the appends of the run (none when nothing is appended)
+        pad = 16 * int(math.ceil((headroom_steps + 1) / 16)) if headroom_steps > 0 else 0
         self.caps = (w.lengths + pad).astype(np.int32)
         self.lengths0 = w.lengths.astype(np.int32)
         B, H, Hq, D, ng = w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, w.num_groups
         gh = H // ng
-        max_pages = int(math.ceil(self.caps.max() / 16))
+        max_pages = max_pages or int(math.ceil(self.caps.max() / 16))
+        self.pad = pad
+        self.max_pages = max_pages
         need = 0
         for g in range(ng):
             need += int(np.ceil(self.caps[:, g * gh:(g + 1) * gh].max(axis=1) / 16).sum())
         num_pages = max(w.num_pages, need)
+        free_list = w.free_list_init
+        if free_list is not None and num_pages > len(free_list):
+            free_list = np.concatenate([free_list, np.arange(len(free_list), num_pages)]).astype(np.int32)
         self.kpool = torch.empty((num_pages, gh, 16, D), dtype=torch.bfloat16, device="cuda")
         self.vpool = torch.empty_like(self.kpool)
         W.fill_normal_bf16_torch(self.kpool, "k")
@@ -77,7 +84,8 @@ class Setup:
                    plan_mode=plan_mode, uniform_splits=uniform_splits)
         self.desc = torch.empty(nup.desc_bytes(**cfg), dtype=torch.uint8, device="cuda")
         self.ctx = nup.Context(**cfg, k_pool=self.kpool, v_pool=self.vpool, desc=self.desc,
-                               free_list_init=w.free_list_init)
+                               free_list_init=free_list)
+        self.free_list = free_list
         nup.kv_alloc_groups(self.ctx, np.arange(B), self.caps, self.lengths0)
         nup.nup_commit(self.ctx)
         self.q = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
@@ -156,7 +164,7 @@ def cpu_baseline(setup, budget_s=15.0):
     from oracle import pager as pg
     w = setup.w
     spec = pg.PagerSpec(w.num_kv_heads, w.num_groups, w.batch, setup.num_pages,
-                        int(math.ceil(setup.caps.max() / 16)), 16, w.free_list_init)
+                        setup.max_pages, 16, setup.free_list)
     assert spec.alloc(np.arange(w.batch), setup.caps, setup.lengths0) == pg.OK
     # the threads the oracle actually runs on: the OpenMP setting of this host
     # (the GPU hosts pin it to the CPU share of one GPU), else the affinity mask
@@ -196,6 +204,149 @@ def cpu_baseline(setup, budget_s=15.0):
                       f"oracle with OpenMP"}
 
 
+def _timed(fn, iters, flush=None):
+    """Average ms of fn() over iters calls, each preceded (outside the timed
+    window) by flush() when given; events on the current stream."""
+    import torch
+    total = 0.0
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+    return total / iters
+
+
+def measure_extras(args):
+    """The other configurations: attention on the Qwen3-4B shape, gather and
+    top-K attention on the Llama-3-8B shape, and the mixed-length churn step
+    (Trim / Reserve / commit on the host, trains, append, attention)."""
+    import torch
+    import non_uniform_paged_amd as nup
+    import workloads as W
+
+    res = {}
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(5)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def flush():
+        nup.probe_read(flush_buf, flush_buf.numel(), sink)
+
+    # -- Qwen3-4B-shaped layer: attention only, caches flushed between launches
+    w = W.qwen3_4b()
+    st = Setup(w, 8)
+    for _ in range(3):
+        st.step(append=False)
+    torch.cuda.synchronize()
+    nup.kernel_time(st.ctx, reset=True)
+    nup.set_timing(st.ctx, True)
+    ms = _timed(lambda: st.step(append=False), 20, flush)
+    nup.set_timing(st.ctx, False)
+    kms, n = nup.kernel_time(st.ctx, reset=True)
+    kms /= max(n, 1)
+    kb = algorithmic_bytes(st.lengths0, st.caps, w.batch, w.num_q_heads, w.num_kv_heads,
+                           w.num_groups) - w.batch * w.num_q_heads * w.head_dim * 4
+    res["qwen3_4b"] = {"kv_bytes": kv_bytes(st.lengths0), "attn_call_ms": round(ms, 4),
+                       "partial_kernel_ms": round(kms, 4),
+                       "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
+                       "note": "cold: 1 GiB read between launches"}
+    st.free()
+    del st
+
+    # -- Llama-3-8B top-K: index gather into staging, then attention over it
+    w = W.llama3_8b_topk()
+    st = Setup(w, 0)
+    K = w.topk
+    idx = torch.from_numpy(W.topk_indices(w.lengths, K)).cuda()
+    ks = torch.empty((w.batch, 8, K, 128), dtype=torch.bfloat16, device="cuda")
+    vs = torch.empty_like(ks)
+    ws = torch.empty(nup.workspace_bytes(st.ctx, K), dtype=torch.uint8, device="cuda")
+    gather = lambda: nup.kv_gather_compact(st.ctx, 1, ks, vs, idx=idx, K=K)
+    topk = lambda: nup.attn_decode_topk(st.ctx, st.q, ks, vs, K, st.out, st.lse, st.scale, ws)
+    for _ in range(3):
+        gather()
+        topk()
+    rows = w.batch * 8 * K
+    g_ms = _timed(gather, 20, flush)
+    t_ms = _timed(topk, 20, flush)
+    both32 = _timed(lambda: [f() for _ in range(32) for f in (gather, topk)], 3) / 32
+    gb = rows * 512 * 2 + rows * 4
+    tb = rows * 512 + w.batch * 32 * 128 * (2 + 4)
+    res["llama3_8b_topk"] = {
+        "gather_ms": round(g_ms, 4), "gather_GBs": round(gb / (g_ms * 1e-3) / 1e9, 1),
+        "topk_attn_ms": round(t_ms, 4), "topk_attn_GBs": round(tb / (t_ms * 1e-3) / 1e9, 1),
+        "gather_plus_attn_ms_32_back_to_back": round(both32, 4),
+        "note": "per call cold (1 GiB read before each); 32 back-to-back pairs for a 32-layer stack"}
+    assert nup.device_errors(st.ctx) == nup.NUP_OK
+    st.free()
+    del st, ks, vs, ws
+
+    # -- mixed-length churn: 10% EOS per step, freed slots refilled next step
+    w = W.mixed_churn()
+    steps_warm, steps = 20, 20
+    pad_steps = steps_warm + steps + 4
+    st = Setup(w, pad_steps, max_pages=int(math.ceil((131072 + 16 * math.ceil((pad_steps + 1) / 16)) / 16)))
+    drv = W.ChurnDriver(w.batch)
+    active = np.ones(w.batch, bool)
+    freed = np.zeros(0, np.int32)
+    host_us, trains, attn_ms = [], [], []
+    nup.kernel_time(st.ctx, reset=True)
+    for it in range(steps_warm + steps):
+        t0 = time.perf_counter()
+        if len(freed):
+            L = drv.refill_lengths(len(freed))
+            Ls = np.repeat(L[:, None], 8, axis=1).astype(np.int32)
+            nup.kv_alloc_groups(st.ctx, freed, Ls + st.pad, Ls)
+            active[freed] = True
+        eos = drv.eos(np.nonzero(active)[0])
+        nup.kv_free_seqs(st.ctx, eos)
+        active[eos] = False
+        freed = eos
+        nup.nup_commit(st.ctx)
+        t1 = time.perf_counter()
+        timed = it >= steps_warm
+        if timed:
+            host_us.append((t1 - t0) * 1e6)
+            trains.append(len(nup.get_runs(st.ctx)))
+            nup.set_timing(st.ctx, True)
+        nup.kv_append(st.ctx, st.k_new, st.v_new)
+        nup.attn_decode_nonuniform(st.ctx, st.q, st.out, st.lse, st.scale, st.ws)
+        if timed:
+            nup.set_timing(st.ctx, False)
+        torch.cuda.synchronize()
+    kms, n = nup.kernel_time(st.ctx, reset=True)
+    kms /= max(n, 1)
+    L_now = nup.get_lengths(st.ctx)
+    kb = kv_bytes(L_now)
+    # train-mode gather of the final state
+    lens = L_now.astype(np.int64).reshape(-1)
+    row_off = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)[:-1]])).cuda()
+    total = int(lens.sum())
+    ksg = torch.empty((total, 128), dtype=torch.bfloat16, device="cuda")
+    vsg = torch.empty_like(ksg)
+    gt = lambda: nup.kv_gather_compact(st.ctx, 0, ksg, vsg, row_off=row_off)
+    gt()
+    g_ms = _timed(gt, 5, flush)
+    res["mixed_churn"] = {
+        "active_slots": int(active.sum()), "kv_bytes": kb,
+        "host_trim_reserve_commit_us_mean": round(float(np.mean(host_us)), 1),
+        "trains_per_step_mean": round(float(np.mean(trains)), 1),
+        "pages_in_use": int(st.num_pages - len(nup.get_free_list(st.ctx))),
+        "partial_kernel_ms": round(kms, 4),
+        "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
+        "gather_trains_ms": round(g_ms, 4),
+        "gather_trains_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1)}
+    st.free()
+    del st, ksg, vsg, flush_buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +354,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-controls", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other configurations (Qwen3-4B, Llama top-K, mixed churn)")
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
                     help="only run the plain streaming copy kernel over BYTES (counter "
@@ -289,6 +442,9 @@ def main():
     extra["read_ceiling_GBs"] = round(5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     extra["partial_over_read_ceiling"] = round(achieved / extra["read_ceiling_GBs"], 4)
     del buf
+
+    if not args.no_extras:
+        extra["configs"] = measure_extras(args)
 
     traffic = traffic_from_profiles(sha)
     line = {
