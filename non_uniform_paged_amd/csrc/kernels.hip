@@ -424,36 +424,64 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
 // ---------------------------------------------------------------------------
 // Gather, index mode: staging[s][h][k] = row of logical position idx[s][h][k].
+// A row is LPR = D/8 lanes of 16 bytes; a wave covers 64/LPR rows per pass
+// and makes kRowsPerLane passes, resolving all its rows' addresses first so
+// that 2*kRowsPerLane 16-byte loads (K and V) are in flight per lane.
 // ---------------------------------------------------------------------------
+constexpr int kRowsPerLane = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void gather_index_kernel(GatherIndexArgs a) {
     constexpr int LPR = D / 8;
-    constexpr int PER = 2 * LPR;
-    const int local = threadIdx.x / PER, sub = threadIdx.x % PER;
-    const long long gr = (long long)blockIdx.x * (256 / PER) + local;  // staging row
+    constexpr int RPP = 64 / LPR;                       // rows per pass of a wave
+    constexpr int RPW = RPP * kRowsPerLane;             // rows per wave
+    const int lane = threadIdx.x & 63;
+    const int piece = lane % LPR, sub = lane / LPR;
+    const long long wave = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     const long long nrows = (long long)a.bmax * a.hkv * a.k;
-    if (gr >= nrows) return;
-    const int sh = (int)(gr / a.k), kk = (int)(gr - (long long)sh * a.k);
-    const int s = sh / a.hkv, h = sh - s * a.hkv;
-    if (!a.active[s]) return;
-    const int t = a.idx[gr];
-    const int L = a.lengths[sh];
-    const bool bad = t < 0 || t >= L || (kk > 0 && a.idx[gr - 1] >= t);
-    const bool isv = sub >= LPR;
-    const int c = sub - (isv ? LPR : 0);
-    uint4 *dst = reinterpret_cast<uint4 *>((isv ? a.v_out : a.k_out) + (size_t)gr * D) + c;
-    if (bad) {
-        *dst = make_uint4(0, 0, 0, 0);
-        if (sub == 0) {
-            if (a.phys_out) a.phys_out[gr] = -1;
-            atomicOr(a.err, 1);
+    size_t src[kRowsPerLane];
+    long long gr[kRowsPerLane];
+    int state[kRowsPerLane];   // 0: skip, 1: copy, 2: bad index
+#pragma unroll
+    for (int u = 0; u < kRowsPerLane; ++u) {
+        gr[u] = wave * RPW + u * RPP + sub;
+        state[u] = 0;
+        src[u] = 0;
+        if (gr[u] >= nrows) continue;
+        const int sh = (int)(gr[u] / a.k), kk = (int)(gr[u] - (long long)sh * a.k);
+        const int s = sh / a.hkv, h = sh - s * a.hkv;
+        if (!a.active[s]) continue;
+        const int t = a.idx[gr[u]];
+        const int L = a.lengths[sh];
+        if (t < 0 || t >= L || (kk > 0 && a.idx[gr[u] - 1] >= t)) {
+            state[u] = 2;
+            continue;
         }
-        return;
+        const int pid = a.page_table[((size_t)a.group_of_head[h] * a.bmax + s) * a.max_pages + t / kPage];
+        src[u] = ((size_t)pid * a.gh + a.slot_of_head[h]) * kPage + t % kPage;
+        state[u] = 1;
     }
-    const int pid = a.page_table[((size_t)a.group_of_head[h] * a.bmax + s) * a.max_pages + t / kPage];
-    const size_t rowid = ((size_t)pid * a.gh + a.slot_of_head[h]) * kPage + t % kPage;
-    *dst = ld_stream(reinterpret_cast<const uint4 *>((isv ? a.v_pool : a.k_pool) + rowid * D) + c);
-    if (a.phys_out && sub == 0) a.phys_out[gr] = (int32_t)rowid;
+    uint4 kv[kRowsPerLane], vv[kRowsPerLane];
+#pragma unroll
+    for (int u = 0; u < kRowsPerLane; ++u) {
+        if (state[u] == 1) {
+            kv[u] = ld_stream(reinterpret_cast<const uint4 *>(a.k_pool + src[u] * D) + piece);
+            vv[u] = ld_stream(reinterpret_cast<const uint4 *>(a.v_pool + src[u] * D) + piece);
+        } else {
+            kv[u] = make_uint4(0, 0, 0, 0);
+            vv[u] = make_uint4(0, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsPerLane; ++u) {
+        if (state[u] == 0) continue;
+        reinterpret_cast<uint4 *>(a.k_out + (size_t)gr[u] * D)[piece] = kv[u];
+        reinterpret_cast<uint4 *>(a.v_out + (size_t)gr[u] * D)[piece] = vv[u];
+        if (piece == 0) {
+            if (a.phys_out) a.phys_out[gr[u]] = state[u] == 1 ? (int32_t)src[u] : -1;
+            if (state[u] == 2) atomicOr(a.err, 1);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -621,9 +649,9 @@ hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t st) {
 }
 
 hipError_t launch_gather_index(const GatherIndexArgs &a, int head_dim, hipStream_t st) {
-    const int per = 2 * (head_dim / 8);
+    const long long rows_per_block = (long long)kWavesPerBlock * (64 / (head_dim / 8)) * kRowsPerLane;
     const long long n = (long long)a.bmax * a.hkv * a.k;
-    const long long blocks = (n + 256 / per - 1) / (256 / per);
+    const long long blocks = (n + rows_per_block - 1) / rows_per_block;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     GatherIndexArgs copy = a;
