@@ -283,6 +283,7 @@ void partial_attn_kernel(PartialArgs a) {
             __builtin_amdgcn_wave_barrier();
         };
 
+#if NUP_PREFETCH == 2
         // Two page buffers: page p+1 is in flight while page p is computed.
         uint4 kA[NJ], vA[TPL], kB[NJ], vB[TPL];
         load(p0, page_base(p0), kA, vA);
@@ -293,6 +294,25 @@ void partial_attn_kernel(PartialArgs a) {
             if (p + 2 <= p1) load(p + 2, page_base(p + 2), kA, vA);
             compute(p + 1, kB, vB);
         }
+#else
+        // Ring of kDepth page buffers: pages p+1 .. p+kDepth-1 are in flight
+        // while page p is computed.
+        uint4 kb[kDepth][NJ], vb[kDepth][TPL];
+#pragma unroll
+        for (int k = 0; k + 1 < kDepth; ++k)
+            if (p0 + k <= p1) load(p0 + k, page_base(p0 + k), kb[k], vb[k]);
+        for (int pb = p0; pb <= p1; pb += kDepth) {
+#pragma unroll
+            for (int k = 0; k < kDepth; ++k) {
+                const int p = pb + k;
+                if (p <= p1) {
+                    const int pf = p + kDepth - 1;
+                    if (pf <= p1) load(pf, page_base(pf), kb[(k + kDepth - 1) % kDepth], vb[(k + kDepth - 1) % kDepth]);
+                    compute(p, kb[k], vb[k]);
+                }
+            }
+        }
+#endif
 
         // Combine: the row sums over the four token quads, the outputs over
         // the token groups of V.
@@ -366,25 +386,35 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         re = rb + a.uniform_splits;
     }
     if (re - rb <= 1) return;   // a head of one row was written by the partial kernel
-    float M = -INFINITY;
-    for (int i = rb; i < re; ++i) M = fmaxf(M, a.ws_ml[((size_t)i * GQA + r) * 2]);
-    float L = 0.f, acc[NJ];
+    // One online pass over the head's rows, eight at a time: all loads of a
+    // batch are issued before any is used, so a batch costs one round trip.
+    constexpr int kBatch = 8;
+    float M = -INFINITY, L = 0.f, acc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 4
-        for (int i = rb; i < re; ++i) {
-            const float mi = a.ws_ml[((size_t)i * GQA + r) * 2];
-            const float li = a.ws_ml[((size_t)i * GQA + r) * 2 + 1];
-            const float wgt = (mi == -INFINITY) ? 0.f : exp2f(mi - M);
-            L = fmaf(wgt, li, L);
-            const float *oi = a.ws_o + ((size_t)i * GQA + r) * D;
+    for (int b = rb; b < re; b += kBatch) {
+        float mi[kBatch], li[kBatch], ov[kBatch][NJ];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                // rows with no tokens carry no o; skip their (unwritten) values
-                const float ov = (mi == -INFINITY) ? 0.f : oi[lane + 64 * j];
-                acc[j] = fmaf(wgt, ov, acc[j]);
-            }
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = b + u;
+            const bool ok = i < re;
+            const size_t mo = ((size_t)(ok ? i : rb) * GQA + r) * 2;
+            mi[u] = ok ? a.ws_ml[mo] : -INFINITY;
+            li[u] = a.ws_ml[mo + 1];
+            const float *oi = a.ws_o + ((size_t)(ok ? i : rb) * GQA + r) * D;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ov[u][j] = oi[lane + 64 * j];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (mi[u] == -INFINITY) continue;   // no tokens (or past the end): no o to read
+            const float Mn = fmaxf(M, mi[u]);
+            const float sc = exp2f(M - Mn);     // 0 while M is -inf
+            const float wg = exp2f(mi[u] - Mn);
+            L = fmaf(L, sc, wg * li[u]);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[j] = fmaf(acc[j], sc, wg * ov[u][j]);
+            M = Mn;
         }
     }
     const size_t qr = (size_t)s * a.hkv * GQA + (size_t)h * GQA + r;
