@@ -113,6 +113,10 @@ struct nup_ctx {
     std::vector<int32_t> goh, soh, head_of_gslot;
     bool grouped = false;
 
+    // trains of each page-table row, rebuilt only for rows that changed
+    std::vector<std::vector<int32_t>> row_runs;  // [ng*B]: (phys, pages, logical) triples
+    std::vector<uint8_t> runs_stale;             // [ng*B]
+
     // edits since the last commit
     std::vector<int32_t> dirty_count;  // [ng*B]: page-table entries to send, 0 = clean
     bool plan_dirty = true;
@@ -300,21 +304,32 @@ void replan(nup_ctx *c) {
 }
 
 // ---- trains (KV-RM, Fig 3) --------------------------------------------------
-// Appends (slot, group, first physical page, pages, first logical page).
-void build_runs(const nup_ctx *c, std::vector<int32_t> &out) {
+// Maximal runs of physically consecutive pages in one page-table row.
+void row_trains(const int32_t *row, int n, std::vector<int32_t> &out) {
+    out.clear();
+    int i = 0;
+    while (i < n) {
+        const int start = i;
+        while (i + 1 < n && row[i + 1] == row[i] + 1) ++i;
+        out.insert(out.end(), {row[start], i - start + 1, start});
+        ++i;
+    }
+}
+
+// Appends (slot, group, first physical page, pages, first logical page) for
+// every active slot in (slot, group, logical page) order.
+void build_runs(nup_ctx *c, std::vector<int32_t> &out) {
     out.clear();
     for (int s = 0; s < c->B; ++s) {
         if (!c->active[s]) continue;
         for (int g = 0; g < c->ng; ++g) {
-            const int32_t *row = &c->pt[((size_t)g * c->B + s) * c->max_pages];
-            const int n = c->npages[(size_t)g * c->B + s];
-            int i = 0;
-            while (i < n) {
-                const int start = i;
-                while (i + 1 < n && row[i + 1] == row[i] + 1) ++i;
-                out.insert(out.end(), {s, g, row[start], i - start + 1, start});
-                ++i;
+            const size_t ri = (size_t)g * c->B + s;
+            if (c->runs_stale[ri]) {
+                row_trains(&c->pt[ri * c->max_pages], c->npages[ri], c->row_runs[ri]);
+                c->runs_stale[ri] = 0;
             }
+            const std::vector<int32_t> &rr = c->row_runs[ri];
+            for (size_t k = 0; k < rr.size(); k += 3) out.insert(out.end(), {s, g, rr[k], rr[k + 1], rr[k + 2]});
         }
     }
 }
@@ -413,6 +428,8 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
     c->soh.assign(c->H, -1);
     c->head_of_gslot.assign(c->H, -1);
     c->dirty_count.assign((size_t)c->ng * c->B, 0);
+    c->row_runs.assign((size_t)c->ng * c->B, {});
+    c->runs_stale.assign((size_t)c->ng * c->B, 0);
     replan(c);
     *out = c;
     return NUP_OK;
@@ -499,6 +516,7 @@ nup_status kv_alloc_groups(nup_ctx *c, int32_t n, const int32_t *slots, const in
             const size_t ri = (size_t)g * c->B + s;
             c->dirty_count[ri] = std::max(c->dirty_count[ri], np);
             c->npages[ri] = np;
+            c->runs_stale[ri] = 1;
         }
         for (int h = 0; h < c->H; ++h) {
             c->cap[(size_t)s * c->H + h] = cap[(size_t)i * c->H + h];
@@ -536,6 +554,7 @@ nup_status kv_free_seqs(nup_ctx *c, int32_t n, const int32_t *slots) {
             }
             c->dirty_count[ri] = std::max(c->dirty_count[ri], c->npages[ri]);
             c->npages[ri] = 0;
+            c->runs_stale[ri] = 1;
         }
         for (int h = 0; h < c->H; ++h) {
             c->cap[(size_t)s * c->H + h] = 0;
@@ -901,7 +920,7 @@ nup_status nup_get_free_list(const nup_ctx *c, int32_t *out, int32_t *n) {
 nup_status nup_get_runs(const nup_ctx *c, int32_t *out, int32_t max_runs, int32_t *n) {
     if (!c || !n) return NUP_E_ARG;
     std::vector<int32_t> runs;
-    build_runs(c, runs);
+    build_runs(const_cast<nup_ctx *>(c), runs);  // refreshes the per-row cache only
     *n = (int32_t)(runs.size() / 5);
     if (!out) return NUP_OK;
     if (*n > max_runs) return NUP_E_ARG;
