@@ -268,19 +268,26 @@ def measure_extras(args):
     ws = torch.empty(nup.workspace_bytes(st.ctx, K), dtype=torch.uint8, device="cuda")
     gather = lambda: nup.kv_gather_compact(st.ctx, 1, ks, vs, idx=idx, K=K)
     topk = lambda: nup.attn_decode_topk(st.ctx, st.q, ks, vs, K, st.out, st.lse, st.scale, ws)
+    fused = lambda: nup.attn_decode_topk_paged(st.ctx, st.q, idx, K, st.out, st.lse, st.scale, ws)
     for _ in range(3):
         gather()
         topk()
+        fused()
     rows = w.batch * 8 * K
     g_ms = _timed(gather, 20, flush)
     t_ms = _timed(topk, 20, flush)
+    f_ms = _timed(fused, 20, flush)
     both32 = _timed(lambda: [f() for _ in range(32) for f in (gather, topk)], 3) / 32
+    fused32 = _timed(lambda: [fused() for _ in range(32)], 3) / 32
     gb = rows * 512 * 2 + rows * 4
     tb = rows * 512 + w.batch * 32 * 128 * (2 + 4)
     res["llama3_8b_topk"] = {
         "gather_ms": round(g_ms, 4), "gather_GBs": round(gb / (g_ms * 1e-3) / 1e9, 1),
         "topk_attn_ms": round(t_ms, 4), "topk_attn_GBs": round(tb / (t_ms * 1e-3) / 1e9, 1),
         "gather_plus_attn_ms_32_back_to_back": round(both32, 4),
+        "topk_in_place_ms": round(f_ms, 4),
+        "topk_in_place_GBs": round((rows * (512 + 4) + w.batch * 32 * 128 * 6) / (f_ms * 1e-3) / 1e9, 1),
+        "topk_in_place_ms_32_back_to_back": round(fused32, 4),
         "note": "per call cold (1 GiB read before each); 32 back-to-back pairs for a 32-layer stack"}
     assert nup.device_errors(st.ctx) == nup.NUP_OK
     st.free()

@@ -214,6 +214,23 @@ nup_status attn_decode_topk(nup_ctx *ctx, const void *q, const void *k_stage,
                             const void *v_stage, int32_t K, float *out, float *lse,
                             float scale, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * attn_decode_topk_paged -- the same attention as attn_decode_topk, read in
+ * place: each of the K entries of an active (slot, KV head) is taken from the
+ * paged pool through its logical position and the head group's page table,
+ * with no staging copy (KVDrive, Fig 1: attention over the fetched critical
+ * entries; here the fetch and the attention are one pass over HBM).
+ *   idx      device int32 [B_max][H_kv][K]: logical positions, ascending,
+ *            distinct, 0 <= idx < L (as for kv_gather_compact mode 1)
+ *   out / lse / scale / workspace as for attn_decode_topk (workspace >=
+ *   nup_workspace_bytes(ctx, K)).
+ * An entry outside 0..L-1 is not read: it is left out of the softmax and
+ * NUP_E_INDEX is latched for nup_device_errors(); an out-of-order entry is
+ * read but also latched.  Errors: NUP_E_ARG, NUP_E_STATE, NUP_E_HIP. */
+nup_status attn_decode_topk_paged(nup_ctx *ctx, const void *q, const int32_t *idx, int32_t K,
+                                  float *out, float *lse, float scale, void *workspace,
+                                  size_t ws_bytes, void *stream);
+
 /* ---- host-side queries (no device call; for tests and reports) ---------- */
 
 /* Shadow page table int32 [n_g][B_max][max_pages]. */

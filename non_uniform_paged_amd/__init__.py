@@ -62,6 +62,7 @@ _sigs = {
     "nup_workspace_bytes": [_P, _I, _P],
     "attn_decode_nonuniform": [_P, _P, _P, _P, ctypes.c_float, _P, _S, _P],
     "attn_decode_topk": [_P, _P, _P, _P, _I, _P, _P, ctypes.c_float, _P, _S, _P],
+    "attn_decode_topk_paged": [_P, _P, _P, _I, _P, _P, ctypes.c_float, _P, _S, _P],
     "nup_get_page_table": [_P, _P],
     "nup_get_lengths": [_P, _P],
     "nup_get_groups": [_P, _P, _P],
@@ -221,6 +222,14 @@ def attn_decode_topk(ctx: Context, q, k_stage, v_stage, K: int, out, lse, scale:
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib.attn_decode_topk(ctx.handle, _ptr(q), _ptr(k_stage), _ptr(v_stage), K, _ptr(out),
                                _ptr(lse), float(scale), _ptr(workspace), nbytes, _stream(stream))
+    return ctx.check(st) if raise_on_error else st
+
+
+def attn_decode_topk_paged(ctx: Context, q, idx, K: int, out, lse, scale: float, workspace,
+                           stream=None, raise_on_error=True):
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.attn_decode_topk_paged(ctx.handle, _ptr(q), _ptr(idx), K, _ptr(out), _ptr(lse),
+                                     float(scale), _ptr(workspace), nbytes, _stream(stream))
     return ctx.check(st) if raise_on_error else st
 
 

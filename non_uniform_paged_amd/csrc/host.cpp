@@ -400,7 +400,7 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
             fprintf(stderr, "nup_create: no HIP device for a device context\n");
             return NUP_E_HIP;
         }
-        const int nb = nup::partial_blocks_per_cu(c->D, c->gqa, false);
+        const int nb = nup::partial_blocks_per_cu(c->D, c->gqa, nup::kModePaged);
         c->workers = prop.multiProcessorCount * std::max(1, nb) * nup::kWavesPerBlock;
     }
     c->sz = compute_sizes(c->cfg, c->workers);
@@ -780,6 +780,7 @@ static void topk_split(const nup_ctx *c, int K, int *splits, int *chunk) {
     const int pages = (K + nup::kPage - 1) / nup::kPage;
     const int target = std::max(1, c->workers / 2);
     int S = std::max(1, (target + heads - 1) / heads);
+    S = std::max(S, (K + nup::kMaxTopkChunk - 1) / nup::kMaxTopkChunk);  // chunk <= LDS row-id room
     S = std::min(S, pages);
     const int ch = nup::kPage * ((pages + S - 1) / S);
     S = (K + ch - 1) / ch;
@@ -802,7 +803,9 @@ nup_status nup_workspace_bytes(const nup_ctx *c, int32_t K, size_t *bytes) {
 }
 
 static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse, float scale, void *ws,
-                              size_t ws_bytes, void *stream, bool topk, const void *ks, const void *vs, int K) {
+                              size_t ws_bytes, void *stream, int mode, const void *ks, const void *vs,
+                              const int32_t *idx, int K) {
+    const bool topk = mode != nup::kModePaged;
     if (!c) return NUP_E_ARG;
     if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
     if (!c->committed) return fail(c, NUP_E_STATE, "no committed descriptor");
@@ -828,8 +831,16 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
     if (topk) {
         int ch;
         topk_split(c, K, &splits, &ch);
-        a.kbase = static_cast<const uint16_t *>(ks);
-        a.vbase = static_cast<const uint16_t *>(vs);
+        if (mode == nup::kModeStaged) {
+            a.kbase = static_cast<const uint16_t *>(ks);
+            a.vbase = static_cast<const uint16_t *>(vs);
+        } else {
+            a.kbase = c->kpool;
+            a.vbase = c->vpool;
+            a.page_table = c->d_pt();
+            a.idx = idx;
+            a.err = c->d_err();
+        }
         a.topk_k = K;
         a.topk_splits = splits;
         a.topk_chunk = ch;
@@ -859,7 +870,7 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
             return hip_fail(c, e, "hipEventCreate");
         if ((e = hipEventRecord(e0, st)) != hipSuccess) return hip_fail(c, e, "hipEventRecord");
     }
-    e = nup::launch_partial(a, c->D, c->gqa, topk, st);
+    e = nup::launch_partial(a, c->D, c->gqa, mode, st);
     if (e != hipSuccess) return hip_fail(c, e, "partial attention launch");
     if (c->timing) {
         if ((e = hipEventRecord(e1, st)) != hipSuccess) return hip_fail(c, e, "hipEventRecord");
@@ -880,7 +891,8 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
 
 nup_status attn_decode_nonuniform(nup_ctx *c, const void *q, float *out, float *lse, float scale,
                                   void *workspace, size_t ws_bytes, void *stream) {
-    return attn_common(c, q, out, lse, scale, workspace, ws_bytes, stream, false, nullptr, nullptr, 0);
+    return attn_common(c, q, out, lse, scale, workspace, ws_bytes, stream, nup::kModePaged, nullptr,
+                       nullptr, nullptr, 0);
 }
 
 nup_status attn_decode_topk(nup_ctx *c, const void *q, const void *k_stage, const void *v_stage, int32_t K,
@@ -888,7 +900,16 @@ nup_status attn_decode_topk(nup_ctx *c, const void *q, const void *k_stage, cons
                             void *stream) {
     if (!c) return NUP_E_ARG;
     if (K <= 0 || !k_stage || !v_stage) return fail(c, NUP_E_ARG, "top-K needs K > 0 and staging buffers");
-    return attn_common(c, q, out, lse, scale, workspace, ws_bytes, stream, true, k_stage, v_stage, K);
+    return attn_common(c, q, out, lse, scale, workspace, ws_bytes, stream, nup::kModeStaged, k_stage,
+                       v_stage, nullptr, K);
+}
+
+nup_status attn_decode_topk_paged(nup_ctx *c, const void *q, const int32_t *idx, int32_t K, float *out,
+                                  float *lse, float scale, void *workspace, size_t ws_bytes, void *stream) {
+    if (!c) return NUP_E_ARG;
+    if (K <= 0 || !idx) return fail(c, NUP_E_ARG, "top-K needs K > 0 and an index list");
+    return attn_common(c, q, out, lse, scale, workspace, ws_bytes, stream, nup::kModeIndexed, nullptr,
+                       nullptr, idx, K);
 }
 
 nup_status nup_get_page_table(const nup_ctx *c, int32_t *out) {

@@ -9,6 +9,12 @@ namespace nup {
 constexpr int kPage = 16;           // tokens per page
 constexpr int kWavesPerBlock = 4;   // split-K workers per 256-thread workgroup
 
+// Where the partial kernel reads K/V from.
+constexpr int kModePaged = 0;     // pool through the page tables, plan rows
+constexpr int kModeStaged = 1;    // contiguous staging [Bmax*Hkv][K][D], equal split
+constexpr int kModeIndexed = 2;   // pool rows named by top-K indices, equal split
+constexpr int kMaxTopkChunk = 2048;  // entries per top-K worker (LDS row ids)
+
 // Split-K decode attention.  One wave is one worker.  In table mode a
 // worker walks rows[worker_start[w] .. worker_start[w+1]) of (head, t0, t1);
 // in top-K mode worker w takes chunk w % splits of head w / splits of a
@@ -26,6 +32,8 @@ struct PartialArgs {
     const int32_t *slot_of_head;
     const int32_t *rows;        // [n][4] (sh, t0, t1, 0) (paged)
     const int32_t *worker_start;// [W+1] (paged)
+    const int32_t *idx;         // [Bmax*Hkv][K] logical positions (indexed top-K)
+    int32_t *err;               // latched error word (indexed top-K)
     const int32_t *head_row_start; // [Bmax*Hkv+1] (paged); top-K rows of head sh are sh*splits..
     float *ws_o;                // [rows][gqa][D]
     float *ws_ml;               // [rows][gqa][2]  (max in log2 units, sum)
@@ -77,9 +85,9 @@ struct GatherRunsArgs {
 };
 
 bool supported_shape(int head_dim, int gqa);
-int partial_blocks_per_cu(int head_dim, int gqa, bool topk);
+int partial_blocks_per_cu(int head_dim, int gqa, int mode);
 
-hipError_t launch_partial(const PartialArgs &a, int head_dim, int gqa, bool topk, hipStream_t st);
+hipError_t launch_partial(const PartialArgs &a, int head_dim, int gqa, int mode, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, int head_dim, int gqa, int n_heads, hipStream_t st);
 hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t st);
 hipError_t launch_gather_index(const GatherIndexArgs &a, int head_dim, hipStream_t st);

@@ -93,7 +93,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // lane as acc[r][j] for dims lane + 64 j), lse in natural log.  With o == NULL
 // (no tokens) writes zeros and lse = -inf.
 template <int D, int GQA>
-__device__ __forceinline__ void write_final(const PartialArgs &a, size_t qh0, int lane, float, float,
+__device__ __forceinline__ void write_final(const PartialArgs &a, size_t qh0, int lane,
                                             const float (*acc)[D / 64]) {
     constexpr int NJ = D / 64;
 #pragma unroll
@@ -103,9 +103,10 @@ __device__ __forceinline__ void write_final(const PartialArgs &a, size_t qh0, in
     if (!acc && a.lse && lane < GQA) a.lse[qh0 + lane] = -INFINITY;
 }
 
-template <int D, int GQA, bool TOPK>
+template <int D, int GQA, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NUP_WAVES_PER_EU, 8)))
 void partial_attn_kernel(PartialArgs a) {
+    constexpr bool TOPK = MODE != kModePaged;   // equal split of K entries per head
     constexpr int NJ = D / 32;     // MFMA steps over the head dim
     constexpr int LPR = D / 8;     // lanes per V row (16-byte pieces)
     constexpr int TPL = LPR / 4;   // tokens per lane for V
@@ -116,6 +117,8 @@ void partial_attn_kernel(PartialArgs a) {
     // writes of the five-plus rows land in distinct LDS banks
     __shared__ float4 p_lds[kWavesPerBlock][8][5];
     __shared__ float alpha_lds[kWavesPerBlock][16];   // rescale factors; final 1/l, lse
+    // indexed top-K: the pool row of every entry of the worker's chunk (-1: not readable)
+    __shared__ int32_t rid_lds[kWavesPerBlock][MODE == kModeIndexed ? kMaxTopkChunk : 1];
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -123,6 +126,7 @@ void partial_attn_kernel(PartialArgs a) {
     if (w >= a.n_workers) return;
     float *pl = reinterpret_cast<float *>(p_lds[wid]);
     float *al = alpha_lds[wid];
+    int32_t *rl = rid_lds[wid];
 
     // MFMA-side coordinates
     const int qn = lane & 15;       // query row (column of S^T)
@@ -143,8 +147,8 @@ void partial_attn_kernel(PartialArgs a) {
         if (TOPK) {
             sh = row / a.topk_splits;
             t0 = (row - sh * a.topk_splits) * a.topk_chunk;
-            const int L = ld_uniform(a.active + sh / a.hkv) ? a.topk_k : 0;
-            t1 = min(t0 + a.topk_chunk, L);
+            const int n = ld_uniform(a.active + sh / a.hkv) ? a.topk_k : 0;
+            t1 = min(t0 + a.topk_chunk, n);
         } else {
             sh = ld_uniform(a.rows + row * 4 + 0);
             t0 = ld_uniform(a.rows + row * 4 + 1);
@@ -163,7 +167,7 @@ void partial_attn_kernel(PartialArgs a) {
         const size_t qh0 = (size_t)s * a.hkv * GQA + (size_t)h * GQA;   // first query head
         if (t0 >= t1) {
             if (nrows == 1) {
-                write_final<D, GQA>(a, qh0, lane, 0.f, -INFINITY, nullptr);
+                write_final<D, GQA>(a, qh0, lane, nullptr);
             } else {
                 if (lane < GQA) {
                     ml[lane * 2 + 0] = -INFINITY;
@@ -193,15 +197,39 @@ void partial_attn_kernel(PartialArgs a) {
 
         const int32_t *ptrow = nullptr;
         size_t slot_off = 0;
-        if (!TOPK) {
+        if (MODE != kModeStaged) {
             ptrow = a.page_table + ((size_t)ld_uniform(a.group_of_head + h) * a.bmax + s) * (size_t)a.max_pages;
             slot_off = (size_t)ld_uniform(a.slot_of_head + h) * kPage * D;
         }
-        const size_t head_base = TOPK ? (size_t)sh * a.topk_k * D : 0;
+        const size_t head_base = MODE == kModeStaged ? (size_t)sh * a.topk_k * D : 0;
         const int p0 = t0 / kPage, p1 = (t1 - 1) / kPage;  // inclusive page range
 
+        if (MODE == kModeIndexed) {
+            // Resolve the chunk's entries to pool rows before streaming: index
+            // -> page table -> row.  Entries outside 0..L-1 are masked and not
+            // read; entries out of order are read but flagged.  Either latches
+            // the error word.
+            const int32_t *il = a.idx + (size_t)sh * a.topk_k;
+            const int L = ld_uniform(a.lengths + sh);
+            const int slot = ld_uniform(a.slot_of_head + h);
+            bool bad = false;
+            for (int e = t0 + lane; e < t1; e += 64) {
+                const int t = il[e];
+                const bool in_range = t >= 0 && t < L;
+                int rid = -1;
+                if (in_range) rid = (ptrow[t / kPage] * a.gh + slot) * kPage + t % kPage;
+                bad |= !in_range || (e > 0 && il[e - 1] >= t);
+                rl[e - t0] = rid;
+            }
+            if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(a.err, 1);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+
         auto page_base = [&](int pi) -> size_t {
-            if (TOPK) return head_base + (size_t)pi * kPage * D;
+            if (MODE == kModeStaged) return head_base + (size_t)pi * kPage * D;
+            if (MODE == kModeIndexed) return 0;
             return (size_t)ld_uniform(ptrow + pi) * a.gh * kPage * D + slot_off;
         };
         // Lane offsets (in 16-byte pieces) inside a head's 16-row block; rows
@@ -210,6 +238,19 @@ void partial_attn_kernel(PartialArgs a) {
         // 32-bit lane offset.
         auto load = [&](int pi, size_t base, uint4 (&k)[NJ], uint4 (&v)[TPL]) {
             const int last = t1 - 1 - pi * kPage;
+            if (MODE == kModeIndexed) {
+                // each row from its own resolved pool row (masked rows read row 0)
+                const int rk = max(rl[pi * kPage + min(qn, last) - t0], 0);
+                const uint4 *kp = reinterpret_cast<const uint4 *>(a.kbase + (size_t)rk * D);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) k[j] = ld_stream(kp + qg + 4 * j);
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    const int rv = max(rl[pi * kPage + min(tg * TPL + i, last) - t0], 0);
+                    v[i] = ld_stream(reinterpret_cast<const uint4 *>(a.vbase + (size_t)rv * D) + ve);
+                }
+                return;
+            }
             const uint4 *kp = reinterpret_cast<const uint4 *>(a.kbase + base);
             const uint4 *vp = reinterpret_cast<const uint4 *>(a.vbase + base);
             const uint32_t koff = (uint32_t)min(qn, last) * (D / 8) + qg;
@@ -231,7 +272,11 @@ void partial_attn_kernel(PartialArgs a) {
             const int tbase = pi * kPage + 4 * qg;
             float sc[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[i] = (tbase + i < t1) ? acc[i] * a.scale_log2 : -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+                bool ok = tbase + i < t1;
+                if (MODE == kModeIndexed && ok) ok = rl[tbase + i - t0] >= 0;
+                sc[i] = ok ? acc[i] * a.scale_log2 : -INFINITY;
+            }
             float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -597,24 +642,34 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const uint4 *src, uint3
     if (x == 0x9e3779b9u) sink[0] = x;  // keeps the loads; practically never stores
 }
 
-template <int D, int GQA, bool TOPK>
-void *partial_fn() { return reinterpret_cast<void *>(&partial_attn_kernel<D, GQA, TOPK>); }
+template <int D, int GQA, int MODE>
+void *partial_fn() { return reinterpret_cast<void *>(&partial_attn_kernel<D, GQA, MODE>); }
 
-template <int D, bool TOPK>
+template <int D, int MODE>
 void *partial_fn_gqa(int gqa) {
     switch (gqa) {
-        case 1: return partial_fn<D, 1, TOPK>();
-        case 2: return partial_fn<D, 2, TOPK>();
-        case 4: return partial_fn<D, 4, TOPK>();
-        case 5: return partial_fn<D, 5, TOPK>();
-        case 8: return partial_fn<D, 8, TOPK>();
+        case 1: return partial_fn<D, 1, MODE>();
+        case 2: return partial_fn<D, 2, MODE>();
+        case 4: return partial_fn<D, 4, MODE>();
+        case 5: return partial_fn<D, 5, MODE>();
+        case 8: return partial_fn<D, 8, MODE>();
         default: return nullptr;
     }
 }
 
-void *partial_ptr(int d, int gqa, bool topk) {
-    if (d == 64) return topk ? partial_fn_gqa<64, true>(gqa) : partial_fn_gqa<64, false>(gqa);
-    if (d == 128) return topk ? partial_fn_gqa<128, true>(gqa) : partial_fn_gqa<128, false>(gqa);
+template <int D>
+void *partial_fn_mode(int gqa, int mode) {
+    switch (mode) {
+        case kModePaged: return partial_fn_gqa<D, kModePaged>(gqa);
+        case kModeStaged: return partial_fn_gqa<D, kModeStaged>(gqa);
+        case kModeIndexed: return partial_fn_gqa<D, kModeIndexed>(gqa);
+        default: return nullptr;
+    }
+}
+
+void *partial_ptr(int d, int gqa, int mode) {
+    if (d == 64) return partial_fn_mode<64>(gqa, mode);
+    if (d == 128) return partial_fn_mode<128>(gqa, mode);
     return nullptr;
 }
 
@@ -639,18 +694,18 @@ hipError_t launch_raw(void *fn, dim3 grid, dim3 block, void *arg, size_t arg_siz
 
 }  // namespace
 
-bool supported_shape(int head_dim, int gqa) { return partial_ptr(head_dim, gqa, false) != nullptr; }
+bool supported_shape(int head_dim, int gqa) { return partial_ptr(head_dim, gqa, kModePaged) != nullptr; }
 
-int partial_blocks_per_cu(int head_dim, int gqa, bool topk) {
-    void *fn = partial_ptr(head_dim, gqa, topk);
+int partial_blocks_per_cu(int head_dim, int gqa, int mode) {
+    void *fn = partial_ptr(head_dim, gqa, mode);
     if (!fn) return 0;
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, 0) != hipSuccess) return 0;
     return nb;
 }
 
-hipError_t launch_partial(const PartialArgs &a, int head_dim, int gqa, bool topk, hipStream_t st) {
-    void *fn = partial_ptr(head_dim, gqa, topk);
+hipError_t launch_partial(const PartialArgs &a, int head_dim, int gqa, int mode, hipStream_t st) {
+    void *fn = partial_ptr(head_dim, gqa, mode);
     if (!fn) return hipErrorInvalidValue;
     if (a.n_workers <= 0) return hipSuccess;
     const unsigned blocks = (unsigned)((a.n_workers + kWavesPerBlock - 1) / kWavesPerBlock);

@@ -454,3 +454,85 @@ def test_repeated_launches_bit_identical():
         nup.attn_decode_topk(c.ctx, c.q, ks.view(torch.bfloat16), vs.view(torch.bfloat16), K,
                              c.out, c.lse, c.scale, ws_k)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("K,gqa,ng,seed", [(96, 4, 1, 30), (37, 5, 2, 31), (16, 1, 4, 32), (1, 8, 2, 33)])
+def test_topk_paged_matches_oracle(K, gqa, ng, seed):
+    """Top-K attention read in place through indices and page tables."""
+    c, L, caps = _gather_case(seed, B=3, H=8, gqa=gqa, ng=ng)
+    c.alloc([0, 2], caps[[0, 2]], L[[0, 2]])      # slot 1 inactive
+    c.commit()
+    lens = np.where(c.spec.active[:, None], c.spec.lengths, 300)
+    idx = W.topk_indices(lens, max(K, 2), salt=seed)[..., :K].copy()
+    idx.sort(axis=-1)
+    ws = torch.empty(nup.workspace_bytes(c.ctx, K), dtype=torch.uint8, device=DEV)
+    nup.attn_decode_topk_paged(c.ctx, c.q, torch.from_numpy(idx).to(DEV), K, c.out, c.lse, c.scale, ws)
+    torch.cuda.synchronize()
+    assert nup.device_errors(c.ctx) == nup.NUP_OK
+    ref, ref_lse = c.oracle(tokens=idx)
+    assert_attention_close(c.out.cpu().numpy().astype(np.float64), c.lse.cpu().numpy().astype(np.float64),
+                           ref, ref_lse, f"topk paged K={K}")
+
+
+def test_topk_paged_masks_bad_entries():
+    """An entry outside the retained range is left out and latched; an
+    out-of-order entry is read and latched."""
+    c, L, caps = _gather_case(34, B=2, H=4, gqa=2, ng=2, maxL=500)
+    c.alloc([0, 1], caps, L)
+    c.commit()
+    K = 40
+    idx = W.topk_indices(c.spec.lengths, K, salt=34)
+    bad = idx.copy()
+    bad[1, 2, 17] = c.spec.lengths[1, 2] + 3           # past the retained length
+    ws = torch.empty(nup.workspace_bytes(c.ctx, K), dtype=torch.uint8, device=DEV)
+    nup.attn_decode_topk_paged(c.ctx, c.q, torch.from_numpy(bad).to(DEV), K, c.out, c.lse, c.scale, ws)
+    torch.cuda.synchronize()
+    assert nup.device_errors(c.ctx) == nup.NUP_E_INDEX
+    out = c.out.cpu().numpy().astype(np.float64)
+    lse = c.lse.cpu().numpy().astype(np.float64)
+    ref, ref_lse = c.oracle(tokens=idx)
+    gqa = c.Hq // c.H
+    keep = np.ones(out.shape[:2], bool)
+    keep[1, 2 * gqa:3 * gqa] = False
+    assert_attention_close(out[keep], lse[keep], ref[keep], ref_lse[keep], "unaffected heads")
+    # the affected head equals attention over its other K-1 entries
+    sub = np.delete(idx, 17, axis=2)                    # every head's list minus entry 17
+    sub[1, 2] = np.delete(idx[1, 2], 17)
+    r2, l2 = c.oracle(tokens=sub)
+    assert_attention_close(out[1, 2 * gqa:3 * gqa], lse[1, 2 * gqa:3 * gqa], r2[1, 2 * gqa:3 * gqa],
+                           l2[1, 2 * gqa:3 * gqa], "masked entry")
+    # an out-of-order list is still read, and latched
+    swapped = idx.copy()
+    swapped[0, 0, [3, 4]] = swapped[0, 0, [4, 3]]
+    nup.attn_decode_topk_paged(c.ctx, c.q, torch.from_numpy(swapped).to(DEV), K, c.out, c.lse, c.scale, ws)
+    torch.cuda.synchronize()
+    assert nup.device_errors(c.ctx) == nup.NUP_E_INDEX
+    assert np.isfinite(c.out.cpu().numpy()).all()
+
+
+def test_full_size_llama_topk_paged_equals_staged():
+    """Llama-3-8B shape: the in-place top-K attention equals the oracle on
+    sampled sequences and the staged path (gather, then attend) bit for bit."""
+    w = W.llama3_8b_topk()
+    c = _full_case(w)
+    c.alloc(list(range(w.batch)), w.caps, w.lengths)
+    c.commit()
+    K = w.topk
+    idx_h = W.topk_indices(w.lengths, K)
+    idx = torch.from_numpy(idx_h).to(DEV)
+    ws = torch.empty(nup.workspace_bytes(c.ctx, K), dtype=torch.uint8, device=DEV)
+    nup.attn_decode_topk_paged(c.ctx, c.q, idx, K, c.out, c.lse, c.scale, ws)
+    torch.cuda.synchronize()
+    out_p = c.out.cpu().numpy().copy()
+    lse_p = c.lse.cpu().numpy().copy()
+    ks = torch.empty((w.batch, 8, K, 128), dtype=torch.bfloat16, device=DEV)
+    vs = torch.empty_like(ks)
+    nup.kv_gather_compact(c.ctx, 1, ks, vs, idx=idx, K=K)
+    nup.attn_decode_topk(c.ctx, c.q, ks, vs, K, c.out, c.lse, c.scale, ws)
+    torch.cuda.synchronize()
+    assert nup.device_errors(c.ctx) == nup.NUP_OK
+    assert np.array_equal(out_p, c.out.cpu().numpy()) and np.array_equal(lse_p, c.lse.cpu().numpy())
+    seqs = [1, 6]
+    ref, ref_lse = sub_oracle(c.spec, c.q, c.kpool, c.vpool, seqs, c.scale, tokens=idx_h)
+    assert_attention_close(out_p[seqs].astype(np.float64), lse_p[seqs].astype(np.float64), ref, ref_lse,
+                           "llama top-K in place")
