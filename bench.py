@@ -301,31 +301,40 @@ def measure_extras(args):
     drv = W.ChurnDriver(w.batch)
     active = np.ones(w.batch, bool)
     freed = np.zeros(0, np.int32)
-    host_us, trains, attn_ms = [], [], []
+    host_us, trains, gpu_ms = [], [], []
     nup.kernel_time(st.ctx, reset=True)
     for it in range(steps_warm + steps):
-        t0 = time.perf_counter()
+        lib = 0.0   # host time inside the library: Reserve, Trim, frame commit
         if len(freed):
             L = drv.refill_lengths(len(freed))
             Ls = np.repeat(L[:, None], 8, axis=1).astype(np.int32)
+            t0 = time.perf_counter()
             nup.kv_alloc_groups(st.ctx, freed, Ls + st.pad, Ls)
+            lib += time.perf_counter() - t0
             active[freed] = True
         eos = drv.eos(np.nonzero(active)[0])
+        t0 = time.perf_counter()
         nup.kv_free_seqs(st.ctx, eos)
+        nup.nup_commit(st.ctx)
+        lib += time.perf_counter() - t0
         active[eos] = False
         freed = eos
-        nup.nup_commit(st.ctx)
-        t1 = time.perf_counter()
         timed = it >= steps_warm
         if timed:
-            host_us.append((t1 - t0) * 1e6)
+            host_us.append(lib * 1e6)
             trains.append(len(nup.get_runs(st.ctx)))
             nup.set_timing(st.ctx, True)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
         nup.kv_append(st.ctx, st.k_new, st.v_new)
         nup.attn_decode_nonuniform(st.ctx, st.q, st.out, st.lse, st.scale, st.ws)
         if timed:
+            e1.record()
             nup.set_timing(st.ctx, False)
         torch.cuda.synchronize()
+        if timed:
+            gpu_ms.append(e0.elapsed_time(e1))
     kms, n = nup.kernel_time(st.ctx, reset=True)
     kms /= max(n, 1)
     L_now = nup.get_lengths(st.ctx)
@@ -342,6 +351,8 @@ def measure_extras(args):
     res["mixed_churn"] = {
         "active_slots": int(active.sum()), "kv_bytes": kb,
         "host_trim_reserve_commit_us_mean": round(float(np.mean(host_us)), 1),
+        "gpu_append_attn_ms_mean": round(float(np.mean(gpu_ms)), 4),
+        "submit_share": round(float(np.mean(host_us)) / (float(np.mean(host_us)) + 1e3 * float(np.mean(gpu_ms))), 4),
         "trains_per_step_mean": round(float(np.mean(trains)), 1),
         "pages_in_use": int(st.num_pages - len(nup.get_free_list(st.ctx))),
         "partial_kernel_ms": round(kms, 4),
@@ -349,7 +360,38 @@ def measure_extras(args):
         "gather_trains_ms": round(g_ms, 4),
         "gather_trains_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1)}
     st.free()
-    del st, ksg, vsg, flush_buf
+    del st, ksg, vsg
+    torch.cuda.empty_cache()
+
+    # -- heads per page (Tangram, Fig 8c): the Qwen2.5-32B batch with 1, 2, 4, 8 groups
+    sweep = []
+    for ng in (8, 4, 2, 1):
+        w = W.qwen25_32b()
+        w.num_groups = ng
+        gh = 8 // ng
+        st = Setup(w, 8)
+        reserved_slots = (st.num_pages - len(nup.get_free_list(st.ctx))) * 16 * gh
+        used = int(st.lengths0.sum())
+        for _ in range(2):
+            st.step(append=False)
+        torch.cuda.synchronize()
+        nup.kernel_time(st.ctx, reset=True)
+        nup.set_timing(st.ctx, True)
+        _timed(lambda: st.step(append=False), 10)
+        nup.set_timing(st.ctx, False)
+        kms, n = nup.kernel_time(st.ctx, reset=True)
+        kms /= max(n, 1)
+        sweep.append({"heads_per_group": gh, "groups": ng,
+                      "reserved_GB": round(reserved_slots * 512 / 1e9, 3),
+                      "internal_fragmentation": round(1 - used / reserved_slots, 4),
+                      "page_table_entries": int(st.num_pages - len(nup.get_free_list(st.ctx))),
+                      "partial_kernel_ms": round(kms, 4),
+                      "partial_kernel_GBs": round(kv_bytes(st.lengths0) / (kms * 1e-3) / 1e9, 1)})
+        st.free()
+        del st
+        torch.cuda.empty_cache()
+    res["qwen25_32b_heads_per_group"] = sweep
+    del flush_buf
     torch.cuda.empty_cache()
     return res
 
