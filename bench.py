@@ -279,6 +279,13 @@ def measure_extras(args):
     f_ms = _timed(fused, 20, flush)
     both32 = _timed(lambda: [f() for _ in range(32) for f in (gather, topk)], 3) / 32
     fused32 = _timed(lambda: [fused() for _ in range(32)], 3) / 32
+    # selection of the 2048 entries (1024 recent) from all 122880 positions
+    sel_idx = torch.empty((w.batch, 8, K), dtype=torch.int32, device="cuda")
+    ws_sel = torch.empty(nup.select_workspace_bytes(st.ctx), dtype=torch.uint8, device="cuda")
+    select = lambda: nup.kv_select_topk(st.ctx, st.q, K, K // 2, sel_idx, ws_sel)
+    select()
+    s_ms = _timed(select, 5, flush)
+    k_bytes = int(w.lengths.sum()) * 256
     gb = rows * 512 * 2 + rows * 4
     tb = rows * 512 + w.batch * 32 * 128 * (2 + 4)
     res["llama3_8b_topk"] = {
@@ -288,10 +295,12 @@ def measure_extras(args):
         "topk_in_place_ms": round(f_ms, 4),
         "topk_in_place_GBs": round((rows * (512 + 4) + w.batch * 32 * 128 * 6) / (f_ms * 1e-3) / 1e9, 1),
         "topk_in_place_ms_32_back_to_back": round(fused32, 4),
+        "select_ms": round(s_ms, 4),
+        "select_score_GBs": round(k_bytes / (s_ms * 1e-3) / 1e9, 1),
         "note": "per call cold (1 GiB read before each); 32 back-to-back pairs for a 32-layer stack"}
     assert nup.device_errors(st.ctx) == nup.NUP_OK
     st.free()
-    del st, ks, vs, ws
+    del st, ks, vs, ws, sel_idx, ws_sel
 
     # -- mixed-length churn: 10% EOS per step, freed slots refilled next step
     w = W.mixed_churn()

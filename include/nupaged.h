@@ -231,6 +231,25 @@ nup_status attn_decode_topk_paged(nup_ctx *ctx, const void *q, const int32_t *id
                                   float *out, float *lse, float scale, void *workspace,
                                   size_t ws_bytes, void *stream);
 
+/*
+ * kv_select_topk -- choose each active (slot, KV head)'s K critical entries
+ * (KVDrive, Fig 1: critical entries fetched at each decode step; Fig 3:
+ * critical KV windows).  The score of position t is the largest q.k over the
+ * head's query rows (fp32 from exact bf16 products).  The `window` most
+ * recent positions L-window .. L-1 are always kept; the other K - window are
+ * the highest-scoring positions of 0 .. L-window-1, ties to the lower
+ * position.  The list is written in ascending order, ready for
+ * kv_gather_compact mode 1 or attn_decode_topk_paged.
+ *   q          device bf16 [B_max][H_q][D]
+ *   idx_out    device int32 [B_max][H_kv][K]; rows of inactive slots untouched
+ *   workspace  device, >= nup_select_workspace_bytes() bytes (fp32 scores)
+ * Requires a committed descriptor and L >= K for every active head (checked
+ * on the host).  Errors: NUP_E_ARG, NUP_E_STATE, NUP_E_HIP. */
+nup_status kv_select_topk(nup_ctx *ctx, const void *q, int32_t K, int32_t window, int32_t *idx_out,
+                          void *workspace, size_t ws_bytes, void *stream);
+/* Workspace bytes for kv_select_topk: B_max * H_kv * max_pages * P fp32 scores. */
+nup_status nup_select_workspace_bytes(const nup_ctx *ctx, size_t *bytes);
+
 /* ---- host-side queries (no device call; for tests and reports) ---------- */
 
 /* Shadow page table int32 [n_g][B_max][max_pages]. */

@@ -63,6 +63,8 @@ _sigs = {
     "attn_decode_nonuniform": [_P, _P, _P, _P, ctypes.c_float, _P, _S, _P],
     "attn_decode_topk": [_P, _P, _P, _P, _I, _P, _P, ctypes.c_float, _P, _S, _P],
     "attn_decode_topk_paged": [_P, _P, _P, _I, _P, _P, ctypes.c_float, _P, _S, _P],
+    "kv_select_topk": [_P, _P, _I, _I, _P, _P, _S, _P],
+    "nup_select_workspace_bytes": [_P, _P],
     "nup_get_page_table": [_P, _P],
     "nup_get_lengths": [_P, _P],
     "nup_get_groups": [_P, _P, _P],
@@ -231,6 +233,20 @@ def attn_decode_topk_paged(ctx: Context, q, idx, K: int, out, lse, scale: float,
     st = _lib.attn_decode_topk_paged(ctx.handle, _ptr(q), _ptr(idx), K, _ptr(out), _ptr(lse),
                                      float(scale), _ptr(workspace), nbytes, _stream(stream))
     return ctx.check(st) if raise_on_error else st
+
+
+def kv_select_topk(ctx: Context, q, K: int, window: int, idx_out, workspace, stream=None,
+                   raise_on_error=True):
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.kv_select_topk(ctx.handle, _ptr(q), K, window, _ptr(idx_out), _ptr(workspace), nbytes,
+                             _stream(stream))
+    return ctx.check(st) if raise_on_error else st
+
+
+def select_workspace_bytes(ctx: Context) -> int:
+    n = ctypes.c_size_t()
+    ctx.check(_lib.nup_select_workspace_bytes(ctx.handle, ctypes.byref(n)))
+    return n.value
 
 
 # ---- host-side queries ------------------------------------------------------

@@ -912,6 +912,62 @@ nup_status attn_decode_topk_paged(nup_ctx *c, const void *q, const int32_t *idx,
                        nullptr, idx, K);
 }
 
+nup_status nup_select_workspace_bytes(const nup_ctx *c, size_t *bytes) {
+    if (!c || !bytes) return NUP_E_ARG;
+    *bytes = align_up((size_t)c->B * c->H * (size_t)c->max_pages * nup::kPage * 4);
+    return NUP_OK;
+}
+
+nup_status kv_select_topk(nup_ctx *c, const void *q, int32_t K, int32_t window, int32_t *idx_out,
+                          void *workspace, size_t ws_bytes, void *stream) {
+    if (!c) return NUP_E_ARG;
+    if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
+    if (!c->committed || c->pending) return fail(c, NUP_E_STATE, "edits pending: nup_commit first");
+    if (!q || !idx_out || !workspace) return fail(c, NUP_E_ARG, "q, idx_out and workspace are required");
+    if (K <= 0 || window < 0 || window > K) return fail(c, NUP_E_ARG, "need K > 0 and 0 <= window <= K");
+    size_t need = 0;
+    nup_select_workspace_bytes(c, &need);
+    if (ws_bytes < need) return fail(c, NUP_E_ARG, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    for (int s = 0; s < c->B; ++s) {
+        if (!c->active[s]) continue;
+        for (int h = 0; h < c->H; ++h)
+            if (c->len[(size_t)s * c->H + h] < K)
+                return fail(c, NUP_E_ARG, "slot %d head %d retains %d < K = %d entries", s, h,
+                            c->len[(size_t)s * c->H + h], K);
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    nup::ScoreArgs sa{};
+    sa.q = static_cast<const uint16_t *>(q);
+    sa.kbase = c->kpool;
+    sa.page_table = c->d_pt();
+    sa.lengths = c->d_len();
+    sa.group_of_head = c->d_goh();
+    sa.slot_of_head = c->d_soh();
+    sa.rows = c->inbox_i32(c->off_rows);
+    sa.worker_start = c->inbox_i32(c->off_ws);
+    sa.scores = static_cast<float *>(workspace);
+    sa.bmax = c->B;
+    sa.hkv = c->H;
+    sa.gh = c->gh;
+    sa.max_pages = c->max_pages;
+    sa.n_workers = c->dev_workers;
+    sa.stride = c->max_pages * nup::kPage;
+    hipError_t e = nup::launch_score(sa, c->D, c->gqa, st);
+    if (e != hipSuccess) return hip_fail(c, e, "score launch");
+    nup::SelectArgs sl{};
+    sl.scores = sa.scores;
+    sl.active = c->d_active();
+    sl.lengths = c->d_len();
+    sl.idx_out = idx_out;
+    sl.hkv = c->H;
+    sl.stride = sa.stride;
+    sl.k = K;
+    sl.window = window;
+    e = nup::launch_select(sl, c->B * c->H, st);
+    if (e != hipSuccess) return hip_fail(c, e, "select launch");
+    return NUP_OK;
+}
+
 nup_status nup_get_page_table(const nup_ctx *c, int32_t *out) {
     if (!c || !out) return NUP_E_ARG;
     std::copy(c->pt.begin(), c->pt.end(), out);

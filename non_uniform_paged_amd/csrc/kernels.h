@@ -55,6 +55,26 @@ struct MergeArgs {
     int32_t n_pairs;               // (slot, query head) pairs; set by the launcher
 };
 
+// Top-K selection.  score_kernel walks the committed plan like the paged
+// attention and writes, for every retained position of every active head,
+// the largest q.k over the head's query rows into scores[sh * stride + t].
+// select_kernel (one workgroup per head) keeps the `window` most recent
+// positions and the K - window highest-scoring older ones (ties to the lower
+// position) and writes them in ascending order.
+struct ScoreArgs {
+    const uint16_t *q, *kbase;
+    const int32_t *page_table, *lengths, *group_of_head, *slot_of_head, *rows, *worker_start;
+    float *scores;
+    int32_t bmax, hkv, gh, max_pages, n_workers, stride;
+};
+
+struct SelectArgs {
+    const float *scores;
+    const int32_t *active, *lengths;
+    int32_t *idx_out;              // [Bmax*Hkv][K]
+    int32_t hkv, stride, k, window;
+};
+
 struct AppendArgs {
     uint16_t *k_pool, *v_pool;
     const uint16_t *k_new, *v_new; // [Bmax][Hkv][D]
@@ -90,6 +110,8 @@ int partial_blocks_per_cu(int head_dim, int gqa, int mode);
 hipError_t launch_partial(const PartialArgs &a, int head_dim, int gqa, int mode, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, int head_dim, int gqa, int n_heads, hipStream_t st);
 hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t st);
+hipError_t launch_score(const ScoreArgs &a, int head_dim, int gqa, hipStream_t st);
+hipError_t launch_select(const SelectArgs &a, int n_heads, hipStream_t st);
 hipError_t launch_gather_index(const GatherIndexArgs &a, int head_dim, hipStream_t st);
 hipError_t launch_gather_runs(const GatherRunsArgs &a, int head_dim, int total_pages, hipStream_t st);
 hipError_t launch_fill(int32_t *p, int n, int32_t value, hipStream_t st);

@@ -470,6 +470,206 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Top-K selection, step 1: scores.  Same work split and q.k tile as the
+// paged partial kernel, but only K is read.  The row maximum over the head's
+// query rows is taken across the 16 lanes of a DPP row (lanes 16g..16g+15
+// hold the query rows of tokens 4g..4g+3).
+// ---------------------------------------------------------------------------
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kRowRor2 = 0x122, kRowRor1 = 0x121;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+template <int D, int GQA>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+    constexpr int NJ = D / 32;
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= a.n_workers) return;
+    const int qn = lane & 15, qg = lane >> 4;
+    const int rb = ld_uniform(a.worker_start + w), re = ld_uniform(a.worker_start + w + 1);
+    for (int row = rb; row < re; ++row) {
+        const int sh = ld_uniform(a.rows + row * 4 + 0);
+        const int t0 = ld_uniform(a.rows + row * 4 + 1);
+        const int t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + sh));
+        if (t0 >= t1) continue;
+        const int s = sh / a.hkv, h = sh - s * a.hkv;
+        uint4 qv[NJ];
+        const uint4 *qh = reinterpret_cast<const uint4 *>(
+            a.q + ((size_t)s * a.hkv * GQA + (size_t)h * GQA + (qn < GQA ? qn : 0)) * D);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) qv[j] = qn < GQA ? qh[4 * j + qg] : make_uint4(0, 0, 0, 0);
+        const int32_t *ptrow =
+            a.page_table + ((size_t)ld_uniform(a.group_of_head + h) * a.bmax + s) * (size_t)a.max_pages;
+        const size_t slot_off = (size_t)ld_uniform(a.slot_of_head + h) * kPage * D;
+        float *out = a.scores + (size_t)sh * a.stride;
+        const int p0 = t0 / kPage, p1 = (t1 - 1) / kPage;
+        auto load = [&](int pi, uint4 (&k)[NJ]) {
+            const uint4 *kp = reinterpret_cast<const uint4 *>(
+                a.kbase + (size_t)ld_uniform(ptrow + pi) * a.gh * kPage * D + slot_off);
+            const uint32_t koff = (uint32_t)min(qn, t1 - 1 - pi * kPage) * (D / 8) + qg;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) k[j] = ld_stream(kp + koff + 4 * j);
+        };
+        auto score = [&](int pi, const uint4 (&k)[NJ]) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k[j]),
+                                                              __builtin_bit_cast(bf16x8_t, qv[j]), acc, 0, 0, 0);
+            float m[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float x = qn < GQA ? acc[i] : -INFINITY;
+                x = fmaxf(x, dpp_f<kRowRor8>(x));
+                x = fmaxf(x, dpp_f<kRowRor4>(x));
+                x = fmaxf(x, dpp_f<kRowRor2>(x));
+                x = fmaxf(x, dpp_f<kRowRor1>(x));
+                m[i] = x;
+            }
+            const int tb = pi * kPage + 4 * qg;
+            if (qn == 0) {
+                if (tb + 3 < t1) {
+                    *reinterpret_cast<float4 *>(out + tb) = make_float4(m[0], m[1], m[2], m[3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (tb + i < t1) out[tb + i] = m[i];
+                }
+            }
+        };
+        uint4 kA[NJ], kB[NJ];
+        load(p0, kA);
+        for (int p = p0; p <= p1; p += 2) {
+            if (p + 1 <= p1) load(p + 1, kB);
+            score(p, kA);
+            if (p + 1 > p1) break;
+            if (p + 2 <= p1) load(p + 2, kA);
+            score(p + 1, kB);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Top-K selection, step 2: one 1024-thread workgroup per head.  A four-pass
+// radix select (8 bits per pass, LDS histogram) finds the (K-window)-th
+// largest score key among the older positions; a scan in position order
+// then writes the positions above it and the lowest-positioned ties.
+// ---------------------------------------------------------------------------
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectItems = 8;   // consecutive positions per thread in the compaction
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0) u = 0;   // -0 counts as +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive scan of v over the workgroup (in thread order); *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *lds, int *total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) lds[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+        int t = lane < kSelectThreads / 64 ? lds[lane] : 0;
+        int incl = t;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        if (lane < kSelectThreads / 64) lds[16 + lane] = incl - t;
+        if (lane == kSelectThreads / 64 - 1) lds[32] = incl;
+    }
+    __syncthreads();
+    const int r = x - v + lds[16 + wid];
+    *total = lds[32];
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
+    __shared__ uint32_t hist[256];
+    __shared__ int scan_lds[40];
+    __shared__ uint32_t pick[2];
+    const int sh = blockIdx.x, tid = threadIdx.x;
+    if (!a.active[sh / a.hkv]) return;
+    const int L = a.lengths[sh];
+    const int n = L - a.window, k = a.k - a.window;
+    int32_t *out = a.idx_out + (size_t)sh * a.k;
+    for (int j = tid; j < a.window; j += kSelectThreads) out[k + j] = n + j;
+    if (k <= 0) return;
+    const float *sc = a.scores + (size_t)sh * a.stride;
+    uint32_t prefix = 0, mask = 0;
+    int remaining = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += kSelectThreads) hist[i] = 0;
+        __syncthreads();
+        for (int t = tid; t < n; t += kSelectThreads) {
+            const uint32_t key = order_key(sc[t]);
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int cum = 0;
+            for (int d = 255; d >= 0; --d) {
+                const int c = (int)hist[d];
+                if (cum + c >= remaining) {
+                    pick[0] = (uint32_t)d;
+                    pick[1] = (uint32_t)(remaining - cum);
+                    break;
+                }
+                cum += c;
+            }
+        }
+        __syncthreads();
+        prefix |= pick[0] << shift;
+        mask |= 255u << shift;
+        remaining = (int)pick[1];
+        __syncthreads();
+    }
+    const uint32_t T = prefix;        // the k-th largest key
+    const int take_eq = remaining;    // keys equal to T that are taken (lowest positions)
+    int out_base = 0, eq_base = 0;
+    for (int c0 = 0; c0 < n; c0 += kSelectThreads * kSelectItems) {
+        const int tb = c0 + tid * kSelectItems;
+        uint32_t keys[kSelectItems];
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int u = 0; u < kSelectItems; ++u) {
+            keys[u] = tb + u < n ? order_key(sc[tb + u]) : 0u;
+            gt += (tb + u < n) && keys[u] > T;
+            eq += (tb + u < n) && keys[u] == T;
+        }
+        int eq_tot = 0, sel_tot = 0;
+        const int eq_pre = block_exclusive_scan(eq, scan_lds, &eq_tot) + eq_base;
+        const int my_eq = max(0, min(eq, take_eq - eq_pre));
+        const int sel_pre = block_exclusive_scan(gt + my_eq, scan_lds, &sel_tot) + out_base;
+        int pos = sel_pre, r = eq_pre;
+#pragma unroll
+        for (int u = 0; u < kSelectItems; ++u) {
+            if (tb + u >= n) break;
+            if (keys[u] > T) {
+                out[pos++] = tb + u;
+            } else if (keys[u] == T) {
+                if (r < take_eq) out[pos++] = tb + u;
+                ++r;
+            }
+        }
+        out_base += sel_tot;
+        eq_base += eq_tot;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Append: one token per active (slot, KV head).  2*(D/8) lanes per head: the
 // first half copies the K row, the second the V row, 16 bytes per lane.
 // ---------------------------------------------------------------------------
@@ -731,6 +931,33 @@ hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t st) {
     if (head_dim == 64) return launch_raw((void *)&append_kernel<64>, dim3(blocks), dim3(256), &copy, sizeof(copy), st);
     if (head_dim == 128) return launch_raw((void *)&append_kernel<128>, dim3(blocks), dim3(256), &copy, sizeof(copy), st);
     return hipErrorInvalidValue;
+}
+
+template <int D>
+void *score_fn_gqa(int gqa) {
+    switch (gqa) {
+        case 1: return reinterpret_cast<void *>(&score_kernel<D, 1>);
+        case 2: return reinterpret_cast<void *>(&score_kernel<D, 2>);
+        case 4: return reinterpret_cast<void *>(&score_kernel<D, 4>);
+        case 5: return reinterpret_cast<void *>(&score_kernel<D, 5>);
+        case 8: return reinterpret_cast<void *>(&score_kernel<D, 8>);
+        default: return nullptr;
+    }
+}
+
+hipError_t launch_score(const ScoreArgs &a, int head_dim, int gqa, hipStream_t st) {
+    void *fn = head_dim == 64 ? score_fn_gqa<64>(gqa) : head_dim == 128 ? score_fn_gqa<128>(gqa) : nullptr;
+    if (!fn) return hipErrorInvalidValue;
+    if (a.n_workers <= 0) return hipSuccess;
+    ScoreArgs copy = a;
+    const unsigned blocks = (unsigned)((a.n_workers + kWavesPerBlock - 1) / kWavesPerBlock);
+    return launch_raw(fn, dim3(blocks), dim3(256), &copy, sizeof(copy), st);
+}
+
+hipError_t launch_select(const SelectArgs &a, int n_heads, hipStream_t st) {
+    if (n_heads <= 0) return hipSuccess;
+    hipLaunchKernelGGL(select_kernel, dim3(n_heads), dim3(kSelectThreads), 0, st, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_gather_index(const GatherIndexArgs &a, int head_dim, hipStream_t st) {

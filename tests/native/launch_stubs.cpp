@@ -10,6 +10,8 @@ int partial_blocks_per_cu(int, int, int) { return 2; }
 hipError_t launch_partial(const PartialArgs &, int, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_merge(const MergeArgs &, int, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_append(const AppendArgs &, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_score(const ScoreArgs &, int, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_select(const SelectArgs &, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_gather_index(const GatherIndexArgs &, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_gather_runs(const GatherRunsArgs &, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_fill(int32_t *, int, int32_t, hipStream_t) { return hipSuccess; }

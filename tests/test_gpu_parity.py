@@ -536,3 +536,133 @@ def test_full_size_llama_topk_paged_equals_staged():
     ref, ref_lse = sub_oracle(c.spec, c.q, c.kpool, c.vpool, seqs, c.scale, tokens=idx_h)
     assert_attention_close(out_p[seqs].astype(np.float64), lse_p[seqs].astype(np.float64), ref, ref_lse,
                            "llama top-K in place")
+
+
+# ---- top-K selection ------------------------------------------------------
+
+from oracle import select as osel  # noqa: E402
+
+
+def _check_selection(got, spec, q, pool_k, K, window, heads, eps=1e-3):
+    """got: int32 [B][H][K] from the GPU.  Structure always; membership against
+    the fp64 oracle outside a margin around its threshold (fp32 scores can
+    order near-ties differently)."""
+    for (s, h) in heads:
+        g = got[s, h]
+        L = int(spec.lengths[s, h])
+        assert (np.diff(g) > 0).all() and g[0] >= 0 and g[-1] < L, (s, h)
+        assert g[K - window:].tolist() == list(range(L - window, L)), (s, h)
+        sc = osel.scores(q, pool_k, spec, s, h)
+        want = osel.select(sc, K, window)
+        if K == window:
+            continue
+        cand = sc[: L - window]
+        thr = np.sort(cand)[::-1][K - window - 1]
+        sure = np.abs(cand - thr) > eps * max(1.0, abs(thr))
+        gs = np.zeros(L - window, bool)
+        gs[g[: K - window]] = True
+        ws_ = np.zeros(L - window, bool)
+        ws_[want[: K - window]] = True
+        assert np.array_equal(gs[sure], ws_[sure]), (s, h)
+        assert gs.sum() == ws_.sum()
+
+
+def test_select_topk_exact_ties():
+    """Exactly representable scores with many ties: the GPU selection equals
+    the oracle's bit for bit (ties to the lower position)."""
+    B, H, gqa, D = 2, 4, 2, 128
+    L = np.array([[300, 257, 64, 129], [512, 96, 400, 33]], np.int32)
+    max_pages = 33
+    c = Case(H=H, Hq=H * gqa, D=D, ng=2, B=B, num_pages=B * 2 * max_pages, max_pages=max_pages,
+             num_workers=13, salt=40)
+    c.alloc([0, 1], L, L)
+    c.commit()
+    # keys: dims 3 and 5 carry small integers (many repeats), all else zero
+    rs = np.random.default_rng(40)
+    kp = torch.zeros_like(c.kpool, dtype=torch.float32)
+    kp[:, :, :, 3] = torch.from_numpy(rs.integers(-4, 5, size=kp.shape[:3]).astype(np.float32)).to(DEV)
+    kp[:, :, :, 5] = torch.from_numpy(rs.integers(-4, 5, size=kp.shape[:3]).astype(np.float32)).to(DEV)
+    c.kpool.copy_(kp.to(torch.bfloat16))
+    qf = torch.zeros((B, H * gqa, D), dtype=torch.float32)
+    qf[:, 0::2, 3] = 1.0
+    qf[:, 0::2, 5] = 0.5
+    qf[:, 1::2, 3] = -0.25
+    qf[:, 1::2, 5] = 2.0
+    c.q.copy_(qf.to(torch.bfloat16).to(DEV))
+    for K, window in ((32, 8), (33, 0), (20, 20), (1, 0)):
+        out = torch.full((B, H, K), -5, dtype=torch.int32, device=DEV)
+        ws = torch.empty(nup.select_workspace_bytes(c.ctx), dtype=torch.uint8, device=DEV)
+        nup.kv_select_topk(c.ctx, c.q, K, window, out, ws)
+        torch.cuda.synchronize()
+        want, _ = osel.select_all(u16(c.q), u16(c.kpool), c.spec, K, window)
+        assert np.array_equal(out.cpu().numpy(), want), (K, window)
+
+
+def test_select_topk_random_and_refused_cases():
+    c, L, caps = _gather_case(41, B=3, H=8, gqa=5, ng=4)
+    c.alloc([0, 2], caps[[0, 2]], L[[0, 2]])
+    c.commit()
+    K, window = 128, 32
+    out = torch.full((c.B, c.H, K), -5, dtype=torch.int32, device=DEV)
+    ws = torch.empty(nup.select_workspace_bytes(c.ctx), dtype=torch.uint8, device=DEV)
+    nup.kv_select_topk(c.ctx, c.q, K, window, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert (got[1] == -5).all()                     # inactive slot untouched
+    _check_selection(got, c.spec, u16(c.q), u16(c.kpool), K, window,
+                     [(s, h) for s in (0, 2) for h in range(c.H)])
+    # more entries than some head retains: refused on the host
+    assert nup.kv_select_topk(c.ctx, c.q, int(L.max()) + 1, 0, out, ws,
+                              raise_on_error=False) == nup.NUP_E_ARG
+    assert nup.kv_select_topk(c.ctx, c.q, 8, 9, out, ws, raise_on_error=False) == nup.NUP_E_ARG
+
+
+def test_full_size_llama_select_then_attend():
+    """Llama-3-8B shape: select 2048 entries (1024 recent) per KV head from
+    122880, then attend in place.  Checked on sampled heads against the
+    oracle's own selection and attention."""
+    w = W.llama3_8b_topk()
+    c = _full_case(w)
+    c.alloc(list(range(w.batch)), w.caps, w.lengths)
+    c.commit()
+    K, window = w.topk, w.topk // 2
+    idx = torch.empty((w.batch, 8, K), dtype=torch.int32, device=DEV)
+    ws_sel = torch.empty(nup.select_workspace_bytes(c.ctx), dtype=torch.uint8, device=DEV)
+    nup.kv_select_topk(c.ctx, c.q, K, window, idx, ws_sel)
+    ws = torch.empty(nup.workspace_bytes(c.ctx, K), dtype=torch.uint8, device=DEV)
+    nup.attn_decode_topk_paged(c.ctx, c.q, idx, K, c.out, c.lse, c.scale, ws)
+    torch.cuda.synchronize()
+    assert nup.device_errors(c.ctx) == nup.NUP_OK
+    got = idx.cpu().numpy()
+    out = c.out.cpu().numpy().astype(np.float64)
+    lse = c.lse.cpu().numpy().astype(np.float64)
+    seqs = [2, 7]
+    # the oracle sees only the sampled sequences' pages (renumbered)
+    sub = c.spec.page_table[:, seqs, :]
+    used = np.unique(sub[sub >= 0])
+    remap = np.full(c.spec.num_pages, -1, np.int64)
+    remap[used] = np.arange(len(used))
+    spec2 = pg.PagerSpec(8, 1, len(seqs), len(used), c.spec.max_pages, 16)
+    spec2.page_table = np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(np.int32)
+    spec2.lengths = c.spec.lengths[seqs].copy()
+    spec2.caps = c.spec.caps[seqs].copy()
+    spec2.active[:] = True
+    spec2.n_pages = c.spec.n_pages[:, seqs].copy()
+    spec2.group_of_head, spec2.slot_of_head = c.spec.group_of_head, c.spec.slot_of_head
+    tsel = torch.from_numpy(used.astype(np.int64)).to(DEV)
+    pk = u16(c.kpool.index_select(0, tsel))
+    pv = u16(c.vpool.index_select(0, tsel))
+    q2 = u16(c.q)[seqs]
+    heads = [(0, 0), (0, 5), (1, 3)]
+    _check_selection(got[seqs], spec2, q2, pk, K, window, heads)
+    want = np.stack([np.stack([osel.select(osel.scores(q2, pk, spec2, i, h), K, window)
+                               for h in range(8)]) for i in range(len(seqs))])
+    same = [(i, h) for i in range(len(seqs)) for h in range(8) if np.array_equal(want[i, h], got[seqs][i, h])]
+    assert len(same) >= 12          # near-ties flip only occasionally
+    ref, ref_lse = oracle.decode(q2, pk, pv, spec2.page_table, spec2.lengths, spec2.group_of_head,
+                                 spec2.slot_of_head, c.scale, tokens=want)
+    gqa = 4
+    for (i, h) in same:
+        rows = slice(h * gqa, (h + 1) * gqa)
+        assert_attention_close(out[seqs[i], rows], lse[seqs[i], rows], ref[i, rows], ref_lse[i, rows],
+                               f"select+attend {seqs[i]},{h}")

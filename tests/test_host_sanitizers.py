@@ -31,7 +31,8 @@ def test_host_plane_is_clean_under_sanitizers(tmp_path):
            os.path.join(ROOT, "non_uniform_paged_amd", "csrc", "host.cpp"),
            os.path.join(NATIVE, "launch_stubs.cpp"), os.path.join(NATIVE, "pager_fuzz.cpp"),
            "-o", exe, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    b = subprocess.run(cmd, capture_output=True, text=True)
+    assert b.returncode == 0, b.stderr[-4000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stacktrace=1")
     for seed in (1, 2, 3):
         r = subprocess.run([exe, str(seed)], capture_output=True, text=True, env=env, timeout=300)
