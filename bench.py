@@ -527,7 +527,7 @@ def main():
                    "step": "kv_append + nup_commit + attn_decode_nonuniform (partial + merge)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": "partial_attn_kernel<128,5,false>"},
+                     "traffic": traffic, "kernel": "partial_attn_kernel<128,5,0>"},
         "cpu_baseline": cpu,
         "extra": extra,
     }
