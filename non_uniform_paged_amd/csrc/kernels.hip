@@ -74,10 +74,11 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 //           core (v_mfma_f32_16x16x32_bf16, D/32 steps).  The GQA query rows
 //           of the head fill columns 0..GQA-1 of Q^T, the rest is zero.  The
 //           bf16 products are exact and accumulate in fp32.
-//           A operand: lane l holds token l%16 and the 16-byte pieces
-//           4j + l/16 of its row (step j), i.e. 64 contiguous bytes of each
-//           row per load instruction.  Lane l of the result holds query row
-//           l%16 for tokens 4(l/16) .. 4(l/16)+3.
+//           K is loaded row-major like V (whole rows per load instruction)
+//           and passes through a padded LDS tile into the A operand layout:
+//           lane l takes token l%16, 16-byte pieces 4j + l/16 (step j).
+//           Lane l of the result holds query row l%16 for tokens
+//           4(l/16) .. 4(l/16)+3.
 //   softmax fp32, online, per query row; the running maximum of a row is
 //           shared by the whole wave, so the output accumulators of all
 //           lanes use one scale and combine by plain sums.
@@ -117,6 +118,14 @@ void partial_attn_kernel(PartialArgs a) {
     // writes of the five-plus rows land in distinct LDS banks
     __shared__ float4 p_lds[kWavesPerBlock][8][5];
     __shared__ float alpha_lds[kWavesPerBlock][16];   // rescale factors; final 1/l, lse
+    // Where K goes on its way to the MFMA A operand.  Paged pages are
+    // 4 KB head blocks: K is loaded straight in the operand layout (16 rows x
+    // 64 bytes per instruction), which measured faster there.  Top-K entries
+    // are single rows: K is loaded as whole rows like V and transposed
+    // through an LDS tile (rows padded by one 16-byte piece: conflict-free).
+    constexpr bool kRowK = MODE != kModePaged;
+    static_assert(NJ == TPL, "one K register per MFMA step either way");
+    __shared__ uint4 k_lds[kWavesPerBlock][kRowK ? kPage : 1][LPR + 1];
     // indexed top-K: the pool row of every entry of the worker's chunk (-1: not readable)
     __shared__ int32_t rid_lds[kWavesPerBlock][MODE == kModeIndexed ? kMaxTopkChunk : 1];
 
@@ -127,6 +136,7 @@ void partial_attn_kernel(PartialArgs a) {
     float *pl = reinterpret_cast<float *>(p_lds[wid]);
     float *al = alpha_lds[wid];
     int32_t *rl = rid_lds[wid];
+    uint4 (*kt)[LPR + 1] = k_lds[wid];
 
     // MFMA-side coordinates
     const int qn = lane & 15;       // query row (column of S^T)
@@ -236,39 +246,59 @@ void partial_attn_kernel(PartialArgs a) {
         // past the end of the range are clamped to the last valid row.  The
         // block base is wave-uniform, so loads take a scalar base and a
         // 32-bit lane offset.
-        auto load = [&](int pi, size_t base, uint4 (&k)[NJ], uint4 (&v)[TPL]) {
+        // K and V are both read as whole rows: lane (tg, ve) takes piece ve of
+        // rows tg*TPL .. tg*TPL+TPL-1 (the tokens it also owns for P.V), so a
+        // load instruction covers RPI whole rows.  Rows past the end of the
+        // range are clamped to the last valid row.
+        auto load = [&](int pi, size_t base, uint4 (&k)[TPL], uint4 (&v)[TPL]) {
             const int last = t1 - 1 - pi * kPage;
             if (MODE == kModeIndexed) {
                 // each row from its own resolved pool row (masked rows read row 0)
-                const int rk = max(rl[pi * kPage + min(qn, last) - t0], 0);
-                const uint4 *kp = reinterpret_cast<const uint4 *>(a.kbase + (size_t)rk * D);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) k[j] = ld_stream(kp + qg + 4 * j);
 #pragma unroll
                 for (int i = 0; i < TPL; ++i) {
-                    const int rv = max(rl[pi * kPage + min(tg * TPL + i, last) - t0], 0);
-                    v[i] = ld_stream(reinterpret_cast<const uint4 *>(a.vbase + (size_t)rv * D) + ve);
+                    const size_t r = (size_t)max(rl[pi * kPage + min(tg * TPL + i, last) - t0], 0);
+                    k[i] = ld_stream(reinterpret_cast<const uint4 *>(a.kbase + r * D) + ve);
+                    v[i] = ld_stream(reinterpret_cast<const uint4 *>(a.vbase + r * D) + ve);
                 }
                 return;
             }
             const uint4 *kp = reinterpret_cast<const uint4 *>(a.kbase + base);
             const uint4 *vp = reinterpret_cast<const uint4 *>(a.vbase + base);
-            const uint32_t koff = (uint32_t)min(qn, last) * (D / 8) + qg;
+            if (!kRowK) {
+                // K straight into the MFMA A layout: token qn, pieces 4j + qg
+                const uint32_t koff = (uint32_t)min(qn, last) * LPR + qg;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) k[j] = ld_stream(kp + koff + 4 * j);
+                for (int j = 0; j < NJ; ++j) k[j] = ld_stream(kp + koff + 4 * j);
+            }
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
-                const uint32_t voff = (uint32_t)min(tg * TPL + i, last) * (D / 8) + ve;
-                v[i] = ld_stream(vp + voff);
+                const uint32_t off = (uint32_t)min(tg * TPL + i, last) * LPR + ve;
+                if (kRowK) k[i] = ld_stream(kp + off);
+                v[i] = ld_stream(vp + off);
             }
         };
-        auto compute = [&](int pi, const uint4 (&k)[NJ], const uint4 (&v)[TPL]) {
+        auto compute = [&](int pi, const uint4 (&k)[TPL], const uint4 (&v)[TPL]) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            if (kRowK) {
+                // K tile -> LDS -> MFMA A operand (lane l: token l%16, pieces 4j + l/16)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k[j]),
-                                                              __builtin_bit_cast(bf16x8_t, qv[j]),
-                                                              acc, 0, 0, 0);
+                for (int i = 0; i < TPL; ++i) kt[tg * TPL + i][ve] = k[i];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kt[qn][4 * j + qg]),
+                                                                  __builtin_bit_cast(bf16x8_t, qv[j]),
+                                                                  acc, 0, 0, 0);
+                __builtin_amdgcn_wave_barrier();   // reads done before the next page's writes
+            } else {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k[j]),
+                                                                  __builtin_bit_cast(bf16x8_t, qv[j]),
+                                                                  acc, 0, 0, 0);
+            }
             const int tbase = pi * kPage + 4 * qg;
             float sc[4];
 #pragma unroll
@@ -330,7 +360,7 @@ void partial_attn_kernel(PartialArgs a) {
 
 #if NUP_PREFETCH == 2
         // Two page buffers: page p+1 is in flight while page p is computed.
-        uint4 kA[NJ], vA[TPL], kB[NJ], vB[TPL];
+        uint4 kA[TPL], vA[TPL], kB[TPL], vB[TPL];
         load(p0, page_base(p0), kA, vA);
         for (int p = p0; p <= p1; p += 2) {
             if (p + 1 <= p1) load(p + 1, page_base(p + 1), kB, vB);
@@ -342,7 +372,7 @@ void partial_attn_kernel(PartialArgs a) {
 #else
         // Ring of kDepth page buffers: pages p+1 .. p+kDepth-1 are in flight
         // while page p is computed.
-        uint4 kb[kDepth][NJ], vb[kDepth][TPL];
+        uint4 kb[kDepth][TPL], vb[kDepth][TPL];
 #pragma unroll
         for (int k = 0; k + 1 < kDepth; ++k)
             if (p0 + k <= p1) load(p0 + k, page_base(p0 + k), kb[k], vb[k]);
@@ -482,13 +512,24 @@ __device__ __forceinline__ float dpp_f(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+constexpr int kScoreDepth = 4;
+
 template <int D, int GQA>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     constexpr int NJ = D / 32;
+    constexpr int LPR = D / 8;      // 16-byte pieces per row
+    constexpr int TPL = LPR / 4;    // rows per lane in the row-major load
+    constexpr int RPI = 64 / LPR;   // rows per load instruction
+    // K tile staged row-major (rows padded by one piece: conflict-free
+    // reads in the MFMA operand layout)
+    __shared__ uint4 k_lds[kWavesPerBlock][kPage][LPR + 1];
     const int lane = threadIdx.x & 63;
-    const int w = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = blockIdx.x * kWavesPerBlock + wid;
     if (w >= a.n_workers) return;
+    uint4 (*kt)[LPR + 1] = k_lds[wid];
     const int qn = lane & 15, qg = lane >> 4;
+    const int tg = lane / LPR, ve = lane % LPR;
     const int rb = ld_uniform(a.worker_start + w), re = ld_uniform(a.worker_start + w + 1);
     for (int row = rb; row < re; ++row) {
         const int sh = ld_uniform(a.rows + row * 4 + 0);
@@ -506,19 +547,26 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         const size_t slot_off = (size_t)ld_uniform(a.slot_of_head + h) * kPage * D;
         float *out = a.scores + (size_t)sh * a.stride;
         const int p0 = t0 / kPage, p1 = (t1 - 1) / kPage;
-        auto load = [&](int pi, uint4 (&k)[NJ]) {
+        // row-major, fully coalesced: an instruction reads RPI whole rows
+        auto load = [&](int pi, uint4 (&k)[TPL]) {
             const uint4 *kp = reinterpret_cast<const uint4 *>(
                 a.kbase + (size_t)ld_uniform(ptrow + pi) * a.gh * kPage * D + slot_off);
-            const uint32_t koff = (uint32_t)min(qn, t1 - 1 - pi * kPage) * (D / 8) + qg;
+            const int last = t1 - 1 - pi * kPage;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) k[j] = ld_stream(kp + koff + 4 * j);
+            for (int i = 0; i < TPL; ++i) k[i] = ld_stream(kp + (size_t)min(i * RPI + tg, last) * LPR + ve);
         };
-        auto score = [&](int pi, const uint4 (&k)[NJ]) {
+        auto score = [&](int pi, const uint4 (&k)[TPL]) {
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) kt[i * RPI + tg][ve] = k[i];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k[j]),
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kt[qn][4 * j + qg]),
                                                               __builtin_bit_cast(bf16x8_t, qv[j]), acc, 0, 0, 0);
+            __builtin_amdgcn_wave_barrier();
             float m[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -540,14 +588,21 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
                 }
             }
         };
-        uint4 kA[NJ], kB[NJ];
-        load(p0, kA);
-        for (int p = p0; p <= p1; p += 2) {
-            if (p + 1 <= p1) load(p + 1, kB);
-            score(p, kA);
-            if (p + 1 > p1) break;
-            if (p + 2 <= p1) load(p + 2, kA);
-            score(p + 1, kB);
+        // only K is read: a ring of kScoreDepth pages keeps as many bytes in
+        // flight as the attention kernel's K+V double buffer
+        uint4 kb[kScoreDepth][TPL];
+#pragma unroll
+        for (int j = 0; j + 1 < kScoreDepth; ++j)
+            if (p0 + j <= p1) load(p0 + j, kb[j]);
+        for (int pb = p0; pb <= p1; pb += kScoreDepth) {
+#pragma unroll
+            for (int j = 0; j < kScoreDepth; ++j) {
+                const int p = pb + j;
+                if (p <= p1) {
+                    if (p + kScoreDepth - 1 <= p1) load(p + kScoreDepth - 1, kb[(j + kScoreDepth - 1) % kScoreDepth]);
+                    score(p, kb[j]);
+                }
+            }
         }
     }
 }
@@ -597,10 +652,14 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *lds, int *total)
 }
 
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
-    __shared__ uint32_t hist[256];
+    constexpr int kWaves = kSelectThreads / 64;
+    // one histogram per wave (the top bytes of the scores fall into a few
+    // bins; private copies keep the LDS atomics from serialising on them)
+    __shared__ uint32_t hist[kWaves][256];
     __shared__ int scan_lds[40];
     __shared__ uint32_t pick[2];
     const int sh = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
     if (!a.active[sh / a.hkv]) return;
     const int L = a.lengths[sh];
     const int n = L - a.window, k = a.k - a.window;
@@ -611,23 +670,68 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     uint32_t prefix = 0, mask = 0;
     int remaining = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += kSelectThreads) hist[i] = 0;
+        for (int i = tid; i < kWaves * 256; i += kSelectThreads) (&hist[0][0])[i] = 0;
         __syncthreads();
-        for (int t = tid; t < n; t += kSelectThreads) {
+        // 16 scores per thread per iteration (four 16-byte loads in flight);
+        // the score rows start 16-byte aligned
+        const float4 *sc4 = reinterpret_cast<const float4 *>(sc);
+        const int n4 = n / 4;
+        for (int b = tid; b < n4; b += 4 * kSelectThreads) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = b + u * kSelectThreads < n4 ? sc4[b + u * kSelectThreads]
+                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (b + u * kSelectThreads >= n4) continue;
+                const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t key = order_key(f[e]);
+                    if ((key & mask) == prefix) atomicAdd(&hist[wid][(key >> shift) & 255u], 1u);
+                }
+            }
+        }
+        for (int t = 4 * n4 + tid; t < n; t += kSelectThreads) {
             const uint32_t key = order_key(sc[t]);
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            if ((key & mask) == prefix) atomicAdd(&hist[wid][(key >> shift) & 255u], 1u);
         }
         __syncthreads();
-        if (tid == 0) {
-            int cum = 0;
-            for (int d = 255; d >= 0; --d) {
-                const int c = (int)hist[d];
-                if (cum + c >= remaining) {
-                    pick[0] = (uint32_t)d;
-                    pick[1] = (uint32_t)(remaining - cum);
-                    break;
+        if (tid < 256) {
+            uint32_t total = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) total += hist[w][tid];
+            hist[0][tid] = total;
+        }
+        __syncthreads();
+        if (wid == 0) {
+            // lane l holds bins 255-4l .. 252-4l (descending); find the bin in
+            // which the running count from the top reaches `remaining`
+            int c[4], local = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[j] = (int)hist[0][255 - (4 * lane + j)];
+                local += c[j];
+            }
+            int incl = local;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off);
+                if (lane >= off) incl += y;
+            }
+            const int excl = incl - local;
+            if (excl < remaining && remaining <= incl) {
+                int cum = excl;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (cum + c[j] >= remaining) {
+                        pick[0] = (uint32_t)(255 - (4 * lane + j));
+                        pick[1] = (uint32_t)(remaining - cum);
+                        break;
+                    }
+                    cum += c[j];
                 }
-                cum += c;
             }
         }
         __syncthreads();
@@ -642,10 +746,19 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     for (int c0 = 0; c0 < n; c0 += kSelectThreads * kSelectItems) {
         const int tb = c0 + tid * kSelectItems;
         uint32_t keys[kSelectItems];
+        if (tb + kSelectItems <= n) {
+            const float4 x0 = reinterpret_cast<const float4 *>(sc + tb)[0];
+            const float4 x1 = reinterpret_cast<const float4 *>(sc + tb)[1];
+            const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int u = 0; u < kSelectItems; ++u) keys[u] = order_key(f[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kSelectItems; ++u) keys[u] = tb + u < n ? order_key(sc[tb + u]) : 0u;
+        }
         int gt = 0, eq = 0;
 #pragma unroll
         for (int u = 0; u < kSelectItems; ++u) {
-            keys[u] = tb + u < n ? order_key(sc[tb + u]) : 0u;
             gt += (tb + u < n) && keys[u] > T;
             eq += (tb + u < n) && keys[u] == T;
         }
