@@ -513,6 +513,7 @@ __device__ __forceinline__ float dpp_f(float x) {
 }
 
 constexpr int kScoreDepth = 4;
+constexpr int kScoreSplit = 1;   // waves per plan worker in the scoring kernel
 
 template <int D, int GQA>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
@@ -525,7 +526,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     __shared__ uint4 k_lds[kWavesPerBlock][kPage][LPR + 1];
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int w = blockIdx.x * kWavesPerBlock + wid;
+    // kScoreSplit waves share each plan worker, taking its pages in turn
+    const int wave = blockIdx.x * kWavesPerBlock + wid;
+    const int w = wave / kScoreSplit, part = wave % kScoreSplit;
     if (w >= a.n_workers) return;
     uint4 (*kt)[LPR + 1] = k_lds[wid];
     const int qn = lane & 15, qg = lane >> 4;
@@ -546,7 +549,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
             a.page_table + ((size_t)ld_uniform(a.group_of_head + h) * a.bmax + s) * (size_t)a.max_pages;
         const size_t slot_off = (size_t)ld_uniform(a.slot_of_head + h) * kPage * D;
         float *out = a.scores + (size_t)sh * a.stride;
-        const int p0 = t0 / kPage, p1 = (t1 - 1) / kPage;
+        const int pa = t0 / kPage, p1 = (t1 - 1) / kPage;
+        const int p0 = pa + part;
+        if (p0 > p1) continue;
         // row-major, fully coalesced: an instruction reads RPI whole rows
         auto load = [&](int pi, uint4 (&k)[TPL]) {
             const uint4 *kp = reinterpret_cast<const uint4 *>(
@@ -590,16 +595,18 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         };
         // only K is read: a ring of kScoreDepth pages keeps as many bytes in
         // flight as the attention kernel's K+V double buffer
+        constexpr int S = kScoreSplit;
         uint4 kb[kScoreDepth][TPL];
 #pragma unroll
         for (int j = 0; j + 1 < kScoreDepth; ++j)
-            if (p0 + j <= p1) load(p0 + j, kb[j]);
-        for (int pb = p0; pb <= p1; pb += kScoreDepth) {
+            if (p0 + j * S <= p1) load(p0 + j * S, kb[j]);
+        for (int pb = p0; pb <= p1; pb += kScoreDepth * S) {
 #pragma unroll
             for (int j = 0; j < kScoreDepth; ++j) {
-                const int p = pb + j;
+                const int p = pb + j * S;
                 if (p <= p1) {
-                    if (p + kScoreDepth - 1 <= p1) load(p + kScoreDepth - 1, kb[(j + kScoreDepth - 1) % kScoreDepth]);
+                    const int pf = p + (kScoreDepth - 1) * S;
+                    if (pf <= p1) load(pf, kb[(j + kScoreDepth - 1) % kScoreDepth]);
                     score(p, kb[j]);
                 }
             }
@@ -1063,7 +1070,7 @@ hipError_t launch_score(const ScoreArgs &a, int head_dim, int gqa, hipStream_t s
     if (!fn) return hipErrorInvalidValue;
     if (a.n_workers <= 0) return hipSuccess;
     ScoreArgs copy = a;
-    const unsigned blocks = (unsigned)((a.n_workers + kWavesPerBlock - 1) / kWavesPerBlock);
+    const unsigned blocks = (unsigned)(((long long)a.n_workers * kScoreSplit + kWavesPerBlock - 1) / kWavesPerBlock);
     return launch_raw(fn, dim3(blocks), dim3(256), &copy, sizeof(copy), st);
 }
 
