@@ -279,6 +279,19 @@ def measure_extras(args):
     f_ms = _timed(fused, 20, flush)
     both32 = _timed(lambda: [f() for _ in range(32) for f in (gather, topk)], 3) / 32
     fused32 = _timed(lambda: [fused() for _ in range(32)], 3) / 32
+    # the same 32-layer stack captured in one HIP graph (launch cost amortised)
+    gstream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gstream):
+        fused()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=gstream):
+        for _ in range(32):
+            nup.attn_decode_topk_paged(st.ctx, st.q, idx, K, st.out, st.lse, st.scale, ws,
+                                       stream=torch.cuda.current_stream())
+    graph.replay()
+    torch.cuda.synchronize()
+    graph32 = _timed(graph.replay, 5) / 32
     # selection of the 2048 entries (1024 recent) from all 122880 positions
     sel_idx = torch.empty((w.batch, 8, K), dtype=torch.int32, device="cuda")
     ws_sel = torch.empty(nup.select_workspace_bytes(st.ctx), dtype=torch.uint8, device="cuda")
@@ -295,10 +308,12 @@ def measure_extras(args):
         "topk_in_place_ms": round(f_ms, 4),
         "topk_in_place_GBs": round((rows * (512 + 4) + w.batch * 32 * 128 * 6) / (f_ms * 1e-3) / 1e9, 1),
         "topk_in_place_ms_32_back_to_back": round(fused32, 4),
+        "topk_in_place_ms_32_layer_graph": round(graph32, 4),
         "select_ms": round(s_ms, 4),
         "select_score_GBs": round(k_bytes / (s_ms * 1e-3) / 1e9, 1),
         "note": "per call cold (1 GiB read before each); 32 back-to-back pairs for a 32-layer stack"}
     assert nup.device_errors(st.ctx) == nup.NUP_OK
+    del graph
     st.free()
     del st, ks, vs, ws, sel_idx, ws_sel
 

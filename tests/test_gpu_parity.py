@@ -666,3 +666,44 @@ def test_full_size_llama_select_then_attend():
         rows = slice(h * gqa, (h + 1) * gqa)
         assert_attention_close(out[seqs[i], rows], lse[seqs[i], rows], ref[i, rows], ref_lse[i, rows],
                                f"select+attend {seqs[i]},{h}")
+
+
+def test_graph_replays_match_eager():
+    """A 4-layer stack of in-place top-K attention calls captured in one HIP
+    graph: every replay, with eager work in between, equals the eager run."""
+    c, L, caps = _gather_case(50, B=2, H=8, gqa=4, ng=1)
+    c.alloc([0, 1], caps, L)
+    c.commit()
+    K = 64
+    idx = torch.from_numpy(W.topk_indices(c.spec.lengths, K, salt=50)).to(DEV)
+    ws = torch.empty(nup.workspace_bytes(c.ctx, K), dtype=torch.uint8, device=DEV)
+    layers = 4
+    outs = [torch.empty_like(c.out) for _ in range(layers)]
+    lses = [torch.empty_like(c.lse) for _ in range(layers)]
+    qs = [c.q.clone() for _ in range(layers)]
+    for i, q in enumerate(qs):
+        q.copy_((q.float() * (1.0 + 0.25 * i)).to(torch.bfloat16))
+    stream = torch.cuda.Stream()
+
+    def run():
+        for i in range(layers):
+            nup.attn_decode_topk_paged(c.ctx, qs[i], idx, K, outs[i], lses[i], c.scale, ws,
+                                       stream=torch.cuda.current_stream())
+
+    with torch.cuda.stream(stream):
+        run()
+    torch.cuda.synchronize()
+    eager = [(o.clone(), l.clone()) for o, l in zip(outs, lses)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        nup.attn_decode_nonuniform(c.ctx, c.q, c.out, c.lse, c.scale,
+                                   torch.empty(nup.workspace_bytes(c.ctx), dtype=torch.uint8, device=DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(layers):
+            assert torch.equal(outs[i], eager[i][0]) and torch.equal(lses[i], eager[i][1]), (rep, i)
