@@ -14,11 +14,16 @@ are the plainest ones and are listed with the others in the design notes):
     its page is its position inside its group.
   * Pages per (sequence, group): the group's largest capacity, in pages
     (one page table per group, sized to the group's most demanding head).
-  * Block pager -- KV-RM, Fig 3 (Reserve / Trim edits).  A FIFO free list,
-    initialised to a given permutation (or 0..N-1).  Reserve pops from the
-    front for the sequences in call order, groups in order, logical pages
-    in order; it is all-or-nothing.  Trim pushes a sequence's pages to the
-    back in (group, logical page) order.
+  * Block pager -- KV-RM, Fig 3 (Reserve / Trim / Alias edits).  A FIFO
+    free list, initialised to a given permutation (or 0..N-1).  Reserve pops
+    from the front for the sequences in call order, groups in order, logical
+    pages in order; it is all-or-nothing.  Every physical page carries a
+    count of the page-table entries that map it.  Alias is a Reserve whose
+    first share[g] logical pages of group g map the pages a live source
+    sequence holds there (their counts grow by one) instead of popping new
+    ones; shared pages must be full in both sequences, so no append ever
+    writes to them.  Trim drops a sequence's references in (group, logical
+    page) order and pushes a page to the back when its count reaches zero.
   * Append -- the decode step writes the new token at logical slot L and
     then L grows by one; a fixed budget means L == capacity is an error.
   * Trains -- KV-RM, Fig 3 (descriptor merging into few large transfers):
@@ -71,6 +76,7 @@ class PagerSpec:
         self.lengths = np.zeros((max_batch, num_kv_heads), dtype=np.int32)
         self.caps = np.zeros((max_batch, num_kv_heads), dtype=np.int32)
         self.active = np.zeros(max_batch, dtype=bool)
+        self.ref = np.zeros(num_pages, dtype=np.int32)
         self.group_of_head = None
         self.slot_of_head = None
 
@@ -106,6 +112,66 @@ class PagerSpec:
             for g in range(self.ng):
                 for j in range(int(need[i, g])):
                     self.page_table[g, s, j] = self.free.popleft()
+                    self.ref[self.page_table[g, s, j]] = 1
+                self.n_pages[g, s] = need[i, g]
+            self.caps[s] = caps[i]
+            self.lengths[s] = lengths[i]
+            self.active[s] = True
+        return OK
+
+    # ---- Alias --------------------------------------------------------------
+    def alias(self, slots, src_slots, share, caps, lengths) -> int:
+        """Reserve slots[i] with its first share[i][g] logical pages of every
+        group g mapped to the pages src_slots[i] holds there.
+
+        Checks, in order: argument ranges (E_ARG); slots inactive and sources
+        active (E_STATE); for every head h of group g, share*P within both the
+        new length and the source's current length (E_ARG); enough free pages
+        for the unshared rest (E_NOPAGES)."""
+        slots = [int(s) for s in slots]
+        src_slots = [int(s) for s in src_slots]
+        n = len(slots)
+        caps = np.asarray(caps, dtype=np.int64).reshape(n, self.hkv)
+        lengths = np.asarray(lengths, dtype=np.int64).reshape(n, self.hkv)
+        share = np.asarray(share, dtype=np.int64).reshape(n, self.ng)
+        if n == 0:
+            return OK
+        if len(src_slots) != n or len(set(slots)) != n:
+            return E_ARG
+        if any(s < 0 or s >= self.bmax for s in slots + src_slots):
+            return E_ARG
+        if set(slots) & set(src_slots):
+            return E_ARG
+        if (caps < 0).any() or (caps > self.max_pages * self.P).any():
+            return E_ARG
+        if (lengths < 0).any() or (lengths > caps).any() or (share < 0).any():
+            return E_ARG
+        if any(self.active[s] for s in slots) or not all(self.active[s] for s in src_slots):
+            return E_STATE
+        goh = self.group_of_head
+        for i in range(n):
+            for h in range(self.hkv):
+                tokens = int(share[i, goh[h]]) * self.P
+                if tokens > lengths[i, h] or tokens > self.lengths[src_slots[i], h]:
+                    return E_ARG
+        need = np.zeros((n, self.ng), dtype=np.int64)
+        for i in range(n):
+            for g in range(self.ng):
+                members = [h for h in range(self.hkv) if goh[h] == g]
+                need[i, g] = math.ceil(max(int(caps[i, h]) for h in members) / self.P)
+        if (need - share).sum() > len(self.free):
+            return E_NOPAGES
+        for i, s in enumerate(slots):
+            src = src_slots[i]
+            for g in range(self.ng):
+                for j in range(int(need[i, g])):
+                    if j < share[i, g]:
+                        page = int(self.page_table[g, src, j])
+                        self.ref[page] += 1
+                    else:
+                        page = self.free.popleft()
+                        self.ref[page] = 1
+                    self.page_table[g, s, j] = page
                 self.n_pages[g, s] = need[i, g]
             self.caps[s] = caps[i]
             self.lengths[s] = lengths[i]
@@ -122,7 +188,10 @@ class PagerSpec:
         for s in slots:
             for g in range(self.ng):
                 for j in range(int(self.n_pages[g, s])):
-                    self.free.append(int(self.page_table[g, s, j]))
+                    page = int(self.page_table[g, s, j])
+                    self.ref[page] -= 1
+                    if self.ref[page] == 0:
+                        self.free.append(page)
                     self.page_table[g, s, j] = -1
                 self.n_pages[g, s] = 0
             self.caps[s] = 0

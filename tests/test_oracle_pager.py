@@ -10,6 +10,7 @@ from hypothesis import given, settings, strategies as st
 from oracle import pager as pg
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_pager.json")))
+ALIAS = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_alias.json")))
 
 
 def _tiny(free_list_init=None):
@@ -43,6 +44,72 @@ def test_tiny_scrambled_fixture():
     p = _tiny(np.array(sc["free_list_init"]))
     runs = pg.coalesce(p.page_table, p.n_pages, p.active)
     assert [list(r) for r in runs] == sc["runs"]
+
+
+def _alias_state():
+    p = pg.PagerSpec(4, 2, 3, 64, 16, 16)
+    b = np.array([ALIAS["slot0_budgets"]])
+    assert p.alloc([0], b, b) == pg.OK
+    return p
+
+
+def _alias_call(p, a):
+    return p.alias([a["slot"]], [a["src"]], np.array([a["share_pages"]]),
+                   np.array([a["caps"]]), np.array([a["lens"]]))
+
+
+def test_tiny_alias_fixture():
+    p = _alias_state()
+    assert _alias_call(p, ALIAS["alias"]) == pg.OK
+    assert p.page_table[:, 2].tolist() == ALIAS["page_table_slot2"]
+    assert p.free_list().tolist() == ALIAS["free_list_after_alias"]
+    assert p.ref.tolist() == ALIAS["refcounts_after_alias"]
+    runs = pg.coalesce(p.page_table, p.n_pages, p.active)
+    assert [list(r) for r in runs] == ALIAS["runs_after_alias"]
+    assert p.physical_row(2, 3, 37) == ALIAS["physical_row_s2_h3_t37"]
+    assert p.physical_row(0, 3, 37) == ALIAS["physical_row_s0_h3_t37"]
+    assert p.physical_row(2, 3, 85) == ALIAS["physical_row_s2_h3_t85"]
+    assert p.lengths[2].tolist() == ALIAS["alias"]["lens"]
+    assert p.free_seqs([0]) == pg.OK
+    assert p.free_list().tolist() == ALIAS["free_list_after_trim_slot0"]
+    assert p.free_seqs([2]) == pg.OK
+    assert p.free_list().tolist() == ALIAS["free_list_after_trim_slot2"]
+    assert (p.ref == 0).all()
+
+
+def test_tiny_alias_errors_are_all_or_nothing():
+    codes = {"E_ARG": pg.E_ARG, "E_STATE": pg.E_STATE, "E_NOPAGES": pg.E_NOPAGES}
+    p = _alias_state()
+    # the source must be live
+    assert p.alias([2], [1], np.zeros((1, 2)), np.full((1, 4), 16), np.zeros((1, 4))) == pg.E_STATE
+    assert _alias_call(p, ALIAS["alias"]) == pg.OK
+    snap = (p.page_table.copy(), p.free_list().copy(), p.ref.copy(), p.lengths.copy(), p.active.copy())
+    for name, case in ALIAS["errors_from_alias_state"].items():
+        assert _alias_call(p, case) == codes[case["status"]], name
+        assert np.array_equal(snap[0], p.page_table) and np.array_equal(snap[1], p.free_list())
+        assert np.array_equal(snap[2], p.ref) and np.array_equal(snap[3], p.lengths)
+        assert np.array_equal(snap[4], p.active)
+    ok = ALIAS["shared_needs_25_of_31"]
+    assert _alias_call(p, ok) == pg.OK
+    assert len(p.free_list()) == ok["free_after"]
+
+
+def test_alias_with_no_shared_pages_is_a_reserve():
+    """share = 0 everywhere: the same page tables, lengths and free list as
+    kv_alloc of the same capacities."""
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(80)
+    a = pg.PagerSpec(4, 2, 4, 80, 8, 16, perm)
+    b = pg.PagerSpec(4, 2, 4, 80, 8, 16, perm)
+    c0 = np.array([[16, 40, 100, 128]])
+    assert a.alloc([0], c0, c0) == pg.OK and b.alloc([0], c0, c0) == pg.OK
+    caps = np.array([[30, 7, 128, 90], [0, 0, 0, 16]])
+    lens = np.array([[3, 7, 0, 90], [0, 0, 0, 1]])
+    assert a.alias([3, 1], [0, 0], np.zeros((2, 2)), caps, lens) == pg.OK
+    assert b.alloc([3, 1], caps, lens) == pg.OK
+    assert np.array_equal(a.page_table, b.page_table)
+    assert np.array_equal(a.free_list(), b.free_list())
+    assert np.array_equal(a.lengths, b.lengths) and np.array_equal(a.ref, b.ref)
 
 
 def test_physical_row_matches_layout_definition():
@@ -83,6 +150,80 @@ def test_append_capacity():
     assert p2.alloc([1], np.array([[17, 4]]), np.array([[15, 3]])) == pg.OK
     st_, pos = p2.append_positions()
     assert st_ == pg.OK and pos[1].tolist() == [15, 3] and p2.lengths[1].tolist() == [16, 4]
+
+
+def _check_refcounts(p):
+    """Counts equal the number of live entries mapping each page; pages in
+    use and the free list partition the pool; the next append of every live
+    head lands on a page that only it maps."""
+    used = p.page_table[p.page_table >= 0]
+    count = np.bincount(used, minlength=p.num_pages) if used.size else np.zeros(p.num_pages, int)
+    assert np.array_equal(count, p.ref)
+    free = p.free_list().tolist()
+    assert len(set(free)) == len(free)
+    assert sorted(set(used.tolist())) + [] == sorted(set(range(p.num_pages)) - set(free))
+    for s in range(p.bmax):
+        if not p.active[s]:
+            continue
+        for h in range(p.hkv):
+            t = int(p.lengths[s, h])
+            if t < p.caps[s, h]:
+                page = p.page_table[p.group_of_head[h], s, t // p.P]
+                assert p.ref[page] == 1, (s, h, t)
+
+
+@settings(max_examples=100, deadline=None)
+@given(st.data())
+def test_pager_alias_invariants(data):
+    """Random Reserve / Alias / Trim / append sequences keep the counts,
+    the partition of the pool and the exclusivity of every page an append
+    can write."""
+    hkv, ng = 4, data.draw(st.sampled_from([1, 2, 4]))
+    bmax, num_pages, max_pages = 6, 60, 8
+    perm = data.draw(st.permutations(list(range(num_pages))))
+    p = pg.PagerSpec(hkv, ng, bmax, num_pages, max_pages, 16, np.array(perm))
+    for _ in range(data.draw(st.integers(1, 14))):
+        op = data.draw(st.sampled_from(["alloc", "alias", "free", "append"]))
+        idle = [s for s in range(bmax) if not p.active[s]]
+        live = [s for s in range(bmax) if p.active[s]]
+        if op == "alloc" and idle:
+            s = data.draw(st.sampled_from(idle))
+            caps = np.array([[data.draw(st.integers(0, max_pages * 16)) for _ in range(hkv)]])
+            lens = np.array([[data.draw(st.just(int(c)) | st.integers(0, int(c))) for c in caps[0]]])
+            rc = p.alloc([s], caps, lens)
+            assert rc in (pg.OK, pg.E_NOPAGES)
+        elif op == "alias" and idle and live:
+            s = data.draw(st.sampled_from(idle))
+            src = data.draw(st.sampled_from(live))
+            share = np.zeros((1, ng), np.int64)
+            caps = np.zeros((1, hkv), np.int64)
+            lens = np.zeros((1, hkv), np.int64)
+            for g in range(ng):
+                members = [h for h in range(hkv) if p.group_of_head[h] == g]
+                most = min(int(p.lengths[src, h]) for h in members) // 16
+                share[0, g] = data.draw(st.integers(0, most + 1))   # one past the limit now and then
+                for h in members:
+                    caps[0, h] = data.draw(st.integers(min(16 * most, max_pages * 16), max_pages * 16))
+                    lens[0, h] = data.draw(st.integers(min(16 * int(share[0, g]), int(caps[0, h])),
+                                                       int(caps[0, h])))
+            before = (p.page_table.copy(), p.free_list().copy(), p.ref.copy())
+            rc = p.alias([s], [src], share, caps, lens)
+            if rc == pg.OK:
+                for g in range(ng):
+                    k = int(share[0, g])
+                    assert np.array_equal(p.page_table[g, s, :k], p.page_table[g, src, :k])
+            else:
+                assert rc in (pg.E_ARG, pg.E_NOPAGES)
+                assert np.array_equal(before[0], p.page_table)
+                assert np.array_equal(before[1], p.free_list())
+                assert np.array_equal(before[2], p.ref)
+        elif op == "free" and live:
+            slots = data.draw(st.lists(st.sampled_from(live), min_size=1, max_size=3, unique=True))
+            assert p.free_seqs(slots) == pg.OK
+        elif op == "append" and live:
+            if (p.lengths[p.active] < p.caps[p.active]).all():
+                assert p.append_positions()[0] == pg.OK
+        _check_refcounts(p)
 
 
 @settings(max_examples=60, deadline=None)
