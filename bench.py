@@ -86,7 +86,21 @@ class Setup:
         self.ctx = nup.Context(**cfg, k_pool=self.kpool, v_pool=self.vpool, desc=self.desc,
                                free_list_init=free_list)
         self.free_list = free_list
-        nup.kv_alloc_groups(self.ctx, np.arange(B), self.caps, self.lengths0)
+        src = w.extra.get("alias_src")
+        if src is None:
+            nup.kv_alloc_groups(self.ctx, np.arange(B), self.caps, self.lengths0)
+        else:
+            # forked sessions: Reserve the sources, then Alias the forks onto
+            # the whole pages of their shared prefix
+            roots = np.nonzero(src < 0)[0]
+            forks = np.nonzero(src >= 0)[0]
+            goh = nup.kv_alloc_groups(self.ctx, roots, self.caps[roots], self.lengths0[roots])
+            pre = w.extra["prefix_tokens"]
+            self.share = np.zeros((len(forks), ng), np.int32)
+            for g in range(ng):
+                self.share[:, g] = pre[forks][:, goh == g].min(axis=1) // 16
+            nup.kv_alias(self.ctx, forks, src[forks], self.share, self.caps[forks], self.lengths0[forks])
+            self.goh = goh
         nup.nup_commit(self.ctx)
         self.q = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
         W.fill_normal_bf16_torch(self.q, "q")
@@ -220,6 +234,30 @@ def _timed(fn, iters, flush=None):
         torch.cuda.synchronize()
         total += e0.elapsed_time(e1)
     return total / iters
+
+
+def _dma_trains(st, ks, vs, row_off, flush):
+    """kv_gather_trains_dma on the current state: cold time, copies, the
+    host's enqueue time, and bit equality with the gather kernel's rows."""
+    import torch
+    import non_uniform_paged_amd as nup
+    ref_k, ref_v = ks.clone(), vs.clone()
+    ks.zero_()
+    vs.zero_()
+    n = nup.kv_gather_trains_dma(st.ctx, ks, vs, row_off)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ks, ref_k) and torch.equal(vs, ref_v))
+    del ref_k, ref_v
+    enq = []
+
+    def run():
+        t0 = time.perf_counter()
+        nup.kv_gather_trains_dma(st.ctx, ks, vs, row_off)
+        enq.append(time.perf_counter() - t0)
+    ms = _timed(run, 3, flush)
+    nbytes = 2 * ks.shape[0] * ks.shape[1] * 2
+    return {"copies": n, "ms": round(ms, 4), "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "host_enqueue_ms": round(1e3 * float(np.mean(enq)), 3), "rows_equal_kernel": same}
 
 
 def measure_extras(args):
@@ -372,6 +410,7 @@ def measure_extras(args):
     gt = lambda: nup.kv_gather_compact(st.ctx, 0, ksg, vsg, row_off=row_off)
     gt()
     g_ms = _timed(gt, 5, flush)
+    dma = _dma_trains(st, ksg, vsg, row_off.cpu().numpy(), flush)
     res["mixed_churn"] = {
         "active_slots": int(active.sum()), "kv_bytes": kb,
         "host_trim_reserve_commit_us_mean": round(float(np.mean(host_us)), 1),
@@ -382,9 +421,60 @@ def measure_extras(args):
         "partial_kernel_ms": round(kms, 4),
         "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
         "gather_trains_ms": round(g_ms, 4),
-        "gather_trains_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1)}
+        "gather_trains_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1),
+        "gather_trains_copy_engine": dma}
     st.free()
     del st, ksg, vsg
+    torch.cuda.empty_cache()
+
+    # -- the Qwen2.5-32B batch (long trains): gather kernel vs copy engines
+    w = W.qwen25_32b()
+    st = Setup(w, 0)
+    lens = st.lengths0.astype(np.int64).reshape(-1)
+    ro = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    total = int(lens.sum())
+    ksg = torch.empty((total, 128), dtype=torch.bfloat16, device="cuda")
+    vsg = torch.empty_like(ksg)
+    ro_dev = torch.from_numpy(ro).cuda()
+    gt = lambda: nup.kv_gather_compact(st.ctx, 0, ksg, vsg, row_off=ro_dev)
+    gt()
+    g_ms = _timed(gt, 5, flush)
+    res["qwen25_32b_trains"] = {"trains": int(len(nup.get_runs(st.ctx))), "bytes": 2 * total * 256,
+                                "gather_kernel_ms": round(g_ms, 4),
+                                "gather_kernel_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1),
+                                "copy_engine": _dma_trains(st, ksg, vsg, ro, flush)}
+    st.free()
+    del st, ksg, vsg, ro_dev
+    torch.cuda.empty_cache()
+
+    # -- forked sessions sharing a prompt prefix (KV-RM Alias): same lengths as
+    #    the Qwen2.5-32B batch, 60 of 64 sessions fork from 4 sources
+    w = W.qwen25_32b_prefix()
+    st = Setup(w, 0)
+    for _ in range(2):
+        st.step(append=False)
+    torch.cuda.synchronize()
+    nup.kernel_time(st.ctx, reset=True)
+    nup.set_timing(st.ctx, True)
+    _timed(lambda: st.step(append=False), 10, flush)
+    nup.set_timing(st.ctx, False)
+    kms, n = nup.kernel_time(st.ctx, reset=True)
+    kms /= max(n, 1)
+    in_use = int(st.num_pages - len(nup.get_free_list(st.ctx)))
+    entries = int(sum(np.count_nonzero(r >= 0) for r in nup.get_page_table(st.ctx)))
+    kb = kv_bytes(st.lengths0)
+    shared_b = int(sum(int(st.share[i, st.goh[h]]) * 16 * 512
+                       for i in range(len(st.share)) for h in range(w.num_kv_heads)))
+    res["qwen25_32b_prefix"] = {
+        "prefix_ctx": w.extra["prefix_ctx"], "sources": int((w.extra["alias_src"] < 0).sum()),
+        "pages_in_use": in_use, "page_table_entries": entries,
+        "reserved_saving": round(1 - in_use / entries, 4),
+        "kv_bytes_logical": kb, "kv_bytes_unique": kb - shared_b,
+        "partial_kernel_ms": round(kms, 4),
+        "partial_kernel_logical_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
+        "note": "cold (1 GiB read before each step); logical bytes count every session's reads"}
+    st.free()
+    del st
     torch.cuda.empty_cache()
 
     # -- heads per page (Tangram, Fig 8c): the Qwen2.5-32B batch with 1, 2, 4, 8 groups

@@ -136,9 +136,32 @@ nup_status kv_alloc_groups(nup_ctx *ctx, int32_t n, const int32_t *slots,
                            const int32_t *cap, const int32_t *len,
                            int32_t *group_of_head_out);
 
-/* kv_free_seqs -- Trim (KV-RM, Fig 3; EOS absorbed by the pager): return the
- * slots' pages to the back of the free list in (group, logical page) order
- * and mark the slots inactive.  Errors: NUP_E_ARG, NUP_E_STATE (not active). */
+/*
+ * kv_alias -- Alias (KV-RM, Fig 3: a mapping edit next to Reserve and Trim):
+ * reserve new slots whose leading pages are the physical pages of a live
+ * source sequence, e.g. a shared prompt prefix.  Sequence i gets, in every
+ * group g, page-table entries 0..share_pages[i][g]-1 equal to those of
+ * src_slots[i] (each such page's reference count grows by one); the rest of
+ * its ceil(max cap over the group / P) pages are popped from the free list
+ * as kv_alloc_groups does.
+ *   slots       [n] new slots (inactive, distinct, none of them a source)
+ *   src_slots   [n] active source slots (repeats allowed)
+ *   share_pages [n][n_g] whole pages shared per group (>= 0)
+ *   cap, len    [n][H_kv] as for kv_alloc_groups; len is required
+ * Shared pages must be full in both sequences: for every head h of group g,
+ * share_pages*P <= len (new) and <= the source's current length, so that no
+ * append ever writes a shared page.  The K/V rows of shared positions are
+ * the source's; rows at len.. of unshared pages are the caller's to fill.
+ * Checks run in this order: arguments (NUP_E_ARG), slot states
+ * (NUP_E_STATE), the shares against both lengths (NUP_E_ARG), free pages
+ * for the unshared rest (NUP_E_NOPAGES); nothing changes on failure. */
+nup_status kv_alias(nup_ctx *ctx, int32_t n, const int32_t *slots, const int32_t *src_slots,
+                    const int32_t *share_pages, const int32_t *cap, const int32_t *len);
+
+/* kv_free_seqs -- Trim (KV-RM, Fig 3; EOS absorbed by the pager): drop the
+ * slots' page references in (group, logical page) order, pushing a page to
+ * the back of the free list when its last reference goes, and mark the
+ * slots inactive.  Errors: NUP_E_ARG, NUP_E_STATE (not active). */
 nup_status kv_free_seqs(nup_ctx *ctx, int32_t n, const int32_t *slots);
 
 /* nup_commit -- seal the step (KV-RM, Fig 3: one Frame commit through a
@@ -180,6 +203,24 @@ nup_status kv_append(nup_ctx *ctx, const void *k_new, const void *v_new, void *s
 nup_status kv_gather_compact(nup_ctx *ctx, int32_t mode, const int32_t *idx, int32_t K,
                              void *k_out, void *v_out, const int64_t *row_off,
                              int32_t *phys_out, void *stream);
+
+/*
+ * kv_gather_trains_dma -- the train copy of kv_gather_compact mode 0 moved by
+ * the copy engines instead of a kernel (KV-RM, Fig 2: the transport turns
+ * the mapping into coalesced transfers for the DMA engine).  Same rows and
+ * destination layout: for every active (s, h), rows 0..L-1 go to k_out/v_out
+ * rows row_off[s*H_kv + h] .. + L - 1, bit-exact.
+ *   row_off   HOST int64 [B_max*H_kv] (the host issues the copies, so it
+ *             needs the offsets; the destination rows must not overlap)
+ *   n_copies  optional host int32: receives the number of copies enqueued
+ * Per (train, head) one strided copy of the full pages (source pitch G_h
+ * pages) and one copy of a partial last page, for K and for V, all enqueued
+ * on `stream` as device-to-device copies that use no compute units.  Reads
+ * the host's view of the trains and lengths, so it needs a committed
+ * descriptor with no pending edits (NUP_E_STATE).  Errors: NUP_E_ARG,
+ * NUP_E_STATE, NUP_E_HIP. */
+nup_status kv_gather_trains_dma(nup_ctx *ctx, void *k_out, void *v_out, const int64_t *row_off,
+                                int32_t *n_copies, void *stream);
 
 /* Workspace bytes attn_decode_nonuniform / attn_decode_topk need for split-K
  * partial results at this configuration (K = top-K count, 0 for the paged
@@ -260,6 +301,9 @@ nup_status nup_get_lengths(const nup_ctx *ctx, int32_t *out);
 nup_status nup_get_groups(const nup_ctx *ctx, int32_t *group_of_head, int32_t *slot_of_head);
 /* Free list front to back: int32 [num_pages] capacity, count in *n. */
 nup_status nup_get_free_list(const nup_ctx *ctx, int32_t *out, int32_t *n);
+/* Reference count of every physical page (host shadow): int32 [num_pages]. */
+nup_status nup_get_refcounts(const nup_ctx *ctx, int32_t *out);
+
 /* Trains of the shadow page tables: int32 [max_runs][5] rows of
  * (slot, group, first physical page, pages, first logical page) in (slot,
  * group, logical page) order; count in *n (NUP_E_ARG if max_runs is short). */

@@ -55,7 +55,9 @@ _sigs = {
     "nup_desc_bytes": [_P, _P],
     "nup_create": [_P, _P],
     "kv_alloc_groups": [_P, _I, _P, _P, _P, _P],
+    "kv_alias": [_P, _I, _P, _P, _P, _P, _P],
     "kv_free_seqs": [_P, _I, _P],
+    "kv_gather_trains_dma": [_P, _P, _P, _P, _P, _P],
     "nup_commit": [_P, _P],
     "kv_append": [_P, _P, _P, _P],
     "kv_gather_compact": [_P, _I, _P, _I, _P, _P, _P, _P, _P],
@@ -69,6 +71,7 @@ _sigs = {
     "nup_get_lengths": [_P, _P],
     "nup_get_groups": [_P, _P, _P],
     "nup_get_free_list": [_P, _P, _P],
+    "nup_get_refcounts": [_P, _P],
     "nup_get_runs": [_P, _P, _I, _P],
     "nup_get_plan": [_P, _P, _P, _P, _P, _P],
     "nup_set_timing": [_P, _I],
@@ -182,6 +185,18 @@ def len_(a) -> int:
     return int(np.asarray(a).shape[0])
 
 
+def kv_alias(ctx: Context, slots, src_slots, share_pages, cap, len, raise_on_error=True):
+    slots = _i32(slots)
+    n = len_(slots)
+    src = _i32(src_slots).reshape(n)
+    share = _i32(share_pages).reshape(n, ctx.ng)
+    cap = _i32(cap).reshape(n, ctx.H)
+    ln = _i32(len).reshape(n, ctx.H)
+    st = _lib.kv_alias(ctx.handle, n, slots.ctypes.data, src.ctypes.data, share.ctypes.data,
+                       cap.ctypes.data, ln.ctypes.data)
+    return ctx.check(st) if raise_on_error else st
+
+
 def kv_free_seqs(ctx: Context, slots, raise_on_error=True):
     slots = _i32(slots)
     st = _lib.kv_free_seqs(ctx.handle, len_(slots), slots.ctypes.data if len_(slots) else None)
@@ -203,6 +218,21 @@ def kv_gather_compact(ctx: Context, mode: int, k_out, v_out, idx=None, K: int = 
     st = _lib.kv_gather_compact(ctx.handle, mode, _ptr(idx), K, _ptr(k_out), _ptr(v_out),
                                 _ptr(row_off), _ptr(phys_out), _stream(stream))
     return ctx.check(st) if raise_on_error else st
+
+
+def kv_gather_trains_dma(ctx: Context, k_out, v_out, row_off, stream=None, raise_on_error=True):
+    """row_off: host int64 array [B_max*H_kv].  Returns the number of copies
+    enqueued (or the status when raise_on_error is False)."""
+    ro = np.ascontiguousarray(np.asarray(row_off, dtype=np.int64).reshape(-1))
+    if ro.size != ctx.B * ctx.H:
+        raise ValueError("row_off must hold B_max*H_kv offsets")
+    n = ctypes.c_int32()
+    st = _lib.kv_gather_trains_dma(ctx.handle, _ptr(k_out), _ptr(v_out), ro.ctypes.data,
+                                   ctypes.byref(n), _stream(stream))
+    if raise_on_error:
+        ctx.check(st)
+        return n.value
+    return st
 
 
 def workspace_bytes(ctx: Context, K: int = 0) -> int:
@@ -275,6 +305,12 @@ def get_free_list(ctx: Context) -> np.ndarray:
     n = ctypes.c_int32()
     ctx.check(_lib.nup_get_free_list(ctx.handle, out.ctypes.data, ctypes.byref(n)))
     return out[: n.value]
+
+
+def get_refcounts(ctx: Context) -> np.ndarray:
+    out = np.zeros(ctx.num_pages, np.int32)
+    ctx.check(_lib.nup_get_refcounts(ctx.handle, out.ctypes.data))
+    return out
 
 
 def get_runs(ctx: Context) -> np.ndarray:

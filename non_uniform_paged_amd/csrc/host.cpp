@@ -85,7 +85,10 @@ Sizes compute_sizes(const nup_config &c, int workers) {
     z.fixed = align_up(4 * (B + B * H + 3 * H));
     z.plan_max = align_up(4 * ((size_t)z.max_workers + 1)) + align_up(4 * (B * H + 1)) +
                  align_up(16 * (size_t)z.max_rows);
-    z.runs_max = align_up(16 * (size_t)c.num_pages) + align_up(4 * ((size_t)c.num_pages + 1));
+    // every train covers at least one live page-table entry; with Alias the
+    // entries (not the physical pages) are what bounds their number
+    const size_t entries = ng * B * (size_t)c.max_pages;
+    z.runs_max = align_up(16 * entries) + align_up(4 * (entries + 1));
     z.patches_max = align_up(16 * ng * B) + align_up(4 * ng * B * (size_t)c.max_pages);
     z.inbox = z.fixed + z.plan_max + z.runs_max + z.patches_max;
     z.pt = align_up(4 * ng * B * (size_t)c.max_pages);
@@ -110,6 +113,7 @@ struct nup_ctx {
     std::vector<int32_t> npages;   // [ng][B]
     std::vector<int32_t> len, cap; // [B][H]
     std::vector<int32_t> active;   // [B]
+    std::vector<int32_t> ref;      // [num_pages]: page-table entries mapping each page
     std::vector<int32_t> goh, soh, head_of_gslot;
     bool grouped = false;
 
@@ -318,20 +322,59 @@ void row_trains(const int32_t *row, int n, std::vector<int32_t> &out) {
 
 // Appends (slot, group, first physical page, pages, first logical page) for
 // every active slot in (slot, group, logical page) order.
+const std::vector<int32_t> &runs_of_row(nup_ctx *c, size_t ri) {
+    if (c->runs_stale[ri]) {
+        row_trains(&c->pt[ri * c->max_pages], c->npages[ri], c->row_runs[ri]);
+        c->runs_stale[ri] = 0;
+    }
+    return c->row_runs[ri];
+}
+
 void build_runs(nup_ctx *c, std::vector<int32_t> &out) {
     out.clear();
     for (int s = 0; s < c->B; ++s) {
         if (!c->active[s]) continue;
         for (int g = 0; g < c->ng; ++g) {
-            const size_t ri = (size_t)g * c->B + s;
-            if (c->runs_stale[ri]) {
-                row_trains(&c->pt[ri * c->max_pages], c->npages[ri], c->row_runs[ri]);
-                c->runs_stale[ri] = 0;
-            }
-            const std::vector<int32_t> &rr = c->row_runs[ri];
+            const std::vector<int32_t> &rr = runs_of_row(c, (size_t)g * c->B + s);
             for (size_t k = 0; k < rr.size(); k += 3) out.insert(out.end(), {s, g, rr[k], rr[k + 1], rr[k + 2]});
         }
     }
+}
+
+// Bring slot s to life with need[g] pages per group.  The first share[g] of
+// them are the pages source slot `src` holds at the same logical positions
+// (Alias, KV-RM Fig 3: their counts grow by one); the rest are popped from
+// the front of the free list.  cap/len: this slot's [H] rows (len NULL = 0).
+// The caller has checked everything, including the free-page count.
+void install(nup_ctx *c, int s, const int32_t *need, int src, const int32_t *share,
+             const int32_t *cap, const int32_t *len) {
+    for (int g = 0; g < c->ng; ++g) {
+        const int np = need[g];
+        const int shared = share ? share[g] : 0;
+        const size_t ri = (size_t)g * c->B + s;
+        int32_t *row = &c->pt[ri * c->max_pages];
+        const int32_t *src_row = src >= 0 ? &c->pt[((size_t)g * c->B + src) * c->max_pages] : nullptr;
+        for (int j = 0; j < np; ++j) {
+            int32_t page;
+            if (j < shared) {
+                page = src_row[j];
+                ++c->ref[page];
+            } else {
+                page = c->free_list.front();
+                c->free_list.pop_front();
+                c->ref[page] = 1;
+            }
+            row[j] = page;
+        }
+        c->dirty_count[ri] = std::max(c->dirty_count[ri], np);
+        c->npages[ri] = np;
+        c->runs_stale[ri] = 1;
+    }
+    for (int h = 0; h < c->H; ++h) {
+        c->cap[(size_t)s * c->H + h] = cap[h];
+        c->len[(size_t)s * c->H + h] = len ? len[h] : 0;
+    }
+    c->active[s] = 1;
 }
 
 }  // namespace
@@ -424,6 +467,7 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
     c->len.assign((size_t)c->B * c->H, 0);
     c->cap.assign((size_t)c->B * c->H, 0);
     c->active.assign(c->B, 0);
+    c->ref.assign(c->num_pages, 0);
     c->goh.assign(c->H, -1);
     c->soh.assign(c->H, -1);
     c->head_of_gslot.assign(c->H, -1);
@@ -504,29 +548,76 @@ nup_status kv_alloc_groups(nup_ctx *c, int32_t n, const int32_t *slots, const in
         return fail(c, NUP_E_NOPAGES, "need %lld pages, %zu free", total, c->free_list.size());
 
     if (!c->grouped) group_heads(c, n, cap);
-    for (int i = 0; i < n; ++i) {
-        const int s = slots[i];
-        for (int g = 0; g < c->ng; ++g) {
-            const int np = need[(size_t)i * c->ng + g];
-            int32_t *row = &c->pt[((size_t)g * c->B + s) * c->max_pages];
-            for (int j = 0; j < np; ++j) {
-                row[j] = c->free_list.front();
-                c->free_list.pop_front();
-            }
-            const size_t ri = (size_t)g * c->B + s;
-            c->dirty_count[ri] = std::max(c->dirty_count[ri], np);
-            c->npages[ri] = np;
-            c->runs_stale[ri] = 1;
-        }
-        for (int h = 0; h < c->H; ++h) {
-            c->cap[(size_t)s * c->H + h] = cap[(size_t)i * c->H + h];
-            c->len[(size_t)s * c->H + h] = len ? len[(size_t)i * c->H + h] : 0;
-        }
-        c->active[s] = 1;
-    }
+    for (int i = 0; i < n; ++i)
+        install(c, slots[i], &need[(size_t)i * c->ng], -1, nullptr, cap + (size_t)i * c->H,
+                len ? len + (size_t)i * c->H : nullptr);
     c->plan_dirty = true;
     c->pending = true;
     if (group_of_head_out) std::copy(c->goh.begin(), c->goh.end(), group_of_head_out);
+    return NUP_OK;
+}
+
+nup_status kv_alias(nup_ctx *c, int32_t n, const int32_t *slots, const int32_t *src_slots,
+                    const int32_t *share_pages, const int32_t *cap, const int32_t *len) {
+    if (!c) return NUP_E_ARG;
+    if (n < 0) return fail(c, NUP_E_ARG, "n < 0");
+    if (n == 0) return NUP_OK;
+    if (!slots || !src_slots || !share_pages || !cap || !len)
+        return fail(c, NUP_E_ARG, "slots, src_slots, share_pages, cap and len are required");
+    std::vector<char> seen(c->B, 0);
+    for (int i = 0; i < n; ++i) {
+        const int s = slots[i];
+        if (s < 0 || s >= c->B) return fail(c, NUP_E_ARG, "slot %d out of range", s);
+        if (seen[s]) return fail(c, NUP_E_ARG, "slot %d repeated", s);
+        seen[s] = 1;
+    }
+    for (int i = 0; i < n; ++i) {
+        const int src = src_slots[i];
+        if (src < 0 || src >= c->B) return fail(c, NUP_E_ARG, "source slot %d out of range", src);
+        if (seen[src]) return fail(c, NUP_E_ARG, "source slot %d is also a new slot", src);
+    }
+    for (int i = 0; i < n; ++i) {
+        for (int h = 0; h < c->H; ++h) {
+            const long long cp = cap[(size_t)i * c->H + h];
+            const long long ln = len[(size_t)i * c->H + h];
+            if (cp < 0 || cp > (long long)c->max_pages * c->P)
+                return fail(c, NUP_E_ARG, "cap %lld of slot %d head %d outside [0, %lld]", cp, slots[i], h,
+                            (long long)c->max_pages * c->P);
+            if (ln < 0 || ln > cp)
+                return fail(c, NUP_E_ARG, "len %lld of slot %d head %d outside [0, cap]", ln, slots[i], h);
+        }
+        for (int g = 0; g < c->ng; ++g)
+            if (share_pages[(size_t)i * c->ng + g] < 0)
+                return fail(c, NUP_E_ARG, "negative share for slot %d group %d", slots[i], g);
+    }
+    for (int i = 0; i < n; ++i) {
+        if (c->active[slots[i]]) return fail(c, NUP_E_STATE, "slot %d is already active", slots[i]);
+        if (!c->active[src_slots[i]]) return fail(c, NUP_E_STATE, "source slot %d is not active", src_slots[i]);
+    }
+    // shared pages must be full in both sequences, so that no append writes them
+    for (int i = 0; i < n; ++i)
+        for (int h = 0; h < c->H; ++h) {
+            const long long tokens = (long long)share_pages[(size_t)i * c->ng + c->goh[h]] * c->P;
+            if (tokens > len[(size_t)i * c->H + h] || tokens > c->len[(size_t)src_slots[i] * c->H + h])
+                return fail(c, NUP_E_ARG, "share of %lld tokens exceeds a length of slot %d or source %d (head %d)",
+                            tokens, slots[i], src_slots[i], h);
+        }
+    std::vector<int32_t> need((size_t)n * c->ng, 0);
+    long long fresh = 0;
+    for (int i = 0; i < n; ++i) {
+        for (int h = 0; h < c->H; ++h) {
+            int32_t &x = need[(size_t)i * c->ng + c->goh[h]];
+            x = std::max<int32_t>(x, (cap[(size_t)i * c->H + h] + c->P - 1) / c->P);
+        }
+        for (int g = 0; g < c->ng; ++g) fresh += need[(size_t)i * c->ng + g] - share_pages[(size_t)i * c->ng + g];
+    }
+    if (fresh > (long long)c->free_list.size())
+        return fail(c, NUP_E_NOPAGES, "need %lld pages, %zu free", fresh, c->free_list.size());
+    for (int i = 0; i < n; ++i)
+        install(c, slots[i], &need[(size_t)i * c->ng], src_slots[i], share_pages + (size_t)i * c->ng,
+                cap + (size_t)i * c->H, len + (size_t)i * c->H);
+    c->plan_dirty = true;
+    c->pending = true;
     return NUP_OK;
 }
 
@@ -549,7 +640,7 @@ nup_status kv_free_seqs(nup_ctx *c, int32_t n, const int32_t *slots) {
             const size_t ri = (size_t)g * c->B + s;
             int32_t *row = &c->pt[ri * c->max_pages];
             for (int j = 0; j < c->npages[ri]; ++j) {
-                c->free_list.push_back(row[j]);
+                if (--c->ref[row[j]] == 0) c->free_list.push_back(row[j]);
                 row[j] = -1;
             }
             c->dirty_count[ri] = std::max(c->dirty_count[ri], c->npages[ri]);
@@ -616,6 +707,8 @@ nup_status nup_commit(nup_ctx *c, void *stream) {
         std::vector<int32_t> runs5;
         build_runs(c, runs5);
         const int nruns = (int)(runs5.size() / 5);
+        if ((size_t)nruns > (size_t)c->ng * c->B * c->max_pages)
+            return fail(c, NUP_E_STATE, "internal: %d trains exceed the page-table entries", nruns);
         c->off_runs = off;
         int32_t *rw = reinterpret_cast<int32_t *>(blob + off);
         for (int r = 0; r < nruns; ++r) {
@@ -768,6 +861,53 @@ nup_status kv_gather_compact(nup_ctx *c, int32_t mode, const int32_t *idx, int32
         return fail(c, NUP_E_ARG, "mode must be 0 (trains) or 1 (indices)");
     }
     if (e != hipSuccess) return hip_fail(c, e, "gather launch");
+    return NUP_OK;
+}
+
+nup_status kv_gather_trains_dma(nup_ctx *c, void *k_out, void *v_out, const int64_t *row_off,
+                                int32_t *n_copies, void *stream) {
+    if (!c) return NUP_E_ARG;
+    if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
+    if (!c->committed || c->pending) return fail(c, NUP_E_STATE, "needs a committed descriptor and no pending edits");
+    if (!k_out || !v_out || !row_off) return fail(c, NUP_E_ARG, "k_out, v_out and row_off are required");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t row_bytes = (size_t)c->D * 2, page_rows = (size_t)c->P;
+    const size_t page_bytes = page_rows * row_bytes;          // one head's rows of one page
+    const size_t src_pitch = (size_t)c->gh * page_bytes;      // next physical page, same head slot
+    int32_t copies = 0;
+    for (int s = 0; s < c->B; ++s) {
+        if (!c->active[s]) continue;
+        for (int g = 0; g < c->ng; ++g) {
+            const std::vector<int32_t> &rr = runs_of_row(c, (size_t)g * c->B + s);
+            for (size_t k = 0; k < rr.size(); k += 3) {
+                const int64_t phys = rr[k], pages = rr[k + 1], logical = rr[k + 2];
+                for (int j = 0; j < c->gh; ++j) {
+                    const int h = c->head_of_gslot[g * c->gh + j];
+                    const int64_t L = c->len[(size_t)s * c->H + h];
+                    const int64_t rows = std::min<int64_t>(std::max<int64_t>(L - logical * c->P, 0), pages * c->P);
+                    if (rows == 0) continue;
+                    const int64_t full = rows / c->P, tail = rows % c->P;
+                    const size_t src_off = ((size_t)phys * c->gh + j) * page_bytes;
+                    const size_t dst_off = (size_t)(row_off[(size_t)s * c->H + h] + logical * c->P) * row_bytes;
+                    for (int kv = 0; kv < 2; ++kv) {
+                        const char *src = reinterpret_cast<const char *>(kv ? c->vpool : c->kpool) + src_off;
+                        char *dst = static_cast<char *>(kv ? v_out : k_out) + dst_off;
+                        hipError_t e = hipSuccess;
+                        if (full > 0)
+                            e = c->gh == 1 ? hipMemcpyAsync(dst, src, full * page_bytes, hipMemcpyDeviceToDeviceNoCU, st)
+                                           : hipMemcpy2DAsync(dst, page_bytes, src, src_pitch, page_bytes, full,
+                                                              hipMemcpyDeviceToDeviceNoCU, st);
+                        if (e == hipSuccess && tail > 0)
+                            e = hipMemcpyAsync(dst + full * page_bytes, src + full * src_pitch, tail * row_bytes,
+                                               hipMemcpyDeviceToDeviceNoCU, st);
+                        if (e != hipSuccess) return hip_fail(c, e, "copy-engine train");
+                        copies += (full > 0) + (tail > 0);
+                    }
+                }
+            }
+        }
+    }
+    if (n_copies) *n_copies = copies;
     return NUP_OK;
 }
 
@@ -991,6 +1131,12 @@ nup_status nup_get_free_list(const nup_ctx *c, int32_t *out, int32_t *n) {
     if (!c || !n) return NUP_E_ARG;
     *n = (int32_t)c->free_list.size();
     if (out) std::copy(c->free_list.begin(), c->free_list.end(), out);
+    return NUP_OK;
+}
+
+nup_status nup_get_refcounts(const nup_ctx *c, int32_t *out) {
+    if (!c || !out) return NUP_E_ARG;
+    std::copy(c->ref.begin(), c->ref.end(), out);
     return NUP_OK;
 }
 

@@ -50,6 +50,12 @@ class Case:
         assert a == b
         return a
 
+    def alias(self, slots, src_slots, share_pages, caps, lengths):
+        a = self.spec.alias(slots, src_slots, share_pages, caps, lengths)
+        b = nup.kv_alias(self.ctx, slots, src_slots, share_pages, caps, lengths, raise_on_error=False)
+        assert a == b
+        return a
+
     def free(self, slots):
         a = self.spec.free_seqs(slots)
         b = nup.kv_free_seqs(self.ctx, slots, raise_on_error=False)

@@ -1,0 +1,137 @@
+"""Alias (KV-RM, Fig 3): forked sequences whose leading pages are the
+physical pages of a live source.  Decode over shared pages, appends after
+the fork, trains gathers and Trim of the source are checked against the
+oracle's own pager and fp64 attention."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import non_uniform_paged_amd as nup
+import oracle
+import workloads as W
+from oracle import pager as pg
+from tests.gpu_common import DEV, Case, assert_attention_close, sub_oracle, u16
+
+pytestmark = pytest.mark.gpu
+
+
+def _group_share(goh, tokens_per_head, ng):
+    """Whole pages every head of a group can share: min over its heads // 16."""
+    share = np.zeros(ng, np.int64)
+    for g in range(ng):
+        share[g] = min(int(tokens_per_head[h]) for h in range(len(goh)) if goh[h] == g) // 16
+    return share
+
+
+def _append_steps(c, steps, salt):
+    """Append through the library and place the same rows in a host copy of
+    the pool by the oracle pager's positions."""
+    kp = u16(c.kpool).copy()
+    vp = u16(c.vpool).copy()
+    fk, fv = kp.reshape(-1, c.D), vp.reshape(-1, c.D)
+    for step in range(steps):
+        kn = W.normal_bf16("k", (c.B, c.H, c.D), salt + step)
+        vn = W.normal_bf16("v", (c.B, c.H, c.D), salt + step)
+        nup.kv_append(c.ctx, torch.from_numpy(kn.view(np.int16)).to(DEV),
+                      torch.from_numpy(vn.view(np.int16)).to(DEV))
+        st, pos = c.spec.append_positions()
+        assert st == pg.OK
+        for s in range(c.B):
+            if c.spec.active[s]:
+                for h in range(c.H):
+                    row = c.spec.physical_row(s, h, int(pos[s, h]))
+                    fk[row], fv[row] = kn[s, h], vn[s, h]
+        c.commit()
+    return kp, vp
+
+
+def test_alias_decode_append_gather_trim():
+    H, gqa, D, B, ng = 8, 4, 128, 6, 2
+    rs = np.random.default_rng(31)
+    L0 = rs.integers(200, 700, size=H)
+    max_pages = 64
+    num_pages = 300
+    c = Case(H=H, Hq=H * gqa, D=D, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages,
+             free_list_init=rs.permutation(num_pages), num_workers=37, salt=31)
+    assert c.alloc([0], (L0 + 20)[None], L0[None]) == pg.OK
+    goh = c.spec.group_of_head
+    forks = [1, 2, 3, 4]
+    share = np.zeros((len(forks), ng), np.int64)
+    lens = np.zeros((len(forks), H), np.int64)
+    for i in range(len(forks)):
+        most = _group_share(goh, L0, ng)
+        share[i] = rs.integers(0, most + 1)
+        share[i, i % ng] = most[i % ng]                   # one group shared in full
+        lens[i] = share[i][goh] * 16 + rs.integers(0, 300, size=H)
+    caps = lens + rs.integers(8, 40, size=lens.shape)
+    assert c.alias(forks, [0] * len(forks), share, caps, lens) == pg.OK
+    assert np.array_equal(nup.get_refcounts(c.ctx), c.spec.ref)
+    assert c.spec.ref.max() == 1 + len(forks)
+    c.commit()
+    out, lse = c.attend()
+    ref, ref_lse = c.oracle()
+    assert_attention_close(out, lse, ref, ref_lse, "forks over shared pages")
+
+    # decode steps after the fork: every write lands on an unshared page
+    kp, vp = _append_steps(c, 6, 3100)
+    assert np.array_equal(u16(c.kpool), kp) and np.array_equal(u16(c.vpool), vp)
+    out, lse = c.attend()
+    ref, ref_lse = c.oracle()
+    assert_attention_close(out, lse, ref, ref_lse, "after appends")
+
+    # trains of the forked rows: bit-exact rows, shared prefix included
+    lens_now = c.spec.lengths.astype(np.int64)
+    row_off = np.concatenate([[0], np.cumsum(lens_now.reshape(-1))[:-1]]).astype(np.int64)
+    total = int(lens_now.sum())
+    ks = torch.zeros((total, D), dtype=torch.int16, device=DEV)
+    vs = torch.zeros_like(ks)
+    phys = torch.full((total,), -1, dtype=torch.int32, device=DEV)
+    nup.kv_gather_compact(c.ctx, 0, ks, vs, row_off=torch.from_numpy(row_off).to(DEV), phys_out=phys)
+    torch.cuda.synchronize()
+    want = pg.gather_pages(c.spec, kp, vp, row_off)
+    gk, gv, gp = ks.cpu().numpy().view(np.uint16), vs.cpu().numpy().view(np.uint16), phys.cpu().numpy()
+    for (s, h), (kr, vr, rows) in want.items():
+        o, n = row_off[s * H + h], len(kr)
+        assert np.array_equal(gk[o:o + n], kr) and np.array_equal(gv[o:o + n], vr), (s, h)
+        assert np.array_equal(gp[o:o + n], rows), (s, h)
+
+    # Trim the source: the shared pages stay with the forks; a new sequence
+    # takes only pages nobody maps
+    c.free([0])
+    assert np.array_equal(nup.get_free_list(c.ctx), c.spec.free_list())
+    assert c.alloc([5], np.full((1, H), 200), np.full((1, H), 150)) == pg.OK
+    c.commit()
+    out, lse = c.attend()
+    ref, ref_lse = c.oracle()
+    assert_attention_close(out, lse, ref, ref_lse, "after Trim of the source")
+    assert np.array_equal(nup.get_refcounts(c.ctx), c.spec.ref)
+
+
+def test_alias_full_size_prefix_batch():
+    """Qwen2.5-32B-shaped batch where 60 of 64 sessions fork from 4 sources
+    (a shared 8192-token prompt); checked on sampled sessions."""
+    w = W.qwen25_32b_prefix()
+    src = w.extra["alias_src"]
+    pre = w.extra["prefix_tokens"]
+    max_pages = int(math.ceil(w.caps.max() / 16))
+    c = Case(H=w.num_kv_heads, Hq=w.num_q_heads, D=w.head_dim, ng=w.num_groups, B=w.batch,
+             num_pages=w.num_pages, max_pages=max_pages, salt=32)
+    roots = [s for s in range(w.batch) if src[s] < 0]
+    forks = [s for s in range(w.batch) if src[s] >= 0]
+    assert c.alloc(roots, w.caps[roots], w.lengths[roots]) == pg.OK
+    goh = c.spec.group_of_head
+    share = np.stack([_group_share(goh, pre[s], w.num_groups) for s in forks])
+    assert c.alias(forks, src[forks], share, w.caps[forks], w.lengths[forks]) == pg.OK
+    c.commit()
+    used = int((c.spec.ref > 0).sum())
+    entries = int(c.spec.n_pages.sum())
+    assert used == entries - int(share.sum())
+    nup.attn_decode_nonuniform(c.ctx, c.q, c.out, c.lse, c.scale, c.ws)
+    torch.cuda.synchronize()
+    sample = [0, 5, 33, 62]                           # a source and three forks
+    ref, ref_lse = sub_oracle(c.spec, c.q, c.kpool, c.vpool, sample, c.scale)
+    out = c.out.cpu().numpy().astype(np.float64)[sample]
+    lse = c.lse.cpu().numpy().astype(np.float64)[sample]
+    assert_attention_close(out, lse, ref, ref_lse, "qwen25_32b_prefix sampled")

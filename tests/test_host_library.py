@@ -62,6 +62,34 @@ def test_tiny_fixture_scrambled():
     assert nup.get_runs(ctx).tolist() == sc["runs"]
 
 
+def test_tiny_alias_fixture_through_the_library():
+    """The hand-worked Alias fixture, through the C ABI."""
+    A = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_alias.json")))
+    ctx = _host_ctx(B=3)
+    b = np.array([A["slot0_budgets"]])
+    nup.kv_alloc_groups(ctx, [0], b, b)
+    a = A["alias"]
+    assert nup.kv_alias(ctx, [2], [1], [[0, 0]], [[16] * 4], [[0] * 4],
+                        raise_on_error=False) == nup.NUP_E_STATE
+    nup.kv_alias(ctx, [a["slot"]], [a["src"]], [a["share_pages"]], [a["caps"]], [a["lens"]])
+    assert nup.get_page_table(ctx)[:, 2].tolist() == A["page_table_slot2"]
+    assert nup.get_free_list(ctx).tolist() == A["free_list_after_alias"]
+    assert nup.get_refcounts(ctx).tolist() == A["refcounts_after_alias"]
+    assert nup.get_runs(ctx).tolist() == A["runs_after_alias"]
+    codes = {"E_ARG": nup.NUP_E_ARG, "E_STATE": nup.NUP_E_STATE, "E_NOPAGES": nup.NUP_E_NOPAGES}
+    pt = nup.get_page_table(ctx)
+    for name, e in A["errors_from_alias_state"].items():
+        rc = nup.kv_alias(ctx, [e["slot"]], [e["src"]], [e["share_pages"]], [e["caps"]], [e["lens"]],
+                          raise_on_error=False)
+        assert rc == codes[e["status"]], name
+        assert np.array_equal(nup.get_page_table(ctx), pt)
+    nup.kv_free_seqs(ctx, [0])
+    assert nup.get_free_list(ctx).tolist() == A["free_list_after_trim_slot0"]
+    nup.kv_free_seqs(ctx, [2])
+    assert nup.get_free_list(ctx).tolist() == A["free_list_after_trim_slot2"]
+    assert not nup.get_refcounts(ctx).any()
+
+
 def test_error_codes_and_atomicity():
     ctx = _host_ctx(H=4, ng=2, B=4, num_pages=10, max_pages=8)
     caps = np.array([[16, 16, 64, 64], [16, 16, 64, 64]])
@@ -99,7 +127,7 @@ def test_bad_configs_rejected():
         _host_ctx(fl=[0] * 64)         # not a permutation
 
 
-@settings(max_examples=40, deadline=None)
+@settings(max_examples=80, deadline=None)
 @given(st.data())
 def test_pager_matches_oracle(data):
     """Random Reserve / Trim sequences give bit-identical pager state."""
@@ -110,13 +138,39 @@ def test_pager_matches_oracle(data):
     ctx = _host_ctx(H=H, Hq=H, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages, fl=perm,
                     num_workers=7)
     spec = pg.PagerSpec(H, ng, B, num_pages, max_pages, 16, perm)
-    for _ in range(data.draw(st.integers(1, 10))):
-        if data.draw(st.booleans()):
+    for step in range(data.draw(st.integers(1, 12))):
+        op = "alloc" if step == 0 else data.draw(st.sampled_from(["alloc", "alias", "free"]))
+        if op == "alloc":
             slots = data.draw(st.lists(st.integers(0, B - 1), min_size=1, max_size=3, unique=True))
             caps = np.array([[data.draw(st.integers(0, max_pages * 16)) for _ in range(H)] for _ in slots])
-            lens = np.array([[data.draw(st.integers(0, int(c))) for c in row] for row in caps])
+            lens = np.array([[data.draw(st.just(int(c)) | st.integers(0, int(c))) for c in row]
+                             for row in caps])
             a = spec.alloc(slots, caps, lens)
             b = nup.kv_alloc_groups(ctx, slots, caps, lens, raise_on_error=False)
+        elif op == "alias":
+            # any slots and sources, shares up to one page past what the
+            # lengths allow: the error paths are compared too
+            idle = [x for x in range(B) if not spec.active[x]]
+            pick = st.sampled_from(idle) if idle and data.draw(st.integers(0, 3)) else st.integers(0, B - 1)
+            slots = data.draw(st.lists(pick, min_size=1, max_size=2, unique=True))
+            live = [x for x in range(B) if spec.active[x] and x not in slots]
+            srcs = [data.draw(st.sampled_from(live) if live else st.integers(0, B - 1)) for _ in slots]
+            share = np.zeros((len(slots), ng), np.int64)
+            caps = np.zeros((len(slots), H), np.int64)
+            lens = np.zeros((len(slots), H), np.int64)
+            for i, src in enumerate(srcs):
+                for g in range(ng):
+                    heads = [h for h in range(H) if spec.group_of_head is not None
+                             and spec.group_of_head[h] == g]
+                    most = min([int(spec.lengths[src, h]) // 16 for h in heads], default=0)
+                    over = data.draw(st.integers(0, 3)) == 0          # now and then one page too many
+                    share[i, g] = data.draw(st.integers(0, most + 1) if over else st.integers(0, most))
+                    for h in heads or range(g * (H // ng), (g + 1) * (H // ng)):
+                        caps[i, h] = data.draw(st.integers(min(16 * most, max_pages * 16), max_pages * 16))
+                        lens[i, h] = data.draw(st.integers(min(16 * int(share[i, g]), int(caps[i, h])),
+                                                           int(caps[i, h])))
+            a = spec.alias(slots, srcs, share, caps, lens)
+            b = nup.kv_alias(ctx, slots, srcs, share, caps, lens, raise_on_error=False)
         else:
             slots = data.draw(st.lists(st.integers(0, B - 1), min_size=1, max_size=3, unique=True))
             a = spec.free_seqs(slots)
@@ -124,6 +178,7 @@ def test_pager_matches_oracle(data):
         assert a == b
         assert np.array_equal(nup.get_page_table(ctx), spec.page_table)
         assert np.array_equal(nup.get_free_list(ctx), spec.free_list())
+        assert np.array_equal(nup.get_refcounts(ctx), spec.ref)
         assert np.array_equal(nup.get_lengths(ctx), spec.lengths)
         runs = [tuple(r) for r in nup.get_runs(ctx).tolist()]
         assert runs == pg.coalesce(spec.page_table, spec.n_pages, spec.active)

@@ -197,6 +197,28 @@ def qwen25_32b(headroom: int = PAGE, control: Optional[str] = None,
                     extra={"contexts": ctx, "ratios": ratios})
 
 
+def qwen25_32b_prefix(prefix_ctx: int = 8192, n_sources: int = 4, batch: int = 64) -> Workload:
+    """The Qwen2.5-32B-shaped batch, with forked sessions: sessions
+    s >= n_sources continue source s % n_sources and share the first
+    prefix_ctx tokens of its context (a common system prompt).  Head h keeps
+    round_to_page(r_h * prefix_ctx) of them (its keep ratio r_h), limited by
+    both sessions' retained lengths.
+
+    extra["alias_src"][s]: the source session, -1 for the sources;
+    extra["prefix_tokens"][s][h]: the retained tokens s shares with it."""
+    w = qwen25_32b(batch=batch)
+    ratios = w.extra["ratios"]
+    keep = round_to_page(ratios * prefix_ctx, prefix_ctx)
+    s_idx = np.arange(batch)
+    src = np.where(s_idx < n_sources, -1, s_idx % n_sources)
+    prefix = np.zeros_like(w.lengths)
+    for s in range(n_sources, batch):
+        prefix[s] = np.minimum(keep, np.minimum(w.lengths[s], w.lengths[src[s]]))
+    w.name = "qwen25_32b_prefix"
+    w.extra.update(alias_src=src, prefix_tokens=prefix, prefix_ctx=prefix_ctx)
+    return w
+
+
 def llama3_8b_topk(batch: int = 8, ctx: int = 122880, k: int = 2048) -> Workload:
     """Llama-3-8B-shaped sparse decode: batch 8, 32 q / 8 KV heads, d128,
     context 122880 held in full, one head group (8 heads per page), pages
@@ -272,6 +294,7 @@ CONFIGS = {
     "tiny": tiny,
     "qwen3_4b": qwen3_4b,
     "qwen25_32b": qwen25_32b,
+    "qwen25_32b_prefix": qwen25_32b_prefix,
     "llama3_8b_topk": llama3_8b_topk,
     "mixed_churn": mixed_churn,
 }
