@@ -427,55 +427,63 @@ def measure_extras(args):
     del st, ksg, vsg
     torch.cuda.empty_cache()
 
-    # -- the Qwen2.5-32B batch (long trains): gather kernel vs copy engines
-    w = W.qwen25_32b()
-    st = Setup(w, 0)
-    lens = st.lengths0.astype(np.int64).reshape(-1)
-    ro = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
-    total = int(lens.sum())
-    ksg = torch.empty((total, 128), dtype=torch.bfloat16, device="cuda")
-    vsg = torch.empty_like(ksg)
-    ro_dev = torch.from_numpy(ro).cuda()
-    gt = lambda: nup.kv_gather_compact(st.ctx, 0, ksg, vsg, row_off=ro_dev)
-    gt()
-    g_ms = _timed(gt, 5, flush)
-    res["qwen25_32b_trains"] = {"trains": int(len(nup.get_runs(st.ctx))), "bytes": 2 * total * 256,
-                                "gather_kernel_ms": round(g_ms, 4),
-                                "gather_kernel_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1),
-                                "copy_engine": _dma_trains(st, ksg, vsg, ro, flush)}
-    st.free()
-    del st, ksg, vsg, ro_dev
-    torch.cuda.empty_cache()
+    # -- the Qwen2.5-32B batch (long trains): gather kernel vs copy engines,
+    #    with one head per group (linear copies) and with the 4-group layout
+    res["qwen25_32b_trains"] = []
+    for ng in (8, 4):
+        w = W.qwen25_32b()
+        w.num_groups = ng
+        st = Setup(w, 0)
+        lens = st.lengths0.astype(np.int64).reshape(-1)
+        ro = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+        total = int(lens.sum())
+        ksg = torch.empty((total, 128), dtype=torch.bfloat16, device="cuda")
+        vsg = torch.empty_like(ksg)
+        ro_dev = torch.from_numpy(ro).cuda()
+        gt = lambda: nup.kv_gather_compact(st.ctx, 0, ksg, vsg, row_off=ro_dev)
+        gt()
+        g_ms = _timed(gt, 5, flush)
+        res["qwen25_32b_trains"].append({
+            "heads_per_group": 8 // ng, "trains": int(len(nup.get_runs(st.ctx))), "bytes": 2 * total * 256,
+            "gather_kernel_ms": round(g_ms, 4),
+            "gather_kernel_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1),
+            "copy_engine": _dma_trains(st, ksg, vsg, ro, flush)})
+        st.free()
+        del st, ksg, vsg, ro_dev
+        torch.cuda.empty_cache()
 
     # -- forked sessions sharing a prompt prefix (KV-RM Alias): same lengths as
-    #    the Qwen2.5-32B batch, 60 of 64 sessions fork from 4 sources
-    w = W.qwen25_32b_prefix()
-    st = Setup(w, 0)
-    for _ in range(2):
-        st.step(append=False)
-    torch.cuda.synchronize()
-    nup.kernel_time(st.ctx, reset=True)
-    nup.set_timing(st.ctx, True)
-    _timed(lambda: st.step(append=False), 10, flush)
-    nup.set_timing(st.ctx, False)
-    kms, n = nup.kernel_time(st.ctx, reset=True)
-    kms /= max(n, 1)
-    in_use = int(st.num_pages - len(nup.get_free_list(st.ctx)))
-    entries = int(sum(np.count_nonzero(r >= 0) for r in nup.get_page_table(st.ctx)))
-    kb = kv_bytes(st.lengths0)
-    shared_b = int(sum(int(st.share[i, st.goh[h]]) * 16 * 512
-                       for i in range(len(st.share)) for h in range(w.num_kv_heads)))
-    res["qwen25_32b_prefix"] = {
-        "prefix_ctx": w.extra["prefix_ctx"], "sources": int((w.extra["alias_src"] < 0).sum()),
-        "pages_in_use": in_use, "page_table_entries": entries,
-        "reserved_saving": round(1 - in_use / entries, 4),
-        "kv_bytes_logical": kb, "kv_bytes_unique": kb - shared_b,
-        "partial_kernel_ms": round(kms, 4),
-        "partial_kernel_logical_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
-        "note": "cold (1 GiB read before each step); logical bytes count every session's reads"}
-    st.free()
-    del st
-    torch.cuda.empty_cache()
+    #    the Qwen2.5-32B batch, 60 of 64 sessions fork from 4 sources; the
+    #    unshared batch is timed the same way for comparison
+    res["qwen25_32b_prefix"] = {}
+    for tag, w in (("unshared", W.qwen25_32b()), ("forked", W.qwen25_32b_prefix())):
+        st = Setup(w, 0)
+        for _ in range(2):
+            st.step(append=False)
+        torch.cuda.synchronize()
+        nup.kernel_time(st.ctx, reset=True)
+        nup.set_timing(st.ctx, True)
+        _timed(lambda: st.step(append=False), 10, flush)
+        nup.set_timing(st.ctx, False)
+        kms, n = nup.kernel_time(st.ctx, reset=True)
+        kms /= max(n, 1)
+        in_use = int(st.num_pages - len(nup.get_free_list(st.ctx)))
+        entries = int(np.count_nonzero(nup.get_page_table(st.ctx) >= 0))
+        kb = kv_bytes(st.lengths0)
+        share = getattr(st, "share", None)
+        shared_b = 0 if share is None else int(sum(int(share[i, st.goh[h]]) * 16 * 512
+                                                   for i in range(len(share)) for h in range(w.num_kv_heads)))
+        res["qwen25_32b_prefix"][tag] = {
+            "pages_in_use": in_use, "page_table_entries": entries,
+            "reserved_saving": round(1 - in_use / entries, 4),
+            "kv_bytes_logical": kb, "kv_bytes_unique": kb - shared_b,
+            "partial_kernel_ms": round(kms, 4),
+            "partial_kernel_logical_GBs": round(kb / (kms * 1e-3) / 1e9, 1)}
+        st.free()
+        del st
+        torch.cuda.empty_cache()
+    res["qwen25_32b_prefix"]["note"] = ("prefix 8192 tokens, 4 sources; cold (1 GiB read before each "
+                                        "step); logical bytes count every session's reads")
 
     # -- heads per page (Tangram, Fig 8c): the Qwen2.5-32B batch with 1, 2, 4, 8 groups
     sweep = []

@@ -213,9 +213,14 @@ nup_status kv_gather_compact(nup_ctx *ctx, int32_t mode, const int32_t *idx, int
  *   row_off   HOST int64 [B_max*H_kv] (the host issues the copies, so it
  *             needs the offsets; the destination rows must not overlap)
  *   n_copies  optional host int32: receives the number of copies enqueued
- * Per (train, head) one strided copy of the full pages (source pitch G_h
- * pages) and one copy of a partial last page, for K and for V, all enqueued
- * on `stream` as device-to-device copies that use no compute units.  Reads
+ * The copies are enqueued on `stream` as device-to-device copies that ask
+ * for no compute units.  With one head per group (G_h = 1) a train's rows
+ * of a head are one byte range: one linear copy per (train, head) and K/V,
+ * which the runtime hands to the SDMA engines when it is large (about
+ * 1 MiB and up; small ones run as its blit kernels).  With G_h > 1 the heads
+ * interleave page by page: one strided copy of the full pages (source pitch
+ * G_h pages) plus one for a partial last page, which the runtime runs as
+ * blit kernels, not on the SDMA engines.  Reads
  * the host's view of the trains and lengths, so it needs a committed
  * descriptor with no pending edits (NUP_E_STATE).  Errors: NUP_E_ARG,
  * NUP_E_STATE, NUP_E_HIP. */

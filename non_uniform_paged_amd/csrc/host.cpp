@@ -893,15 +893,22 @@ nup_status kv_gather_trains_dma(nup_ctx *c, void *k_out, void *v_out, const int6
                         const char *src = reinterpret_cast<const char *>(kv ? c->vpool : c->kpool) + src_off;
                         char *dst = static_cast<char *>(kv ? v_out : k_out) + dst_off;
                         hipError_t e = hipSuccess;
-                        if (full > 0)
-                            e = c->gh == 1 ? hipMemcpyAsync(dst, src, full * page_bytes, hipMemcpyDeviceToDeviceNoCU, st)
-                                           : hipMemcpy2DAsync(dst, page_bytes, src, src_pitch, page_bytes, full,
-                                                              hipMemcpyDeviceToDeviceNoCU, st);
-                        if (e == hipSuccess && tail > 0)
-                            e = hipMemcpyAsync(dst + full * page_bytes, src + full * src_pitch, tail * row_bytes,
-                                               hipMemcpyDeviceToDeviceNoCU, st);
+                        if (c->gh == 1) {
+                            // one head per page: the train's rows of this head are one range
+                            e = hipMemcpyAsync(dst, src, rows * row_bytes, hipMemcpyDeviceToDeviceNoCU, st);
+                            ++copies;
+                        } else {
+                            // G_h heads interleave page by page: a strided copy of the
+                            // full pages, then the partial last page
+                            if (full > 0)
+                                e = hipMemcpy2DAsync(dst, page_bytes, src, src_pitch, page_bytes, full,
+                                                     hipMemcpyDeviceToDeviceNoCU, st);
+                            if (e == hipSuccess && tail > 0)
+                                e = hipMemcpyAsync(dst + full * page_bytes, src + full * src_pitch, tail * row_bytes,
+                                                   hipMemcpyDeviceToDeviceNoCU, st);
+                            copies += (full > 0) + (tail > 0);
+                        }
                         if (e != hipSuccess) return hip_fail(c, e, "copy-engine train");
-                        copies += (full > 0) + (tail > 0);
                     }
                 }
             }
