@@ -260,6 +260,64 @@ def _dma_trains(st, ks, vs, row_off, flush):
             "host_enqueue_ms": round(1e3 * float(np.mean(enq)), 3), "rows_equal_kernel": same}
 
 
+def _layer_group_sweep(flush):
+    """Reserved memory, page-table entries, host Reserve+commit time and the
+    36-layer decode time for each head-group size on the 36-layer batch."""
+    import torch
+    import non_uniform_paged_amd as nup
+    import workloads as W
+    w = W.qwen3_4b_layers()
+    NL, H, D, B = w.extra["num_layers"], w.num_kv_heads, w.head_dim, w.batch
+    V = NL * H
+    caps, lens = w.caps.astype(np.int32), w.lengths.astype(np.int32)
+    max_pages = int(math.ceil(caps.max() / 16))
+    used = int(lens.sum()) * 2 * D * 2
+    out = []
+    q = torch.empty((B, w.num_q_heads, D), dtype=torch.bfloat16, device="cuda")
+    W.fill_normal_bf16_torch(q, "q")
+    o = torch.empty((B, w.num_q_heads, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, w.num_q_heads), dtype=torch.float32, device="cuda")
+    for G in (1, 2, 4, 8, 16, 32):
+        ng = V // G
+        cfg = dict(num_kv_heads=H, num_q_heads=w.num_q_heads, head_dim=D, num_groups=ng, max_batch=B,
+                   max_pages=max_pages, num_layers=NL)
+        # exact page need from a host-only pager, then pools of that size
+        probe = nup.Context(**cfg, num_pages=B * ng * max_pages)
+        nup.kv_alloc_groups(probe, np.arange(B), caps, lens)
+        pages = B * ng * max_pages - len(nup.get_free_list(probe))
+        del probe
+        kpool = torch.empty((pages, G, 16, D), dtype=torch.bfloat16, device="cuda")
+        vpool = torch.empty_like(kpool)
+        W.fill_normal_bf16_torch(kpool, "k")
+        W.fill_normal_bf16_torch(vpool, "v")
+        desc = torch.empty(nup.desc_bytes(**cfg, num_pages=pages), dtype=torch.uint8, device="cuda")
+        ctx = nup.Context(**cfg, num_pages=pages, k_pool=kpool, v_pool=vpool, desc=desc)
+        t0 = time.perf_counter()
+        nup.kv_alloc_groups(ctx, np.arange(B), caps, lens)
+        nup.nup_commit(ctx)
+        host_us = (time.perf_counter() - t0) * 1e6
+        ws = torch.empty(nup.workspace_bytes(ctx), dtype=torch.uint8, device="cuda")
+
+        def step():
+            for layer in range(NL):
+                nup.set_layer(ctx, layer)
+                nup.attn_decode_nonuniform(ctx, q, o, lse, 1.0 / math.sqrt(D), ws)
+        step()
+        torch.cuda.synchronize()
+        ms = _timed(step, 5, flush)
+        reserved = pages * G * 16 * 2 * D * 2
+        out.append({"heads_per_group": G, "groups": ng, "groups_spanning_layers": G > H,
+                    "reserved_GB": round(reserved / 1e9, 3),
+                    "internal_fragmentation": round(1 - used / reserved, 4),
+                    "page_table_entries": pages,
+                    "host_reserve_commit_us": round(host_us, 1),
+                    "decode_36_layers_ms": round(ms, 4),
+                    "decode_GBs": round(used / (ms * 1e-3) / 1e9, 1)})
+        del ctx, kpool, vpool, desc, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_extras(args):
     """The other configurations: attention on the Qwen3-4B shape, gather and
     top-K attention on the Llama-3-8B shape, and the mixed-length churn step
@@ -484,6 +542,10 @@ def measure_extras(args):
         torch.cuda.empty_cache()
     res["qwen25_32b_prefix"]["note"] = ("prefix 8192 tokens, 4 sources; cold (1 GiB read before each "
                                         "step); logical bytes count every session's reads")
+
+    # -- head groups across layers (Tangram, Fig 11): the 36-layer Qwen3-4B
+    #    shape in one pager, heads per group 1 .. 32 (groups beyond 8 span layers)
+    res["qwen3_4b_36_layers_heads_per_group"] = _layer_group_sweep(flush)
 
     # -- heads per page (Tangram, Fig 8c): the Qwen2.5-32B batch with 1, 2, 4, 8 groups
     sweep = []

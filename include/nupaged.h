@@ -88,14 +88,21 @@ typedef struct nup_config {
     int32_t num_q_heads;    /* H_q, a multiple of H_kv; H_q/H_kv in {1,2,4,5,8} */
     int32_t head_dim;       /* D: 64 or 128 */
     int32_t page_size;      /* P: must be 16 */
-    int32_t num_groups;     /* n_g, divides H_kv; heads per group G_h = H_kv / n_g */
+    int32_t num_groups;     /* n_g, divides V = num_layers * H_kv; heads per group
+                               G_h = V / n_g (a group may span layers) */
     int32_t max_batch;      /* B_max: sequence slots in the fixed-shape descriptor */
     int32_t num_pages;      /* physical pages in each pool */
     int32_t max_pages;      /* logical pages per (slot, group): page-table row length */
     int32_t num_workers;    /* split-K workers (waves); 0 = chosen from the device */
     int32_t plan_mode;      /* NUP_PLAN_BALANCED or NUP_PLAN_UNIFORM */
     int32_t uniform_splits; /* chunks per head for NUP_PLAN_UNIFORM (0 = 8) */
-    int32_t reserved0;
+    int32_t num_layers;     /* layers sharing the pager (0 or 1: a single layer).
+                               The pager's heads are the V = num_layers * H_kv
+                               (layer, KV head) pairs, numbered layer * H_kv + h:
+                               grouping, capacities and lengths are per pair
+                               (Tangram, Fig 11: group sizes beyond one layer's
+                               heads).  Per-layer calls act on the layer chosen
+                               by nup_set_layer(). */
     void *k_pool;           /* device, bf16 pool for K (caller-owned) */
     void *v_pool;           /* device, bf16 pool for V (caller-owned) */
     void *desc;             /* device, descriptor arena of nup_desc_bytes() bytes,
@@ -117,13 +124,25 @@ void nup_destroy(nup_ctx *ctx);
 const char *nup_last_error(const nup_ctx *ctx);
 
 /*
+ * nup_set_layer -- choose the layer that the per-layer calls act on:
+ * kv_append, kv_gather_compact, kv_gather_trains_dma, the attention calls,
+ * kv_select_topk and nup_get_plan.  Host state, read when a call is made (a
+ * captured graph keeps the layer of each captured call).  Reserve, Alias,
+ * Trim and nup_commit cover all layers at once: one frame per step carries
+ * every layer's split-K plan.  Errors: NUP_E_ARG (layer outside
+ * [0, num_layers)).
+ */
+nup_status nup_set_layer(nup_ctx *ctx, int32_t layer);
+
+/*
  * kv_alloc_groups -- Reserve (KV-RM, Fig 3) for n sequence slots under fixed
  * per-head budgets (Tangram, abstract: a static footprint per head).
+ * "Head" below is a (layer, KV head) pair: V = num_layers * H_kv of them.
  *   slots [n]           slot ids in [0, B_max), distinct, currently inactive
- *   cap   [n][H_kv]     capacity in tokens per (slot, KV head): the head's
+ *   cap   [n][V]        capacity in tokens per (slot, head): the head's
  *                       fixed budget plus any decode headroom; <= max_pages*P
- *   len   [n][H_kv]     tokens already present (0..cap), or NULL for 0
- *   group_of_head_out [H_kv] or NULL: receives each head's group
+ *   len   [n][V]        tokens already present (0..cap), or NULL for 0
+ *   group_of_head_out [V] or NULL: receives each head's group
  * On the first successful call the heads are grouped (Tangram, Fig 8):
  * ordered by the sum of their capacities over this call's slots (ties by
  * head index) and cut into n_g equal groups; the grouping is fixed after
@@ -147,7 +166,7 @@ nup_status kv_alloc_groups(nup_ctx *ctx, int32_t n, const int32_t *slots,
  *   slots       [n] new slots (inactive, distinct, none of them a source)
  *   src_slots   [n] active source slots (repeats allowed)
  *   share_pages [n][n_g] whole pages shared per group (>= 0)
- *   cap, len    [n][H_kv] as for kv_alloc_groups; len is required
+ *   cap, len    [n][V] as for kv_alloc_groups; len is required
  * Shared pages must be full in both sequences: for every head h of group g,
  * share_pages*P <= len (new) and <= the source's current length, so that no
  * append ever writes a shared page.  The K/V rows of shared positions are
@@ -177,7 +196,9 @@ nup_status nup_commit(nup_ctx *ctx, void *stream);
  * store the new token's K and V rows at logical position L (page table
  * entry L / P of the head's group, row L % P of the head's slot) and
  * advance L by one, on the device and in the shadow.
- *   k_new, v_new   device bf16 [B_max][H_kv][D]; rows of inactive slots ignored
+ *   k_new, v_new   device bf16 [B_max][H_kv][D], the current layer's new
+ *                  rows; rows of inactive slots ignored.  Only the current
+ *                  layer's heads advance.
  * Requires a committed descriptor (NUP_E_STATE if edits are pending).
  * NUP_E_CAPACITY, checked on the host before launch, if any active head
  * has L == cap (a fixed budget is never exceeded; nothing is written). */
@@ -300,9 +321,9 @@ nup_status nup_select_workspace_bytes(const nup_ctx *ctx, size_t *bytes);
 
 /* Shadow page table int32 [n_g][B_max][max_pages]. */
 nup_status nup_get_page_table(const nup_ctx *ctx, int32_t *out);
-/* Shadow lengths int32 [B_max][H_kv] (0 for inactive slots). */
+/* Shadow lengths int32 [B_max][V] (0 for inactive slots). */
 nup_status nup_get_lengths(const nup_ctx *ctx, int32_t *out);
-/* group_of_head / slot_of_head int32 [H_kv] each (-1 before the first Reserve). */
+/* group_of_head / slot_of_head int32 [V] each (-1 before the first Reserve). */
 nup_status nup_get_groups(const nup_ctx *ctx, int32_t *group_of_head, int32_t *slot_of_head);
 /* Free list front to back: int32 [num_pages] capacity, count in *n. */
 nup_status nup_get_free_list(const nup_ctx *ctx, int32_t *out, int32_t *n);
@@ -313,7 +334,7 @@ nup_status nup_get_refcounts(const nup_ctx *ctx, int32_t *out);
  * (slot, group, first physical page, pages, first logical page) in (slot,
  * group, logical page) order; count in *n (NUP_E_ARG if max_runs is short). */
 nup_status nup_get_runs(const nup_ctx *ctx, int32_t *out, int32_t max_runs, int32_t *n);
-/* Split-K plan of the shadow: counts first (any pointer may be NULL).
+/* Split-K plan of the shadow for the current layer: counts first (any pointer may be NULL).
  *   rows           int32 [n_rows][4] = (slot*H_kv + head, t0, t1, 0)
  *   worker_start   int32 [n_workers + 1]
  *   head_row_start int32 [B_max*H_kv + 1] */

@@ -39,7 +39,7 @@ class NupConfig(ctypes.Structure):
                 ("num_groups", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_pages", ctypes.c_int32),
                 ("num_workers", ctypes.c_int32), ("plan_mode", ctypes.c_int32),
-                ("uniform_splits", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("uniform_splits", ctypes.c_int32), ("num_layers", ctypes.c_int32),
                 ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("desc", ctypes.c_void_p), ("free_list_init", ctypes.c_void_p)]
 
@@ -72,6 +72,7 @@ _sigs = {
     "nup_get_groups": [_P, _P, _P],
     "nup_get_free_list": [_P, _P, _P],
     "nup_get_refcounts": [_P, _P],
+    "nup_set_layer": [_P, _I],
     "nup_get_runs": [_P, _P, _I, _P],
     "nup_get_plan": [_P, _P, _P, _P, _P, _P],
     "nup_set_timing": [_P, _I],
@@ -124,9 +125,9 @@ class Context:
     def __init__(self, *, num_kv_heads, num_q_heads, head_dim, num_groups, max_batch,
                  num_pages, max_pages, k_pool=None, v_pool=None, desc=None,
                  free_list_init=None, num_workers=0, plan_mode=PLAN_BALANCED,
-                 uniform_splits=0):
+                 uniform_splits=0, num_layers=1):
         cfg = NupConfig(num_kv_heads, num_q_heads, head_dim, PAGE, num_groups, max_batch,
-                        num_pages, max_pages, num_workers, plan_mode, uniform_splits, 0,
+                        num_pages, max_pages, num_workers, plan_mode, uniform_splits, num_layers,
                         _ptr(k_pool), _ptr(v_pool), _ptr(desc), None)
         self._fl = None
         if free_list_init is not None:
@@ -141,6 +142,8 @@ class Context:
         self.handle = h
         self.H, self.Hq, self.D = num_kv_heads, num_q_heads, head_dim
         self.ng, self.B, self.num_pages, self.max_pages = num_groups, max_batch, num_pages, max_pages
+        self.num_layers = max(1, num_layers)
+        self.V = self.num_layers * num_kv_heads      # the pager's (layer, KV head) pairs
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -158,7 +161,7 @@ def desc_bytes(**cfg) -> int:
     c = NupConfig(cfg["num_kv_heads"], cfg["num_q_heads"], cfg["head_dim"], PAGE,
                   cfg["num_groups"], cfg["max_batch"], cfg["num_pages"], cfg["max_pages"],
                   cfg.get("num_workers", 0), cfg.get("plan_mode", 0),
-                  cfg.get("uniform_splits", 0), 0, None, None, None, None)
+                  cfg.get("uniform_splits", 0), cfg.get("num_layers", 1), None, None, None, None)
     n = ctypes.c_size_t()
     st = _lib.nup_desc_bytes(ctypes.byref(c), ctypes.byref(n))
     if st != NUP_OK:
@@ -170,9 +173,9 @@ def desc_bytes(**cfg) -> int:
 
 def kv_alloc_groups(ctx: Context, slots, cap, len=None, raise_on_error=True):
     slots = _i32(slots)
-    cap = _i32(cap).reshape(len_(slots), ctx.H)
-    ln = None if len is None else _i32(len).reshape(len_(slots), ctx.H)
-    goh = np.zeros(ctx.H, np.int32)
+    cap = _i32(cap).reshape(len_(slots), ctx.V)
+    ln = None if len is None else _i32(len).reshape(len_(slots), ctx.V)
+    goh = np.zeros(ctx.V, np.int32)
     st = _lib.kv_alloc_groups(ctx.handle, len_(slots), slots.ctypes.data, cap.ctypes.data,
                               None if ln is None else ln.ctypes.data, goh.ctypes.data)
     if raise_on_error:
@@ -190,8 +193,8 @@ def kv_alias(ctx: Context, slots, src_slots, share_pages, cap, len, raise_on_err
     n = len_(slots)
     src = _i32(src_slots).reshape(n)
     share = _i32(share_pages).reshape(n, ctx.ng)
-    cap = _i32(cap).reshape(n, ctx.H)
-    ln = _i32(len).reshape(n, ctx.H)
+    cap = _i32(cap).reshape(n, ctx.V)
+    ln = _i32(len).reshape(n, ctx.V)
     st = _lib.kv_alias(ctx.handle, n, slots.ctypes.data, src.ctypes.data, share.ctypes.data,
                        cap.ctypes.data, ln.ctypes.data)
     return ctx.check(st) if raise_on_error else st
@@ -288,14 +291,14 @@ def get_page_table(ctx: Context) -> np.ndarray:
 
 
 def get_lengths(ctx: Context) -> np.ndarray:
-    out = np.zeros((ctx.B, ctx.H), np.int32)
+    out = np.zeros((ctx.B, ctx.V), np.int32)
     ctx.check(_lib.nup_get_lengths(ctx.handle, out.ctypes.data))
     return out
 
 
 def get_groups(ctx: Context):
-    g = np.zeros(ctx.H, np.int32)
-    s = np.zeros(ctx.H, np.int32)
+    g = np.zeros(ctx.V, np.int32)
+    s = np.zeros(ctx.V, np.int32)
     ctx.check(_lib.nup_get_groups(ctx.handle, g.ctypes.data, s.ctypes.data))
     return g, s
 
@@ -305,6 +308,11 @@ def get_free_list(ctx: Context) -> np.ndarray:
     n = ctypes.c_int32()
     ctx.check(_lib.nup_get_free_list(ctx.handle, out.ctypes.data, ctypes.byref(n)))
     return out[: n.value]
+
+
+def set_layer(ctx: Context, layer: int):
+    """Choose the layer the per-layer calls act on."""
+    ctx.check(_lib.nup_set_layer(ctx.handle, int(layer)))
 
 
 def get_refcounts(ctx: Context) -> np.ndarray:

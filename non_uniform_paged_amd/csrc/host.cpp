@@ -36,8 +36,8 @@ size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
 // Byte sizes of the packed descriptor sections, all int32 words.
 struct Sizes {
-    size_t fixed;        // active[B] lengths[B*H] goh[H] soh[H] head_of_gslot[H]
-    size_t plan_max;     // worker_start[W+1] head_row_start[B*H+1] rows[R][4]
+    size_t fixed;        // active[B] lengths[B*V] goh[V] soh[V] head_of_gslot[V] (V = layers*H)
+    size_t plan_max;     // per layer: worker_start[W+1] head_row_start[B*H+1] rows[R][4]
     size_t runs_max;     // runs[N][4] run_prefix[N+1]
     size_t patches_max;  // hdr[ng*B][4] data[ng*B*max_pages]
     size_t inbox;        // fixed + plan_max + runs_max + patches_max (aligned)
@@ -60,9 +60,13 @@ nup_status validate(const nup_config *c, std::string *why) {
     if (!valid_gqa(c->num_q_heads / c->num_kv_heads)) return bad("num_q_heads/num_kv_heads must be 1, 2, 4, 5 or 8");
     if (c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 64 or 128");
     if (c->page_size != nup::kPage) return bad("page_size must be 16");
-    if (c->num_groups <= 0 || c->num_kv_heads % c->num_groups) return bad("num_groups must divide num_kv_heads");
+    if (c->num_layers < 0) return bad("num_layers must be >= 0");
+    const long long nl = c->num_layers > 0 ? c->num_layers : 1;
+    if (nl > 4096) return bad("num_layers too large");
+    if (c->num_groups <= 0 || (nl * c->num_kv_heads) % c->num_groups)
+        return bad("num_groups must divide num_layers * num_kv_heads");
     if (c->max_batch <= 0 || c->num_pages <= 0 || c->max_pages <= 0) return bad("max_batch, num_pages, max_pages must be positive");
-    if ((long long)c->num_pages * (c->num_kv_heads / c->num_groups) * nup::kPage > 0x7fffffffLL)
+    if ((long long)c->num_pages * (nl * c->num_kv_heads / c->num_groups) * nup::kPage > 0x7fffffffLL)
         return bad("pool too large for 32-bit row ids");
     if ((long long)c->max_pages * nup::kPage > 0x7fffffffLL) return bad("max_pages too large");
     if (c->num_workers < 0) return bad("num_workers must be >= 0");
@@ -74,6 +78,7 @@ nup_status validate(const nup_config *c, std::string *why) {
 Sizes compute_sizes(const nup_config &c, int workers) {
     Sizes z{};
     const size_t B = c.max_batch, H = c.num_kv_heads, ng = c.num_groups;
+    const size_t NL = c.num_layers > 0 ? c.num_layers : 1, V = NL * H;
     const int splits = c.uniform_splits > 0 ? c.uniform_splits : 8;
     if (c.plan_mode == NUP_PLAN_UNIFORM) {
         z.max_rows = (int)(B * H * splits);
@@ -82,9 +87,9 @@ Sizes compute_sizes(const nup_config &c, int workers) {
         z.max_rows = workers + 2 * (int)(B * H);
         z.max_workers = workers;
     }
-    z.fixed = align_up(4 * (B + B * H + 3 * H));
-    z.plan_max = align_up(4 * ((size_t)z.max_workers + 1)) + align_up(4 * (B * H + 1)) +
-                 align_up(16 * (size_t)z.max_rows);
+    z.fixed = align_up(4 * (B + B * V + 3 * V));
+    z.plan_max = NL * (align_up(4 * ((size_t)z.max_workers + 1)) + align_up(4 * (B * H + 1)) +
+                       align_up(16 * (size_t)z.max_rows));
     // every train covers at least one live page-table entry; with Alias the
     // entries (not the physical pages) are what bounds their number
     const size_t entries = ng * B * (size_t)c.max_pages;
@@ -102,6 +107,8 @@ Sizes compute_sizes(const nup_config &c, int workers) {
 struct nup_ctx {
     nup_config cfg{};
     int H = 0, Hq = 0, D = 0, P = 0, ng = 0, gh = 0, B = 0, num_pages = 0, max_pages = 0, gqa = 0;
+    int NL = 1, V = 0;    // layers, and KV heads of all layers (V = NL*H): the pager's heads
+    int layer = 0;        // the layer per-layer calls act on
     int workers = 0;      // balanced-plan worker count
     Sizes sz{};
     std::string err;
@@ -111,7 +118,7 @@ struct nup_ctx {
     std::deque<int32_t> free_list;
     std::vector<int32_t> pt;       // [ng][B][max_pages]
     std::vector<int32_t> npages;   // [ng][B]
-    std::vector<int32_t> len, cap; // [B][H]
+    std::vector<int32_t> len, cap; // [B][V]
     std::vector<int32_t> active;   // [B]
     std::vector<int32_t> ref;      // [num_pages]: page-table entries mapping each page
     std::vector<int32_t> goh, soh, head_of_gslot;
@@ -126,15 +133,20 @@ struct nup_ctx {
     bool plan_dirty = true;
     bool pending = true;               // no commit yet, or edits since
 
-    // plan (shadow)
-    std::vector<int32_t> rows;         // [n][4]
-    std::vector<int32_t> worker_start; // [W+1]
-    std::vector<int32_t> head_row_start; // [B*H+1]
+    // plan of each layer (shadow)
+    struct Plan {
+        std::vector<int32_t> rows;           // [n][4] (s*H + h, t0, t1, 0)
+        std::vector<int32_t> worker_start;   // [W+1]
+        std::vector<int32_t> head_row_start; // [B*H+1]
+    };
+    std::vector<Plan> plan;                  // [NL]
 
     // active descriptor on the device (offsets into the inbox, in bytes)
     bool committed = false;
-    size_t off_ws = 0, off_hrs = 0, off_rows = 0, off_runs = 0, off_runpre = 0;
-    int dev_workers = 0, dev_rows = 0, dev_runs = 0, dev_run_pages = 0;
+    std::vector<size_t> off_ws, off_hrs, off_rows;   // [NL]
+    std::vector<int> dev_workers, dev_rows;          // [NL]
+    size_t off_runs = 0, off_runpre = 0;
+    int dev_runs = 0, dev_run_pages = 0;
 
     // device pointers
     char *desc = nullptr;
@@ -155,9 +167,11 @@ struct nup_ctx {
     int32_t *inbox_i32(size_t off) { return reinterpret_cast<int32_t *>(desc + off); }
     int32_t *d_active() { return inbox_i32(0); }
     int32_t *d_len() { return inbox_i32(4 * (size_t)B); }
-    int32_t *d_goh() { return inbox_i32(4 * ((size_t)B + (size_t)B * H)); }
-    int32_t *d_soh() { return d_goh() + H; }
-    int32_t *d_hog() { return d_goh() + 2 * H; }
+    int32_t *d_goh() { return inbox_i32(4 * ((size_t)B + (size_t)B * V)); }
+    int32_t *d_soh() { return d_goh() + V; }
+    int32_t *d_hog() { return d_goh() + 2 * V; }
+    // this layer's view of the per-head arrays (rows of lengths are V apart)
+    size_t lbase() const { return (size_t)layer * H; }
     int32_t *d_pt() { return reinterpret_cast<int32_t *>(desc + sz.inbox); }
     int32_t *d_err() { return reinterpret_cast<int32_t *>(desc + sz.inbox + sz.pt); }
 };
@@ -180,13 +194,13 @@ nup_status hip_fail(nup_ctx *c, hipError_t e, const char *what) {
 
 // ---- grouping (Tangram, Fig 8) --------------------------------------------
 void group_heads(nup_ctx *c, int n, const int32_t *cap) {
-    std::vector<long long> key(c->H, 0);
+    std::vector<long long> key(c->V, 0);
     for (int i = 0; i < n; ++i)
-        for (int h = 0; h < c->H; ++h) key[h] += cap[(size_t)i * c->H + h];
-    std::vector<int> order(c->H);
+        for (int h = 0; h < c->V; ++h) key[h] += cap[(size_t)i * c->V + h];
+    std::vector<int> order(c->V);
     std::iota(order.begin(), order.end(), 0);
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return key[a] < key[b]; });
-    for (int rank = 0; rank < c->H; ++rank) {
+    for (int rank = 0; rank < c->V; ++rank) {
         const int h = order[rank];
         c->goh[h] = rank / c->gh;
         c->soh[h] = rank % c->gh;
@@ -201,14 +215,15 @@ void group_heads(nup_ctx *c, int n, const int32_t *cap) {
 // into rows at head boundaries.  A head with no pages gets one empty row on
 // the worker at its position, so that its (zero) output is written too.
 // Rows come out sorted by head and, within that, by worker.
-void plan_balanced(nup_ctx *c) {
+void plan_balanced(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
     const int B = c->B, H = c->H, W = c->workers;
+    const int32_t *capl = c->cap.data() + (size_t)layer * H;   // row s at capl + s*V
     const int NH = B * H;
     static_assert(nup::kPage == 16, "page arithmetic below uses shifts");
     std::vector<long long> base((size_t)NH + 1, 0);  // first page of each head
     for (int s = 0, sh = 0; s < B; ++s)
         for (int h = 0; h < H; ++h, ++sh)
-            base[sh + 1] = base[sh] + (c->active[s] ? ((long long)c->cap[sh] + 15) >> 4 : 0);
+            base[sh + 1] = base[sh] + (c->active[s] ? ((long long)capl[(size_t)s * c->V + h] + 15) >> 4 : 0);
     const long long T = base[NH];
     // share boundaries floor(T*w/W), built without divisions in the loop
     std::vector<long long> bound((size_t)W + 1);
@@ -227,13 +242,13 @@ void plan_balanced(nup_ctx *c) {
     }
     const size_t max_rows = (size_t)W + 2 * (size_t)NH;
     std::vector<int32_t> owner(max_rows);
-    c->rows.resize(4 * max_rows);
-    c->head_row_start.resize((size_t)NH + 1);
-    int32_t *rw = c->rows.data();
+    pl.rows.resize(4 * max_rows);
+    pl.head_row_start.resize((size_t)NH + 1);
+    int32_t *rw = pl.rows.data();
     size_t n = 0;
     int w = 0;  // worker holding the current page; only moves forward
-    for (int sh = 0; sh < NH; ++sh) {
-        c->head_row_start[sh] = (int32_t)n;
+    for (int sh = 0, s = 0, h = 0; sh < NH; ++sh, (++h == H ? (h = 0, ++s) : 0)) {
+        pl.head_row_start[sh] = (int32_t)n;
         const long long lo = base[sh], hi = base[sh + 1];
         if (lo == hi) {
             int ow;
@@ -251,7 +266,7 @@ void plan_balanced(nup_ctx *c) {
             owner[n++] = ow;
             continue;
         }
-        const long long cap = c->cap[sh];
+        const long long cap = capl[(size_t)s * c->V + h];
         long long p = lo;
         while (p < hi) {
             while (bound[w + 1] <= p) ++w;
@@ -264,47 +279,50 @@ void plan_balanced(nup_ctx *c) {
             p = end;
         }
     }
-    c->head_row_start[NH] = (int32_t)n;
-    c->rows.resize(4 * n);
-    c->worker_start.resize((size_t)W + 1);
+    pl.head_row_start[NH] = (int32_t)n;
+    pl.rows.resize(4 * n);
+    pl.worker_start.resize((size_t)W + 1);
     size_t r = 0;
     for (int k = 0; k <= W; ++k) {
         while (r < n && owner[r] < k) ++r;
-        c->worker_start[k] = (int32_t)r;
+        pl.worker_start[k] = (int32_t)r;
     }
-    c->worker_start[W] = (int32_t)n;
+    pl.worker_start[W] = (int32_t)n;
 }
 
 // The uniform split (the control): every head is cut into the same number of
 // page-aligned chunks regardless of its length, one chunk per worker.
-void plan_uniform(nup_ctx *c) {
+void plan_uniform(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
     const int B = c->B, H = c->H, P = c->P;
     const int S = c->cfg.uniform_splits > 0 ? c->cfg.uniform_splits : 8;
-    c->rows.clear();
-    c->head_row_start.assign((size_t)B * H + 1, 0);
+    pl.rows.clear();
+    pl.head_row_start.assign((size_t)B * H + 1, 0);
     for (int sh = 0; sh < B * H; ++sh) {
         const int s = sh / H;
-        const int cap = c->active[s] ? c->cap[sh] : 0;
+        const int cap = c->active[s] ? c->cap[(size_t)s * c->V + (size_t)layer * H + sh % H] : 0;
         int nr = 0;
         if (cap > 0) {
             const long long chunk = (long long)P * ((((long long)cap + S - 1) / S + P - 1) / P);
             for (long long t0 = 0; t0 < cap; t0 += chunk) {
-                c->rows.insert(c->rows.end(), {sh, (int32_t)t0, (int32_t)std::min<long long>(t0 + chunk, cap), 0});
+                pl.rows.insert(pl.rows.end(), {sh, (int32_t)t0, (int32_t)std::min<long long>(t0 + chunk, cap), 0});
                 ++nr;
             }
         } else {
-            c->rows.insert(c->rows.end(), {sh, 0, 0, 0});
+            pl.rows.insert(pl.rows.end(), {sh, 0, 0, 0});
             nr = 1;
         }
-        c->head_row_start[sh + 1] = c->head_row_start[sh] + nr;
+        pl.head_row_start[sh + 1] = pl.head_row_start[sh] + nr;
     }
-    const int n = (int)(c->rows.size() / 4);
-    c->worker_start.resize(n + 1);
-    std::iota(c->worker_start.begin(), c->worker_start.end(), 0);
+    const int n = (int)(pl.rows.size() / 4);
+    pl.worker_start.resize(n + 1);
+    std::iota(pl.worker_start.begin(), pl.worker_start.end(), 0);
 }
 
 void replan(nup_ctx *c) {
-    if (c->cfg.plan_mode == NUP_PLAN_UNIFORM) plan_uniform(c); else plan_balanced(c);
+    for (int l = 0; l < c->NL; ++l) {
+        if (c->cfg.plan_mode == NUP_PLAN_UNIFORM) plan_uniform(c, l, c->plan[l]);
+        else plan_balanced(c, l, c->plan[l]);
+    }
 }
 
 // ---- trains (KV-RM, Fig 3) --------------------------------------------------
@@ -370,9 +388,9 @@ void install(nup_ctx *c, int s, const int32_t *need, int src, const int32_t *sha
         c->npages[ri] = np;
         c->runs_stale[ri] = 1;
     }
-    for (int h = 0; h < c->H; ++h) {
-        c->cap[(size_t)s * c->H + h] = cap[h];
-        c->len[(size_t)s * c->H + h] = len ? len[h] : 0;
+    for (int h = 0; h < c->V; ++h) {
+        c->cap[(size_t)s * c->V + h] = cap[h];
+        c->len[(size_t)s * c->V + h] = len ? len[h] : 0;
     }
     c->active[s] = 1;
 }
@@ -417,7 +435,9 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
     c->D = cfg->head_dim;
     c->P = cfg->page_size;
     c->ng = cfg->num_groups;
-    c->gh = c->H / c->ng;
+    c->NL = cfg->num_layers > 0 ? cfg->num_layers : 1;
+    c->V = c->NL * c->H;
+    c->gh = c->V / c->ng;
     c->B = cfg->max_batch;
     c->num_pages = cfg->num_pages;
     c->max_pages = cfg->max_pages;
@@ -464,13 +484,19 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
     }
     c->pt.assign((size_t)c->ng * c->B * c->max_pages, -1);
     c->npages.assign((size_t)c->ng * c->B, 0);
-    c->len.assign((size_t)c->B * c->H, 0);
-    c->cap.assign((size_t)c->B * c->H, 0);
+    c->len.assign((size_t)c->B * c->V, 0);
+    c->cap.assign((size_t)c->B * c->V, 0);
     c->active.assign(c->B, 0);
     c->ref.assign(c->num_pages, 0);
-    c->goh.assign(c->H, -1);
-    c->soh.assign(c->H, -1);
-    c->head_of_gslot.assign(c->H, -1);
+    c->goh.assign(c->V, -1);
+    c->soh.assign(c->V, -1);
+    c->head_of_gslot.assign(c->V, -1);
+    c->plan.assign(c->NL, {});
+    c->off_ws.assign(c->NL, 0);
+    c->off_hrs.assign(c->NL, 0);
+    c->off_rows.assign(c->NL, 0);
+    c->dev_workers.assign(c->NL, 0);
+    c->dev_rows.assign(c->NL, 0);
     c->dirty_count.assign((size_t)c->ng * c->B, 0);
     c->row_runs.assign((size_t)c->ng * c->B, {});
     c->runs_stale.assign((size_t)c->ng * c->B, 0);
@@ -512,9 +538,9 @@ nup_status kv_alloc_groups(nup_ctx *c, int32_t n, const int32_t *slots, const in
         if (s < 0 || s >= c->B) return fail(c, NUP_E_ARG, "slot %d out of range", s);
         if (seen[s]) return fail(c, NUP_E_ARG, "slot %d repeated", s);
         seen[s] = 1;
-        for (int h = 0; h < c->H; ++h) {
-            const long long cp = cap[(size_t)i * c->H + h];
-            const long long ln = len ? len[(size_t)i * c->H + h] : 0;
+        for (int h = 0; h < c->V; ++h) {
+            const long long cp = cap[(size_t)i * c->V + h];
+            const long long ln = len ? len[(size_t)i * c->V + h] : 0;
             if (cp < 0 || cp > (long long)c->max_pages * c->P)
                 return fail(c, NUP_E_ARG, "cap %lld of slot %d head %d outside [0, %lld]", cp, s, h,
                             (long long)c->max_pages * c->P);
@@ -529,19 +555,20 @@ nup_status kv_alloc_groups(nup_ctx *c, int32_t n, const int32_t *slots, const in
     if (!c->grouped) {
         nup_ctx tmp;  // reuse group_heads on a scratch context
         tmp.H = c->H;
+        tmp.V = c->V;
         tmp.gh = c->gh;
-        tmp.goh.assign(c->H, 0);
-        tmp.soh.assign(c->H, 0);
-        tmp.head_of_gslot.assign(c->H, 0);
+        tmp.goh.assign(c->V, 0);
+        tmp.soh.assign(c->V, 0);
+        tmp.head_of_gslot.assign(c->V, 0);
         group_heads(&tmp, n, cap);
         goh = tmp.goh;
     }
     std::vector<int32_t> need((size_t)n * c->ng, 0);
     long long total = 0;
     for (int i = 0; i < n; ++i)
-        for (int h = 0; h < c->H; ++h) {
+        for (int h = 0; h < c->V; ++h) {
             int32_t &x = need[(size_t)i * c->ng + goh[h]];
-            x = std::max<int32_t>(x, (cap[(size_t)i * c->H + h] + c->P - 1) / c->P);
+            x = std::max<int32_t>(x, (cap[(size_t)i * c->V + h] + c->P - 1) / c->P);
         }
     for (int32_t x : need) total += x;
     if (total > (long long)c->free_list.size())
@@ -549,8 +576,8 @@ nup_status kv_alloc_groups(nup_ctx *c, int32_t n, const int32_t *slots, const in
 
     if (!c->grouped) group_heads(c, n, cap);
     for (int i = 0; i < n; ++i)
-        install(c, slots[i], &need[(size_t)i * c->ng], -1, nullptr, cap + (size_t)i * c->H,
-                len ? len + (size_t)i * c->H : nullptr);
+        install(c, slots[i], &need[(size_t)i * c->ng], -1, nullptr, cap + (size_t)i * c->V,
+                len ? len + (size_t)i * c->V : nullptr);
     c->plan_dirty = true;
     c->pending = true;
     if (group_of_head_out) std::copy(c->goh.begin(), c->goh.end(), group_of_head_out);
@@ -577,9 +604,9 @@ nup_status kv_alias(nup_ctx *c, int32_t n, const int32_t *slots, const int32_t *
         if (seen[src]) return fail(c, NUP_E_ARG, "source slot %d is also a new slot", src);
     }
     for (int i = 0; i < n; ++i) {
-        for (int h = 0; h < c->H; ++h) {
-            const long long cp = cap[(size_t)i * c->H + h];
-            const long long ln = len[(size_t)i * c->H + h];
+        for (int h = 0; h < c->V; ++h) {
+            const long long cp = cap[(size_t)i * c->V + h];
+            const long long ln = len[(size_t)i * c->V + h];
             if (cp < 0 || cp > (long long)c->max_pages * c->P)
                 return fail(c, NUP_E_ARG, "cap %lld of slot %d head %d outside [0, %lld]", cp, slots[i], h,
                             (long long)c->max_pages * c->P);
@@ -596,18 +623,18 @@ nup_status kv_alias(nup_ctx *c, int32_t n, const int32_t *slots, const int32_t *
     }
     // shared pages must be full in both sequences, so that no append writes them
     for (int i = 0; i < n; ++i)
-        for (int h = 0; h < c->H; ++h) {
+        for (int h = 0; h < c->V; ++h) {
             const long long tokens = (long long)share_pages[(size_t)i * c->ng + c->goh[h]] * c->P;
-            if (tokens > len[(size_t)i * c->H + h] || tokens > c->len[(size_t)src_slots[i] * c->H + h])
+            if (tokens > len[(size_t)i * c->V + h] || tokens > c->len[(size_t)src_slots[i] * c->V + h])
                 return fail(c, NUP_E_ARG, "share of %lld tokens exceeds a length of slot %d or source %d (head %d)",
                             tokens, slots[i], src_slots[i], h);
         }
     std::vector<int32_t> need((size_t)n * c->ng, 0);
     long long fresh = 0;
     for (int i = 0; i < n; ++i) {
-        for (int h = 0; h < c->H; ++h) {
+        for (int h = 0; h < c->V; ++h) {
             int32_t &x = need[(size_t)i * c->ng + c->goh[h]];
-            x = std::max<int32_t>(x, (cap[(size_t)i * c->H + h] + c->P - 1) / c->P);
+            x = std::max<int32_t>(x, (cap[(size_t)i * c->V + h] + c->P - 1) / c->P);
         }
         for (int g = 0; g < c->ng; ++g) fresh += need[(size_t)i * c->ng + g] - share_pages[(size_t)i * c->ng + g];
     }
@@ -615,7 +642,7 @@ nup_status kv_alias(nup_ctx *c, int32_t n, const int32_t *slots, const int32_t *
         return fail(c, NUP_E_NOPAGES, "need %lld pages, %zu free", fresh, c->free_list.size());
     for (int i = 0; i < n; ++i)
         install(c, slots[i], &need[(size_t)i * c->ng], src_slots[i], share_pages + (size_t)i * c->ng,
-                cap + (size_t)i * c->H, len + (size_t)i * c->H);
+                cap + (size_t)i * c->V, len + (size_t)i * c->V);
     c->plan_dirty = true;
     c->pending = true;
     return NUP_OK;
@@ -647,9 +674,9 @@ nup_status kv_free_seqs(nup_ctx *c, int32_t n, const int32_t *slots) {
             c->npages[ri] = 0;
             c->runs_stale[ri] = 1;
         }
-        for (int h = 0; h < c->H; ++h) {
-            c->cap[(size_t)s * c->H + h] = 0;
-            c->len[(size_t)s * c->H + h] = 0;
+        for (int h = 0; h < c->V; ++h) {
+            c->cap[(size_t)s * c->V + h] = 0;
+            c->len[(size_t)s * c->V + h] = 0;
         }
         c->active[s] = 0;
     }
@@ -679,30 +706,34 @@ nup_status nup_commit(nup_ctx *c, void *stream) {
     }
     char *blob = c->pinned[i];
     int32_t *w = reinterpret_cast<int32_t *>(blob);
-    const size_t B = c->B, H = c->H;
+    const size_t B = c->B, V = c->V;
     for (size_t s = 0; s < B; ++s) w[s] = c->active[s];
-    for (size_t k = 0; k < B * H; ++k) w[B + k] = c->active[k / H] ? c->len[k] : 0;
-    std::copy(c->goh.begin(), c->goh.end(), w + B + B * H);
-    std::copy(c->soh.begin(), c->soh.end(), w + B + B * H + H);
-    std::copy(c->head_of_gslot.begin(), c->head_of_gslot.end(), w + B + B * H + 2 * H);
+    for (size_t k = 0; k < B * V; ++k) w[B + k] = c->active[k / V] ? c->len[k] : 0;
+    std::copy(c->goh.begin(), c->goh.end(), w + B + B * V);
+    std::copy(c->soh.begin(), c->soh.end(), w + B + B * V + V);
+    std::copy(c->head_of_gslot.begin(), c->head_of_gslot.end(), w + B + B * V + 2 * V);
     size_t used = c->sz.fixed;
     int n_patches = 0;
     size_t off_hdr = 0, off_data = 0;
     if (c->plan_dirty || !c->committed) {
         // plan (once per commit, however many Reserve / Trim edits came before)
         replan(c);
-        const int nw = (int)c->worker_start.size() - 1;
-        const int nr = (int)(c->rows.size() / 4);
         size_t off = used;
-        c->off_ws = off;
-        std::memcpy(blob + off, c->worker_start.data(), 4 * c->worker_start.size());
-        off = align_up(off + 4 * c->worker_start.size());
-        c->off_hrs = off;
-        std::memcpy(blob + off, c->head_row_start.data(), 4 * c->head_row_start.size());
-        off = align_up(off + 4 * c->head_row_start.size());
-        c->off_rows = off;
-        if (nr) std::memcpy(blob + off, c->rows.data(), 16 * (size_t)nr);
-        off = align_up(off + 16 * (size_t)nr);
+        for (int l = 0; l < c->NL; ++l) {
+            const nup_ctx::Plan &pl = c->plan[l];
+            const int nr = (int)(pl.rows.size() / 4);
+            c->off_ws[l] = off;
+            std::memcpy(blob + off, pl.worker_start.data(), 4 * pl.worker_start.size());
+            off = align_up(off + 4 * pl.worker_start.size());
+            c->off_hrs[l] = off;
+            std::memcpy(blob + off, pl.head_row_start.data(), 4 * pl.head_row_start.size());
+            off = align_up(off + 4 * pl.head_row_start.size());
+            c->off_rows[l] = off;
+            if (nr) std::memcpy(blob + off, pl.rows.data(), 16 * (size_t)nr);
+            off = align_up(off + 16 * (size_t)nr);
+            c->dev_workers[l] = (int)pl.worker_start.size() - 1;
+            c->dev_rows[l] = nr;
+        }
         // trains
         std::vector<int32_t> runs5;
         build_runs(c, runs5);
@@ -745,8 +776,6 @@ nup_status nup_commit(nup_ctx *c, void *stream) {
             ++p;
         }
         used = off + 4 * dpos;
-        c->dev_workers = nw;
-        c->dev_rows = nr;
         c->dev_runs = nruns;
         c->dev_run_pages = pre[nruns];
     }
@@ -782,9 +811,10 @@ nup_status kv_append(nup_ctx *c, const void *k_new, const void *v_new, void *str
     for (int s = 0; s < c->B; ++s) {
         if (!c->active[s]) continue;
         for (int h = 0; h < c->H; ++h) {
-            const size_t k = (size_t)s * c->H + h;
+            const size_t k = (size_t)s * c->V + c->lbase() + h;
             if (c->len[k] >= c->cap[k])
-                return fail(c, NUP_E_CAPACITY, "slot %d head %d is at its budget (%d tokens)", s, h, c->cap[k]);
+                return fail(c, NUP_E_CAPACITY, "slot %d layer %d head %d is at its budget (%d tokens)", s,
+                            c->layer, h, c->cap[k]);
         }
     }
     nup::AppendArgs a{};
@@ -794,18 +824,19 @@ nup_status kv_append(nup_ctx *c, const void *k_new, const void *v_new, void *str
     a.v_new = static_cast<const uint16_t *>(v_new);
     a.page_table = c->d_pt();
     a.active = c->d_active();
-    a.group_of_head = c->d_goh();
-    a.slot_of_head = c->d_soh();
-    a.lengths = c->d_len();
+    a.group_of_head = c->d_goh() + c->lbase();
+    a.slot_of_head = c->d_soh() + c->lbase();
+    a.lengths = c->d_len() + c->lbase();
     a.bmax = c->B;
     a.hkv = c->H;
     a.gh = c->gh;
     a.max_pages = c->max_pages;
+    a.lstride = c->V;
     hipError_t e = nup::launch_append(a, c->D, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(c, e, "append launch");
     for (int s = 0; s < c->B; ++s)
         if (c->active[s])
-            for (int h = 0; h < c->H; ++h) c->len[(size_t)s * c->H + h]++;
+            for (int h = 0; h < c->H; ++h) c->len[(size_t)s * c->V + c->lbase() + h]++;
     return NUP_OK;
 }
 
@@ -824,9 +855,10 @@ nup_status kv_gather_compact(nup_ctx *c, int32_t mode, const int32_t *idx, int32
         a.v_pool = c->vpool;
         a.page_table = c->d_pt();
         a.active = c->d_active();
-        a.lengths = c->d_len();
-        a.group_of_head = c->d_goh();
-        a.slot_of_head = c->d_soh();
+        a.lengths = c->d_len() + c->lbase();
+        a.group_of_head = c->d_goh() + c->lbase();
+        a.slot_of_head = c->d_soh() + c->lbase();
+        a.lstride = c->V;
         a.idx = idx;
         a.k_out = static_cast<uint16_t *>(k_out);
         a.v_out = static_cast<uint16_t *>(v_out);
@@ -846,7 +878,9 @@ nup_status kv_gather_compact(nup_ctx *c, int32_t mode, const int32_t *idx, int32
         a.runs = c->inbox_i32(c->off_runs);
         a.run_prefix = c->inbox_i32(c->off_runpre);
         a.active = c->d_active();
-        a.lengths = c->d_len();
+        a.lengths = c->d_len() + c->lbase();
+        a.lstride = c->V;
+        a.layer_base = (int32_t)c->lbase();
         a.head_of_gslot = c->d_hog();
         a.row_off = row_off;
         a.k_out = static_cast<uint16_t *>(k_out);
@@ -882,8 +916,9 @@ nup_status kv_gather_trains_dma(nup_ctx *c, void *k_out, void *v_out, const int6
             for (size_t k = 0; k < rr.size(); k += 3) {
                 const int64_t phys = rr[k], pages = rr[k + 1], logical = rr[k + 2];
                 for (int j = 0; j < c->gh; ++j) {
-                    const int h = c->head_of_gslot[g * c->gh + j];
-                    const int64_t L = c->len[(size_t)s * c->H + h];
+                    const int h = c->head_of_gslot[g * c->gh + j] - (int)c->lbase();  // this layer's?
+                    if (h < 0 || h >= c->H) continue;
+                    const int64_t L = c->len[(size_t)s * c->V + c->lbase() + h];
                     const int64_t rows = std::min<int64_t>(std::max<int64_t>(L - logical * c->P, 0), pages * c->P);
                     if (rows == 0) continue;
                     const int64_t full = rows / c->P, tail = rows % c->P;
@@ -965,9 +1000,10 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
     nup::PartialArgs a{};
     a.q = static_cast<const uint16_t *>(q);
     a.active = c->d_active();
-    a.lengths = c->d_len();
-    a.group_of_head = c->d_goh();
-    a.slot_of_head = c->d_soh();
+    a.lengths = c->d_len() + c->lbase();
+    a.group_of_head = c->d_goh() + c->lbase();
+    a.slot_of_head = c->d_soh() + c->lbase();
+    a.lstride = c->V;
     a.bmax = c->B;
     a.hkv = c->H;
     a.gh = c->gh;
@@ -997,9 +1033,9 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
         a.kbase = c->kpool;
         a.vbase = c->vpool;
         a.page_table = c->d_pt();
-        a.rows = c->inbox_i32(c->off_rows);
-        a.worker_start = c->inbox_i32(c->off_ws);
-        a.n_workers = c->dev_workers;
+        a.rows = c->inbox_i32(c->off_rows[c->layer]);
+        a.worker_start = c->inbox_i32(c->off_ws[c->layer]);
+        a.n_workers = c->dev_workers[c->layer];
         rows_max = c->sz.max_rows;
     }
     float *wso = static_cast<float *>(ws);
@@ -1009,7 +1045,7 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
     a.ws_ml = wsml;
     a.out = out;
     a.lse = lse;
-    a.head_row_start = topk ? nullptr : c->inbox_i32(c->off_hrs);
+    a.head_row_start = topk ? nullptr : c->inbox_i32(c->off_hrs[c->layer]);
     hipError_t e;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (c->timing) {
@@ -1078,33 +1114,35 @@ nup_status kv_select_topk(nup_ctx *c, const void *q, int32_t K, int32_t window, 
     for (int s = 0; s < c->B; ++s) {
         if (!c->active[s]) continue;
         for (int h = 0; h < c->H; ++h)
-            if (c->len[(size_t)s * c->H + h] < K)
+            if (c->len[(size_t)s * c->V + c->lbase() + h] < K)
                 return fail(c, NUP_E_ARG, "slot %d head %d retains %d < K = %d entries", s, h,
-                            c->len[(size_t)s * c->H + h], K);
+                            c->len[(size_t)s * c->V + c->lbase() + h], K);
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     nup::ScoreArgs sa{};
     sa.q = static_cast<const uint16_t *>(q);
     sa.kbase = c->kpool;
     sa.page_table = c->d_pt();
-    sa.lengths = c->d_len();
-    sa.group_of_head = c->d_goh();
-    sa.slot_of_head = c->d_soh();
-    sa.rows = c->inbox_i32(c->off_rows);
-    sa.worker_start = c->inbox_i32(c->off_ws);
+    sa.lengths = c->d_len() + c->lbase();
+    sa.group_of_head = c->d_goh() + c->lbase();
+    sa.slot_of_head = c->d_soh() + c->lbase();
+    sa.lstride = c->V;
+    sa.rows = c->inbox_i32(c->off_rows[c->layer]);
+    sa.worker_start = c->inbox_i32(c->off_ws[c->layer]);
     sa.scores = static_cast<float *>(workspace);
     sa.bmax = c->B;
     sa.hkv = c->H;
     sa.gh = c->gh;
     sa.max_pages = c->max_pages;
-    sa.n_workers = c->dev_workers;
+    sa.n_workers = c->dev_workers[c->layer];
     sa.stride = c->max_pages * nup::kPage;
     hipError_t e = nup::launch_score(sa, c->D, c->gqa, st);
     if (e != hipSuccess) return hip_fail(c, e, "score launch");
     nup::SelectArgs sl{};
     sl.scores = sa.scores;
     sl.active = c->d_active();
-    sl.lengths = c->d_len();
+    sl.lengths = c->d_len() + c->lbase();
+    sl.lstride = c->V;
     sl.idx_out = idx_out;
     sl.hkv = c->H;
     sl.stride = sa.stride;
@@ -1123,7 +1161,7 @@ nup_status nup_get_page_table(const nup_ctx *c, int32_t *out) {
 
 nup_status nup_get_lengths(const nup_ctx *c, int32_t *out) {
     if (!c || !out) return NUP_E_ARG;
-    for (size_t k = 0; k < c->len.size(); ++k) out[k] = c->active[k / c->H] ? c->len[k] : 0;
+    for (size_t k = 0; k < c->len.size(); ++k) out[k] = c->active[k / c->V] ? c->len[k] : 0;
     return NUP_OK;
 }
 
@@ -1162,11 +1200,19 @@ nup_status nup_get_plan(const nup_ctx *c, int32_t *n_rows, int32_t *n_workers, i
                         int32_t *worker_start, int32_t *head_row_start) {
     if (!c) return NUP_E_ARG;
     if (c->plan_dirty) replan(const_cast<nup_ctx *>(c));  // the plan of the shadow
-    if (n_rows) *n_rows = (int32_t)(c->rows.size() / 4);
-    if (n_workers) *n_workers = (int32_t)c->worker_start.size() - 1;
-    if (rows) std::copy(c->rows.begin(), c->rows.end(), rows);
-    if (worker_start) std::copy(c->worker_start.begin(), c->worker_start.end(), worker_start);
-    if (head_row_start) std::copy(c->head_row_start.begin(), c->head_row_start.end(), head_row_start);
+    const nup_ctx::Plan &pl = c->plan[c->layer];
+    if (n_rows) *n_rows = (int32_t)(pl.rows.size() / 4);
+    if (n_workers) *n_workers = (int32_t)pl.worker_start.size() - 1;
+    if (rows) std::copy(pl.rows.begin(), pl.rows.end(), rows);
+    if (worker_start) std::copy(pl.worker_start.begin(), pl.worker_start.end(), worker_start);
+    if (head_row_start) std::copy(pl.head_row_start.begin(), pl.head_row_start.end(), head_row_start);
+    return NUP_OK;
+}
+
+nup_status nup_set_layer(nup_ctx *c, int32_t layer) {
+    if (!c) return NUP_E_ARG;
+    if (layer < 0 || layer >= c->NL) return fail(c, NUP_E_ARG, "layer %d outside [0, %d)", layer, c->NL);
+    c->layer = layer;
     return NUP_OK;
 }
 

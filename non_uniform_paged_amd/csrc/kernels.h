@@ -1,5 +1,9 @@
 // Internal interface between the host control plane (host.cpp) and the
 // gfx950 kernels (kernels.hip).  Not part of the public ABI.
+//
+// Per-head arrays (lengths, group_of_head, slot_of_head) are passed already
+// offset to the layer being processed; lengths rows are `lstride` entries
+// apart (the KV heads of all layers), so entry (s, h) is lengths[s*lstride + h].
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -27,7 +31,7 @@ struct PartialArgs {
     const uint16_t *vbase;
     const int32_t *page_table;  // [ng][Bmax][max_pages] (paged)
     const int32_t *active;      // [Bmax]
-    const int32_t *lengths;     // [Bmax*Hkv] (paged)
+    const int32_t *lengths;     // this layer's lengths: entry (s, h) at s*lstride + h (paged)
     const int32_t *group_of_head;
     const int32_t *slot_of_head;
     const int32_t *rows;        // [n][4] (sh, t0, t1, 0) (paged)
@@ -40,6 +44,7 @@ struct PartialArgs {
     float *out;                 // fp32 [Bmax][Hq][D]
     float *lse;                 // fp32 [Bmax][Hq] or NULL
     int32_t bmax, hkv, gh, max_pages, n_workers;
+    int32_t lstride;            // length-row stride: KV heads of all layers
     int32_t topk_k, topk_splits, topk_chunk;
     float scale_log2;           // softmax scale * log2(e)
 };
@@ -65,14 +70,14 @@ struct ScoreArgs {
     const uint16_t *q, *kbase;
     const int32_t *page_table, *lengths, *group_of_head, *slot_of_head, *rows, *worker_start;
     float *scores;
-    int32_t bmax, hkv, gh, max_pages, n_workers, stride;
+    int32_t bmax, hkv, gh, max_pages, n_workers, stride, lstride;
 };
 
 struct SelectArgs {
     const float *scores;
     const int32_t *active, *lengths;
     int32_t *idx_out;              // [Bmax*Hkv][K]
-    int32_t hkv, stride, k, window;
+    int32_t hkv, stride, k, window, lstride;
 };
 
 struct AppendArgs {
@@ -80,7 +85,7 @@ struct AppendArgs {
     const uint16_t *k_new, *v_new; // [Bmax][Hkv][D]
     const int32_t *page_table, *active, *group_of_head, *slot_of_head;
     int32_t *lengths;
-    int32_t bmax, hkv, gh, max_pages;
+    int32_t bmax, hkv, gh, max_pages, lstride;
 };
 
 struct GatherIndexArgs {
@@ -90,18 +95,19 @@ struct GatherIndexArgs {
     uint16_t *k_out, *v_out;       // [Bmax*Hkv][K][D]
     int32_t *phys_out;             // [Bmax*Hkv][K] or NULL
     int32_t *err;                  // latched error word
-    int32_t bmax, hkv, gh, max_pages, k;
+    int32_t bmax, hkv, gh, max_pages, k, lstride;
 };
 
 struct GatherRunsArgs {
     const uint16_t *k_pool, *v_pool;
     const int32_t *runs;           // [n_runs][4] (slot*ng+g, phys, pages, logical)
     const int32_t *run_prefix;     // [n_runs+1] page prefix sums
-    const int32_t *active, *lengths, *head_of_gslot;
+    const int32_t *active, *lengths, *head_of_gslot;  // head_of_gslot: all layers' heads
     const int64_t *row_off;        // [Bmax*Hkv]
     uint16_t *k_out, *v_out;       // packed rows of D
     int32_t *phys_out;             // packed like the rows, or NULL
-    int32_t n_runs, ng, gh, hkv;
+    int32_t n_runs, ng, gh, hkv, lstride;
+    int32_t layer_base;            // first head of this layer in head_of_gslot numbering
 };
 
 bool supported_shape(int head_dim, int gqa);

@@ -162,9 +162,9 @@ void partial_attn_kernel(PartialArgs a) {
         } else {
             sh = ld_uniform(a.rows + row * 4 + 0);
             t0 = ld_uniform(a.rows + row * 4 + 1);
-            t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + sh));
         }
         const int s = sh / a.hkv, h = sh - s * a.hkv;
+        if (!TOPK) t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + s * a.lstride + h));
         float *ml = a.ws_ml + (size_t)row * GQA * 2;
         int hr0, nrows;   // the rows of this head
         if (TOPK) {
@@ -220,7 +220,7 @@ void partial_attn_kernel(PartialArgs a) {
             // read; entries out of order are read but flagged.  Either latches
             // the error word.
             const int32_t *il = a.idx + (size_t)sh * a.topk_k;
-            const int L = ld_uniform(a.lengths + sh);
+            const int L = ld_uniform(a.lengths + s * a.lstride + h);
             const int slot = ld_uniform(a.slot_of_head + h);
             bool bad = false;
             for (int e = t0 + lane; e < t1; e += 64) {
@@ -537,9 +537,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     for (int row = rb; row < re; ++row) {
         const int sh = ld_uniform(a.rows + row * 4 + 0);
         const int t0 = ld_uniform(a.rows + row * 4 + 1);
-        const int t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + sh));
-        if (t0 >= t1) continue;
         const int s = sh / a.hkv, h = sh - s * a.hkv;
+        const int t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + s * a.lstride + h));
+        if (t0 >= t1) continue;
         uint4 qv[NJ];
         const uint4 *qh = reinterpret_cast<const uint4 *>(
             a.q + ((size_t)s * a.hkv * GQA + (size_t)h * GQA + (qn < GQA ? qn : 0)) * D);
@@ -667,8 +667,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     __shared__ uint32_t pick[2];
     const int sh = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
-    if (!a.active[sh / a.hkv]) return;
-    const int L = a.lengths[sh];
+    const int s = sh / a.hkv;
+    if (!a.active[s]) return;
+    const int L = a.lengths[s * a.lstride + (sh - s * a.hkv)];
     const int n = L - a.window, k = a.k - a.window;
     int32_t *out = a.idx_out + (size_t)sh * a.k;
     for (int j = tid; j < a.window; j += kSelectThreads) out[k + j] = n + j;
@@ -804,7 +805,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const bool act = ok && a.active[s];
     int L = 0;
     if (act) {
-        L = a.lengths[sh];
+        L = a.lengths[s * a.lstride + h];
         const int pid = a.page_table[((size_t)a.group_of_head[h] * a.bmax + s) * a.max_pages + L / kPage];
         const size_t rowid = ((size_t)pid * a.gh + a.slot_of_head[h]) * kPage + L % kPage;
         const bool isv = sub >= LPR;
@@ -814,7 +815,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         *dst = *src;
     }
     __syncthreads();
-    if (act && sub == 0) a.lengths[sh] = L + 1;
+    if (act && sub == 0) a.lengths[s * a.lstride + h] = L + 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -847,7 +848,7 @@ __global__ __launch_bounds__(256) void gather_index_kernel(GatherIndexArgs a) {
         const int s = sh / a.hkv, h = sh - s * a.hkv;
         if (!a.active[s]) continue;
         const int t = a.idx[gr[u]];
-        const int L = a.lengths[sh];
+        const int L = a.lengths[s * a.lstride + h];
         if (t < 0 || t >= L || (kk > 0 && a.idx[gr[u] - 1] >= t)) {
             state[u] = 2;
             continue;
@@ -906,10 +907,11 @@ __global__ __launch_bounds__(256) void gather_runs_kernel(GatherRunsArgs a) {
         const int j = cc / (kPage * LPR);             // slot in the group
         const int row = (cc / LPR) % kPage;           // row in the page
         const int piece = cc % LPR;
-        const int h = a.head_of_gslot[g * a.gh + j];
+        const int h = a.head_of_gslot[g * a.gh + j] - a.layer_base;   // head of this layer?
+        if (h < 0 || h >= a.hkv) continue;
         const int sh = s * a.hkv + h;
         const int t = lp * kPage + row;
-        if (t >= a.lengths[sh]) continue;
+        if (t >= a.lengths[s * a.lstride + h]) continue;
         const size_t rowid = ((size_t)pid * a.gh + j) * kPage + row;
         const uint4 v = ld_stream(reinterpret_cast<const uint4 *>((isv ? a.v_pool : a.k_pool) + rowid * D) + piece);
         const long long dr = a.row_off[sh] + t;

@@ -23,9 +23,10 @@ def u16(t: torch.Tensor) -> np.ndarray:
 
 class Case:
     def __init__(self, *, H, Hq, D, ng, B, num_pages, max_pages, free_list_init=None,
-                 num_workers=0, plan_mode=0, uniform_splits=0, salt=0):
+                 num_workers=0, plan_mode=0, uniform_splits=0, salt=0, num_layers=1):
         self.H, self.Hq, self.D, self.ng, self.B = H, Hq, D, ng, B
-        self.gh = H // ng
+        self.NL, self.V = num_layers, num_layers * H      # the pager's (layer, head) pairs
+        self.gh = self.V // ng
         self.num_pages, self.max_pages = num_pages, max_pages
         self.kpool = torch.empty((num_pages, self.gh, 16, D), dtype=torch.bfloat16, device=DEV)
         self.vpool = torch.empty_like(self.kpool)
@@ -33,11 +34,11 @@ class Case:
         fill_normal_bf16_torch(self.vpool, "v", salt)
         cfg = dict(num_kv_heads=H, num_q_heads=Hq, head_dim=D, num_groups=ng, max_batch=B,
                    num_pages=num_pages, max_pages=max_pages, num_workers=num_workers,
-                   plan_mode=plan_mode, uniform_splits=uniform_splits)
+                   plan_mode=plan_mode, uniform_splits=uniform_splits, num_layers=num_layers)
         self.desc = torch.empty(nup.desc_bytes(**cfg), dtype=torch.uint8, device=DEV)
         self.ctx = nup.Context(**cfg, k_pool=self.kpool, v_pool=self.vpool, desc=self.desc,
                                free_list_init=free_list_init)
-        self.spec = pg.PagerSpec(H, ng, B, num_pages, max_pages, 16, free_list_init)
+        self.spec = pg.PagerSpec(self.V, ng, B, num_pages, max_pages, 16, free_list_init)
         self.q = torch.from_numpy(normal_bf16("q", (B, Hq, D), salt).view(np.int16)).to(DEV).view(torch.bfloat16)
         self.ws = torch.empty(nup.workspace_bytes(self.ctx), dtype=torch.uint8, device=DEV)
         self.out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=DEV)

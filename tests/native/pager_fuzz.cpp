@@ -14,12 +14,15 @@ int main(int argc, char **argv) {
     std::mt19937 rng(seed);
     long ops = 0, aliased = 0;
     for (int trial = 0; trial < 40; ++trial) {
-        const int H = 1 << (rng() % 4);               // 1, 2, 4, 8 KV heads
+        const int Hl = 1 << (rng() % 4);              // 1, 2, 4, 8 KV heads per layer
+        const int NL = 1 + rng() % 3;                 // layers sharing the pager
+        const int H = NL * Hl;                        // the pager's heads
         const int ng = 1 << (rng() % 4);
         if (H % ng) continue;
         nup_config c{};
-        c.num_kv_heads = H;
-        c.num_q_heads = H * (int[]){1, 2, 4, 5, 8}[rng() % 5];
+        c.num_kv_heads = Hl;
+        c.num_layers = NL;
+        c.num_q_heads = Hl * (int[]){1, 2, 4, 5, 8}[rng() % 5];
         c.head_dim = rng() % 2 ? 128 : 64;
         c.page_size = 16;
         c.num_groups = ng;
@@ -86,8 +89,9 @@ int main(int argc, char **argv) {
                     for (int32_t s : slots) live[s] = 0;
             }
             int32_t nr = 0, nw = 0, nruns = 0, nfree = 0;
+            nup_set_layer(ctx, (int32_t)(rng() % (NL + 1)) - (rng() % 16 == 0));   // sometimes invalid
             nup_get_plan(ctx, &nr, &nw, nullptr, nullptr, nullptr);
-            std::vector<int32_t> rows((size_t)4 * nr + 4), ws(nw + 1), hrs((size_t)c.max_batch * H + 1);
+            std::vector<int32_t> rows((size_t)4 * nr + 4), ws(nw + 1), hrs((size_t)c.max_batch * Hl + 1);
             nup_get_plan(ctx, nullptr, nullptr, rows.data(), ws.data(), hrs.data());
             nup_get_runs(ctx, runs.data(), c.num_pages + 1, &nruns);
             nup_get_page_table(ctx, pt.data());

@@ -189,6 +189,45 @@ def test_pager_matches_oracle(data):
         wt.check(rows, ws, hrs, spec.caps, spec.active)
 
 
+@settings(max_examples=25, deadline=None)
+@given(st.data())
+def test_layers_share_one_pager(data):
+    """Several layers in one pager: grouping over (layer, head) pairs, page
+    tables and lengths equal the oracle pager's over those pairs, and each
+    layer's plan covers exactly that layer's heads."""
+    NL = data.draw(st.sampled_from([2, 3, 4]))
+    H = data.draw(st.sampled_from([2, 4]))
+    V = NL * H
+    ng = data.draw(st.sampled_from([g for g in (1, 2, 3, 4, 6, 8, 12) if V % g == 0]))
+    B, num_pages, max_pages = 4, 200, 8
+    perm = np.array(data.draw(st.permutations(list(range(num_pages)))), np.int32)
+    ctx = _host_ctx(H=H, Hq=2 * H, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages, fl=perm,
+                    num_workers=11, num_layers=NL)
+    spec = pg.PagerSpec(V, ng, B, num_pages, max_pages, 16, perm)
+    for step in range(data.draw(st.integers(1, 6))):
+        if step == 0 or data.draw(st.booleans()):
+            slots = data.draw(st.lists(st.integers(0, B - 1), min_size=1, max_size=2, unique=True))
+            caps = np.array([[data.draw(st.integers(0, max_pages * 16)) for _ in range(V)] for _ in slots])
+            lens = np.array([[data.draw(st.integers(0, int(c))) for c in row] for row in caps])
+            assert spec.alloc(slots, caps, lens) == nup.kv_alloc_groups(ctx, slots, caps, lens,
+                                                                       raise_on_error=False)
+        else:
+            slots = data.draw(st.lists(st.integers(0, B - 1), min_size=1, max_size=2, unique=True))
+            assert spec.free_seqs(slots) == nup.kv_free_seqs(ctx, slots, raise_on_error=False)
+        assert np.array_equal(nup.get_page_table(ctx), spec.page_table)
+        assert np.array_equal(nup.get_lengths(ctx), spec.lengths)
+        assert np.array_equal(nup.get_free_list(ctx), spec.free_list())
+        if spec.group_of_head is not None:
+            g, sl = nup.get_groups(ctx)
+            assert np.array_equal(g, spec.group_of_head) and np.array_equal(sl, spec.slot_of_head)
+        for layer in range(NL):
+            nup.set_layer(ctx, layer)
+            rows, ws, hrs = nup.get_plan(ctx)
+            wt.check(rows, ws, hrs, spec.caps[:, layer * H:(layer + 1) * H], spec.active)
+    with pytest.raises(nup.NupError):
+        nup.set_layer(ctx, NL)
+
+
 @pytest.mark.parametrize("name", ["qwen3_4b", "qwen25_32b", "mixed_churn"])
 def test_plan_on_config_shapes(name):
     import workloads as W

@@ -171,6 +171,31 @@ def qwen3_4b(headroom: int = PAGE) -> Workload:
                     extra={"scale_factor": hi, "context": ctx})
 
 
+def qwen3_4b_layers(num_layers: int = 36, headroom: int = PAGE, batch: int = 16) -> Workload:
+    """The Qwen3-4B shape over all its layers: 36 layers x 8 KV heads, one
+    budget per (layer, KV head), log-uniform in [256, 16384] and scaled so the
+    mean over all 288 heads is half the context (the same reading as the
+    one-layer shape), rounded to the page.  num_kv_heads is per layer;
+    lengths and caps are [batch][num_layers * 8], head index layer * 8 + h."""
+    ctx = 16384
+    g = rng("budgets", 21)
+    n = num_layers * 8
+    raw = np.exp(g.uniform(math.log(256), math.log(ctx), size=n))
+    lo, hi = 1.0, 64.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if np.minimum(raw * mid, ctx).mean() < ctx / 2:
+            lo = mid
+        else:
+            hi = mid
+    budgets = round_to_page(np.minimum(raw * hi, ctx), ctx)
+    lengths = np.tile(budgets, (batch, 1))
+    caps = lengths + headroom
+    pool = int(math.ceil(1.25 * _group_footprint_pages(caps, 1) * 8))
+    return Workload("qwen3_4b_layers", batch, 32, 8, 128, num_layers, lengths, caps, pool,
+                    extra={"num_layers": num_layers, "context": ctx})
+
+
 def qwen25_32b(headroom: int = PAGE, control: Optional[str] = None,
                batch: int = 64) -> Workload:
     """Qwen2.5-32B-shaped multi-turn layer: 64 sessions, 40 q / 8 KV heads,
@@ -295,6 +320,7 @@ CONFIGS = {
     "qwen3_4b": qwen3_4b,
     "qwen25_32b": qwen25_32b,
     "qwen25_32b_prefix": qwen25_32b_prefix,
+    "qwen3_4b_layers": qwen3_4b_layers,
     "llama3_8b_topk": llama3_8b_topk,
     "mixed_churn": mixed_churn,
 }
