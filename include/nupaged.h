@@ -335,7 +335,9 @@ nup_status nup_get_refcounts(const nup_ctx *ctx, int32_t *out);
  * group, logical page) order; count in *n (NUP_E_ARG if max_runs is short). */
 nup_status nup_get_runs(const nup_ctx *ctx, int32_t *out, int32_t max_runs, int32_t *n);
 /* Split-K plan of the shadow for the current layer: counts first (any pointer may be NULL).
- *   rows           int32 [n_rows][4] = (slot*H_kv + head, t0, t1, 0)
+ *   rows           int32 [n_rows][4] = (slot*H_kv + head, t0, t1, slot*V + head);
+ *                  the last word indexes the head's length from the current
+ *                  layer's first head, length rows being V apart
  *   worker_start   int32 [n_workers + 1]
  *   head_row_start int32 [B_max*H_kv + 1] */
 nup_status nup_get_plan(const nup_ctx *ctx, int32_t *n_rows, int32_t *n_workers,

@@ -214,7 +214,10 @@ void group_heads(nup_ctx *c, int n, const int32_t *cap) {
 // order, are cut into `workers` equal contiguous shares; a share is split
 // into rows at head boundaries.  A head with no pages gets one empty row on
 // the worker at its position, so that its (zero) output is written too.
-// Rows come out sorted by head and, within that, by worker.
+// Rows come out sorted by head and, within that, by worker.  A row is
+// (s*H + h, t0, t1, s*V + h): the last word indexes the head's length in
+// the layer's view of the lengths (rows V apart), so the kernels read it
+// without a division.
 void plan_balanced(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
     const int B = c->B, H = c->H, W = c->workers;
     const int32_t *capl = c->cap.data() + (size_t)layer * H;   // row s at capl + s*V
@@ -262,7 +265,7 @@ void plan_balanced(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
             rw[4 * n + 0] = sh;
             rw[4 * n + 1] = 0;
             rw[4 * n + 2] = 0;
-            rw[4 * n + 3] = 0;
+            rw[4 * n + 3] = s * c->V + h;
             owner[n++] = ow;
             continue;
         }
@@ -274,7 +277,7 @@ void plan_balanced(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
             rw[4 * n + 0] = sh;
             rw[4 * n + 1] = (int32_t)((p - lo) << 4);
             rw[4 * n + 2] = (int32_t)std::min<long long>((end - lo) << 4, cap);
-            rw[4 * n + 3] = 0;
+            rw[4 * n + 3] = s * c->V + h;
             owner[n++] = w;
             p = end;
         }
@@ -304,11 +307,12 @@ void plan_uniform(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
         if (cap > 0) {
             const long long chunk = (long long)P * ((((long long)cap + S - 1) / S + P - 1) / P);
             for (long long t0 = 0; t0 < cap; t0 += chunk) {
-                pl.rows.insert(pl.rows.end(), {sh, (int32_t)t0, (int32_t)std::min<long long>(t0 + chunk, cap), 0});
+                pl.rows.insert(pl.rows.end(), {sh, (int32_t)t0, (int32_t)std::min<long long>(t0 + chunk, cap),
+                                               s * c->V + sh % H});
                 ++nr;
             }
         } else {
-            pl.rows.insert(pl.rows.end(), {sh, 0, 0, 0});
+            pl.rows.insert(pl.rows.end(), {sh, 0, 0, s * c->V + sh % H});
             nr = 1;
         }
         pl.head_row_start[sh + 1] = pl.head_row_start[sh] + nr;

@@ -34,7 +34,7 @@ struct PartialArgs {
     const int32_t *lengths;     // this layer's lengths: entry (s, h) at s*lstride + h (paged)
     const int32_t *group_of_head;
     const int32_t *slot_of_head;
-    const int32_t *rows;        // [n][4] (sh, t0, t1, 0) (paged)
+    const int32_t *rows;        // [n][4] (sh, t0, t1, s*lstride + h) (paged)
     const int32_t *worker_start;// [W+1] (paged)
     const int32_t *idx;         // [Bmax*Hkv][K] logical positions (indexed top-K)
     int32_t *err;               // latched error word (indexed top-K)

@@ -162,9 +162,10 @@ void partial_attn_kernel(PartialArgs a) {
         } else {
             sh = ld_uniform(a.rows + row * 4 + 0);
             t0 = ld_uniform(a.rows + row * 4 + 1);
+            // the row's fourth word is its head's index into lengths
+            t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + ld_uniform(a.rows + row * 4 + 3)));
         }
         const int s = sh / a.hkv, h = sh - s * a.hkv;
-        if (!TOPK) t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + s * a.lstride + h));
         float *ml = a.ws_ml + (size_t)row * GQA * 2;
         int hr0, nrows;   // the rows of this head
         if (TOPK) {
@@ -537,9 +538,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     for (int row = rb; row < re; ++row) {
         const int sh = ld_uniform(a.rows + row * 4 + 0);
         const int t0 = ld_uniform(a.rows + row * 4 + 1);
-        const int s = sh / a.hkv, h = sh - s * a.hkv;
-        const int t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + s * a.lstride + h));
+        const int t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + ld_uniform(a.rows + row * 4 + 3)));
         if (t0 >= t1) continue;
+        const int s = sh / a.hkv, h = sh - s * a.hkv;
         uint4 qv[NJ];
         const uint4 *qh = reinterpret_cast<const uint4 *>(
             a.q + ((size_t)s * a.hkv * GQA + (size_t)h * GQA + (qn < GQA ? qn : 0)) * D);
