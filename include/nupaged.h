@@ -309,12 +309,14 @@ nup_status attn_decode_topk_paged(nup_ctx *ctx, const void *q, const int32_t *id
  * kv_gather_compact mode 1 or attn_decode_topk_paged.
  *   q          device bf16 [B_max][H_q][D]
  *   idx_out    device int32 [B_max][H_kv][K]; rows of inactive slots untouched
- *   workspace  device, >= nup_select_workspace_bytes() bytes (fp32 scores)
+ *   workspace  device, >= nup_select_workspace_bytes() bytes, 256-byte aligned
+ *              (fp32 scores, then the selection's histograms and counts)
  * Requires a committed descriptor and L >= K for every active head (checked
  * on the host).  Errors: NUP_E_ARG, NUP_E_STATE, NUP_E_HIP. */
 nup_status kv_select_topk(nup_ctx *ctx, const void *q, int32_t K, int32_t window, int32_t *idx_out,
                           void *workspace, size_t ws_bytes, void *stream);
-/* Workspace bytes for kv_select_topk: B_max * H_kv * max_pages * P fp32 scores. */
+/* Workspace bytes for kv_select_topk: B_max * H_kv * max_pages * P fp32
+ * scores, plus per head a 2048-bin histogram, a threshold and per-slice counts. */
 nup_status nup_select_workspace_bytes(const nup_ctx *ctx, size_t *bytes);
 
 /* ---- host-side queries (no device call; for tests and reports) ---------- */

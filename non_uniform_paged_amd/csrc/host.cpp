@@ -1099,9 +1099,23 @@ nup_status attn_decode_topk_paged(nup_ctx *c, const void *q, const int32_t *idx,
                        nullptr, idx, K);
 }
 
+// Selection workspace: scores [heads][max_pages*P] fp32, then the select
+// kernels' histogram [heads][kSelBins], thresholds [heads][2] and per-slice
+// counts [heads][kSelSplit][2].
+struct SelectWs { size_t hist, thr, cnt, total; };
+static SelectWs select_ws(const nup_ctx *c) {
+    const size_t heads = (size_t)c->B * c->H;
+    SelectWs w;
+    w.hist = align_up(heads * (size_t)c->max_pages * nup::kPage * 4);
+    w.thr = w.hist + align_up(heads * nup::kSelBins * 4);
+    w.cnt = w.thr + align_up(heads * 2 * 4);
+    w.total = w.cnt + align_up(heads * nup::kSelSplit * 2 * 4);
+    return w;
+}
+
 nup_status nup_select_workspace_bytes(const nup_ctx *c, size_t *bytes) {
     if (!c || !bytes) return NUP_E_ARG;
-    *bytes = align_up((size_t)c->B * c->H * (size_t)c->max_pages * nup::kPage * 4);
+    *bytes = select_ws(c).total;
     return NUP_OK;
 }
 
@@ -1134,6 +1148,7 @@ nup_status kv_select_topk(nup_ctx *c, const void *q, int32_t K, int32_t window, 
     sa.rows = c->inbox_i32(c->off_rows[c->layer]);
     sa.worker_start = c->inbox_i32(c->off_ws[c->layer]);
     sa.scores = static_cast<float *>(workspace);
+    sa.hist = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + select_ws(c).hist);
     sa.bmax = c->B;
     sa.hkv = c->H;
     sa.gh = c->gh;
@@ -1142,8 +1157,12 @@ nup_status kv_select_topk(nup_ctx *c, const void *q, int32_t K, int32_t window, 
     sa.stride = c->max_pages * nup::kPage;
     hipError_t e = nup::launch_score(sa, c->D, c->gqa, st);
     if (e != hipSuccess) return hip_fail(c, e, "score launch");
+    const SelectWs sw = select_ws(c);
     nup::SelectArgs sl{};
     sl.scores = sa.scores;
+    sl.hist = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + sw.hist);
+    sl.thr = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + sw.thr);
+    sl.cnt = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + sw.cnt);
     sl.active = c->d_active();
     sl.lengths = c->d_len() + c->lbase();
     sl.lstride = c->V;

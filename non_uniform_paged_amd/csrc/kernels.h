@@ -63,13 +63,18 @@ struct MergeArgs {
 // Top-K selection.  score_kernel walks the committed plan like the paged
 // attention and writes, for every retained position of every active head,
 // the largest q.k over the head's query rows into scores[sh * stride + t].
-// select_kernel (one workgroup per head) keeps the `window` most recent
-// positions and the K - window highest-scoring older ones (ties to the lower
-// position) and writes them in ascending order.
+// The select kernels keep the `window` most recent positions and the
+// K - window highest-scoring older ones (ties to the lower position) and
+// write them in ascending order.
+constexpr int kSelBins = 2048;      // histogram of the top 11 key bits
+constexpr int kSelSplit = 16;       // slices (workgroups) per head in the parallel select kernels
+constexpr int kSelCap = 8192;       // threshold-bin entries the select keeps in LDS
+
 struct ScoreArgs {
     const uint16_t *q, *kbase;
     const int32_t *page_table, *lengths, *group_of_head, *slot_of_head, *rows, *worker_start;
     float *scores;
+    uint32_t *hist;             // [heads][kSelBins]: cleared by each head's first row (or NULL)
     int32_t bmax, hkv, gh, max_pages, n_workers, stride, lstride;
 };
 
@@ -77,6 +82,9 @@ struct SelectArgs {
     const float *scores;
     const int32_t *active, *lengths;
     int32_t *idx_out;              // [Bmax*Hkv][K]
+    uint32_t *hist;                // [heads][kSelBins], zeroed by the launcher
+    int32_t *thr;                  // [heads][2]: threshold key, ties taken
+    int32_t *cnt;                  // [heads][kSelSplit][2]: per slice, above and equal
     int32_t hkv, stride, k, window, lstride;
 };
 

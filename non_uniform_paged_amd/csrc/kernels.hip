@@ -514,7 +514,6 @@ __device__ __forceinline__ float dpp_f(float x) {
 }
 
 constexpr int kScoreDepth = 4;
-constexpr int kScoreSplit = 1;   // waves per plan worker in the scoring kernel
 
 template <int D, int GQA>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
@@ -527,9 +526,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     __shared__ uint4 k_lds[kWavesPerBlock][kPage][LPR + 1];
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // kScoreSplit waves share each plan worker, taking its pages in turn
-    const int wave = blockIdx.x * kWavesPerBlock + wid;
-    const int w = wave / kScoreSplit, part = wave % kScoreSplit;
+    const int w = blockIdx.x * kWavesPerBlock + wid;
     if (w >= a.n_workers) return;
     uint4 (*kt)[LPR + 1] = k_lds[wid];
     const int qn = lane & 15, qg = lane >> 4;
@@ -539,6 +536,11 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         const int sh = ld_uniform(a.rows + row * 4 + 0);
         const int t0 = ld_uniform(a.rows + row * 4 + 1);
         const int t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + ld_uniform(a.rows + row * 4 + 3)));
+        if (t0 == 0 && a.hist) {
+            // the head's first row clears its histogram for the select kernels
+            uint4 *hz = reinterpret_cast<uint4 *>(a.hist + (size_t)sh * kSelBins);
+            for (int i = lane; i < kSelBins / 4; i += 64) hz[i] = make_uint4(0, 0, 0, 0);
+        }
         if (t0 >= t1) continue;
         const int s = sh / a.hkv, h = sh - s * a.hkv;
         uint4 qv[NJ];
@@ -550,9 +552,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
             a.page_table + ((size_t)ld_uniform(a.group_of_head + h) * a.bmax + s) * (size_t)a.max_pages;
         const size_t slot_off = (size_t)ld_uniform(a.slot_of_head + h) * kPage * D;
         float *out = a.scores + (size_t)sh * a.stride;
-        const int pa = t0 / kPage, p1 = (t1 - 1) / kPage;
-        const int p0 = pa + part;
-        if (p0 > p1) continue;
+        const int p0 = t0 / kPage, p1 = (t1 - 1) / kPage;
         // row-major, fully coalesced: an instruction reads RPI whole rows
         auto load = [&](int pi, uint4 (&k)[TPL]) {
             const uint4 *kp = reinterpret_cast<const uint4 *>(
@@ -583,6 +583,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
                 x = fmaxf(x, dpp_f<kRowRor1>(x));
                 m[i] = x;
             }
+            // 16 bytes of scores per lane of the first row; the 31 MB these
+            // writes add to a 2 GB read stream cost the kernel about a sixth
+            // of its time, however they are batched
             const int tb = pi * kPage + 4 * qg;
             if (qn == 0) {
                 if (tb + 3 < t1) {
@@ -596,17 +599,16 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         };
         // only K is read: a ring of kScoreDepth pages keeps as many bytes in
         // flight as the attention kernel's K+V double buffer
-        constexpr int S = kScoreSplit;
         uint4 kb[kScoreDepth][TPL];
 #pragma unroll
         for (int j = 0; j + 1 < kScoreDepth; ++j)
-            if (p0 + j * S <= p1) load(p0 + j * S, kb[j]);
-        for (int pb = p0; pb <= p1; pb += kScoreDepth * S) {
+            if (p0 + j <= p1) load(p0 + j, kb[j]);
+        for (int pb = p0; pb <= p1; pb += kScoreDepth) {
 #pragma unroll
             for (int j = 0; j < kScoreDepth; ++j) {
-                const int p = pb + j * S;
+                const int p = pb + j;
                 if (p <= p1) {
-                    const int pf = p + (kScoreDepth - 1) * S;
+                    const int pf = p + kScoreDepth - 1;
                     if (pf <= p1) load(pf, kb[(j + kScoreDepth - 1) % kScoreDepth]);
                     score(p, kb[j]);
                 }
@@ -616,13 +618,26 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-K selection, step 2: one 1024-thread workgroup per head.  A four-pass
-// radix select (8 bits per pass, LDS histogram) finds the (K-window)-th
-// largest score key among the older positions; a scan in position order
-// then writes the positions above it and the lowest-positioned ties.
+// Top-K selection, step 2: find each head's (K-window)-th largest score key
+// among its older positions, then write the chosen positions in order.
+//   sel_hist_kernel:   kSelSplit workgroups per head histogram the top 11
+//                      key bits of their slice into a global histogram;
+//   sel_thresh_kernel: one workgroup per head finds the bin holding the
+//                      threshold, gathers that bin's entries into LDS and
+//                      finishes the radix select there (passes over the
+//                      scores instead when the bin does not fit), then
+//                      counts per slice the entries above the threshold and
+//                      equal to it;
+//   sel_write_kernel:  kSelSplit workgroups per head write their slice's
+//                      chosen positions in order, offset by the counts of
+//                      the slices before them.
+// Slices are whole multiples of 4096 positions, so a 1024-thread pass of
+// float4 loads stays inside one slice per step.
 // ---------------------------------------------------------------------------
-constexpr int kSelectThreads = 1024;
-constexpr int kSelectItems = 8;   // consecutive positions per thread in the compaction
+constexpr int kSelShift = 32 - 11;   // first digit: the top 11 key bits
+constexpr int kSelThreads = 1024;     // sel_thresh_kernel
+constexpr int kSelItems = 8;          // consecutive positions per thread in sel_write_kernel
+constexpr int kSelUnroll = 4;         // float4 loads in flight per thread
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -630,8 +645,62 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan of v over the workgroup (in thread order); *total gets the sum.
+// The head's candidate count n (older positions), entries to pick k, and
+// slice length cs; false for an inactive slot.
+__device__ __forceinline__ bool sel_head(const SelectArgs &a, int sh, int &n, int &k, int &cs) {
+    const int s = sh / a.hkv;
+    if (!a.active[s]) return false;
+    const int L = a.lengths[s * a.lstride + (sh - s * a.hkv)];
+    n = L - a.window;
+    k = a.k - a.window;
+    cs = ((n + kSelSplit - 1) / kSelSplit + 4095) & ~4095;
+    return true;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+// LDS bins are padded by one word per 32 so that the digit search, where
+// lane l reads bins l*PER .. l*PER+PER-1, hits distinct banks.
+__device__ __forceinline__ int padb(int i) { return i + (i >> 5); }
+
+// Wave 0: find the bin (of NB, searched from the top) in which the running
+// count reaches `remaining`; writes (bin, remaining within it) to pick.
+template <int NB>
+__device__ __forceinline__ void find_digit(const uint32_t *bins, int remaining, uint32_t *pick) {
+    constexpr int PER = NB / 64;
+    const int lane = threadIdx.x & 63;
+    int local = 0;
+#pragma unroll 8
+    for (int j = 0; j < PER; ++j) local += (int)bins[padb(NB - 1 - (PER * lane + j))];
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    const int excl = incl - local;
+    if (excl < remaining && remaining <= incl) {
+        int cum = excl;
+        for (int j = 0; j < PER; ++j) {
+            const int c = (int)bins[padb(NB - 1 - (PER * lane + j))];
+            if (cum + c >= remaining) {
+                pick[0] = (uint32_t)(NB - 1 - (PER * lane + j));
+                pick[1] = (uint32_t)(remaining - cum);
+                break;
+            }
+            cum += c;
+        }
+    }
+}
+
+// Exclusive scan of v over an NT-thread workgroup (in thread order); *total gets the sum.
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int *lds, int *total) {
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     int x = v;
 #pragma unroll
@@ -642,15 +711,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *lds, int *total)
     if (lane == 63) lds[wid] = x;
     __syncthreads();
     if (wid == 0) {
-        int t = lane < kSelectThreads / 64 ? lds[lane] : 0;
+        int t = lane < NW ? lds[lane] : 0;
         int incl = t;
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
+        for (int off = 1; off < NW; off <<= 1) {
             const int y = __shfl_up(incl, off);
             if (lane >= off) incl += y;
         }
-        if (lane < kSelectThreads / 64) lds[16 + lane] = incl - t;
-        if (lane == kSelectThreads / 64 - 1) lds[32] = incl;
+        if (lane < NW) lds[16 + lane] = incl - t;
+        if (lane == NW - 1) lds[32] = incl;
     }
     __syncthreads();
     const int r = x - v + lds[16 + wid];
@@ -659,130 +728,255 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *lds, int *total)
     return r;
 }
 
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
-    constexpr int kWaves = kSelectThreads / 64;
-    // one histogram per wave (the top bytes of the scores fall into a few
-    // bins; private copies keep the LDS atomics from serialising on them)
-    __shared__ uint32_t hist[kWaves][256];
-    __shared__ int scan_lds[40];
-    __shared__ uint32_t pick[2];
-    const int sh = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
-    const int s = sh / a.hkv;
-    if (!a.active[s]) return;
-    const int L = a.lengths[s * a.lstride + (sh - s * a.hkv)];
-    const int n = L - a.window, k = a.k - a.window;
-    int32_t *out = a.idx_out + (size_t)sh * a.k;
-    for (int j = tid; j < a.window; j += kSelectThreads) out[k + j] = n + j;
-    if (k <= 0) return;
+__global__ __launch_bounds__(256) void sel_hist_kernel(SelectArgs a) {
+    __shared__ uint32_t hist[4][kSelBins];   // one copy per wave
+    const int sh = blockIdx.y, j = blockIdx.x, tid = threadIdx.x, wid = tid >> 6;
+    int n, k, cs;
+    if (!sel_head(a, sh, n, k, cs) || k <= 0) return;
+    const int b = j * cs, e = min(n, b + cs);
+    if (b >= e) return;
+    for (int i = tid; i < 4 * kSelBins; i += 256) (&hist[0][0])[i] = 0;
+    __syncthreads();
     const float *sc = a.scores + (size_t)sh * a.stride;
-    uint32_t prefix = 0, mask = 0;
-    int remaining = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < kWaves * 256; i += kSelectThreads) (&hist[0][0])[i] = 0;
-        __syncthreads();
-        // 16 scores per thread per iteration (four 16-byte loads in flight);
-        // the score rows start 16-byte aligned
-        const float4 *sc4 = reinterpret_cast<const float4 *>(sc);
-        const int n4 = n / 4;
-        for (int b = tid; b < n4; b += 4 * kSelectThreads) {
-            float4 v[4];
+    const int e4 = b + ((e - b) & ~3);
+    for (int t0 = b + 4 * tid; t0 < e4; t0 += 4 * 256 * kSelUnroll) {
+        float4 v[kSelUnroll];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                v[u] = b + u * kSelectThreads < n4 ? sc4[b + u * kSelectThreads]
-                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int u = 0; u < kSelUnroll; ++u) {
+            const int t = t0 + u * 4 * 256;
+            v[u] = t < e4 ? *reinterpret_cast<const float4 *>(sc + t) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (b + u * kSelectThreads >= n4) continue;
-                const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        for (int u = 0; u < kSelUnroll; ++u) {
+            if (t0 + u * 4 * 256 >= e4) break;
+            atomicAdd(&hist[wid][order_key(v[u].x) >> kSelShift], 1u);
+            atomicAdd(&hist[wid][order_key(v[u].y) >> kSelShift], 1u);
+            atomicAdd(&hist[wid][order_key(v[u].z) >> kSelShift], 1u);
+            atomicAdd(&hist[wid][order_key(v[u].w) >> kSelShift], 1u);
+        }
+    }
+    for (int t = e4 + tid; t < e; t += 256) atomicAdd(&hist[wid][order_key(sc[t]) >> kSelShift], 1u);
+    __syncthreads();
+    uint32_t *g = a.hist + (size_t)sh * kSelBins;
+    for (int i = tid; i < kSelBins; i += 256) {
+        const uint32_t v = hist[0][i] + hist[1][i] + hist[2][i] + hist[3][i];
+        if (v) atomicAdd(g + i, v);
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void sel_thresh_kernel(SelectArgs a) {
+    __shared__ uint32_t bins[kSelBins + kSelBins / 32];
+    __shared__ uint32_t cand_key[kSelCap];
+    __shared__ int32_t cand_pos[kSelCap];
+    __shared__ int slice_gt[kSelSplit], slice_eq[kSelSplit];
+    __shared__ int ncand;
+    __shared__ uint32_t pick[2];
+    const int sh = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    int n, k, cs;
+    if (!sel_head(a, sh, n, k, cs) || k <= 0) return;
+    const float *sc = a.scores + (size_t)sh * a.stride;
+    const int n4 = n & ~3;
+
+    // 1. the first digit, from the global histogram
+    for (int i = tid; i < kSelBins; i += kSelThreads) bins[padb(i)] = a.hist[(size_t)sh * kSelBins + i];
+    if (tid < kSelSplit) {
+        slice_gt[tid] = 0;
+        slice_eq[tid] = 0;
+    }
+    if (tid == 0) ncand = 0;
+    __syncthreads();
+    if (tid < 64) find_digit<kSelBins>(bins, k, pick);
+    __syncthreads();
+    const uint32_t d1 = pick[0];
+    int remaining = (int)pick[1];
+    __syncthreads();
+
+    // 2. one pass over the scores: per slice, the entries above bin d1; the
+    //    entries in bin d1 go to LDS (while they fit)
+    for (int t0 = 4 * tid; t0 - 4 * tid < n4; t0 += 4 * kSelThreads * kSelUnroll) {
+        float4 v[kSelUnroll];
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+            const int t = t0 + u * 4 * kSelThreads;
+            v[u] = t < n4 ? *reinterpret_cast<const float4 *>(sc + t) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+            const int step = t0 - 4 * tid + u * 4 * kSelThreads;   // uniform: inside one slice
+            if (step >= n4) break;
+            const int t = t0 + u * 4 * kSelThreads;
+            int gt = 0;
+            uint32_t key[4];
+            bool in_bin[4];
+            const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                key[e] = order_key(f[e]);
+                const uint32_t top = key[e] >> kSelShift;
+                gt += t < n4 && top > d1;
+                in_bin[e] = t < n4 && top == d1;
+            }
+            // the wave appends its bin entries with one LDS atomic
+            uint64_t m[4];
+            int before[4], tot = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                m[e] = __builtin_amdgcn_ballot_w64(in_bin[e]);
+                before[e] = tot;
+                tot += __popcll(m[e]);
+            }
+            if (tot) {
+                int base = 0;
+                if (lane == 0) base = atomicAdd(&ncand, tot);
+                base = __shfl(base, 0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t key = order_key(f[e]);
-                    if ((key & mask) == prefix) atomicAdd(&hist[wid][(key >> shift) & 255u], 1u);
-                }
-            }
-        }
-        for (int t = 4 * n4 + tid; t < n; t += kSelectThreads) {
-            const uint32_t key = order_key(sc[t]);
-            if ((key & mask) == prefix) atomicAdd(&hist[wid][(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (tid < 256) {
-            uint32_t total = 0;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) total += hist[w][tid];
-            hist[0][tid] = total;
-        }
-        __syncthreads();
-        if (wid == 0) {
-            // lane l holds bins 255-4l .. 252-4l (descending); find the bin in
-            // which the running count from the top reaches `remaining`
-            int c[4], local = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                c[j] = (int)hist[0][255 - (4 * lane + j)];
-                local += c[j];
-            }
-            int incl = local;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(incl, off);
-                if (lane >= off) incl += y;
-            }
-            const int excl = incl - local;
-            if (excl < remaining && remaining <= incl) {
-                int cum = excl;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (cum + c[j] >= remaining) {
-                        pick[0] = (uint32_t)(255 - (4 * lane + j));
-                        pick[1] = (uint32_t)(remaining - cum);
-                        break;
+                    if (!in_bin[e]) continue;
+                    const int p = base + before[e] +
+                                  (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], 0u));
+                    if (p < kSelCap) {
+                        cand_key[p] = key[e];
+                        cand_pos[p] = t + e;
                     }
-                    cum += c[j];
                 }
             }
+            gt = wave_sum(gt);
+            if (lane == 0 && gt) atomicAdd(&slice_gt[step / cs], gt);
+        }
+    }
+    for (int t = n4 + tid; t < n; t += kSelThreads) {
+        const uint32_t key = order_key(sc[t]);
+        const uint32_t top = key >> kSelShift;
+        if (top > d1) atomicAdd(&slice_gt[t / cs], 1);
+        if (top == d1) {
+            const int p = atomicAdd(&ncand, 1);
+            if (p < kSelCap) {
+                cand_key[p] = key;
+                cand_pos[p] = t;
+            }
+        }
+    }
+    __syncthreads();
+    const int nc = ncand;
+    const bool in_lds = nc <= kSelCap;
+
+    // 3. the remaining 21 bits: an 11-bit digit, then a 10-bit one, over the
+    //    bin's entries (in LDS, or re-read from the scores)
+    uint32_t prefix = d1 << kSelShift, mask = 0xFFFFFFFFu << kSelShift;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = pass == 0 ? 10 : 0;
+        const uint32_t nb_mask = pass == 0 ? 2047u : 1023u;
+        for (int i = tid; i < kSelBins; i += kSelThreads) bins[padb(i)] = 0;
+        __syncthreads();
+        if (in_lds) {
+            for (int i = tid; i < nc; i += kSelThreads) {
+                const uint32_t key = cand_key[i];
+                if ((key & mask) == prefix) atomicAdd(&bins[padb((key >> shift) & nb_mask)], 1u);
+            }
+        } else {
+            for (int t = tid; t < n; t += kSelThreads) {
+                const uint32_t key = order_key(sc[t]);
+                if ((key & mask) == prefix) atomicAdd(&bins[padb((key >> shift) & nb_mask)], 1u);
+            }
+        }
+        __syncthreads();
+        if (tid < 64) {
+            if (pass == 0) find_digit<2048>(bins, remaining, pick);
+            else find_digit<1024>(bins, remaining, pick);
         }
         __syncthreads();
         prefix |= pick[0] << shift;
-        mask |= 255u << shift;
+        mask |= nb_mask << shift;
         remaining = (int)pick[1];
         __syncthreads();
     }
-    const uint32_t T = prefix;        // the k-th largest key
-    const int take_eq = remaining;    // keys equal to T that are taken (lowest positions)
+    const uint32_t T = prefix;   // the k-th largest key; `remaining` of its ties are taken
+
+    // 4. per slice, the bin's entries above T and equal to T
+    if (in_lds) {
+        for (int i = tid; i < nc; i += kSelThreads) {
+            const uint32_t key = cand_key[i];
+            if (key > T) atomicAdd(&slice_gt[cand_pos[i] / cs], 1);
+            else if (key == T) atomicAdd(&slice_eq[cand_pos[i] / cs], 1);
+        }
+    } else {
+        for (int t = tid; t < n; t += kSelThreads) {
+            const uint32_t key = order_key(sc[t]);
+            if ((key >> kSelShift) != d1) continue;
+            if (key > T) atomicAdd(&slice_gt[t / cs], 1);
+            else if (key == T) atomicAdd(&slice_eq[t / cs], 1);
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        a.thr[2 * sh + 0] = (int32_t)T;
+        a.thr[2 * sh + 1] = remaining;
+    }
+    if (tid < kSelSplit) {
+        a.cnt[((size_t)sh * kSelSplit + tid) * 2 + 0] = slice_gt[tid];
+        a.cnt[((size_t)sh * kSelSplit + tid) * 2 + 1] = slice_eq[tid];
+    }
+}
+
+__global__ __launch_bounds__(256) void sel_write_kernel(SelectArgs a) {
+    __shared__ int scan_lds[40];
+    const int sh = blockIdx.y, j = blockIdx.x, tid = threadIdx.x;
+    int n, k, cs;
+    if (!sel_head(a, sh, n, k, cs)) return;
+    int32_t *out = a.idx_out + (size_t)sh * a.k;
+    if (j == 0)
+        for (int i = tid; i < a.window; i += 256) out[k + i] = n + i;
+    if (k <= 0) return;
+    const int b = j * cs, e = min(n, b + cs);
+    if (b >= e) return;
+    const uint32_t T = (uint32_t)a.thr[2 * sh + 0];
+    const int take_eq = a.thr[2 * sh + 1];
     int out_base = 0, eq_base = 0;
-    for (int c0 = 0; c0 < n; c0 += kSelectThreads * kSelectItems) {
-        const int tb = c0 + tid * kSelectItems;
-        uint32_t keys[kSelectItems];
-        if (tb + kSelectItems <= n) {
+    for (int i = 0; i < j; ++i) {
+        const int gt_i = a.cnt[((size_t)sh * kSelSplit + i) * 2 + 0];
+        const int eq_i = a.cnt[((size_t)sh * kSelSplit + i) * 2 + 1];
+        out_base += gt_i + max(0, min(eq_i, take_eq - eq_base));
+        eq_base += eq_i;
+    }
+    const float *sc = a.scores + (size_t)sh * a.stride;
+    for (int c0 = b; c0 < e; c0 += 256 * kSelItems) {
+        const int tb = c0 + tid * kSelItems;
+        uint32_t keys[kSelItems];
+        if (tb + kSelItems <= e) {
             const float4 x0 = reinterpret_cast<const float4 *>(sc + tb)[0];
             const float4 x1 = reinterpret_cast<const float4 *>(sc + tb)[1];
             const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-            for (int u = 0; u < kSelectItems; ++u) keys[u] = order_key(f[u]);
+            for (int u = 0; u < kSelItems; ++u) keys[u] = order_key(f[u]);
         } else {
 #pragma unroll
-            for (int u = 0; u < kSelectItems; ++u) keys[u] = tb + u < n ? order_key(sc[tb + u]) : 0u;
+            for (int u = 0; u < kSelItems; ++u) keys[u] = tb + u < e ? order_key(sc[tb + u]) : 0u;
         }
         int gt = 0, eq = 0;
 #pragma unroll
-        for (int u = 0; u < kSelectItems; ++u) {
-            gt += (tb + u < n) && keys[u] > T;
-            eq += (tb + u < n) && keys[u] == T;
+        for (int u = 0; u < kSelItems; ++u) {
+            gt += (tb + u < e) && keys[u] > T;
+            eq += (tb + u < e) && keys[u] == T;
         }
         int eq_tot = 0, sel_tot = 0;
-        const int eq_pre = block_exclusive_scan(eq, scan_lds, &eq_tot) + eq_base;
+        const int eq_pre = block_exclusive_scan<256>(eq, scan_lds, &eq_tot) + eq_base;
         const int my_eq = max(0, min(eq, take_eq - eq_pre));
-        const int sel_pre = block_exclusive_scan(gt + my_eq, scan_lds, &sel_tot) + out_base;
+        const int sel_pre = block_exclusive_scan<256>(gt + my_eq, scan_lds, &sel_tot) + out_base;
         int pos = sel_pre, r = eq_pre;
+        // the counts are exact, so pos stays below k; the bound only keeps a
+        // row from spilling into the next head's if they ever were not
 #pragma unroll
-        for (int u = 0; u < kSelectItems; ++u) {
-            if (tb + u >= n) break;
+        for (int u = 0; u < kSelItems; ++u) {
+            if (tb + u >= e) break;
             if (keys[u] > T) {
-                out[pos++] = tb + u;
+                if (pos < k) out[pos] = tb + u;
+                ++pos;
             } else if (keys[u] == T) {
-                if (r < take_eq) out[pos++] = tb + u;
+                if (r < take_eq) {
+                    if (pos < k) out[pos] = tb + u;
+                    ++pos;
+                }
                 ++r;
             }
         }
@@ -1073,13 +1267,20 @@ hipError_t launch_score(const ScoreArgs &a, int head_dim, int gqa, hipStream_t s
     if (!fn) return hipErrorInvalidValue;
     if (a.n_workers <= 0) return hipSuccess;
     ScoreArgs copy = a;
-    const unsigned blocks = (unsigned)(((long long)a.n_workers * kScoreSplit + kWavesPerBlock - 1) / kWavesPerBlock);
+    const unsigned blocks = (unsigned)(((long long)a.n_workers + kWavesPerBlock - 1) / kWavesPerBlock);
     return launch_raw(fn, dim3(blocks), dim3(256), &copy, sizeof(copy), st);
 }
 
 hipError_t launch_select(const SelectArgs &a, int n_heads, hipStream_t st) {
     if (n_heads <= 0) return hipSuccess;
-    hipLaunchKernelGGL(select_kernel, dim3(n_heads), dim3(kSelectThreads), 0, st, a);
+    if ((long long)n_heads * kSelBins > 0x7fffffffLL || n_heads > 65535) return hipErrorInvalidValue;
+    // the histogram was cleared by the score kernel (first row of each head)
+    hipLaunchKernelGGL(sel_hist_kernel, dim3(kSelSplit, n_heads), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sel_thresh_kernel, dim3(n_heads), dim3(kSelThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(sel_write_kernel, dim3(kSelSplit, n_heads), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -617,6 +617,38 @@ def test_select_topk_random_and_refused_cases():
     assert nup.kv_select_topk(c.ctx, c.q, 8, 9, out, ws, raise_on_error=False) == nup.NUP_E_ARG
 
 
+def test_select_topk_threshold_bin_beyond_lds():
+    """More than 8192 older entries share the threshold's top key bits (all
+    scores tie at 0 except a few): the select finishes with passes over the
+    scores instead of in LDS, and still takes the lowest tied positions."""
+    B, H, D = 1, 2, 64
+    L = np.array([[12000, 20000]], np.int32)
+    max_pages = 1250
+    c = Case(H=H, Hq=H, D=D, ng=1, B=B, num_pages=2 * max_pages, max_pages=max_pages,
+             num_workers=17, salt=42)
+    c.alloc([0], L, L)
+    c.commit()
+    kp = torch.zeros_like(c.kpool, dtype=torch.float32)
+    # a few keys with a positive score, scattered; everything else scores 0
+    rs = np.random.default_rng(42)
+    pt = c.spec.page_table
+    for h in range(H):
+        for t in rs.choice(int(L[0, h]) - 100, 40, replace=False):
+            page = pt[c.spec.group_of_head[h], 0, t // 16]
+            kp[page, c.spec.slot_of_head[h], t % 16, 0] = float(1 + t % 7)
+    c.kpool.copy_(kp.to(torch.bfloat16))
+    qf = torch.zeros((B, H, D), dtype=torch.float32)
+    qf[:, :, 0] = 1.0
+    c.q.copy_(qf.to(torch.bfloat16).to(DEV))
+    for K, window in ((300, 50), (9000, 100)):
+        out = torch.full((B, H, K), -5, dtype=torch.int32, device=DEV)
+        ws = torch.empty(nup.select_workspace_bytes(c.ctx), dtype=torch.uint8, device=DEV)
+        nup.kv_select_topk(c.ctx, c.q, K, window, out, ws)
+        torch.cuda.synchronize()
+        want, _ = osel.select_all(u16(c.q), u16(c.kpool), c.spec, K, window)
+        assert np.array_equal(out.cpu().numpy(), want), (K, window)
+
+
 def test_full_size_llama_select_then_attend():
     """Llama-3-8B shape: select 2048 entries (1024 recent) per KV head from
     122880, then attend in place.  Checked on sampled heads against the
