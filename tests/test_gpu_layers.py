@@ -124,3 +124,33 @@ def test_layers_decode_append_gather(NL, H, gqa, ng):
         assert_attention_close(c.out.cpu().numpy().astype(np.float64)[[0, 2]],
                                c.lse.cpu().numpy().astype(np.float64)[[0, 2]], ref[[0, 2]], ref_lse[[0, 2]],
                                f"top-K in place, layer {l}")
+
+    # selection on that layer: structure and membership against the oracle's
+    # scores of the layer's heads
+    from oracle import select as osel
+    window = 4
+    sel = torch.full((B, H, K), -5, dtype=torch.int32, device=DEV)
+    ws_sel = torch.empty(nup.select_workspace_bytes(c.ctx), dtype=torch.uint8, device=DEV)
+    nup.kv_select_topk(c.ctx, qs[l], K, window, sel, ws_sel)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    assert (got[1] == -5).all()
+    view = pg.PagerSpec(H, ng, B, num_pages, max_pages, 16)   # the layer's heads over the same pages
+    view.page_table, view.n_pages, view.active = c.spec.page_table, c.spec.n_pages, c.spec.active
+    view.lengths = c.spec.lengths[:, sl].copy()
+    view.group_of_head, view.slot_of_head = c.spec.group_of_head[sl], c.spec.slot_of_head[sl]
+    view.g_h = c.gh
+    for s in (0, 2):
+        for h in range(H):
+            Lh = int(view.lengths[s, h])
+            g = got[s, h]
+            assert (np.diff(g) > 0).all() and g[-window:].tolist() == list(range(Lh - window, Lh))
+            sc = osel.scores(u16(qs[l]), kp, view, s, h)
+            want = osel.select(sc, K, window)
+            cand = sc[: Lh - window]
+            thr = np.sort(cand)[::-1][K - window - 1]
+            sure = np.abs(cand - thr) > 1e-3 * max(1.0, abs(thr))
+            a_, b_ = np.zeros(Lh - window, bool), np.zeros(Lh - window, bool)
+            a_[g[: K - window]] = True
+            b_[want[: K - window]] = True
+            assert np.array_equal(a_[sure], b_[sure]), (s, h)

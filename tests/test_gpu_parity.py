@@ -211,6 +211,42 @@ def test_append_errors():
     assert_attention_close(out, lse, ref, ref_lse, "after refused append")
 
 
+def test_all_slots_inactive():
+    """Every slot ended (Reserve then Trim of all): attention writes zeros and
+    -inf for every head, the gathers and the selection write nothing, an
+    append is a no-op, and the next Reserve works on the returned pages."""
+    H, gqa, D, B = 4, 2, 64, 3
+    c = Case(H=H, Hq=H * gqa, D=D, ng=2, B=B, num_pages=40, max_pages=8, salt=19)
+    caps = np.full((B, H), 100, np.int32)
+    c.alloc([0, 1, 2], caps, caps - 3)
+    c.commit()
+    c.free([0, 1, 2])
+    c.commit()
+    out, lse = c.attend()
+    assert (out == 0).all() and np.isneginf(lse).all()
+    kn = torch.zeros((B, H, D), dtype=torch.bfloat16, device=DEV)
+    before = u16(c.kpool).copy()
+    nup.kv_append(c.ctx, kn, kn)
+    assert np.array_equal(u16(c.kpool), before)
+    ks = torch.full((64, D), -3, dtype=torch.int16, device=DEV)
+    nup.kv_gather_compact(c.ctx, 0, ks, ks, row_off=torch.zeros(B * H, dtype=torch.int64, device=DEV))
+    assert nup.kv_gather_trains_dma(c.ctx, ks, ks, np.zeros(B * H, np.int64)) == 0
+    idx = torch.zeros((B, H, 8), dtype=torch.int32, device=DEV)
+    nup.kv_gather_compact(c.ctx, 1, ks, ks, idx=idx, K=8)
+    sel = torch.full((B, H, 8), -5, dtype=torch.int32, device=DEV)
+    ws = torch.empty(nup.select_workspace_bytes(c.ctx), dtype=torch.uint8, device=DEV)
+    nup.kv_select_topk(c.ctx, c.q, 8, 2, sel, ws)
+    torch.cuda.synchronize()
+    assert (ks.cpu().numpy() == -3).all() and (sel.cpu().numpy() == -5).all()
+    assert nup.device_errors(c.ctx) == nup.NUP_OK
+    assert len(nup.get_free_list(c.ctx)) == 40
+    c.alloc([1], caps[:1], caps[:1] - 50)
+    c.commit()
+    out, lse = c.attend()
+    ref, ref_lse = c.oracle()
+    assert_attention_close(out, lse, ref, ref_lse, "after the pool emptied and refilled")
+
+
 def test_shadow_edits_invisible_until_commit():
     H, gqa, D, B = 8, 4, 128, 4
     L, caps = _ragged(16, B, H, 200, p_zero=0)
