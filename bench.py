@@ -318,10 +318,17 @@ def _layer_group_sweep(flush):
     return out
 
 
-def measure_extras(args):
-    """The other configurations: attention on the Qwen3-4B shape, gather and
-    top-K attention on the Llama-3-8B shape, and the mixed-length churn step
-    (Trim / Reserve / commit on the host, trains, append, attention)."""
+EXTRA_SECTIONS = ("qwen3_4b", "llama3_8b_topk", "mixed_churn", "qwen25_32b_trains", "qwen25_32b_prefix",
+                  "qwen3_4b_36_layers", "qwen25_32b_heads_per_group")
+
+
+def measure_extras(args, only=None):
+    """The other configurations: attention on the Qwen3-4B shape, gather,
+    selection and top-K attention on the Llama-3-8B shape, the mixed-length
+    churn step (Trim / Reserve / commit on the host, trains, append,
+    attention), trains by copy engines, forked sessions (Alias), head groups
+    across 36 layers, and heads per group.  only: one name of
+    EXTRA_SECTIONS, or None for all."""
     import torch
     import non_uniform_paged_amd as nup
     import workloads as W
@@ -333,248 +340,258 @@ def measure_extras(args):
     def flush():
         nup.probe_read(flush_buf, flush_buf.numel(), sink)
 
+    def want(name):
+        return only is None or only == name
+
     # -- Qwen3-4B-shaped layer: attention only, caches flushed between launches
-    w = W.qwen3_4b()
-    st = Setup(w, 8)
-    for _ in range(3):
-        st.step(append=False)
-    torch.cuda.synchronize()
-    nup.kernel_time(st.ctx, reset=True)
-    nup.set_timing(st.ctx, True)
-    ms = _timed(lambda: st.step(append=False), 20, flush)
-    nup.set_timing(st.ctx, False)
-    kms, n = nup.kernel_time(st.ctx, reset=True)
-    kms /= max(n, 1)
-    kb = algorithmic_bytes(st.lengths0, st.caps, w.batch, w.num_q_heads, w.num_kv_heads,
-                           w.num_groups) - w.batch * w.num_q_heads * w.head_dim * 4
-    res["qwen3_4b"] = {"kv_bytes": kv_bytes(st.lengths0), "attn_call_ms": round(ms, 4),
-                       "partial_kernel_ms": round(kms, 4),
-                       "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
-                       "note": "cold: 1 GiB read between launches"}
-    st.free()
-    del st
+    if want("qwen3_4b"):
+        w = W.qwen3_4b()
+        st = Setup(w, 8)
+        for _ in range(3):
+            st.step(append=False)
+        torch.cuda.synchronize()
+        nup.kernel_time(st.ctx, reset=True)
+        nup.set_timing(st.ctx, True)
+        ms = _timed(lambda: st.step(append=False), 20, flush)
+        nup.set_timing(st.ctx, False)
+        kms, n = nup.kernel_time(st.ctx, reset=True)
+        kms /= max(n, 1)
+        kb = algorithmic_bytes(st.lengths0, st.caps, w.batch, w.num_q_heads, w.num_kv_heads,
+                               w.num_groups) - w.batch * w.num_q_heads * w.head_dim * 4
+        res["qwen3_4b"] = {"kv_bytes": kv_bytes(st.lengths0), "attn_call_ms": round(ms, 4),
+                           "partial_kernel_ms": round(kms, 4),
+                           "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
+                           "note": "cold: 1 GiB read between launches"}
+        st.free()
+        del st
 
     # -- Llama-3-8B top-K: index gather into staging, then attention over it
-    w = W.llama3_8b_topk()
-    st = Setup(w, 0)
-    K = w.topk
-    idx = torch.from_numpy(W.topk_indices(w.lengths, K)).cuda()
-    ks = torch.empty((w.batch, 8, K, 128), dtype=torch.bfloat16, device="cuda")
-    vs = torch.empty_like(ks)
-    ws = torch.empty(nup.workspace_bytes(st.ctx, K), dtype=torch.uint8, device="cuda")
-    gather = lambda: nup.kv_gather_compact(st.ctx, 1, ks, vs, idx=idx, K=K)
-    topk = lambda: nup.attn_decode_topk(st.ctx, st.q, ks, vs, K, st.out, st.lse, st.scale, ws)
-    fused = lambda: nup.attn_decode_topk_paged(st.ctx, st.q, idx, K, st.out, st.lse, st.scale, ws)
-    for _ in range(3):
-        gather()
-        topk()
-        fused()
-    rows = w.batch * 8 * K
-    g_ms = _timed(gather, 20, flush)
-    t_ms = _timed(topk, 20, flush)
-    f_ms = _timed(fused, 20, flush)
-    both32 = _timed(lambda: [f() for _ in range(32) for f in (gather, topk)], 3) / 32
-    fused32 = _timed(lambda: [fused() for _ in range(32)], 3) / 32
-    # the same 32-layer stack captured in one HIP graph (launch cost amortised)
-    gstream = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(gstream):
-        fused()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph, stream=gstream):
-        for _ in range(32):
-            nup.attn_decode_topk_paged(st.ctx, st.q, idx, K, st.out, st.lse, st.scale, ws,
-                                       stream=torch.cuda.current_stream())
-    graph.replay()
-    torch.cuda.synchronize()
-    graph32 = _timed(graph.replay, 5) / 32
-    # selection of the 2048 entries (1024 recent) from all 122880 positions
-    sel_idx = torch.empty((w.batch, 8, K), dtype=torch.int32, device="cuda")
-    ws_sel = torch.empty(nup.select_workspace_bytes(st.ctx), dtype=torch.uint8, device="cuda")
-    select = lambda: nup.kv_select_topk(st.ctx, st.q, K, K // 2, sel_idx, ws_sel)
-    select()
-    s_ms = _timed(select, 5, flush)
-    k_bytes = int(w.lengths.sum()) * 256
-    gb = rows * 512 * 2 + rows * 4
-    tb = rows * 512 + w.batch * 32 * 128 * (2 + 4)
-    res["llama3_8b_topk"] = {
-        "gather_ms": round(g_ms, 4), "gather_GBs": round(gb / (g_ms * 1e-3) / 1e9, 1),
-        "topk_attn_ms": round(t_ms, 4), "topk_attn_GBs": round(tb / (t_ms * 1e-3) / 1e9, 1),
-        "gather_plus_attn_ms_32_back_to_back": round(both32, 4),
-        "topk_in_place_ms": round(f_ms, 4),
-        "topk_in_place_GBs": round((rows * (512 + 4) + w.batch * 32 * 128 * 6) / (f_ms * 1e-3) / 1e9, 1),
-        "topk_in_place_ms_32_back_to_back": round(fused32, 4),
-        "topk_in_place_ms_32_layer_graph": round(graph32, 4),
-        "select_ms": round(s_ms, 4),
-        "select_score_GBs": round(k_bytes / (s_ms * 1e-3) / 1e9, 1),
-        "note": "per call cold (1 GiB read before each); 32 back-to-back pairs for a 32-layer stack"}
-    assert nup.device_errors(st.ctx) == nup.NUP_OK
-    del graph
-    st.free()
-    del st, ks, vs, ws, sel_idx, ws_sel
+    if want("llama3_8b_topk"):
+        w = W.llama3_8b_topk()
+        st = Setup(w, 0)
+        K = w.topk
+        idx = torch.from_numpy(W.topk_indices(w.lengths, K)).cuda()
+        ks = torch.empty((w.batch, 8, K, 128), dtype=torch.bfloat16, device="cuda")
+        vs = torch.empty_like(ks)
+        ws = torch.empty(nup.workspace_bytes(st.ctx, K), dtype=torch.uint8, device="cuda")
+        gather = lambda: nup.kv_gather_compact(st.ctx, 1, ks, vs, idx=idx, K=K)
+        topk = lambda: nup.attn_decode_topk(st.ctx, st.q, ks, vs, K, st.out, st.lse, st.scale, ws)
+        fused = lambda: nup.attn_decode_topk_paged(st.ctx, st.q, idx, K, st.out, st.lse, st.scale, ws)
+        for _ in range(3):
+            gather()
+            topk()
+            fused()
+        rows = w.batch * 8 * K
+        g_ms = _timed(gather, 20, flush)
+        t_ms = _timed(topk, 20, flush)
+        f_ms = _timed(fused, 20, flush)
+        both32 = _timed(lambda: [f() for _ in range(32) for f in (gather, topk)], 3) / 32
+        fused32 = _timed(lambda: [fused() for _ in range(32)], 3) / 32
+        # the same 32-layer stack captured in one HIP graph (launch cost amortised)
+        gstream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gstream):
+            fused()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=gstream):
+            for _ in range(32):
+                nup.attn_decode_topk_paged(st.ctx, st.q, idx, K, st.out, st.lse, st.scale, ws,
+                                           stream=torch.cuda.current_stream())
+        graph.replay()
+        torch.cuda.synchronize()
+        graph32 = _timed(graph.replay, 5) / 32
+        # selection of the 2048 entries (1024 recent) from all 122880 positions
+        sel_idx = torch.empty((w.batch, 8, K), dtype=torch.int32, device="cuda")
+        ws_sel = torch.empty(nup.select_workspace_bytes(st.ctx), dtype=torch.uint8, device="cuda")
+        select = lambda: nup.kv_select_topk(st.ctx, st.q, K, K // 2, sel_idx, ws_sel)
+        select()
+        s_ms = _timed(select, 5, flush)
+        k_bytes = int(w.lengths.sum()) * 256
+        gb = rows * 512 * 2 + rows * 4
+        tb = rows * 512 + w.batch * 32 * 128 * (2 + 4)
+        res["llama3_8b_topk"] = {
+            "gather_ms": round(g_ms, 4), "gather_GBs": round(gb / (g_ms * 1e-3) / 1e9, 1),
+            "topk_attn_ms": round(t_ms, 4), "topk_attn_GBs": round(tb / (t_ms * 1e-3) / 1e9, 1),
+            "gather_plus_attn_ms_32_back_to_back": round(both32, 4),
+            "topk_in_place_ms": round(f_ms, 4),
+            "topk_in_place_GBs": round((rows * (512 + 4) + w.batch * 32 * 128 * 6) / (f_ms * 1e-3) / 1e9, 1),
+            "topk_in_place_ms_32_back_to_back": round(fused32, 4),
+            "topk_in_place_ms_32_layer_graph": round(graph32, 4),
+            "select_ms": round(s_ms, 4),
+            "select_score_GBs": round(k_bytes / (s_ms * 1e-3) / 1e9, 1),
+            "note": "per call cold (1 GiB read before each); 32 back-to-back pairs for a 32-layer stack"}
+        assert nup.device_errors(st.ctx) == nup.NUP_OK
+        del graph
+        st.free()
+        del st, ks, vs, ws, sel_idx, ws_sel
 
     # -- mixed-length churn: 10% EOS per step, freed slots refilled next step
-    w = W.mixed_churn()
-    steps_warm, steps = 20, 20
-    pad_steps = steps_warm + steps + 4
-    st = Setup(w, pad_steps, max_pages=int(math.ceil((131072 + 16 * math.ceil((pad_steps + 1) / 16)) / 16)))
-    drv = W.ChurnDriver(w.batch)
-    active = np.ones(w.batch, bool)
-    freed = np.zeros(0, np.int32)
-    host_us, trains, gpu_ms = [], [], []
-    nup.kernel_time(st.ctx, reset=True)
-    for it in range(steps_warm + steps):
-        lib = 0.0   # host time inside the library: Reserve, Trim, frame commit
-        if len(freed):
-            L = drv.refill_lengths(len(freed))
-            Ls = np.repeat(L[:, None], 8, axis=1).astype(np.int32)
+    if want("mixed_churn"):
+        w = W.mixed_churn()
+        steps_warm, steps = 20, 20
+        pad_steps = steps_warm + steps + 4
+        st = Setup(w, pad_steps, max_pages=int(math.ceil((131072 + 16 * math.ceil((pad_steps + 1) / 16)) / 16)))
+        drv = W.ChurnDriver(w.batch)
+        active = np.ones(w.batch, bool)
+        freed = np.zeros(0, np.int32)
+        host_us, trains, gpu_ms = [], [], []
+        nup.kernel_time(st.ctx, reset=True)
+        for it in range(steps_warm + steps):
+            lib = 0.0   # host time inside the library: Reserve, Trim, frame commit
+            if len(freed):
+                L = drv.refill_lengths(len(freed))
+                Ls = np.repeat(L[:, None], 8, axis=1).astype(np.int32)
+                t0 = time.perf_counter()
+                nup.kv_alloc_groups(st.ctx, freed, Ls + st.pad, Ls)
+                lib += time.perf_counter() - t0
+                active[freed] = True
+            eos = drv.eos(np.nonzero(active)[0])
             t0 = time.perf_counter()
-            nup.kv_alloc_groups(st.ctx, freed, Ls + st.pad, Ls)
+            nup.kv_free_seqs(st.ctx, eos)
+            nup.nup_commit(st.ctx)
             lib += time.perf_counter() - t0
-            active[freed] = True
-        eos = drv.eos(np.nonzero(active)[0])
-        t0 = time.perf_counter()
-        nup.kv_free_seqs(st.ctx, eos)
-        nup.nup_commit(st.ctx)
-        lib += time.perf_counter() - t0
-        active[eos] = False
-        freed = eos
-        timed = it >= steps_warm
-        if timed:
-            host_us.append(lib * 1e6)
-            trains.append(len(nup.get_runs(st.ctx)))
-            nup.set_timing(st.ctx, True)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-        nup.kv_append(st.ctx, st.k_new, st.v_new)
-        nup.attn_decode_nonuniform(st.ctx, st.q, st.out, st.lse, st.scale, st.ws)
-        if timed:
-            e1.record()
-            nup.set_timing(st.ctx, False)
-        torch.cuda.synchronize()
-        if timed:
-            gpu_ms.append(e0.elapsed_time(e1))
-    kms, n = nup.kernel_time(st.ctx, reset=True)
-    kms /= max(n, 1)
-    L_now = nup.get_lengths(st.ctx)
-    kb = kv_bytes(L_now)
-    # train-mode gather of the final state
-    lens = L_now.astype(np.int64).reshape(-1)
-    row_off = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)[:-1]])).cuda()
-    total = int(lens.sum())
-    ksg = torch.empty((total, 128), dtype=torch.bfloat16, device="cuda")
-    vsg = torch.empty_like(ksg)
-    gt = lambda: nup.kv_gather_compact(st.ctx, 0, ksg, vsg, row_off=row_off)
-    gt()
-    g_ms = _timed(gt, 5, flush)
-    dma = _dma_trains(st, ksg, vsg, row_off.cpu().numpy(), flush)
-    res["mixed_churn"] = {
-        "active_slots": int(active.sum()), "kv_bytes": kb,
-        "host_trim_reserve_commit_us_mean": round(float(np.mean(host_us)), 1),
-        "gpu_append_attn_ms_mean": round(float(np.mean(gpu_ms)), 4),
-        "submit_share": round(float(np.mean(host_us)) / (float(np.mean(host_us)) + 1e3 * float(np.mean(gpu_ms))), 4),
-        "trains_per_step_mean": round(float(np.mean(trains)), 1),
-        "pages_in_use": int(st.num_pages - len(nup.get_free_list(st.ctx))),
-        "partial_kernel_ms": round(kms, 4),
-        "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
-        "gather_trains_ms": round(g_ms, 4),
-        "gather_trains_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1),
-        "gather_trains_copy_engine": dma}
-    st.free()
-    del st, ksg, vsg
-    torch.cuda.empty_cache()
-
-    # -- the Qwen2.5-32B batch (long trains): gather kernel vs copy engines,
-    #    with one head per group (linear copies) and with the 4-group layout
-    res["qwen25_32b_trains"] = []
-    for ng in (8, 4):
-        w = W.qwen25_32b()
-        w.num_groups = ng
-        st = Setup(w, 0)
-        lens = st.lengths0.astype(np.int64).reshape(-1)
-        ro = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+            active[eos] = False
+            freed = eos
+            timed = it >= steps_warm
+            if timed:
+                host_us.append(lib * 1e6)
+                trains.append(len(nup.get_runs(st.ctx)))
+                nup.set_timing(st.ctx, True)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            nup.kv_append(st.ctx, st.k_new, st.v_new)
+            nup.attn_decode_nonuniform(st.ctx, st.q, st.out, st.lse, st.scale, st.ws)
+            if timed:
+                e1.record()
+                nup.set_timing(st.ctx, False)
+            torch.cuda.synchronize()
+            if timed:
+                gpu_ms.append(e0.elapsed_time(e1))
+        kms, n = nup.kernel_time(st.ctx, reset=True)
+        kms /= max(n, 1)
+        L_now = nup.get_lengths(st.ctx)
+        kb = kv_bytes(L_now)
+        # train-mode gather of the final state
+        lens = L_now.astype(np.int64).reshape(-1)
+        row_off = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)[:-1]])).cuda()
         total = int(lens.sum())
         ksg = torch.empty((total, 128), dtype=torch.bfloat16, device="cuda")
         vsg = torch.empty_like(ksg)
-        ro_dev = torch.from_numpy(ro).cuda()
-        gt = lambda: nup.kv_gather_compact(st.ctx, 0, ksg, vsg, row_off=ro_dev)
+        gt = lambda: nup.kv_gather_compact(st.ctx, 0, ksg, vsg, row_off=row_off)
         gt()
         g_ms = _timed(gt, 5, flush)
-        res["qwen25_32b_trains"].append({
-            "heads_per_group": 8 // ng, "trains": int(len(nup.get_runs(st.ctx))), "bytes": 2 * total * 256,
-            "gather_kernel_ms": round(g_ms, 4),
-            "gather_kernel_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1),
-            "copy_engine": _dma_trains(st, ksg, vsg, ro, flush)})
+        dma = None if args.no_copy_engine else _dma_trains(st, ksg, vsg, row_off.cpu().numpy(), flush)
+        res["mixed_churn"] = {
+            "active_slots": int(active.sum()), "kv_bytes": kb,
+            "host_trim_reserve_commit_us_mean": round(float(np.mean(host_us)), 1),
+            "gpu_append_attn_ms_mean": round(float(np.mean(gpu_ms)), 4),
+            "submit_share": round(float(np.mean(host_us)) / (float(np.mean(host_us)) + 1e3 * float(np.mean(gpu_ms))), 4),
+            "trains_per_step_mean": round(float(np.mean(trains)), 1),
+            "pages_in_use": int(st.num_pages - len(nup.get_free_list(st.ctx))),
+            "partial_kernel_ms": round(kms, 4),
+            "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
+            "gather_trains_ms": round(g_ms, 4),
+            "gather_trains_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1),
+            "gather_trains_copy_engine": dma}
         st.free()
-        del st, ksg, vsg, ro_dev
+        del st, ksg, vsg
         torch.cuda.empty_cache()
+
+    # -- the Qwen2.5-32B batch (long trains): gather kernel vs copy engines,
+    #    with one head per group (linear copies) and with the 4-group layout
+    if want("qwen25_32b_trains"):
+        res["qwen25_32b_trains"] = []
+        for ng in (8, 4):
+            w = W.qwen25_32b()
+            w.num_groups = ng
+            st = Setup(w, 0)
+            lens = st.lengths0.astype(np.int64).reshape(-1)
+            ro = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+            total = int(lens.sum())
+            ksg = torch.empty((total, 128), dtype=torch.bfloat16, device="cuda")
+            vsg = torch.empty_like(ksg)
+            ro_dev = torch.from_numpy(ro).cuda()
+            gt = lambda: nup.kv_gather_compact(st.ctx, 0, ksg, vsg, row_off=ro_dev)
+            gt()
+            g_ms = _timed(gt, 5, flush)
+            res["qwen25_32b_trains"].append({
+                "heads_per_group": 8 // ng, "trains": int(len(nup.get_runs(st.ctx))), "bytes": 2 * total * 256,
+                "gather_kernel_ms": round(g_ms, 4),
+                "gather_kernel_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1),
+                "copy_engine": None if args.no_copy_engine else _dma_trains(st, ksg, vsg, ro, flush)})
+            st.free()
+            del st, ksg, vsg, ro_dev
+            torch.cuda.empty_cache()
 
     # -- forked sessions sharing a prompt prefix (KV-RM Alias): same lengths as
     #    the Qwen2.5-32B batch, 60 of 64 sessions fork from 4 sources; the
     #    unshared batch is timed the same way for comparison
-    res["qwen25_32b_prefix"] = {}
-    for tag, w in (("unshared", W.qwen25_32b()), ("forked", W.qwen25_32b_prefix())):
-        st = Setup(w, 0)
-        for _ in range(2):
-            st.step(append=False)
-        torch.cuda.synchronize()
-        nup.kernel_time(st.ctx, reset=True)
-        nup.set_timing(st.ctx, True)
-        _timed(lambda: st.step(append=False), 10, flush)
-        nup.set_timing(st.ctx, False)
-        kms, n = nup.kernel_time(st.ctx, reset=True)
-        kms /= max(n, 1)
-        in_use = int(st.num_pages - len(nup.get_free_list(st.ctx)))
-        entries = int(np.count_nonzero(nup.get_page_table(st.ctx) >= 0))
-        kb = kv_bytes(st.lengths0)
-        share = getattr(st, "share", None)
-        shared_b = 0 if share is None else int(sum(int(share[i, st.goh[h]]) * 16 * 512
-                                                   for i in range(len(share)) for h in range(w.num_kv_heads)))
-        res["qwen25_32b_prefix"][tag] = {
-            "pages_in_use": in_use, "page_table_entries": entries,
-            "reserved_saving": round(1 - in_use / entries, 4),
-            "kv_bytes_logical": kb, "kv_bytes_unique": kb - shared_b,
-            "partial_kernel_ms": round(kms, 4),
-            "partial_kernel_logical_GBs": round(kb / (kms * 1e-3) / 1e9, 1)}
-        st.free()
-        del st
-        torch.cuda.empty_cache()
-    res["qwen25_32b_prefix"]["note"] = ("prefix 8192 tokens, 4 sources; cold (1 GiB read before each "
-                                        "step); logical bytes count every session's reads")
+    if want("qwen25_32b_prefix"):
+        res["qwen25_32b_prefix"] = {}
+        for tag, w in (("unshared", W.qwen25_32b()), ("forked", W.qwen25_32b_prefix())):
+            st = Setup(w, 0)
+            for _ in range(2):
+                st.step(append=False)
+            torch.cuda.synchronize()
+            nup.kernel_time(st.ctx, reset=True)
+            nup.set_timing(st.ctx, True)
+            _timed(lambda: st.step(append=False), 10, flush)
+            nup.set_timing(st.ctx, False)
+            kms, n = nup.kernel_time(st.ctx, reset=True)
+            kms /= max(n, 1)
+            in_use = int(st.num_pages - len(nup.get_free_list(st.ctx)))
+            entries = int(np.count_nonzero(nup.get_page_table(st.ctx) >= 0))
+            kb = kv_bytes(st.lengths0)
+            share = getattr(st, "share", None)
+            shared_b = 0 if share is None else int(sum(int(share[i, st.goh[h]]) * 16 * 512
+                                                       for i in range(len(share)) for h in range(w.num_kv_heads)))
+            res["qwen25_32b_prefix"][tag] = {
+                "pages_in_use": in_use, "page_table_entries": entries,
+                "reserved_saving": round(1 - in_use / entries, 4),
+                "kv_bytes_logical": kb, "kv_bytes_unique": kb - shared_b,
+                "partial_kernel_ms": round(kms, 4),
+                "partial_kernel_logical_GBs": round(kb / (kms * 1e-3) / 1e9, 1)}
+            st.free()
+            del st
+            torch.cuda.empty_cache()
+        res["qwen25_32b_prefix"]["note"] = ("prefix 8192 tokens, 4 sources; cold (1 GiB read before each "
+                                            "step); logical bytes count every session's reads")
 
     # -- head groups across layers (Tangram, Fig 11): the 36-layer Qwen3-4B
     #    shape in one pager, heads per group 1 .. 32 (groups beyond 8 span layers)
-    res["qwen3_4b_36_layers_heads_per_group"] = _layer_group_sweep(flush)
+    if want("qwen3_4b_36_layers"):
+        res["qwen3_4b_36_layers"] = _layer_group_sweep(flush)
 
     # -- heads per page (Tangram, Fig 8c): the Qwen2.5-32B batch with 1, 2, 4, 8 groups
-    sweep = []
-    for ng in (8, 4, 2, 1):
-        w = W.qwen25_32b()
-        w.num_groups = ng
-        gh = 8 // ng
-        st = Setup(w, 8)
-        reserved_slots = (st.num_pages - len(nup.get_free_list(st.ctx))) * 16 * gh
-        used = int(st.lengths0.sum())
-        for _ in range(2):
-            st.step(append=False)
-        torch.cuda.synchronize()
-        nup.kernel_time(st.ctx, reset=True)
-        nup.set_timing(st.ctx, True)
-        _timed(lambda: st.step(append=False), 10)
-        nup.set_timing(st.ctx, False)
-        kms, n = nup.kernel_time(st.ctx, reset=True)
-        kms /= max(n, 1)
-        sweep.append({"heads_per_group": gh, "groups": ng,
-                      "reserved_GB": round(reserved_slots * 512 / 1e9, 3),
-                      "internal_fragmentation": round(1 - used / reserved_slots, 4),
-                      "page_table_entries": int(st.num_pages - len(nup.get_free_list(st.ctx))),
-                      "partial_kernel_ms": round(kms, 4),
-                      "partial_kernel_GBs": round(kv_bytes(st.lengths0) / (kms * 1e-3) / 1e9, 1)})
-        st.free()
-        del st
-        torch.cuda.empty_cache()
-    res["qwen25_32b_heads_per_group"] = sweep
+    if want("qwen25_32b_heads_per_group"):
+        sweep = []
+        for ng in (8, 4, 2, 1):
+            w = W.qwen25_32b()
+            w.num_groups = ng
+            gh = 8 // ng
+            st = Setup(w, 8)
+            reserved_slots = (st.num_pages - len(nup.get_free_list(st.ctx))) * 16 * gh
+            used = int(st.lengths0.sum())
+            for _ in range(2):
+                st.step(append=False)
+            torch.cuda.synchronize()
+            nup.kernel_time(st.ctx, reset=True)
+            nup.set_timing(st.ctx, True)
+            _timed(lambda: st.step(append=False), 10)
+            nup.set_timing(st.ctx, False)
+            kms, n = nup.kernel_time(st.ctx, reset=True)
+            kms /= max(n, 1)
+            sweep.append({"heads_per_group": gh, "groups": ng,
+                          "reserved_GB": round(reserved_slots * 512 / 1e9, 3),
+                          "internal_fragmentation": round(1 - used / reserved_slots, 4),
+                          "page_table_entries": int(st.num_pages - len(nup.get_free_list(st.ctx))),
+                          "partial_kernel_ms": round(kms, 4),
+                          "partial_kernel_GBs": round(kv_bytes(st.lengths0) / (kms * 1e-3) / 1e9, 1)})
+            st.free()
+            del st
+            torch.cuda.empty_cache()
+        res["qwen25_32b_heads_per_group"] = sweep
     del flush_buf
     torch.cuda.empty_cache()
     return res
@@ -590,6 +607,10 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other configurations (Qwen3-4B, Llama top-K, mixed churn)")
     ap.add_argument("--workers", type=int, default=0)
+    ap.add_argument("--no-copy-engine", action="store_true",
+                    help="skip the copy-engine train measurements (thousands of copies)")
+    ap.add_argument("--only-extra", choices=EXTRA_SECTIONS, default=None,
+                    help="run just this one of the other configurations and print its JSON")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
                     help="only run the plain streaming copy kernel over BYTES (counter "
                          "calibration and achievable-bandwidth ceiling), then exit")
@@ -622,6 +643,11 @@ def main():
         ms = e0.elapsed_time(e1) / reps
         print(json.dumps({"probe_copy_bytes": n, "ms": round(ms, 4),
                           "read_plus_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
+
+    if args.only_extra:
+        print(json.dumps({"extra": args.only_extra,
+                          "result": measure_extras(args, only=args.only_extra)[args.only_extra]}), flush=True)
         return
 
     src = open(os.path.join(ROOT, "non_uniform_paged_amd", "csrc", "kernels.hip"), "rb").read()
