@@ -170,7 +170,7 @@ def traffic_from_profiles(kernel_src_sha):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(setup, budget_s=15.0):
+def cpu_baseline(setup, budget_s=12.0):
     """The fp64 oracle on the first n sessions of the same workload, n chosen so
     that the run takes roughly budget_s seconds of CPU time."""
     import torch
@@ -208,7 +208,7 @@ def cpu_baseline(setup, budget_s=15.0):
     if n > 1:
         dt, b = run(list(range(n)))
     reps, total_t, total_b = 1, dt, b
-    while total_t < budget_s * 0.6 and reps < 50:   # whole batch is quick: repeat it
+    while total_t < budget_s and reps < 50:   # whole batch is quick: repeat it
         dt, b = run(list(range(n)))
         reps, total_t, total_b = reps + 1, total_t + dt, total_b + b
     return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": threads,
