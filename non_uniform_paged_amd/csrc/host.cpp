@@ -19,7 +19,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <deque>
 #include <new>
 #include <numeric>
 #include <string>
@@ -104,6 +103,36 @@ Sizes compute_sizes(const nup_config &c, int workers) {
 
 }  // namespace
 
+// FIFO free list of physical pages: a ring over a fixed array of num_pages
+// entries (the list never holds more), so Reserve takes its pages with at
+// most two block copies.
+struct PageRing {
+    std::vector<int32_t> a;
+    size_t head = 0, n = 0;
+    void init(size_t cap) { a.assign(cap, 0); head = n = 0; }
+    size_t size() const { return n; }
+    void push_back(int32_t v) {
+        size_t i = head + n;
+        if (i >= a.size()) i -= a.size();
+        a[i] = v;
+        ++n;
+    }
+    // moves the first k entries to out (k <= size())
+    void pop_front(int32_t *out, size_t k) {
+        const size_t first = std::min(k, a.size() - head);
+        std::memcpy(out, a.data() + head, first * sizeof(int32_t));
+        if (k > first) std::memcpy(out + first, a.data(), (k - first) * sizeof(int32_t));
+        head += k;
+        if (head >= a.size()) head -= a.size();
+        n -= k;
+    }
+    void copy_to(int32_t *out) const {
+        const size_t first = std::min(n, a.size() - head);
+        std::memcpy(out, a.data() + head, first * sizeof(int32_t));
+        if (n > first) std::memcpy(out + first, a.data(), (n - first) * sizeof(int32_t));
+    }
+};
+
 struct nup_ctx {
     nup_config cfg{};
     int H = 0, Hq = 0, D = 0, P = 0, ng = 0, gh = 0, B = 0, num_pages = 0, max_pages = 0, gqa = 0;
@@ -115,7 +144,7 @@ struct nup_ctx {
     bool has_device = false;
 
     // pager shadow
-    std::deque<int32_t> free_list;
+    PageRing free_list;
     std::vector<int32_t> pt;       // [ng][B][max_pages]
     std::vector<int32_t> npages;   // [ng][B]
     std::vector<int32_t> len, cap; // [B][V]
@@ -244,12 +273,19 @@ void plan_balanced(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
         }
     }
     const size_t max_rows = (size_t)W + 2 * (size_t)NH;
-    std::vector<int32_t> owner(max_rows);
     pl.rows.resize(4 * max_rows);
     pl.head_row_start.resize((size_t)NH + 1);
+    pl.worker_start.resize((size_t)W + 1);
     int32_t *rw = pl.rows.data();
+    int32_t *wst = pl.worker_start.data();
     size_t n = 0;
-    int w = 0;  // worker holding the current page; only moves forward
+    int w = 0;      // worker holding the current page; only moves forward
+    int next = 0;   // first worker whose start row is not set yet
+    // the row about to be written belongs to worker `o`: it starts every
+    // worker up to o that has no row yet (owners never decrease)
+    auto own = [&](int o) {
+        while (next <= o) wst[next++] = (int32_t)n;
+    };
     for (int sh = 0, s = 0, h = 0; sh < NH; ++sh, (++h == H ? (h = 0, ++s) : 0)) {
         pl.head_row_start[sh] = (int32_t)n;
         const long long lo = base[sh], hi = base[sh + 1];
@@ -262,11 +298,12 @@ void plan_balanced(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
             } else {
                 ow = (int)((long long)sh * W / NH);
             }
+            own(ow);
             rw[4 * n + 0] = sh;
             rw[4 * n + 1] = 0;
             rw[4 * n + 2] = 0;
             rw[4 * n + 3] = s * c->V + h;
-            owner[n++] = ow;
+            ++n;
             continue;
         }
         const long long cap = capl[(size_t)s * c->V + h];
@@ -274,23 +311,18 @@ void plan_balanced(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
         while (p < hi) {
             while (bound[w + 1] <= p) ++w;
             const long long end = std::min(hi, bound[w + 1]);
+            own(w);
             rw[4 * n + 0] = sh;
             rw[4 * n + 1] = (int32_t)((p - lo) << 4);
             rw[4 * n + 2] = (int32_t)std::min<long long>((end - lo) << 4, cap);
             rw[4 * n + 3] = s * c->V + h;
-            owner[n++] = w;
+            ++n;
             p = end;
         }
     }
     pl.head_row_start[NH] = (int32_t)n;
     pl.rows.resize(4 * n);
-    pl.worker_start.resize((size_t)W + 1);
-    size_t r = 0;
-    for (int k = 0; k <= W; ++k) {
-        while (r < n && owner[r] < k) ++r;
-        pl.worker_start[k] = (int32_t)r;
-    }
-    pl.worker_start[W] = (int32_t)n;
+    while (next <= W) wst[next++] = (int32_t)n;
 }
 
 // The uniform split (the control): every head is cut into the same number of
@@ -376,17 +408,13 @@ void install(nup_ctx *c, int s, const int32_t *need, int src, const int32_t *sha
         const size_t ri = (size_t)g * c->B + s;
         int32_t *row = &c->pt[ri * c->max_pages];
         const int32_t *src_row = src >= 0 ? &c->pt[((size_t)g * c->B + src) * c->max_pages] : nullptr;
-        for (int j = 0; j < np; ++j) {
-            int32_t page;
-            if (j < shared) {
-                page = src_row[j];
-                ++c->ref[page];
-            } else {
-                page = c->free_list.front();
-                c->free_list.pop_front();
-                c->ref[page] = 1;
-            }
-            row[j] = page;
+        for (int j = 0; j < shared; ++j) {
+            row[j] = src_row[j];
+            ++c->ref[row[j]];
+        }
+        if (np > shared) {
+            c->free_list.pop_front(row + shared, (size_t)(np - shared));
+            for (int j = shared; j < np; ++j) c->ref[row[j]] = 1;
         }
         c->dirty_count[ri] = std::max(c->dirty_count[ri], np);
         c->npages[ri] = np;
@@ -471,6 +499,7 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
         c->workers = prop.multiProcessorCount * std::max(1, nb) * nup::kWavesPerBlock;
     }
     c->sz = compute_sizes(c->cfg, c->workers);
+    c->free_list.init((size_t)c->num_pages);
     if (cfg->free_list_init) {
         std::vector<char> seen(c->num_pages, 0);
         for (int i = 0; i < c->num_pages; ++i) {
@@ -1198,7 +1227,7 @@ nup_status nup_get_groups(const nup_ctx *c, int32_t *goh, int32_t *soh) {
 nup_status nup_get_free_list(const nup_ctx *c, int32_t *out, int32_t *n) {
     if (!c || !n) return NUP_E_ARG;
     *n = (int32_t)c->free_list.size();
-    if (out) std::copy(c->free_list.begin(), c->free_list.end(), out);
+    if (out) c->free_list.copy_to(out);
     return NUP_OK;
 }
 
