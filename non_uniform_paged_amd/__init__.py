@@ -147,7 +147,7 @@ class Context:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
+        if h and _lib is not None:        # at interpreter exit the module may be torn down first
             _lib.nup_destroy(h)
             self.handle = None
 
