@@ -64,3 +64,77 @@ def test_scores_exact_on_representable_inputs():
     # value 3 occurs at t = 6, 13, 20, 27, 34, 41: the first 8 highest go to the
     # lowest positions (six 3s, then 2s at t = 5, 12)
     assert idx.tolist()[:8] == [5, 6, 12, 13, 20, 27, 34, 41]
+
+
+# ---- centroid variant ------------------------------------------------------
+
+import json  # noqa: E402
+import os  # noqa: E402
+
+CENT = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_centroids.json")))
+
+
+def _csr(clusters):
+    start = np.concatenate([[0], np.cumsum([len(c) for c in clusters])]).astype(np.int32)
+    pos = np.concatenate([np.array(c, np.int32) for c in clusters]) if clusters else np.zeros(0, np.int32)
+    return start, pos
+
+
+def test_centroid_fixture():
+    start, pos = _csr(CENT["clusters"])
+    cs = np.array(CENT["cluster_scores"])
+    for case in CENT["cases"]:
+        got = sel.select_clusters(cs, start, pos, CENT["L"], case["K"], case["window"])
+        assert got.tolist() == case["want"], case["note"]
+
+
+def test_centroids_equal_exact_selection_for_singleton_clusters():
+    """One position per cluster, centroid = that position's key: the cluster
+    order is the position order by (score desc, position asc), so the result
+    is the exact selection."""
+    rs = np.random.default_rng(7)
+    H, gqa, D = 2, 3, 16
+    for trial in range(30):
+        L = int(rs.integers(2, 60))
+        p = pg.PagerSpec(H, 1, 1, 64, 64, 16)
+        assert p.alloc([0], np.array([[L] * H]), np.array([[L] * H])) == pg.OK
+        keys = rs.integers(-3, 4, size=(64, H, 16, D)).astype(np.float32)   # ties on purpose
+        q = rs.integers(-2, 3, size=(1, H * gqa, D)).astype(np.float32)
+        kb, qb = f32_to_bf16_bits(keys), f32_to_bf16_bits(q)
+        for h in range(H):
+            rows = [p.physical_row(0, h, t) for t in range(L)]
+            cent = kb.reshape(-1, D)[rows][None, None].repeat(H, axis=1)   # [1][H][L][D]
+            cs = sel.centroid_scores(qb, cent, 0, h, gqa)
+            exact = sel.scores(qb, kb, p, 0, h)
+            np.testing.assert_array_equal(cs, exact)
+            K = int(rs.integers(1, L + 1))
+            window = int(rs.integers(0, K + 1))
+            start, pos = _csr([[t] for t in range(L)])
+            assert sel.select_clusters(cs, start, pos, L, K, window).tolist() == \
+                sel.select(exact, K, window).tolist()
+
+
+def test_centroid_selection_structure():
+    """Exactly K ascending entries with the window; the clusters fully taken
+    score at least as high as every cluster left untouched."""
+    rs = np.random.default_rng(8)
+    for trial in range(100):
+        L = int(rs.integers(5, 400))
+        C = int(rs.integers(1, 40))
+        assign = rs.integers(0, C, size=L)
+        clusters = [sorted(np.nonzero(assign == c)[0].tolist()) for c in range(C)]
+        start, pos = _csr(clusters)
+        cs = rs.integers(-5, 6, size=C).astype(np.float64)
+        K = int(rs.integers(1, L + 1))
+        window = int(rs.integers(0, K + 1))
+        got = sel.select_clusters(cs, start, pos, L, K, window)
+        n = L - window
+        assert len(got) == K and (np.diff(got) > 0).all()
+        assert got[K - window:].tolist() == list(range(n, L))
+        taken = set(got[:K - window].tolist())
+        full = [c for c in range(C) if all(t in taken for t in clusters[c] if t < n)
+                and any(t < n for t in clusters[c])]
+        none = [c for c in range(C) if not any(t in taken for t in clusters[c] if t < n)
+                and any(t < n for t in clusters[c])]
+        if full and none:
+            assert min(cs[full]) >= max(cs[none])
