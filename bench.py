@@ -260,6 +260,62 @@ def _dma_trains(st, ks, vs, row_off, flush):
             "host_enqueue_ms": round(1e3 * float(np.mean(enq)), 3), "rows_equal_kernel": same}
 
 
+def _centroid_sweep(flush):
+    """For C clusters per KV head on the Llama-3-8B shape: keys are the
+    cluster centre plus noise (bf16), positions assigned to clusters at
+    random.  Reports the centroid selection's time and the share of the
+    exact selection's older entries it finds (the recent window, kept by
+    both, is left out)."""
+    import torch
+    import non_uniform_paged_amd as nup
+    import workloads as W
+    w = W.llama3_8b_topk()
+    st = Setup(w, 0)
+    B, H, D, K = w.batch, w.num_kv_heads, w.head_dim, w.topk
+    window = K // 2
+    L = int(w.lengths[0, 0])
+    gh = H // w.num_groups
+    pt = nup.get_page_table(st.ctx)
+    goh, soh = nup.get_groups(st.ctx)
+    t = np.arange(L)
+    exact = torch.empty((B, H, K), dtype=torch.int32, device="cuda")
+    approx = torch.empty_like(exact)
+    ws_sel = torch.empty(nup.select_workspace_bytes(st.ctx), dtype=torch.uint8, device="cuda")
+    out = []
+    g = torch.Generator(device="cuda")
+    for C in (2048, 4096, 8192):
+        start, pos = W.cluster_lists(w.lengths, C, salt=C)
+        g.manual_seed(W.torch_seed("k", C))
+        cent = torch.randn((B, H, C, D), generator=g, device="cuda").to(torch.bfloat16)
+        kflat = st.kpool.view(-1, D)
+        for s in range(B):
+            for h in range(H):
+                counts = np.diff(start[s, h])
+                assign = np.empty(L, np.int64)
+                assign[pos[s, h, :L]] = np.repeat(np.arange(C), counts)
+                rows = (pt[goh[h], s, t // 16].astype(np.int64) * gh + soh[h]) * 16 + t % 16
+                keys = cent[s, h][torch.from_numpy(assign).cuda()].float()
+                keys += 0.5 * torch.randn(keys.shape, generator=g, device="cuda")
+                kflat[torch.from_numpy(rows).cuda()] = keys.to(torch.bfloat16)
+        torch.cuda.synchronize()
+        nup.kv_select_topk(st.ctx, st.q, K, window, exact, ws_sel)
+        ws_c = torch.empty(nup.centroid_workspace_bytes(st.ctx, C), dtype=torch.uint8, device="cuda")
+        cs, ps = torch.from_numpy(start).cuda(), torch.from_numpy(pos).cuda()
+        sel = lambda: nup.kv_select_topk_centroids(st.ctx, st.q, cent, C, cs, ps, pos.shape[2], K, window,
+                                                   approx, ws_c)
+        sel()
+        torch.cuda.synchronize()
+        ms = _timed(sel, 10, flush)
+        e, a = exact.cpu().numpy()[..., :K - window], approx.cpu().numpy()[..., :K - window]
+        recall = np.mean([len(np.intersect1d(e[s, h], a[s, h])) / (K - window)
+                          for s in range(B) for h in range(H)])
+        assert nup.device_errors(st.ctx) == nup.NUP_OK
+        out.append({"centroids": C, "select_ms": round(ms, 4), "recall_of_exact_topk": round(float(recall), 4)})
+        del cent, ws_c, cs, ps
+    st.free()
+    return out
+
+
 def _layer_group_sweep(flush):
     """Reserved memory, page-table entries, host Reserve+commit time and the
     36-layer decode time for each head-group size on the 36-layer batch."""
@@ -318,7 +374,7 @@ def _layer_group_sweep(flush):
     return out
 
 
-EXTRA_SECTIONS = ("qwen3_4b", "llama3_8b_topk", "mixed_churn", "qwen25_32b_trains", "qwen25_32b_prefix",
+EXTRA_SECTIONS = ("qwen3_4b", "llama3_8b_topk", "llama3_8b_centroids", "mixed_churn", "qwen25_32b_trains", "qwen25_32b_prefix",
                   "qwen3_4b_36_layers", "qwen25_32b_heads_per_group")
 
 
@@ -424,6 +480,11 @@ def measure_extras(args, only=None):
         del graph
         st.free()
         del st, ks, vs, ws, sel_idx, ws_sel
+
+    # -- centroid selection (KVDrive, Fig 18 / Fig 19): time and recall of the
+    #    exact top-K on keys drawn around 2048, 4096 or 8192 cluster centres
+    if want("llama3_8b_centroids"):
+        res["llama3_8b_centroids"] = _centroid_sweep(flush)
 
     # -- mixed-length churn: 10% EOS per step, freed slots refilled next step
     if want("mixed_churn"):

@@ -321,6 +321,39 @@ nup_status nup_select_workspace_bytes(const nup_ctx *ctx, size_t *bytes);
 
 /* ---- host-side queries (no device call; for tests and reports) ---------- */
 
+/*
+ * kv_select_topk_centroids -- approximate selection through key clusters
+ * (KVDrive, Fig 18 and Fig 19 vary the number of centroids, 2048 to 8192).
+ * The older positions of each (slot, KV head) of the current layer are
+ * partitioned into C clusters, given by a centroid key each and a member
+ * list (the clustering happens before decode).  A cluster's score is the
+ * largest q.c over the head's query rows (fp32 from bf16 products).
+ * Clusters are taken whole in descending score, ties to the lower cluster
+ * id, until K - window positions below L - window are covered; the cluster
+ * that crosses the count gives its lowest positions.  The list is written
+ * ascending, followed by the window L-window .. L-1 (as kv_select_topk).
+ *   centroids  device bf16 [B_max][H_kv][C][D]
+ *   cl_start   device int32 [B_max][H_kv][C+1]: cluster c's members are
+ *              cl_pos[... + cl_start[c] .. cl_start[c+1]), with
+ *              0 <= cl_start[c] <= cl_start[c+1] <= P
+ *   cl_pos     device int32 [B_max][H_kv][P]: positions, ascending within a
+ *              cluster, each older position in at most one cluster;
+ *              members at or past L - window are ignored
+ *   C          1 .. 8192;  max_pages * P must not exceed 262144
+ *   idx_out    device int32 [B_max][H_kv][K]; rows of inactive slots untouched
+ *   workspace  device, >= nup_centroid_workspace_bytes(ctx, C) bytes
+ * A head whose lists are malformed or hold fewer than K - window older
+ * positions latches NUP_E_INDEX (nup_device_errors) and gets -1 for its
+ * selected entries, which attn_decode_topk_paged masks.  Requires a
+ * committed descriptor with no pending edits and L >= K for every active
+ * head (host checks).  Errors: NUP_E_ARG, NUP_E_STATE, NUP_E_HIP. */
+nup_status kv_select_topk_centroids(nup_ctx *ctx, const void *q, const void *centroids, int32_t C,
+                                    const int32_t *cl_start, const int32_t *cl_pos, int32_t P,
+                                    int32_t K, int32_t window, int32_t *idx_out, void *workspace,
+                                    size_t ws_bytes, void *stream);
+/* Workspace bytes for kv_select_topk_centroids: B_max * H_kv * C fp32 cluster scores. */
+nup_status nup_centroid_workspace_bytes(const nup_ctx *ctx, int32_t C, size_t *bytes);
+
 /* Shadow page table int32 [n_g][B_max][max_pages]. */
 nup_status nup_get_page_table(const nup_ctx *ctx, int32_t *out);
 /* Shadow lengths int32 [B_max][V] (0 for inactive slots). */

@@ -72,6 +72,8 @@ _sigs = {
     "nup_get_groups": [_P, _P, _P],
     "nup_get_free_list": [_P, _P, _P],
     "nup_get_refcounts": [_P, _P],
+    "kv_select_topk_centroids": [_P, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _S, _P],
+    "nup_centroid_workspace_bytes": [_P, _I, _P],
     "nup_set_layer": [_P, _I],
     "nup_get_runs": [_P, _P, _I, _P],
     "nup_get_plan": [_P, _P, _P, _P, _P, _P],
@@ -274,6 +276,20 @@ def kv_select_topk(ctx: Context, q, K: int, window: int, idx_out, workspace, str
     st = _lib.kv_select_topk(ctx.handle, _ptr(q), K, window, _ptr(idx_out), _ptr(workspace), nbytes,
                              _stream(stream))
     return ctx.check(st) if raise_on_error else st
+
+
+def kv_select_topk_centroids(ctx: Context, q, centroids, C: int, cl_start, cl_pos, P: int, K: int,
+                             window: int, idx_out, workspace, stream=None, raise_on_error=True):
+    st = _lib.kv_select_topk_centroids(ctx.handle, _ptr(q), _ptr(centroids), C, _ptr(cl_start),
+                                       _ptr(cl_pos), P, K, window, _ptr(idx_out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream))
+    return ctx.check(st) if raise_on_error else st
+
+
+def centroid_workspace_bytes(ctx: Context, C: int) -> int:
+    n = ctypes.c_size_t()
+    ctx.check(_lib.nup_centroid_workspace_bytes(ctx.handle, C, ctypes.byref(n)))
+    return n.value
 
 
 def select_workspace_bytes(ctx: Context) -> int:

@@ -1205,6 +1205,58 @@ nup_status kv_select_topk(nup_ctx *c, const void *q, int32_t K, int32_t window, 
     return NUP_OK;
 }
 
+nup_status nup_centroid_workspace_bytes(const nup_ctx *c, int32_t C, size_t *bytes) {
+    if (!c || !bytes || C <= 0) return NUP_E_ARG;
+    *bytes = align_up((size_t)c->B * c->H * (size_t)C * 4);
+    return NUP_OK;
+}
+
+nup_status kv_select_topk_centroids(nup_ctx *c, const void *q, const void *centroids, int32_t C,
+                                    const int32_t *cl_start, const int32_t *cl_pos, int32_t P, int32_t K,
+                                    int32_t window, int32_t *idx_out, void *workspace, size_t ws_bytes,
+                                    void *stream) {
+    if (!c) return NUP_E_ARG;
+    if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
+    if (!c->committed || c->pending) return fail(c, NUP_E_STATE, "edits pending: nup_commit first");
+    if (!q || !centroids || !cl_start || !cl_pos || !idx_out || !workspace)
+        return fail(c, NUP_E_ARG, "q, centroids, cluster lists, idx_out and workspace are required");
+    if (C <= 0 || C > nup::kMaxClusters) return fail(c, NUP_E_ARG, "C = %d outside [1, %d]", C, nup::kMaxClusters);
+    if (P < 0) return fail(c, NUP_E_ARG, "P < 0");
+    if (K <= 0 || window < 0 || window > K) return fail(c, NUP_E_ARG, "need K > 0 and 0 <= window <= K");
+    if ((long long)c->max_pages * c->P > nup::kMaxSelectPositions)
+        return fail(c, NUP_E_ARG, "max_pages * P = %lld exceeds the %d positions the cluster select holds",
+                    (long long)c->max_pages * c->P, nup::kMaxSelectPositions);
+    size_t need = 0;
+    nup_centroid_workspace_bytes(c, C, &need);
+    if (ws_bytes < need) return fail(c, NUP_E_ARG, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    for (int s = 0; s < c->B; ++s) {
+        if (!c->active[s]) continue;
+        for (int h = 0; h < c->H; ++h)
+            if (c->len[(size_t)s * c->V + c->lbase() + h] < K)
+                return fail(c, NUP_E_ARG, "slot %d head %d retains %d < K = %d entries", s, h,
+                            c->len[(size_t)s * c->V + c->lbase() + h], K);
+    }
+    nup::CentroidArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.centroids = static_cast<const uint16_t *>(centroids);
+    a.active = c->d_active();
+    a.lengths = c->d_len() + c->lbase();
+    a.cl_start = cl_start;
+    a.cl_pos = cl_pos;
+    a.cscore = static_cast<float *>(workspace);
+    a.idx_out = idx_out;
+    a.err = c->d_err();
+    a.hkv = c->H;
+    a.lstride = c->V;
+    a.C = C;
+    a.P = P;
+    a.k = K;
+    a.window = window;
+    hipError_t e = nup::launch_centroid_select(a, c->D, c->gqa, c->B * c->H, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "centroid select launch");
+    return NUP_OK;
+}
+
 nup_status nup_get_page_table(const nup_ctx *c, int32_t *out) {
     if (!c || !out) return NUP_E_ARG;
     std::copy(c->pt.begin(), c->pt.end(), out);

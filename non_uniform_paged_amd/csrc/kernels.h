@@ -88,6 +88,27 @@ struct SelectArgs {
     int32_t hkv, stride, k, window, lstride;
 };
 
+// Top-K selection through key clusters.  centroid_score_kernel writes, for
+// every active head, the largest q.c over its query rows for each of its C
+// centroids into cscore[sh * C + c]; cluster_select_kernel takes clusters
+// whole in descending score (ties to the lower id) until K - window older
+// positions are covered, the cut cluster giving its lowest positions, and
+// writes them in order followed by the window.
+constexpr int kMaxClusters = 8192;          // clusters per head (LDS sort)
+constexpr int kMaxSelectPositions = 262144; // older positions per head (LDS bitmap)
+
+struct CentroidArgs {
+    const uint16_t *q;              // bf16 [Bmax][Hq][D]
+    const uint16_t *centroids;      // bf16 [Bmax*Hkv][C][D]
+    const int32_t *active, *lengths;
+    const int32_t *cl_start;        // [Bmax*Hkv][C+1] member-list offsets
+    const int32_t *cl_pos;          // [Bmax*Hkv][P] positions, ascending within a cluster
+    float *cscore;                  // [Bmax*Hkv][C]
+    int32_t *idx_out;               // [Bmax*Hkv][K]
+    int32_t *err;                   // latched error word
+    int32_t hkv, lstride, C, P, k, window;
+};
+
 struct AppendArgs {
     uint16_t *k_pool, *v_pool;
     const uint16_t *k_new, *v_new; // [Bmax][Hkv][D]
@@ -126,6 +147,7 @@ hipError_t launch_merge(const MergeArgs &a, int head_dim, int gqa, int n_heads, 
 hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t st);
 hipError_t launch_score(const ScoreArgs &a, int head_dim, int gqa, hipStream_t st);
 hipError_t launch_select(const SelectArgs &a, int n_heads, hipStream_t st);
+hipError_t launch_centroid_select(const CentroidArgs &a, int head_dim, int gqa, int n_heads, hipStream_t st);
 hipError_t launch_gather_index(const GatherIndexArgs &a, int head_dim, hipStream_t st);
 hipError_t launch_gather_runs(const GatherRunsArgs &a, int head_dim, int total_pages, hipStream_t st);
 hipError_t launch_fill(int32_t *p, int n, int32_t value, hipStream_t st);

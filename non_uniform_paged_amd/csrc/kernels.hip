@@ -986,6 +986,198 @@ __global__ __launch_bounds__(256) void sel_write_kernel(SelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Top-K selection through key clusters (KVDrive, Fig 18 / Fig 19 vary the
+// number of centroids).
+//   centroid_score_kernel: one wave per 16 centroids of a head, the q.k
+//     MFMA tile of the score kernel, max over the head's query rows;
+//   cluster_select_kernel: one workgroup per head counts each cluster's
+//     members below L - window (member lists are ascending: a binary
+//     search), sorts the clusters by (score descending, id ascending) in
+//     LDS, finds the cut where the running count reaches K - window, marks
+//     the chosen positions in an LDS bitmap (one wave per cluster) and
+//     writes the bitmap's positions in order, then the window.  Malformed
+//     member lists (offsets out of range, positions out of range or repeated,
+//     too few positions) latch the error word and give -1 entries.
+// ---------------------------------------------------------------------------
+template <int D, int GQA>
+__global__ __launch_bounds__(256) void centroid_score_kernel(CentroidArgs a) {
+    constexpr int NJ = D / 32;
+    constexpr int LPR = D / 8;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sh = blockIdx.y;
+    const int c0 = (blockIdx.x * kWavesPerBlock + wid) * 16;
+    if (c0 >= a.C) return;
+    const int s = sh / a.hkv, h = sh - s * a.hkv;
+    if (!a.active[s]) return;
+    const int qn = lane & 15, qg = lane >> 4;
+    const uint4 *qh = reinterpret_cast<const uint4 *>(
+        a.q + ((size_t)s * a.hkv * GQA + (size_t)h * GQA + (qn < GQA ? qn : 0)) * D);
+    const uint4 *cp = reinterpret_cast<const uint4 *>(a.centroids + (size_t)sh * a.C * D);
+    const size_t row = (size_t)min(c0 + qn, a.C - 1);
+    uint4 kv[NJ], qv[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        kv[j] = ld_stream(cp + row * LPR + 4 * j + qg);
+        qv[j] = qn < GQA ? qh[4 * j + qg] : make_uint4(0, 0, 0, 0);
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv[j]),
+                                                      __builtin_bit_cast(bf16x8_t, qv[j]), acc, 0, 0, 0);
+    float m[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float x = qn < GQA ? acc[i] : -INFINITY;
+        x = fmaxf(x, dpp_f<kRowRor8>(x));
+        x = fmaxf(x, dpp_f<kRowRor4>(x));
+        x = fmaxf(x, dpp_f<kRowRor2>(x));
+        x = fmaxf(x, dpp_f<kRowRor1>(x));
+        m[i] = x;
+    }
+    if (qn == 0) {
+        float *out = a.cscore + (size_t)sh * a.C;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (c0 + 4 * qg + i < a.C) out[c0 + 4 * qg + i] = m[i];
+    }
+}
+
+constexpr int kClThreads = 1024;
+
+__global__ __launch_bounds__(kClThreads) void cluster_select_kernel(CentroidArgs a) {
+    constexpr int kPer = kMaxClusters / kClThreads;
+    constexpr int kWords = kMaxSelectPositions / 32;
+    __shared__ uint64_t order[kMaxClusters];   // (~score key) << 32 | cluster id, sorted ascending
+    __shared__ int32_t cnt[kMaxClusters];      // members below n, by cluster id
+    __shared__ uint32_t bits[kWords];          // chosen older positions
+    __shared__ int scan_lds[40];
+    __shared__ int cut_info[2];
+    __shared__ int bad_lds;
+    const int sh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int s = sh / a.hkv;
+    if (!a.active[s]) return;
+    const int L = a.lengths[s * a.lstride + (sh - s * a.hkv)];
+    const int n = L - a.window, need = a.k - a.window;
+    int32_t *out = a.idx_out + (size_t)sh * a.k;
+    for (int j = tid; j < a.window; j += kClThreads) out[need + j] = n + j;
+    if (need <= 0) return;
+    const float *cs = a.cscore + (size_t)sh * a.C;
+    const int32_t *st = a.cl_start + (size_t)sh * (a.C + 1);
+    const int32_t *ps = a.cl_pos + (size_t)sh * a.P;
+    int np2 = 1;
+    while (np2 < a.C) np2 <<= 1;
+    if (tid == 0) {
+        bad_lds = 0;
+        cut_info[0] = -1;
+        cut_info[1] = 0;
+    }
+    // 1. sort keys; members below n (member offsets must lie in [0, P], in order)
+    for (int c = tid; c < np2; c += kClThreads) {
+        if (c < a.C) {
+            const uint32_t key = order_key(cs[c]);
+            order[c] = ((uint64_t)(~key) << 32) | (uint32_t)c;
+            const int b = st[c], e = st[c + 1];
+            int m = 0;
+            if (b < 0 || e < b || e > a.P) {
+                atomicOr(&bad_lds, 1);
+            } else {
+                int lo = b, hi = e;      // first member >= n
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (ps[mid] < n) lo = mid + 1; else hi = mid;
+                }
+                m = lo - b;
+            }
+            cnt[c] = m;
+        } else {
+            order[c] = ~0ull;
+        }
+    }
+    __syncthreads();
+    // 2. bitonic sort, ascending
+    for (int k2 = 2; k2 <= np2; k2 <<= 1) {
+        for (int j = k2 >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < np2; i += kClThreads) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint64_t x = order[i], y = order[ixj];
+                    if ((x > y) == ((i & k2) == 0)) {
+                        order[i] = y;
+                        order[ixj] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // 3. the cut: first sorted entry at which the running count reaches need
+    int local[kPer], sum = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int i = tid * kPer + u;
+        local[u] = i < a.C ? cnt[(uint32_t)order[i]] : 0;
+        sum += local[u];
+    }
+    int total = 0;
+    int run = block_exclusive_scan<kClThreads>(sum, scan_lds, &total);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        if (run < need && run + local[u] >= need) {
+            cut_info[0] = tid * kPer + u;
+            cut_info[1] = need - run;
+        }
+        run += local[u];
+    }
+    const int words = (n + 31) >> 5;
+    for (int i = tid; i < words; i += kClThreads) bits[i] = 0;
+    __syncthreads();
+    const int cut = cut_info[0], rem = cut_info[1];
+    const bool short_of = total < need || cut < 0;
+    // 4. mark the chosen positions, one wave per cluster
+    if (!short_of && !bad_lds) {
+        for (int i = wid; i <= cut; i += kClThreads / 64) {
+            const int c = (int)(uint32_t)order[i];
+            const int b = st[c];
+            const int m = i < cut ? cnt[c] : rem;
+            for (int e = lane; e < m; e += 64) {
+                const int t = ps[b + e];
+                if (t < 0 || t >= n) {
+                    atomicOr(&bad_lds, 1);
+                } else {
+                    const uint32_t bit = 1u << (t & 31);
+                    if (atomicOr(&bits[t >> 5], bit) & bit) atomicOr(&bad_lds, 1);   // repeated
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const bool bad = short_of || bad_lds != 0;
+    if (bad) {
+        if (tid == 0) atomicOr(a.err, 1);
+        for (int j = tid; j < need; j += kClThreads) out[j] = -1;
+        return;
+    }
+    // 5. the bitmap's positions in order: each thread a contiguous run of words
+    const int wpt = (words + kClThreads - 1) / kClThreads;
+    const int w0 = tid * wpt, w1 = min(words, w0 + wpt);
+    int pc = 0;
+    for (int w = w0; w < w1; ++w) pc += __popc(bits[w]);
+    int tot = 0;
+    int pos = block_exclusive_scan<kClThreads>(pc, scan_lds, &tot);
+    for (int w = w0; w < w1; ++w) {
+        uint32_t x = bits[w];
+        while (x) {
+            const int b = __ffs(x) - 1;
+            x &= x - 1;
+            if (pos < need) out[pos] = w * 32 + b;
+            ++pos;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Append: one token per active (slot, KV head).  2*(D/8) lanes per head: the
 // first half copies the K row, the second the V row, 16 bytes per lane.
 // ---------------------------------------------------------------------------
@@ -1281,6 +1473,31 @@ hipError_t launch_select(const SelectArgs &a, int n_heads, hipStream_t st) {
     hipLaunchKernelGGL(sel_thresh_kernel, dim3(n_heads), dim3(kSelThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(sel_write_kernel, dim3(kSelSplit, n_heads), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int D>
+void *centroid_fn_gqa(int gqa) {
+    switch (gqa) {
+        case 1: return reinterpret_cast<void *>(&centroid_score_kernel<D, 1>);
+        case 2: return reinterpret_cast<void *>(&centroid_score_kernel<D, 2>);
+        case 4: return reinterpret_cast<void *>(&centroid_score_kernel<D, 4>);
+        case 5: return reinterpret_cast<void *>(&centroid_score_kernel<D, 5>);
+        case 8: return reinterpret_cast<void *>(&centroid_score_kernel<D, 8>);
+        default: return nullptr;
+    }
+}
+
+hipError_t launch_centroid_select(const CentroidArgs &a, int head_dim, int gqa, int n_heads, hipStream_t st) {
+    if (n_heads <= 0) return hipSuccess;
+    if (n_heads > 65535 || a.C <= 0 || a.C > kMaxClusters) return hipErrorInvalidValue;
+    void *fn = head_dim == 64 ? centroid_fn_gqa<64>(gqa) : head_dim == 128 ? centroid_fn_gqa<128>(gqa) : nullptr;
+    if (!fn) return hipErrorInvalidValue;
+    CentroidArgs copy = a;
+    const unsigned bx = (unsigned)((a.C + 16 * kWavesPerBlock - 1) / (16 * kWavesPerBlock));
+    hipError_t e = launch_raw(fn, dim3(bx, n_heads), dim3(256), &copy, sizeof(copy), st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(cluster_select_kernel, dim3(n_heads), dim3(kClThreads), 0, st, a);
     return hipGetLastError();
 }
 

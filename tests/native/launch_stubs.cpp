@@ -12,6 +12,7 @@ hipError_t launch_merge(const MergeArgs &, int, int, int, hipStream_t) { return 
 hipError_t launch_append(const AppendArgs &, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_score(const ScoreArgs &, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_select(const SelectArgs &, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_centroid_select(const CentroidArgs &, int, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_gather_index(const GatherIndexArgs &, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_gather_runs(const GatherRunsArgs &, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_fill(int32_t *, int, int32_t, hipStream_t) { return hipSuccess; }

@@ -271,6 +271,26 @@ def topk_indices(lengths: np.ndarray, k: int, salt: int = 4) -> np.ndarray:
     return out
 
 
+def cluster_lists(lengths: np.ndarray, C: int, salt: int = 5):
+    """Member lists for C clusters per (s, h): every position 0..L-1 is
+    assigned to a cluster uniformly at random and each list is ascending.
+    Returns cl_start int32 [B][H][C+1] and cl_pos int32 [B][H][P] with
+    P = max L (unused tail entries are -1)."""
+    g = rng("indices", salt)
+    b, h = lengths.shape
+    P = int(lengths.max())
+    start = np.zeros((b, h, C + 1), np.int32)
+    pos = np.full((b, h, P), -1, np.int32)
+    for s in range(b):
+        for j in range(h):
+            L = int(lengths[s, j])
+            assign = g.integers(0, C, size=L)
+            order = np.argsort(assign, kind="stable")          # ascending positions within a cluster
+            pos[s, j, :L] = order
+            start[s, j, 1:] = np.cumsum(np.bincount(assign, minlength=C))
+    return start, pos
+
+
 def lognormal_lengths(n: int, g: np.random.Generator, median: float = 2048.0,
                       sigma: float = 1.0, lo: int = 16, hi: int = 131072) -> np.ndarray:
     """Mixed request lengths: lognormal with the given median, clipped."""
