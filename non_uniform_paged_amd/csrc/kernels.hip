@@ -992,10 +992,11 @@ __global__ __launch_bounds__(256) void sel_write_kernel(SelectArgs a) {
 //     MFMA tile of the score kernel, max over the head's query rows;
 //   cluster_select_kernel: one workgroup per head counts each cluster's
 //     members below L - window (member lists are ascending: a binary
-//     search), sorts the clusters by (score descending, id ascending) in
-//     LDS, finds the cut where the running count reaches K - window, marks
-//     the chosen positions in an LDS bitmap (one wave per cluster) and
-//     writes the bitmap's positions in order, then the window.  Malformed
+//     search), finds by a radix select weighted with those counts the score
+//     key T at which the running count from the top reaches K - window,
+//     takes the clusters above T whole and those at T in id order (the
+//     last partly), marks the chosen positions in an LDS bitmap (one wave
+//     per cluster) and writes them in order, then the window.  Malformed
 //     member lists (offsets out of range, positions out of range or repeated,
 //     too few positions) latch the error word and give -1 entries.
 // ---------------------------------------------------------------------------
@@ -1049,10 +1050,13 @@ constexpr int kClThreads = 1024;
 __global__ __launch_bounds__(kClThreads) void cluster_select_kernel(CentroidArgs a) {
     constexpr int kPer = kMaxClusters / kClThreads;
     constexpr int kWords = kMaxSelectPositions / 32;
-    __shared__ uint64_t order[kMaxClusters];   // (~score key) << 32 | cluster id, sorted ascending
+    __shared__ uint32_t ckey[kMaxClusters];    // order key of each cluster's score
     __shared__ int32_t cnt[kMaxClusters];      // members below n, by cluster id
+    __shared__ int32_t take[kMaxClusters];     // members to take, by cluster id
     __shared__ uint32_t bits[kWords];          // chosen older positions
+    __shared__ uint32_t hist[256 + 8];         // digit weights (padded bins)
     __shared__ int scan_lds[40];
+    __shared__ uint32_t pick[2];
     __shared__ int cut_info[2];
     __shared__ int bad_lds;
     const int sh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -1066,81 +1070,93 @@ __global__ __launch_bounds__(kClThreads) void cluster_select_kernel(CentroidArgs
     const float *cs = a.cscore + (size_t)sh * a.C;
     const int32_t *st = a.cl_start + (size_t)sh * (a.C + 1);
     const int32_t *ps = a.cl_pos + (size_t)sh * a.P;
-    int np2 = 1;
-    while (np2 < a.C) np2 <<= 1;
     if (tid == 0) {
         bad_lds = 0;
         cut_info[0] = -1;
         cut_info[1] = 0;
     }
-    // 1. sort keys; members below n (member offsets must lie in [0, P], in order)
-    for (int c = tid; c < np2; c += kClThreads) {
-        if (c < a.C) {
-            const uint32_t key = order_key(cs[c]);
-            order[c] = ((uint64_t)(~key) << 32) | (uint32_t)c;
-            const int b = st[c], e = st[c + 1];
-            int m = 0;
-            if (b < 0 || e < b || e > a.P) {
-                atomicOr(&bad_lds, 1);
-            } else {
-                int lo = b, hi = e;      // first member >= n
-                while (lo < hi) {
+    // 1. keys; members below n (member offsets must lie in [0, P], in order)
+    int mine = 0;
+    for (int c = tid; c < a.C; c += kClThreads) {
+        ckey[c] = order_key(cs[c]);
+        const int b = st[c], e = st[c + 1];
+        int m = 0;
+        if (b < 0 || e < b || e > a.P) {
+            atomicOr(&bad_lds, 1);
+        } else {
+            // members at or past n are the window's, at the end of the
+            // ascending list: step back a few, then search what is left
+            int hi = e;
+            for (int k = 0; k < 4 && hi > b && ps[hi - 1] >= n; ++k) --hi;
+            int lo = b;
+            if (hi > b && ps[hi - 1] >= n) {
+                while (lo < hi) {    // first member >= n
                     const int mid = (lo + hi) >> 1;
                     if (ps[mid] < n) lo = mid + 1; else hi = mid;
                 }
-                m = lo - b;
+            } else {
+                lo = hi;
             }
-            cnt[c] = m;
-        } else {
-            order[c] = ~0ull;
+            m = lo - b;
         }
+        cnt[c] = m;
+        take[c] = 0;
+        mine += m;
     }
-    __syncthreads();
-    // 2. bitonic sort, ascending
-    for (int k2 = 2; k2 <= np2; k2 <<= 1) {
-        for (int j = k2 >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < np2; i += kClThreads) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint64_t x = order[i], y = order[ixj];
-                    if ((x > y) == ((i & k2) == 0)) {
-                        order[i] = y;
-                        order[ixj] = x;
-                    }
-                }
-            }
+    int total = 0;
+    block_exclusive_scan<kClThreads>(mine, scan_lds, &total);
+    const bool short_of = total < need;
+    // 2. weighted radix select: the key T of the cluster that crosses `need`
+    //    when clusters are counted from the highest score down; `remaining`
+    //    is what the clusters scoring exactly T must still give
+    uint32_t prefix = 0, mask = 0;
+    int remaining = need;
+    if (!short_of && !bad_lds) {
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256 + 8; i += kClThreads) hist[i] = 0;
+            __syncthreads();
+            for (int c = tid; c < a.C; c += kClThreads)
+                if ((ckey[c] & mask) == prefix && cnt[c] > 0)
+                    atomicAdd(&hist[padb((ckey[c] >> shift) & 255u)], (uint32_t)cnt[c]);
+            __syncthreads();
+            if (tid < 64) find_digit<256>(hist, remaining, pick);
+            __syncthreads();
+            prefix |= pick[0] << shift;
+            mask |= 255u << shift;
+            remaining = (int)pick[1];
             __syncthreads();
         }
     }
-    // 3. the cut: first sorted entry at which the running count reaches need
-    int local[kPer], sum = 0;
+    const uint32_t T = prefix;
+    // 3. clusters above T are taken whole; those at T in ascending id order
+    //    until `remaining` is covered (the last one partly).  Each thread
+    //    looks at a contiguous run of ids so the order is the thread order.
+    int tie_w[kPer], tsum = 0;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-        const int i = tid * kPer + u;
-        local[u] = i < a.C ? cnt[(uint32_t)order[i]] : 0;
-        sum += local[u];
+        const int c = tid * kPer + u;
+        const bool ok = !short_of && c < a.C;
+        tie_w[u] = ok && ckey[c] == T ? cnt[c] : 0;
+        if (ok && ckey[c] > T) take[c] = cnt[c];
+        tsum += tie_w[u];
     }
-    int total = 0;
-    int run = block_exclusive_scan<kClThreads>(sum, scan_lds, &total);
+    int tie_total = 0;
+    int run = block_exclusive_scan<kClThreads>(tsum, scan_lds, &tie_total);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-        if (run < need && run + local[u] >= need) {
-            cut_info[0] = tid * kPer + u;
-            cut_info[1] = need - run;
-        }
-        run += local[u];
+        const int c = tid * kPer + u;
+        if (tie_w[u] > 0 && run < remaining) take[c] = min(tie_w[u], remaining - run);
+        run += tie_w[u];
     }
     const int words = (n + 31) >> 5;
     for (int i = tid; i < words; i += kClThreads) bits[i] = 0;
     __syncthreads();
-    const int cut = cut_info[0], rem = cut_info[1];
-    const bool short_of = total < need || cut < 0;
     // 4. mark the chosen positions, one wave per cluster
     if (!short_of && !bad_lds) {
-        for (int i = wid; i <= cut; i += kClThreads / 64) {
-            const int c = (int)(uint32_t)order[i];
+        for (int c = wid; c < a.C; c += kClThreads / 64) {
+            const int m = take[c];
+            if (m <= 0) continue;
             const int b = st[c];
-            const int m = i < cut ? cnt[c] : rem;
             for (int e = lane; e < m; e += 64) {
                 const int t = ps[b + e];
                 if (t < 0 || t >= n) {
