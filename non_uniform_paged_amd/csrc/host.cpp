@@ -1131,12 +1131,15 @@ nup_status attn_decode_topk_paged(nup_ctx *c, const void *q, const int32_t *idx,
 // Selection workspace: scores [heads][max_pages*P] fp32, then the select
 // kernels' histogram [heads][kSelBins], thresholds [heads][2] and per-slice
 // counts [heads][kSelSplit][2].
-struct SelectWs { size_t hist, thr, cnt, total; };
+struct SelectWs { size_t hist, ckey, cpos, sgt, thr, cnt, total; };
 static SelectWs select_ws(const nup_ctx *c) {
     const size_t heads = (size_t)c->B * c->H;
     SelectWs w;
     w.hist = align_up(heads * (size_t)c->max_pages * nup::kPage * 4);
-    w.thr = w.hist + align_up(heads * nup::kSelBins * 4);
+    w.ckey = w.hist + align_up(heads * nup::kSelHistStride * 4);
+    w.cpos = w.ckey + align_up(heads * nup::kSelCap * 4);
+    w.sgt = w.cpos + align_up(heads * nup::kSelCap * 4);
+    w.thr = w.sgt + align_up(heads * nup::kSelSplit * 4);
     w.cnt = w.thr + align_up(heads * 2 * 4);
     w.total = w.cnt + align_up(heads * nup::kSelSplit * 2 * 4);
     return w;
@@ -1190,6 +1193,9 @@ nup_status kv_select_topk(nup_ctx *c, const void *q, int32_t K, int32_t window, 
     nup::SelectArgs sl{};
     sl.scores = sa.scores;
     sl.hist = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + sw.hist);
+    sl.cand_key = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + sw.ckey);
+    sl.cand_pos = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + sw.cpos);
+    sl.slice_gt = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + sw.sgt);
     sl.thr = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + sw.thr);
     sl.cnt = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + sw.cnt);
     sl.active = c->d_active();

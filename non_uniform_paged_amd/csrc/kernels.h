@@ -69,12 +69,13 @@ struct MergeArgs {
 constexpr int kSelBins = 2048;      // histogram of the top 11 key bits
 constexpr int kSelSplit = 16;       // slices (workgroups) per head in the parallel select kernels
 constexpr int kSelCap = 8192;       // threshold-bin entries the select keeps in LDS
+constexpr int kSelHistStride = kSelBins + 64;   // a head's histogram row; word kSelBins counts candidates
 
 struct ScoreArgs {
     const uint16_t *q, *kbase;
     const int32_t *page_table, *lengths, *group_of_head, *slot_of_head, *rows, *worker_start;
     float *scores;
-    uint32_t *hist;             // [heads][kSelBins]: cleared by each head's first row (or NULL)
+    uint32_t *hist;             // [heads][kSelHistStride]: cleared by each head's first row (or NULL)
     int32_t bmax, hkv, gh, max_pages, n_workers, stride, lstride;
 };
 
@@ -82,7 +83,10 @@ struct SelectArgs {
     const float *scores;
     const int32_t *active, *lengths;
     int32_t *idx_out;              // [Bmax*Hkv][K]
-    uint32_t *hist;                // [heads][kSelBins], zeroed by the launcher
+    uint32_t *hist;                // [heads][kSelHistStride]: bins, then the candidate count
+    uint32_t *cand_key;            // [heads][kSelCap]: entries of the threshold's top bin
+    int32_t *cand_pos;             // [heads][kSelCap]
+    int32_t *slice_gt;             // [heads][kSelSplit]: entries above the threshold's top bin
     int32_t *thr;                  // [heads][2]: threshold key, ties taken
     int32_t *cnt;                  // [heads][kSelSplit][2]: per slice, above and equal
     int32_t hkv, stride, k, window, lstride;

@@ -538,8 +538,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         const int t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + ld_uniform(a.rows + row * 4 + 3)));
         if (t0 == 0 && a.hist) {
             // the head's first row clears its histogram for the select kernels
-            uint4 *hz = reinterpret_cast<uint4 *>(a.hist + (size_t)sh * kSelBins);
-            for (int i = lane; i < kSelBins / 4; i += 64) hz[i] = make_uint4(0, 0, 0, 0);
+            uint4 *hz = reinterpret_cast<uint4 *>(a.hist + (size_t)sh * kSelHistStride);
+            for (int i = lane; i < kSelHistStride / 4; i += 64) hz[i] = make_uint4(0, 0, 0, 0);
         }
         if (t0 >= t1) continue;
         const int s = sh / a.hkv, h = sh - s * a.hkv;
@@ -622,12 +622,14 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 // among its older positions, then write the chosen positions in order.
 //   sel_hist_kernel:   kSelSplit workgroups per head histogram the top 11
 //                      key bits of their slice into a global histogram;
-//   sel_thresh_kernel: one workgroup per head finds the bin holding the
-//                      threshold, gathers that bin's entries into LDS and
-//                      finishes the radix select there (passes over the
-//                      scores instead when the bin does not fit), then
-//                      counts per slice the entries above the threshold and
-//                      equal to it;
+//   sel_collect_kernel: kSelSplit workgroups per head find the bin holding
+//                      the threshold, count their slice's entries above it
+//                      and append the bin's entries to a candidate list;
+//   sel_thresh_kernel: one workgroup per head finishes the radix select over
+//                      the candidates in LDS (passes over the scores instead
+//                      when the bin holds more than kSelCap), then counts
+//                      per slice the entries above the threshold and equal
+//                      to it;
 //   sel_write_kernel:  kSelSplit workgroups per head write their slice's
 //                      chosen positions in order, offset by the counts of
 //                      the slices before them.
@@ -757,11 +759,105 @@ __global__ __launch_bounds__(256) void sel_hist_kernel(SelectArgs a) {
     }
     for (int t = e4 + tid; t < e; t += 256) atomicAdd(&hist[wid][order_key(sc[t]) >> kSelShift], 1u);
     __syncthreads();
-    uint32_t *g = a.hist + (size_t)sh * kSelBins;
+    uint32_t *g = a.hist + (size_t)sh * kSelHistStride;
     for (int i = tid; i < kSelBins; i += 256) {
         const uint32_t v = hist[0][i] + hist[1][i] + hist[2][i] + hist[3][i];
         if (v) atomicAdd(g + i, v);
     }
+}
+
+// kSelSplit workgroups per head: each finds the threshold's top bin d1 from
+// the finished histogram, counts its slice's entries above d1 and appends the
+// slice's entries in d1 to the head's candidate list (one atomic per wave).
+__global__ __launch_bounds__(256) void sel_collect_kernel(SelectArgs a) {
+    __shared__ uint32_t bins[kSelBins + kSelBins / 32];
+    __shared__ uint32_t pick[2];
+    __shared__ int gt_lds;
+    const int sh = blockIdx.y, j = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    int n, k, cs;
+    if (!sel_head(a, sh, n, k, cs) || k <= 0) return;
+    const int b = j * cs, e = min(n, b + cs);
+    int32_t *sgt = a.slice_gt + (size_t)sh * kSelSplit + j;
+    if (b >= e) {
+        if (tid == 0) *sgt = 0;
+        return;
+    }
+    const uint32_t *row = a.hist + (size_t)sh * kSelHistStride;
+    for (int i = tid; i < kSelBins; i += 256) bins[padb(i)] = row[i];
+    if (tid == 0) gt_lds = 0;
+    __syncthreads();
+    if (tid < 64) find_digit<kSelBins>(bins, k, pick);
+    __syncthreads();
+    const uint32_t d1 = pick[0];
+    uint32_t *ncand = const_cast<uint32_t *>(row) + kSelBins;
+    uint32_t *ck = a.cand_key + (size_t)sh * kSelCap;
+    int32_t *cp = a.cand_pos + (size_t)sh * kSelCap;
+    const float *sc = a.scores + (size_t)sh * a.stride;
+    const int e4 = b + ((e - b) & ~3);
+    int gt = 0;
+    for (int t0 = b + 4 * tid; t0 - 4 * tid < e4; t0 += 4 * 256 * kSelUnroll) {
+        float4 v[kSelUnroll];
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+            const int t = t0 + u * 4 * 256;
+            v[u] = t < e4 ? *reinterpret_cast<const float4 *>(sc + t) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+            if (t0 - 4 * tid + u * 4 * 256 >= e4) break;      // uniform
+            const int t = t0 + u * 4 * 256;
+            uint32_t key[4];
+            bool in_bin[4];
+            const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                key[q] = order_key(f[q]);
+                const uint32_t top = key[q] >> kSelShift;
+                gt += t < e4 && top > d1;
+                in_bin[q] = t < e4 && top == d1;
+            }
+            uint64_t m[4];
+            int before[4], tot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                m[q] = __builtin_amdgcn_ballot_w64(in_bin[q]);
+                before[q] = tot;
+                tot += __popcll(m[q]);
+            }
+            if (tot) {
+                int base = 0;
+                if (lane == 0) base = (int)atomicAdd(ncand, (uint32_t)tot);
+                base = __shfl(base, 0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (!in_bin[q]) continue;
+                    const int p = base + before[q] +
+                                  (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[q] >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m[q], 0u));
+                    if (p < kSelCap) {
+                        ck[p] = key[q];
+                        cp[p] = t + q;
+                    }
+                }
+            }
+        }
+    }
+    for (int t = e4 + tid; t < e; t += 256) {
+        const uint32_t key = order_key(sc[t]);
+        const uint32_t top = key >> kSelShift;
+        gt += top > d1;
+        if (top == d1) {
+            const int p = (int)atomicAdd(ncand, 1u);
+            if (p < kSelCap) {
+                ck[p] = key;
+                cp[p] = t;
+            }
+        }
+    }
+    gt = wave_sum(gt);
+    if (lane == 0 && gt) atomicAdd(&gt_lds, gt);
+    __syncthreads();
+    if (tid == 0) *sgt = gt_lds;
 }
 
 __global__ __launch_bounds__(kSelThreads) void sel_thresh_kernel(SelectArgs a) {
@@ -769,21 +865,15 @@ __global__ __launch_bounds__(kSelThreads) void sel_thresh_kernel(SelectArgs a) {
     __shared__ uint32_t cand_key[kSelCap];
     __shared__ int32_t cand_pos[kSelCap];
     __shared__ int slice_gt[kSelSplit], slice_eq[kSelSplit];
-    __shared__ int ncand;
     __shared__ uint32_t pick[2];
-    const int sh = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int sh = blockIdx.x, tid = threadIdx.x;
     int n, k, cs;
     if (!sel_head(a, sh, n, k, cs) || k <= 0) return;
     const float *sc = a.scores + (size_t)sh * a.stride;
-    const int n4 = n & ~3;
 
     // 1. the first digit, from the global histogram
-    for (int i = tid; i < kSelBins; i += kSelThreads) bins[padb(i)] = a.hist[(size_t)sh * kSelBins + i];
-    if (tid < kSelSplit) {
-        slice_gt[tid] = 0;
-        slice_eq[tid] = 0;
-    }
-    if (tid == 0) ncand = 0;
+    for (int i = tid; i < kSelBins; i += kSelThreads) bins[padb(i)] = a.hist[(size_t)sh * kSelHistStride + i];
+    if (tid < kSelSplit) slice_eq[tid] = 0;
     __syncthreads();
     if (tid < 64) find_digit<kSelBins>(bins, k, pick);
     __syncthreads();
@@ -791,75 +881,21 @@ __global__ __launch_bounds__(kSelThreads) void sel_thresh_kernel(SelectArgs a) {
     int remaining = (int)pick[1];
     __syncthreads();
 
-    // 2. one pass over the scores: per slice, the entries above bin d1; the
-    //    entries in bin d1 go to LDS (while they fit)
-    for (int t0 = 4 * tid; t0 - 4 * tid < n4; t0 += 4 * kSelThreads * kSelUnroll) {
-        float4 v[kSelUnroll];
-#pragma unroll
-        for (int u = 0; u < kSelUnroll; ++u) {
-            const int t = t0 + u * 4 * kSelThreads;
-            v[u] = t < n4 ? *reinterpret_cast<const float4 *>(sc + t) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int u = 0; u < kSelUnroll; ++u) {
-            const int step = t0 - 4 * tid + u * 4 * kSelThreads;   // uniform: inside one slice
-            if (step >= n4) break;
-            const int t = t0 + u * 4 * kSelThreads;
-            int gt = 0;
-            uint32_t key[4];
-            bool in_bin[4];
-            const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                key[e] = order_key(f[e]);
-                const uint32_t top = key[e] >> kSelShift;
-                gt += t < n4 && top > d1;
-                in_bin[e] = t < n4 && top == d1;
-            }
-            // the wave appends its bin entries with one LDS atomic
-            uint64_t m[4];
-            int before[4], tot = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                m[e] = __builtin_amdgcn_ballot_w64(in_bin[e]);
-                before[e] = tot;
-                tot += __popcll(m[e]);
-            }
-            if (tot) {
-                int base = 0;
-                if (lane == 0) base = atomicAdd(&ncand, tot);
-                base = __shfl(base, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (!in_bin[e]) continue;
-                    const int p = base + before[e] +
-                                  (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], 0u));
-                    if (p < kSelCap) {
-                        cand_key[p] = key[e];
-                        cand_pos[p] = t + e;
-                    }
-                }
-            }
-            gt = wave_sum(gt);
-            if (lane == 0 && gt) atomicAdd(&slice_gt[step / cs], gt);
-        }
-    }
-    for (int t = n4 + tid; t < n; t += kSelThreads) {
-        const uint32_t key = order_key(sc[t]);
-        const uint32_t top = key >> kSelShift;
-        if (top > d1) atomicAdd(&slice_gt[t / cs], 1);
-        if (top == d1) {
-            const int p = atomicAdd(&ncand, 1);
-            if (p < kSelCap) {
-                cand_key[p] = key;
-                cand_pos[p] = t;
-            }
-        }
-    }
-    __syncthreads();
-    const int nc = ncand;
+    // 2. the candidates sel_collect_kernel gathered (the entries in bin d1)
+    //    and its per-slice counts above d1
+    const uint32_t *row = a.hist + (size_t)sh * kSelHistStride;
+    const int nc = (int)row[kSelBins];
     const bool in_lds = nc <= kSelCap;
+    if (in_lds) {
+        const uint32_t *ck = a.cand_key + (size_t)sh * kSelCap;
+        const int32_t *cp = a.cand_pos + (size_t)sh * kSelCap;
+        for (int i = tid; i < nc; i += kSelThreads) {
+            cand_key[i] = ck[i];
+            cand_pos[i] = cp[i];
+        }
+    }
+    if (tid < kSelSplit) slice_gt[tid] = a.slice_gt[(size_t)sh * kSelSplit + tid];
+    __syncthreads();
 
     // 3. the remaining 21 bits: an 11-bit digit, then a 10-bit one, over the
     //    bin's entries (in LDS, or re-read from the scores)
@@ -1482,10 +1518,13 @@ hipError_t launch_score(const ScoreArgs &a, int head_dim, int gqa, hipStream_t s
 hipError_t launch_select(const SelectArgs &a, int n_heads, hipStream_t st) {
     if (n_heads <= 0) return hipSuccess;
     if ((long long)n_heads * kSelBins > 0x7fffffffLL || n_heads > 65535) return hipErrorInvalidValue;
-    // the histogram was cleared by the score kernel (first row of each head)
+    // the histogram and candidate count were cleared by the score kernel
+    // (first row of each head)
     hipLaunchKernelGGL(sel_hist_kernel, dim3(kSelSplit, n_heads), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sel_collect_kernel, dim3(kSelSplit, n_heads), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(sel_thresh_kernel, dim3(n_heads), dim3(kSelThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(sel_write_kernel, dim3(kSelSplit, n_heads), dim3(256), 0, st, a);
