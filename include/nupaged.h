@@ -188,7 +188,13 @@ nup_status kv_free_seqs(nup_ctx *ctx, int32_t n, const int32_t *slots);
  * shadow (activity, lengths, and when they changed: the split-K plan, the
  * trains and page-table row patches) into the arena, then, if rows changed,
  * one small kernel that applies the patches.  Kernels enqueued earlier on
- * the stream see the previous descriptor.  Errors: NUP_E_STATE, NUP_E_HIP. */
+ * the stream see the previous descriptor.  Every kernel argument the
+ * library derives from the descriptor (plan, lengths and page-table
+ * addresses, worker counts) is the same after every commit of a context, so
+ * a decode step captured into a HIP graph once stays valid while commits
+ * between its replays change the mapping (KV-RM, abstract and Fig 2: a
+ * fixed-shape decoder over a per-step descriptor).  Always eager: refused
+ * with NUP_E_STATE on a capturing stream.  Errors: NUP_E_STATE, NUP_E_HIP. */
 nup_status nup_commit(nup_ctx *ctx, void *stream);
 
 /*
@@ -201,8 +207,25 @@ nup_status nup_commit(nup_ctx *ctx, void *stream);
  *                  layer's heads advance.
  * Requires a committed descriptor (NUP_E_STATE if edits are pending).
  * NUP_E_CAPACITY, checked on the host before launch, if any active head
- * has L == cap (a fixed budget is never exceeded; nothing is written). */
+ * has L == cap (a fixed budget is never exceeded; nothing is written).
+ * On a stream under graph capture the call only records the launch: the
+ * host check and the shadow's advance are skipped, since the kernel runs at
+ * each replay.  The kernel itself drops the token of a head at L == cap and
+ * latches NUP_E_CAPACITY for nup_device_errors(); the other heads advance.
+ * Report the replays with nup_note_appends before the next edit. */
 nup_status kv_append(nup_ctx *ctx, const void *k_new, const void *v_new, void *stream);
+
+/*
+ * nup_note_appends -- bring the shadow lengths up to date after `steps`
+ * replays of a graph that holds kv_append for `layer` (-1: every layer):
+ * each active head of those layers advances by steps, stopping at its
+ * budget exactly as the replayed kernel did.  Host only.  Call it after
+ * the replays and before any Reserve / Alias / Trim, since the next commit
+ * sends the shadow lengths to the device.  NUP_E_CAPACITY if a head
+ * reached its budget (the lengths are still updated, matching the
+ * device); NUP_E_STATE if edits are pending; NUP_E_ARG on a bad layer or
+ * steps < 0. */
+nup_status nup_note_appends(nup_ctx *ctx, int32_t layer, int32_t steps);
 
 /*
  * kv_gather_compact -- copy cache rows into contiguous staging (KV-RM,
@@ -383,12 +406,14 @@ nup_status nup_get_plan(const nup_ctx *ctx, int32_t *n_rows, int32_t *n_workers,
 /* When enabled, the library brackets each split-K partial-attention launch
  * with HIP events on the caller's stream; nup_kernel_time() returns the
  * summed milliseconds and launch count since the last reset (synchronises
- * on the recorded events). */
+ * on the recorded events).  Launches recorded into a graph are not timed. */
 nup_status nup_set_timing(nup_ctx *ctx, int32_t enable);
 nup_status nup_kernel_time(nup_ctx *ctx, double *partial_ms, int32_t *launches, int32_t reset);
 
 /* Read and clear the latched device error word (synchronises the stream).
- * *code receives NUP_OK or NUP_E_INDEX. */
+ * *code receives NUP_OK, NUP_E_INDEX (a bad top-K index or cluster list) or
+ * NUP_E_CAPACITY (a replayed append found a head at its budget), the
+ * former when both were latched. */
 nup_status nup_device_errors(nup_ctx *ctx, void *stream, int32_t *code);
 
 /* Plain streaming copy of `bytes` (a multiple of 16) from src to dst with

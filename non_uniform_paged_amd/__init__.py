@@ -75,6 +75,7 @@ _sigs = {
     "kv_select_topk_centroids": [_P, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _S, _P],
     "nup_centroid_workspace_bytes": [_P, _I, _P],
     "nup_set_layer": [_P, _I],
+    "nup_note_appends": [_P, _I, _I],
     "nup_get_runs": [_P, _P, _I, _P],
     "nup_get_plan": [_P, _P, _P, _P, _P, _P],
     "nup_set_timing": [_P, _I],
@@ -329,6 +330,13 @@ def get_free_list(ctx: Context) -> np.ndarray:
 def set_layer(ctx: Context, layer: int):
     """Choose the layer the per-layer calls act on."""
     ctx.check(_lib.nup_set_layer(ctx.handle, int(layer)))
+
+
+def note_appends(ctx: Context, steps: int, layer: int = -1):
+    """Advance the host's lengths by `steps` replayed appends of `layer`
+    (-1: all layers); raises NupError(NUP_E_CAPACITY) if a head hit its
+    budget, after updating the lengths as the device did."""
+    ctx.check(_lib.nup_note_appends(ctx.handle, int(layer), int(steps)))
 
 
 def get_refcounts(ctx: Context) -> np.ndarray:

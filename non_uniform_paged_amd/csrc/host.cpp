@@ -36,7 +36,9 @@ size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 // Byte sizes of the packed descriptor sections, all int32 words.
 struct Sizes {
     size_t fixed;        // active[B] lengths[B*V] goh[V] soh[V] head_of_gslot[V] (V = layers*H)
+    size_t caps;         // cap[B*V], sent with the plan (both change only on Reserve / Alias / Trim)
     size_t plan_max;     // per layer: worker_start[W+1] head_row_start[B*H+1] rows[R][4]
+    size_t plan_layer;   // one layer's plan section (each layer's sits at a fixed offset)
     size_t runs_max;     // runs[N][4] run_prefix[N+1]
     size_t patches_max;  // hdr[ng*B][4] data[ng*B*max_pages]
     size_t inbox;        // fixed + plan_max + runs_max + patches_max (aligned)
@@ -87,14 +89,16 @@ Sizes compute_sizes(const nup_config &c, int workers) {
         z.max_workers = workers;
     }
     z.fixed = align_up(4 * (B + B * V + 3 * V));
-    z.plan_max = NL * (align_up(4 * ((size_t)z.max_workers + 1)) + align_up(4 * (B * H + 1)) +
-                       align_up(16 * (size_t)z.max_rows));
+    z.caps = align_up(4 * B * V);
+    z.plan_layer = align_up(4 * ((size_t)z.max_workers + 1)) + align_up(4 * (B * H + 1)) +
+                   align_up(16 * (size_t)z.max_rows);
+    z.plan_max = NL * z.plan_layer;
     // every train covers at least one live page-table entry; with Alias the
     // entries (not the physical pages) are what bounds their number
     const size_t entries = ng * B * (size_t)c.max_pages;
     z.runs_max = align_up(16 * entries) + align_up(4 * (entries + 1));
     z.patches_max = align_up(16 * ng * B) + align_up(4 * ng * B * (size_t)c.max_pages);
-    z.inbox = z.fixed + z.plan_max + z.runs_max + z.patches_max;
+    z.inbox = z.fixed + z.caps + z.plan_max + z.runs_max + z.patches_max;
     z.pt = align_up(4 * ng * B * (size_t)c.max_pages);
     z.err = kAlign;
     z.total = z.inbox + z.pt + z.err;
@@ -199,6 +203,7 @@ struct nup_ctx {
     int32_t *d_goh() { return inbox_i32(4 * ((size_t)B + (size_t)B * V)); }
     int32_t *d_soh() { return d_goh() + V; }
     int32_t *d_hog() { return d_goh() + 2 * V; }
+    int32_t *d_cap() { return inbox_i32(sz.fixed); }
     // this layer's view of the per-head arrays (rows of lengths are V apart)
     size_t lbase() const { return (size_t)layer * H; }
     int32_t *d_pt() { return reinterpret_cast<int32_t *>(desc + sz.inbox); }
@@ -215,6 +220,11 @@ nup_status fail(nup_ctx *c, nup_status st, const char *fmt, ...) {
     va_end(ap);
     c->err = buf;
     return st;
+}
+
+bool capturing(hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
 }
 
 nup_status hip_fail(nup_ctx *c, hipError_t e, const char *what) {
@@ -525,9 +535,17 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
     c->soh.assign(c->V, -1);
     c->head_of_gslot.assign(c->V, -1);
     c->plan.assign(c->NL, {});
+    // each layer's plan at a fixed place in the inbox, so that the kernels'
+    // plan pointers never change for a context (a captured decode graph
+    // stays valid across commits)
     c->off_ws.assign(c->NL, 0);
     c->off_hrs.assign(c->NL, 0);
     c->off_rows.assign(c->NL, 0);
+    for (int l = 0; l < c->NL; ++l) {
+        c->off_ws[l] = c->sz.fixed + c->sz.caps + (size_t)l * c->sz.plan_layer;
+        c->off_hrs[l] = c->off_ws[l] + align_up(4 * ((size_t)c->sz.max_workers + 1));
+        c->off_rows[l] = c->off_hrs[l] + align_up(4 * ((size_t)c->B * c->H + 1));
+    }
     c->dev_workers.assign(c->NL, 0);
     c->dev_rows.assign(c->NL, 0);
     c->dirty_count.assign((size_t)c->ng * c->B, 0);
@@ -722,6 +740,9 @@ nup_status nup_commit(nup_ctx *c, void *stream) {
     if (!c) return NUP_E_ARG;
     if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // a captured copy would replay this call's staging buffer, which later
+    // commits rewrite: the commit always runs eagerly, between replays
+    if (capturing(st)) return fail(c, NUP_E_STATE, "nup_commit cannot be captured into a graph");
     // Nothing edited since the last commit: the device already holds this
     // frame (appends advance the device lengths themselves), so the commit
     // sends nothing.
@@ -749,24 +770,25 @@ nup_status nup_commit(nup_ctx *c, void *stream) {
     int n_patches = 0;
     size_t off_hdr = 0, off_data = 0;
     if (c->plan_dirty || !c->committed) {
+        int32_t *cw = reinterpret_cast<int32_t *>(blob + c->sz.fixed);
+        for (size_t k = 0; k < B * V; ++k) cw[k] = c->active[k / V] ? c->cap[k] : 0;
         // plan (once per commit, however many Reserve / Trim edits came before)
         replan(c);
-        size_t off = used;
         for (int l = 0; l < c->NL; ++l) {
             const nup_ctx::Plan &pl = c->plan[l];
             const int nr = (int)(pl.rows.size() / 4);
-            c->off_ws[l] = off;
-            std::memcpy(blob + off, pl.worker_start.data(), 4 * pl.worker_start.size());
-            off = align_up(off + 4 * pl.worker_start.size());
-            c->off_hrs[l] = off;
-            std::memcpy(blob + off, pl.head_row_start.data(), 4 * pl.head_row_start.size());
-            off = align_up(off + 4 * pl.head_row_start.size());
-            c->off_rows[l] = off;
-            if (nr) std::memcpy(blob + off, pl.rows.data(), 16 * (size_t)nr);
-            off = align_up(off + 16 * (size_t)nr);
-            c->dev_workers[l] = (int)pl.worker_start.size() - 1;
+            int32_t *wsd = reinterpret_cast<int32_t *>(blob + c->off_ws[l]);
+            std::memcpy(wsd, pl.worker_start.data(), 4 * pl.worker_start.size());
+            // the launch always has max_workers workers (the balanced plan
+            // has exactly that many; the uniform one's surplus get no rows),
+            // so a captured launch stays valid when the plan changes
+            for (size_t w = pl.worker_start.size(); w <= (size_t)c->sz.max_workers; ++w) wsd[w] = nr;
+            std::memcpy(blob + c->off_hrs[l], pl.head_row_start.data(), 4 * pl.head_row_start.size());
+            if (nr) std::memcpy(blob + c->off_rows[l], pl.rows.data(), 16 * (size_t)nr);
+            c->dev_workers[l] = c->sz.max_workers;
             c->dev_rows[l] = nr;
         }
+        size_t off = c->sz.fixed + c->sz.caps + c->sz.plan_max;
         // trains
         std::vector<int32_t> runs5;
         build_runs(c, runs5);
@@ -841,7 +863,8 @@ nup_status kv_append(nup_ctx *c, const void *k_new, const void *v_new, void *str
     if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
     if (!k_new || !v_new) return fail(c, NUP_E_ARG, "k_new and v_new are required");
     if (!c->committed || c->pending) return fail(c, NUP_E_STATE, "edits pending: nup_commit first");
-    for (int s = 0; s < c->B; ++s) {
+    const bool cap_mode = capturing(static_cast<hipStream_t>(stream));
+    for (int s = 0; s < c->B && !cap_mode; ++s) {
         if (!c->active[s]) continue;
         for (int h = 0; h < c->H; ++h) {
             const size_t k = (size_t)s * c->V + c->lbase() + h;
@@ -860,6 +883,8 @@ nup_status kv_append(nup_ctx *c, const void *k_new, const void *v_new, void *str
     a.group_of_head = c->d_goh() + c->lbase();
     a.slot_of_head = c->d_soh() + c->lbase();
     a.lengths = c->d_len() + c->lbase();
+    a.caps = c->d_cap() + c->lbase();
+    a.err = c->d_err();
     a.bmax = c->B;
     a.hkv = c->H;
     a.gh = c->gh;
@@ -867,6 +892,9 @@ nup_status kv_append(nup_ctx *c, const void *k_new, const void *v_new, void *str
     a.lstride = c->V;
     hipError_t e = nup::launch_append(a, c->D, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(c, e, "append launch");
+    // a captured append runs at each replay, after this call: the caller
+    // reports the replays with nup_note_appends
+    if (cap_mode) return NUP_OK;
     for (int s = 0; s < c->B; ++s)
         if (c->active[s])
             for (int h = 0; h < c->H; ++h) c->len[(size_t)s * c->V + c->lbase() + h]++;
@@ -1081,14 +1109,15 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
     a.head_row_start = topk ? nullptr : c->inbox_i32(c->off_hrs[c->layer]);
     hipError_t e;
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (c->timing) {
+    const bool timed = c->timing && !capturing(st);   // a graph's launches are not timed
+    if (timed) {
         if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess)
             return hip_fail(c, e, "hipEventCreate");
         if ((e = hipEventRecord(e0, st)) != hipSuccess) return hip_fail(c, e, "hipEventRecord");
     }
     e = nup::launch_partial(a, c->D, c->gqa, mode, st);
     if (e != hipSuccess) return hip_fail(c, e, "partial attention launch");
-    if (c->timing) {
+    if (timed) {
         if ((e = hipEventRecord(e1, st)) != hipSuccess) return hip_fail(c, e, "hipEventRecord");
         c->tev.emplace_back(e0, e1);
     }
@@ -1319,6 +1348,28 @@ nup_status nup_get_plan(const nup_ctx *c, int32_t *n_rows, int32_t *n_workers, i
     return NUP_OK;
 }
 
+nup_status nup_note_appends(nup_ctx *c, int32_t layer, int32_t steps) {
+    if (!c) return NUP_E_ARG;
+    if (layer < -1 || layer >= c->NL) return fail(c, NUP_E_ARG, "layer %d outside [-1, %d)", layer, c->NL);
+    if (steps < 0) return fail(c, NUP_E_ARG, "steps must be >= 0");
+    if (!c->committed || c->pending)
+        return fail(c, NUP_E_STATE, "appends are reported before any edit of the next step");
+    const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->NL : layer + 1;
+    int full = 0;
+    for (int s = 0; s < c->B; ++s) {
+        if (!c->active[s]) continue;
+        for (size_t k = (size_t)s * c->V + (size_t)l0 * c->H; k < (size_t)s * c->V + (size_t)l1 * c->H; ++k) {
+            // the replayed kernel stops a head at its budget, as this does
+            const long long n = (long long)c->len[k] + steps;
+            if (n > c->cap[k]) ++full;
+            c->len[k] = (int32_t)std::min<long long>(n, c->cap[k]);
+        }
+    }
+    if (full)
+        return fail(c, NUP_E_CAPACITY, "%d heads reached their budget; their extra tokens were not stored", full);
+    return NUP_OK;
+}
+
 nup_status nup_set_layer(nup_ctx *c, int32_t layer) {
     if (!c) return NUP_E_ARG;
     if (layer < 0 || layer >= c->NL) return fail(c, NUP_E_ARG, "layer %d outside [0, %d)", layer, c->NL);
@@ -1367,7 +1418,7 @@ nup_status nup_device_errors(nup_ctx *c, void *stream, int32_t *code) {
     e = hipMemcpyAsync(c->d_err(), &zero, 4, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(c, e, "clear device error word");
-    *code = h ? NUP_E_INDEX : NUP_OK;
+    *code = (h & 1) ? NUP_E_INDEX : (h & 2) ? NUP_E_CAPACITY : NUP_OK;
     return NUP_OK;
 }
 

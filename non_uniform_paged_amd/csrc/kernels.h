@@ -118,6 +118,8 @@ struct AppendArgs {
     const uint16_t *k_new, *v_new; // [Bmax][Hkv][D]
     const int32_t *page_table, *active, *group_of_head, *slot_of_head;
     int32_t *lengths;
+    const int32_t *caps;           // each head's budget: an append at L == cap is dropped
+    int32_t *err;                  // latched error word (bit 2: a head was full)
     int32_t bmax, hkv, gh, max_pages, lstride;
 };
 

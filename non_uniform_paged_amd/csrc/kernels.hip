@@ -1241,10 +1241,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int sh = blockIdx.x * (256 / PER) + local;
     const bool ok = sh < a.bmax * a.hkv;
     const int s = ok ? sh / a.hkv : 0, h = ok ? sh - s * a.hkv : 0;
-    const bool act = ok && a.active[s];
+    bool act = ok && a.active[s];
     int L = 0;
     if (act) {
+        // a head at its budget takes no more tokens (the host refuses such an
+        // append before launch; a replayed graph relies on this check)
         L = a.lengths[s * a.lstride + h];
+        act = L < a.caps[s * a.lstride + h];
+        if (!act && sub == 0) atomicOr(a.err, 2);
+    }
+    if (act) {
         const int pid = a.page_table[((size_t)a.group_of_head[h] * a.bmax + s) * a.max_pages + L / kPage];
         const size_t rowid = ((size_t)pid * a.gh + a.slot_of_head[h]) * kPage + L % kPage;
         const bool isv = sub >= LPR;

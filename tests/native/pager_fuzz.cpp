@@ -90,6 +90,7 @@ int main(int argc, char **argv) {
             }
             int32_t nr = 0, nw = 0, nruns = 0, nfree = 0;
             nup_set_layer(ctx, (int32_t)(rng() % (NL + 1)) - (rng() % 16 == 0));   // sometimes invalid
+            nup_note_appends(ctx, (int32_t)(rng() % (NL + 2)) - 1, (int32_t)(rng() % 40) - (rng() % 16 == 0));
             nup_get_plan(ctx, &nr, &nw, nullptr, nullptr, nullptr);
             std::vector<int32_t> rows((size_t)4 * nr + 4), ws(nw + 1), hrs((size_t)c.max_batch * Hl + 1);
             nup_get_plan(ctx, nullptr, nullptr, rows.data(), ws.data(), hrs.data());
