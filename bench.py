@@ -115,13 +115,20 @@ class Setup:
         self.num_pages = num_pages
         self.steps_done = 0
 
-    def step(self, append=True):
+    def step(self, append=True, fused=True):
+        """One decode step: frame commit, the new token's K/V append and the
+        attention -- fused (two launches) or as separate calls (three)."""
         import non_uniform_paged_amd as nup
-        if append:
-            nup.kv_append(self.ctx, self.k_new, self.v_new)
-            self.steps_done += 1
         nup.nup_commit(self.ctx)
-        nup.attn_decode_nonuniform(self.ctx, self.q, self.out, self.lse, self.scale, self.ws)
+        if append and fused:
+            nup.attn_decode_nonuniform_append(self.ctx, self.k_new, self.v_new, self.q, self.out, self.lse,
+                                              self.scale, self.ws)
+        else:
+            if append:
+                nup.kv_append(self.ctx, self.k_new, self.v_new)
+            nup.attn_decode_nonuniform(self.ctx, self.q, self.out, self.lse, self.scale, self.ws)
+        if append:
+            self.steps_done += 1
 
     def free(self):
         import torch
@@ -130,12 +137,12 @@ class Setup:
         torch.cuda.empty_cache()
 
 
-def time_steps(setup, steps, warmup, append=True):
+def time_steps(setup, steps, warmup, append=True, fused=True):
     """Returns (ms per step, partial-kernel ms per launch, mean lengths)."""
     import torch
     import non_uniform_paged_amd as nup
     for _ in range(warmup):
-        setup.step(append)
+        setup.step(append, fused)
     torch.cuda.synchronize()
     nup.kernel_time(setup.ctx, reset=True)
     nup.set_timing(setup.ctx, True)
@@ -145,7 +152,7 @@ def time_steps(setup, steps, warmup, append=True):
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        setup.step(append)
+        setup.step(append, fused)
     e1.record()
     torch.cuda.synchronize()
     nup.set_timing(setup.ctx, False)
@@ -374,8 +381,111 @@ def _layer_group_sweep(flush):
     return out
 
 
+def _graph_decode(flush, context, steps=10, warmup=2):
+    """The 36-layer decode step (fused append + attention in every layer, 72
+    launches; the three-launch form for comparison) issued call by call and
+    replayed from a HIP graph captured once, each with and without a Trim +
+    Reserve + commit of one session before every step.  Heads per group 8; the context sets the session
+    lengths (16384: the Qwen3-4B batch; 1024: short sessions)."""
+    import torch
+    import non_uniform_paged_amd as nup
+    import workloads as W
+    w = W.qwen3_4b_layers(headroom=128, context=context)
+    NL, H, Hq, D, B = w.extra["num_layers"], w.num_kv_heads, w.num_q_heads, w.head_dim, w.batch
+    V, G = NL * H, 8
+    ng = V // G
+    caps, lens = w.caps.astype(np.int32), w.lengths.astype(np.int32)
+    max_pages = int(math.ceil(caps.max() / 16))
+    cfg = dict(num_kv_heads=H, num_q_heads=Hq, head_dim=D, num_groups=ng, max_batch=B,
+               max_pages=max_pages, num_layers=NL)
+    probe = nup.Context(**cfg, num_pages=B * ng * max_pages)
+    nup.kv_alloc_groups(probe, np.arange(B), caps, lens)
+    pages = B * ng * max_pages - len(nup.get_free_list(probe))
+    del probe
+    kpool = torch.empty((pages, G, 16, D), dtype=torch.bfloat16, device="cuda")
+    vpool = torch.empty_like(kpool)
+    W.fill_normal_bf16_torch(kpool, "k")
+    W.fill_normal_bf16_torch(vpool, "v")
+    desc = torch.empty(nup.desc_bytes(**cfg, num_pages=pages), dtype=torch.uint8, device="cuda")
+    ctx = nup.Context(**cfg, num_pages=pages, k_pool=kpool, v_pool=vpool, desc=desc)
+    nup.kv_alloc_groups(ctx, np.arange(B), caps, lens)
+    nup.nup_commit(ctx)
+    ws = torch.empty(nup.workspace_bytes(ctx), dtype=torch.uint8, device="cuda")
+    q = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    kn = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    vn = torch.empty_like(kn)
+    W.fill_normal_bf16_torch(q, "q")
+    W.fill_normal_bf16_torch(kn, "k", 77)
+    W.fill_normal_bf16_torch(vn, "v", 77)
+    o = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    turn = [0]
+
+    def churn():
+        s = turn[0] % B
+        turn[0] += 1
+        nup.kv_free_seqs(ctx, [s])
+        nup.kv_alloc_groups(ctx, [s], caps[s:s + 1], lens[s:s + 1])
+        nup.nup_commit(ctx)
+
+    def eager():
+        for layer in range(NL):
+            nup.set_layer(ctx, layer)
+            nup.attn_decode_nonuniform_append(ctx, kn, vn, q, o, lse, scale, ws)
+
+    def eager3():   # the same step as three launches per layer
+        for layer in range(NL):
+            nup.set_layer(ctx, layer)
+            nup.kv_append(ctx, kn, vn)
+            nup.attn_decode_nonuniform(ctx, q, o, lse, scale, ws)
+
+    g = torch.cuda.CUDAGraph()
+
+    def replay():
+        g.replay()
+        nup.note_appends(ctx, 1)
+
+    def run(fn, with_churn):
+        for _ in range(warmup):
+            if with_churn:
+                churn()
+            fn()
+        torch.cuda.synchronize()
+        flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        host = 0.0
+        e0.record()
+        for _ in range(steps):
+            t0 = time.perf_counter()
+            if with_churn:
+                churn()
+            fn()
+            host += time.perf_counter() - t0
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, host / steps * 1e6
+
+    res = {"context": context, "batch": B, "heads_per_group": G, "launches_per_step": 2 * NL,
+           "kv_GB_per_step": round(float(lens.astype(np.int64).sum()) * 2 * D * 2 / 1e9, 3)}
+    res["eager_3_launches_ms"], res["eager_3_launches_host_us"] = run(eager3, False)
+    res["eager_ms"], res["eager_host_us"] = run(eager, False)
+    res["eager_churn_ms"], res["eager_churn_host_us"] = run(eager, True)
+    with torch.cuda.graph(g):
+        eager()
+    res["graph_ms"], res["graph_host_us"] = run(replay, False)
+    res["graph_churn_ms"], res["graph_churn_host_us"] = run(replay, True)
+    for k in list(res):
+        if isinstance(res[k], float):
+            res[k] = round(res[k], 4 if k.endswith("_ms") else 1)
+    del g, ctx, kpool, vpool, desc, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 EXTRA_SECTIONS = ("qwen3_4b", "llama3_8b_topk", "llama3_8b_centroids", "mixed_churn", "qwen25_32b_trains", "qwen25_32b_prefix",
-                  "qwen3_4b_36_layers", "qwen25_32b_heads_per_group")
+                  "qwen3_4b_36_layers", "qwen3_4b_36_layers_graph", "qwen25_32b_heads_per_group")
 
 
 def measure_extras(args, only=None):
@@ -521,8 +631,7 @@ def measure_extras(args, only=None):
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-            nup.kv_append(st.ctx, st.k_new, st.v_new)
-            nup.attn_decode_nonuniform(st.ctx, st.q, st.out, st.lse, st.scale, st.ws)
+            nup.attn_decode_nonuniform_append(st.ctx, st.k_new, st.v_new, st.q, st.out, st.lse, st.scale, st.ws)
             if timed:
                 e1.record()
                 nup.set_timing(st.ctx, False)
@@ -624,6 +733,12 @@ def measure_extras(args, only=None):
     if want("qwen3_4b_36_layers"):
         res["qwen3_4b_36_layers"] = _layer_group_sweep(flush)
 
+    # -- the same 36-layer step replayed from a HIP graph captured once, with
+    #    Trim / Reserve / commit between replays (KV-RM: a static-graph
+    #    decoder over one committed descriptor per step)
+    if want("qwen3_4b_36_layers_graph"):
+        res["qwen3_4b_36_layers_graph"] = [_graph_decode(flush, 16384), _graph_decode(flush, 1024)]
+
     # -- heads per page (Tangram, Fig 8c): the Qwen2.5-32B batch with 1, 2, 4, 8 groups
     if want("qwen25_32b_heads_per_group"):
         sweep = []
@@ -668,6 +783,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other configurations (Qwen3-4B, Llama top-K, mixed churn)")
     ap.add_argument("--workers", type=int, default=0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the step as kv_append + attn_decode_nonuniform (three launches)")
     ap.add_argument("--no-copy-engine", action="store_true",
                     help="skip the copy-engine train measurements (thousands of copies)")
     ap.add_argument("--only-extra", choices=EXTRA_SECTIONS, default=None,
@@ -715,9 +832,9 @@ def main():
     sha = hashlib.sha256(src).hexdigest()
 
     w = W.qwen25_32b()
-    headroom = args.warmup + args.steps + 8
+    headroom = 2 * (args.warmup + args.steps) + 8
     st = Setup(w, headroom, num_workers=args.workers)
-    ms, kms, mean_L = time_steps(st, args.steps, args.warmup)
+    ms, kms, mean_L = time_steps(st, args.steps, args.warmup, fused=not args.unfused)
     B, Hq, H, D, ng = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_groups
     step_bytes = algorithmic_bytes(mean_L, st.caps, B, Hq, H, ng) + B * H * D * 2 * 2 * 2
     kern_bytes = algorithmic_bytes(mean_L, st.caps, B, Hq, H, ng) - B * Hq * D * 4
@@ -725,6 +842,15 @@ def main():
     achieved = kern_bytes / (kms * 1e-3) / 1e9
     extra = {"kv_bytes_per_step": kv_bytes(mean_L), "partial_kernel_ms": round(kms, 4),
              "pct_of_peak_step": round(100 * value / PEAK_HBM_GBS, 2)}
+
+    extra["step_launches"] = 3 if args.unfused else 2
+    if not args.no_controls:
+        # the other form of the same step on the same batch (a few tokens longer)
+        oms, _, oL = time_steps(st, args.steps, args.warmup, fused=args.unfused)
+        ob = algorithmic_bytes(oL, st.caps, B, Hq, H, ng) + B * H * D * 2 * 2 * 2
+        tag = "fused" if args.unfused else "unfused_3_launches"
+        extra[f"{tag}_ms_per_step"] = round(oms, 4)
+        extra[f"{tag}_step_GBs"] = round(ob / (oms * 1e-3) / 1e9, 1)
 
     cpu = None
     if not args.no_cpu_baseline:

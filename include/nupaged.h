@@ -293,6 +293,26 @@ nup_status attn_decode_nonuniform(nup_ctx *ctx, const void *q, float *out, float
                                   void *stream);
 
 /*
+ * attn_decode_nonuniform_append -- kv_append followed by
+ * attn_decode_nonuniform for the current layer, in two launches instead of
+ * three (the decode step of KV-RM, abstract: the step's write and the
+ * fixed-shape attention over the committed mapping).  The split-K worker
+ * whose work row holds a head's position L stores the new K and V rows
+ * there before it reads the row's pages, every row of the head reads up to
+ * L + 1, and the merge launch advances L.  Results, pools and lengths are
+ * bit-identical to the two calls made separately.
+ *   k_new, v_new   device bf16 [B_max][H_kv][D], as for kv_append
+ *   q, out, lse, scale, workspace as for attn_decode_nonuniform
+ * Capacity and capture behave as for kv_append: NUP_E_CAPACITY on the host
+ * if any active head is at its budget (nothing launched); under graph
+ * capture the device drops the token of a full head, latches
+ * NUP_E_CAPACITY, and nup_note_appends reports the replays.
+ * Errors: NUP_E_ARG, NUP_E_STATE, NUP_E_CAPACITY, NUP_E_HIP. */
+nup_status attn_decode_nonuniform_append(nup_ctx *ctx, const void *k_new, const void *v_new,
+                                         const void *q, float *out, float *lse, float scale,
+                                         void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * attn_decode_topk -- decode attention over K gathered entries per active
  * (slot, KV head) held contiguously (KVDrive, Fig 1: sparse attention over
  * critical entries), e.g. the output of kv_gather_compact mode 1.

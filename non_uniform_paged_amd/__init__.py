@@ -63,6 +63,7 @@ _sigs = {
     "kv_gather_compact": [_P, _I, _P, _I, _P, _P, _P, _P, _P],
     "nup_workspace_bytes": [_P, _I, _P],
     "attn_decode_nonuniform": [_P, _P, _P, _P, ctypes.c_float, _P, _S, _P],
+    "attn_decode_nonuniform_append": [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _S, _P],
     "attn_decode_topk": [_P, _P, _P, _P, _I, _P, _P, ctypes.c_float, _P, _S, _P],
     "attn_decode_topk_paged": [_P, _P, _P, _I, _P, _P, ctypes.c_float, _P, _S, _P],
     "kv_select_topk": [_P, _P, _I, _I, _P, _P, _S, _P],
@@ -252,6 +253,14 @@ def attn_decode_nonuniform(ctx: Context, q, out, lse, scale: float, workspace, s
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib.attn_decode_nonuniform(ctx.handle, _ptr(q), _ptr(out), _ptr(lse), float(scale),
                                      _ptr(workspace), nbytes, _stream(stream))
+    return ctx.check(st) if raise_on_error else st
+
+
+def attn_decode_nonuniform_append(ctx: Context, k_new, v_new, q, out, lse, scale: float, workspace,
+                                  stream=None, raise_on_error=True):
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.attn_decode_nonuniform_append(ctx.handle, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                            _ptr(lse), float(scale), _ptr(workspace), nbytes, _stream(stream))
     return ctx.check(st) if raise_on_error else st
 
 

@@ -1047,7 +1047,8 @@ nup_status nup_workspace_bytes(const nup_ctx *c, int32_t K, size_t *bytes) {
 
 static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse, float scale, void *ws,
                               size_t ws_bytes, void *stream, int mode, const void *ks, const void *vs,
-                              const int32_t *idx, int K) {
+                              const int32_t *idx, int K, const void *k_new = nullptr,
+                              const void *v_new = nullptr) {
     const bool topk = mode != nup::kModePaged;
     if (!c) return NUP_E_ARG;
     if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
@@ -1098,6 +1099,10 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
         a.worker_start = c->inbox_i32(c->off_ws[c->layer]);
         a.n_workers = c->dev_workers[c->layer];
         rows_max = c->sz.max_rows;
+        a.k_new = static_cast<const uint16_t *>(k_new);
+        a.v_new = static_cast<const uint16_t *>(v_new);
+        a.caps = c->d_cap() + c->lbase();
+        a.err = c->d_err();
     }
     float *wso = static_cast<float *>(ws);
     float *wsml = reinterpret_cast<float *>(static_cast<char *>(ws) +
@@ -1129,6 +1134,13 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
     m.out = out;
     m.lse = lse;
     m.hkv = c->H;
+    if (k_new) {
+        m.lengths = c->d_len() + c->lbase();
+        m.caps = c->d_cap() + c->lbase();
+        m.active = c->d_active();
+        m.err = c->d_err();
+        m.lstride = c->V;
+    }
     e = nup::launch_merge(m, c->D, c->gqa, c->B * c->H, st);
     if (e != hipSuccess) return hip_fail(c, e, "merge launch");
     return NUP_OK;
@@ -1138,6 +1150,32 @@ nup_status attn_decode_nonuniform(nup_ctx *c, const void *q, float *out, float *
                                   void *workspace, size_t ws_bytes, void *stream) {
     return attn_common(c, q, out, lse, scale, workspace, ws_bytes, stream, nup::kModePaged, nullptr,
                        nullptr, nullptr, 0);
+}
+
+nup_status attn_decode_nonuniform_append(nup_ctx *c, const void *k_new, const void *v_new, const void *q,
+                                         float *out, float *lse, float scale, void *workspace, size_t ws_bytes,
+                                         void *stream) {
+    if (!c) return NUP_E_ARG;
+    if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
+    if (!k_new || !v_new) return fail(c, NUP_E_ARG, "k_new and v_new are required");
+    if (!c->committed || c->pending) return fail(c, NUP_E_STATE, "edits pending: nup_commit first");
+    const bool cap_mode = capturing(static_cast<hipStream_t>(stream));
+    for (int s = 0; s < c->B && !cap_mode; ++s) {
+        if (!c->active[s]) continue;
+        for (int h = 0; h < c->H; ++h) {
+            const size_t k = (size_t)s * c->V + c->lbase() + h;
+            if (c->len[k] >= c->cap[k])
+                return fail(c, NUP_E_CAPACITY, "slot %d layer %d head %d is at its budget (%d tokens)", s,
+                            c->layer, h, c->cap[k]);
+        }
+    }
+    nup_status r = attn_common(c, q, out, lse, scale, workspace, ws_bytes, stream, nup::kModePaged, nullptr,
+                               nullptr, nullptr, 0, k_new, v_new);
+    if (r != NUP_OK || cap_mode) return r;
+    for (int s = 0; s < c->B; ++s)
+        if (c->active[s])
+            for (int h = 0; h < c->H; ++h) c->len[(size_t)s * c->V + c->lbase() + h]++;
+    return NUP_OK;
 }
 
 nup_status attn_decode_topk(nup_ctx *c, const void *q, const void *k_stage, const void *v_stage, int32_t K,

@@ -47,6 +47,11 @@ struct PartialArgs {
     int32_t lstride;            // length-row stride: KV heads of all layers
     int32_t topk_k, topk_splits, topk_chunk;
     float scale_log2;           // softmax scale * log2(e)
+    // fused append (paged mode; k_new NULL: none): the new token's rows
+    // [Bmax][Hkv][D] are stored at each head's position L and attended to;
+    // the merge kernel then advances L
+    const uint16_t *k_new, *v_new;
+    const int32_t *caps;        // this layer's budgets, indexed like lengths
 };
 
 struct MergeArgs {
@@ -58,6 +63,11 @@ struct MergeArgs {
     float *lse;                    // fp32 [Bmax][Hq] or NULL
     int32_t hkv;
     int32_t n_pairs;               // (slot, query head) pairs; set by the launcher
+    // fused append: advance each active head's length (NULL: no append)
+    int32_t *lengths;
+    const int32_t *caps, *active;
+    int32_t *err;                  // latched error word (bit 2: a head was full)
+    int32_t lstride;
 };
 
 // Top-K selection.  score_kernel walks the committed plan like the paged

@@ -154,16 +154,28 @@ void partial_attn_kernel(PartialArgs a) {
     }
     for (int row = rb; row < re; ++row) {
         int sh, t0, t1;
+        int app_at = -1;   // fused append: the position this row stores and reads the new token at
         if (TOPK) {
             sh = row / a.topk_splits;
             t0 = (row - sh * a.topk_splits) * a.topk_chunk;
             const int n = ld_uniform(a.active + sh / a.hkv) ? a.topk_k : 0;
             t1 = min(t0 + a.topk_chunk, n);
-        } else {
+        } else if (!a.k_new) {
             sh = ld_uniform(a.rows + row * 4 + 0);
             t0 = ld_uniform(a.rows + row * 4 + 1);
             // the row's fourth word is its head's index into lengths
             t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + ld_uniform(a.rows + row * 4 + 3)));
+        } else {
+            sh = ld_uniform(a.rows + row * 4 + 0);
+            t0 = ld_uniform(a.rows + row * 4 + 1);
+            const int li = ld_uniform(a.rows + row * 4 + 3);
+            const int r2 = ld_uniform(a.rows + row * 4 + 2);
+            const int L = ld_uniform(a.lengths + li);
+            // a head below its budget takes the token at L: the one row whose
+            // range holds L stores it; every row of the head reads up to L
+            const int app = L < ld_uniform(a.caps + li) ? 1 : 0;
+            t1 = min(r2, L + app);
+            if (app && t0 <= L && L < r2) app_at = L;
         }
         const int s = sh / a.hkv, h = sh - s * a.hkv;
         float *ml = a.ws_ml + (size_t)row * GQA * 2;
@@ -214,6 +226,21 @@ void partial_attn_kernel(PartialArgs a) {
         }
         const size_t head_base = MODE == kModeStaged ? (size_t)sh * a.topk_k * D : 0;
         const int p0 = t0 / kPage, p1 = (t1 - 1) / kPage;  // inclusive page range
+
+        if (MODE == kModePaged && app_at >= 0) {
+            // store the new K and V rows before any page of the row is read
+            // (only this wave reads this head's position app_at)
+            if (lane < 2 * LPR) {
+                const bool isv = lane >= LPR;
+                const int c = lane - (isv ? LPR : 0);
+                const uint4 *src = reinterpret_cast<const uint4 *>((isv ? a.v_new : a.k_new) + (size_t)sh * D) + c;
+                const size_t off = (size_t)ld_uniform(ptrow + app_at / kPage) * a.gh * kPage * D + slot_off +
+                                   (size_t)(app_at % kPage) * D;
+                uint4 *dst = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(isv ? a.vbase : a.kbase) + off) + c;
+                *dst = *src;
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+        }
 
         if (MODE == kModeIndexed) {
             // Resolve the chunk's entries to pool rows before streaming: index
@@ -453,6 +480,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     if (wv >= a.n_pairs) return;
     const int sh = wv / GQA, r = wv - sh * GQA;
     const int s = sh / a.hkv, h = sh - s * a.hkv;
+    if (a.lengths && r == 0 && lane == 0 && a.active[s]) {
+        // fused append: the partial kernel stored and read the token at L
+        // (every wave of it has finished reading L)
+        const int li = s * a.lstride + h;
+        const int L = a.lengths[li];
+        if (L < a.caps[li]) a.lengths[li] = L + 1;
+        else atomicOr(a.err, 2);
+    }
     int rb, re;
     if (a.head_row_start) {
         rb = a.head_row_start[sh];
@@ -1475,6 +1510,15 @@ hipError_t launch_partial(const PartialArgs &a, int head_dim, int gqa, int mode,
     void *fn = partial_ptr(head_dim, gqa, mode);
     if (!fn) return hipErrorInvalidValue;
     if (a.n_workers <= 0) return hipSuccess;
+    // every pointer the chosen paths dereference must be set
+    if (!a.q || !a.kbase || !a.vbase || !a.active || !a.ws_o || !a.ws_ml || !a.out) return hipErrorInvalidValue;
+    if (mode == kModePaged && (!a.page_table || !a.lengths || !a.group_of_head || !a.slot_of_head || !a.rows ||
+                               !a.worker_start || !a.head_row_start))
+        return hipErrorInvalidValue;
+    if (mode == kModeIndexed && (!a.page_table || !a.lengths || !a.group_of_head || !a.slot_of_head || !a.idx ||
+                                 !a.err))
+        return hipErrorInvalidValue;
+    if (a.k_new && (mode != kModePaged || !a.v_new || !a.caps)) return hipErrorInvalidValue;
     const unsigned blocks = (unsigned)((a.n_workers + kWavesPerBlock - 1) / kWavesPerBlock);
     PartialArgs copy = a;
     return launch_raw(fn, dim3(blocks), dim3(256), &copy, sizeof(copy), st);
@@ -1484,6 +1528,7 @@ hipError_t launch_merge(const MergeArgs &a, int head_dim, int gqa, int n_heads, 
     void *fn = head_dim == 64 ? merge_fn_gqa<64>(gqa) : head_dim == 128 ? merge_fn_gqa<128>(gqa) : nullptr;
     if (!fn) return hipErrorInvalidValue;
     if (n_heads <= 0) return hipSuccess;
+    if (a.lengths && (!a.caps || !a.active || !a.err)) return hipErrorInvalidValue;
     MergeArgs copy = a;
     copy.n_pairs = n_heads * gqa;
     const unsigned blocks = (unsigned)((copy.n_pairs + kWavesPerBlock - 1) / kWavesPerBlock);

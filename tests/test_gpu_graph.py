@@ -3,7 +3,9 @@ changes the mapping between replays (KV-RM, abstract and Fig 2: a
 fixed-shape decoder reads one committed descriptor per step, so Reserve,
 Alias and Trim need no new launch shapes).  The graph's outputs, pools and
 lengths are compared bit for bit with the same calls made eagerly on a twin
-context, and the last step with the oracle."""
+context, and the last step with the oracle.  The graph holds either
+kv_append + attn_decode_nonuniform or the fused
+attn_decode_nonuniform_append; the twin always makes the separate calls."""
 import numpy as np
 import pytest
 import torch
@@ -46,8 +48,18 @@ def _mirror_append(c, kn, vn, fk, fv, layer):
             sp.lengths[s, v] += 1
 
 
-@pytest.mark.parametrize("plan_mode", [nup.PLAN_BALANCED, nup.PLAN_UNIFORM])
-def test_graph_replay_across_commits(plan_mode):
+def _step(c, layer, kn, vn, q, out, lse, fused):
+    nup.set_layer(c.ctx, layer)
+    if fused:
+        nup.attn_decode_nonuniform_append(c.ctx, kn, vn, q, out, lse, c.scale, c.ws)
+    else:
+        nup.kv_append(c.ctx, kn, vn)
+        nup.attn_decode_nonuniform(c.ctx, q, out, lse, c.scale, c.ws)
+
+
+@pytest.mark.parametrize("plan_mode,fused", [(nup.PLAN_BALANCED, False), (nup.PLAN_UNIFORM, False),
+                                             (nup.PLAN_BALANCED, True), (nup.PLAN_UNIFORM, True)])
+def test_graph_replay_across_commits(plan_mode, fused):
     rs = np.random.default_rng(70 + plan_mode)
     steps = 8
     max_pages = 22
@@ -76,9 +88,7 @@ def test_graph_replay_across_commits(plan_mode):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for l in range(NL):
-            nup.set_layer(G.ctx, l)
-            nup.kv_append(G.ctx, kn[l], vn[l])
-            nup.attn_decode_nonuniform(G.ctx, qs[l], outs[l], lses[l], G.scale, G.ws)
+            _step(G, l, kn[l], vn[l], qs[l], outs[l], lses[l], fused)
         # a commit is never captured
         assert nup.nup_commit(G.ctx, raise_on_error=False) == nup.NUP_E_STATE
     # capture recorded the appends without advancing the shadow
@@ -142,7 +152,8 @@ def test_graph_replay_across_commits(plan_mode):
                                lses[l].cpu().numpy().astype(np.float64), ref, ref_lse, f"graph layer {l}")
 
 
-def test_graph_append_stops_at_budget():
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_append_stops_at_budget(fused):
     """A replayed append cannot be refused on the host: the kernel drops the
     token of a head at its budget, latches NUP_E_CAPACITY, and
     nup_note_appends mirrors exactly that."""
@@ -161,12 +172,17 @@ def test_graph_append_stops_at_budget():
     vn = torch.empty_like(kn)
     nup.set_layer(c.ctx, 1)      # eagerly, the full head refuses the whole step
     assert nup.kv_append(c.ctx, kn, vn, raise_on_error=False) == nup.NUP_E_CAPACITY
+    assert nup.attn_decode_nonuniform_append(c.ctx, kn, vn, c.q, c.out, c.lse, c.scale, c.ws,
+                                             raise_on_error=False) == nup.NUP_E_CAPACITY
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for l in range(NL):
-            nup.set_layer(c.ctx, l)
-            nup.kv_append(c.ctx, kn, vn)
+            if fused:
+                _step(c, l, kn, vn, c.q, c.out, c.lse, True)
+            else:
+                nup.set_layer(c.ctx, l)
+                nup.kv_append(c.ctx, kn, vn)
     fk, fv = u16(c.kpool).copy().reshape(-1, D), u16(c.vpool).copy().reshape(-1, D)
     sp = c.spec
     for i in range(3):

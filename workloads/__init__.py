@@ -171,13 +171,15 @@ def qwen3_4b(headroom: int = PAGE) -> Workload:
                     extra={"scale_factor": hi, "context": ctx})
 
 
-def qwen3_4b_layers(num_layers: int = 36, headroom: int = PAGE, batch: int = 16) -> Workload:
+def qwen3_4b_layers(num_layers: int = 36, headroom: int = PAGE, batch: int = 16,
+                    context: int = 16384) -> Workload:
     """The Qwen3-4B shape over all its layers: 36 layers x 8 KV heads, one
-    budget per (layer, KV head), log-uniform in [256, 16384] and scaled so the
-    mean over all 288 heads is half the context (the same reading as the
+    budget per (layer, KV head), log-uniform in [256, context] and scaled so
+    the mean over all 288 heads is half the context (the same reading as the
     one-layer shape), rounded to the page.  num_kv_heads is per layer;
-    lengths and caps are [batch][num_layers * 8], head index layer * 8 + h."""
-    ctx = 16384
+    lengths and caps are [batch][num_layers * 8], head index layer * 8 + h.
+    A shorter context gives the same shape with short sessions."""
+    ctx = context
     g = rng("budgets", 21)
     n = num_layers * 8
     raw = np.exp(g.uniform(math.log(256), math.log(ctx), size=n))
