@@ -137,8 +137,10 @@ class Setup:
         torch.cuda.empty_cache()
 
 
-def time_steps(setup, steps, warmup, append=True, fused=True):
-    """Returns (ms per step, partial-kernel ms per launch, mean lengths)."""
+def time_steps(setup, steps, warmup, append=True, fused=True, per_step=None):
+    """Returns (ms per step, partial-kernel ms per launch, mean lengths).
+    per_step: a list that receives each timed step's milliseconds (an event
+    between consecutive steps on the launch stream)."""
     import torch
     import non_uniform_paged_amd as nup
     for _ in range(warmup):
@@ -148,15 +150,21 @@ def time_steps(setup, steps, warmup, append=True, fused=True):
     nup.set_timing(setup.ctx, True)
     L_before = setup.lengths0 + setup.steps_done
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    # per-step events only when asked: each one is a barrier between steps
+    n_ev = steps + 1 if per_step is not None else 2
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev[0].record()
+    for i in range(steps):
         setup.step(append, fused)
-    e1.record()
+        if per_step is not None:
+            ev[i + 1].record()
+    if per_step is None:
+        ev[1].record()
     torch.cuda.synchronize()
     nup.set_timing(setup.ctx, False)
-    ms = e0.elapsed_time(e1) / steps
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    if per_step is not None:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     kms, n = nup.kernel_time(setup.ctx, reset=True)
     L_after = setup.lengths0 + setup.steps_done
     # lengths seen by the attention of each timed step: L_before+1 .. L_after
@@ -218,11 +226,26 @@ def cpu_baseline(setup, budget_s=12.0):
     while total_t < budget_s and reps < 50:   # whole batch is quick: repeat it
         dt, b = run(list(range(n)))
         reps, total_t, total_b = reps + 1, total_t + dt, total_b + b
-    return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": threads,
+    # the same oracle on one thread, over a few sessions (about 3 s)
+    threads_all, threads = threads, 1
+    d1, b1 = run([0])
+    n1 = int(max(1, min(w.batch, math.floor(3.0 / max(d1, 1e-3)))))
+    if n1 > 1:
+        d1, b1 = run(list(range(n1)))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": threads_all,
             "kind": "oracle",
             "sample": f"first {n} of {w.batch} sessions of the same batch (all their KV heads), "
                       f"one decode step of attention, x{reps} runs, {total_t:.1f} s wall; fp64 C "
-                      f"oracle with OpenMP"}
+                      f"oracle with OpenMP",
+            "one_thread_value": round(b1 / d1 / 1e9, 4),
+            "one_thread_sample": f"first {n1} sessions, {d1:.1f} s",
+            "cpu_model": model}
 
 
 def _timed(fn, iters, flush=None):
@@ -832,7 +855,7 @@ def main():
     sha = hashlib.sha256(src).hexdigest()
 
     w = W.qwen25_32b()
-    headroom = 2 * (args.warmup + args.steps) + 8
+    headroom = 2 * args.warmup + 3 * args.steps + 8
     st = Setup(w, headroom, num_workers=args.workers)
     ms, kms, mean_L = time_steps(st, args.steps, args.warmup, fused=not args.unfused)
     B, Hq, H, D, ng = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_groups
@@ -845,6 +868,12 @@ def main():
 
     extra["step_launches"] = 3 if args.unfused else 2
     if not args.no_controls:
+        # the distribution of single steps, in a pass of its own (an event
+        # between steps keeps them from overlapping, so these run slower)
+        step_ms = []
+        time_steps(st, args.steps, 0, fused=not args.unfused, per_step=step_ms)
+        extra["single_step_ms_median"] = round(float(np.median(step_ms)), 4)
+        extra["single_step_ms_p90"] = round(float(np.percentile(step_ms, 90)), 4)
         # the other form of the same step on the same batch (a few tokens longer)
         oms, _, oL = time_steps(st, args.steps, args.warmup, fused=args.unfused)
         ob = algorithmic_bytes(oL, st.caps, B, Hq, H, ng) + B * H * D * 2 * 2 * 2
@@ -912,7 +941,9 @@ def main():
                                "heads, head_dim 128, contexts U[8192,65536], keep ratio Beta(0.5,2) "
                                "per KV head, 4 head groups, 16-token pages",
                    "kv_dtype": "bf16", "batch": B, "kv_bytes": kv_bytes(mean_L),
-                   "step": "kv_append + nup_commit + attn_decode_nonuniform (partial + merge)"},
+                   "step": ("kv_append + nup_commit + attn_decode_nonuniform (append, partial, merge)"
+                            if args.unfused else
+                            "nup_commit + attn_decode_nonuniform_append (partial with the append, merge)")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": "partial_attn_kernel<128,5,0>"},

@@ -114,6 +114,16 @@ def test_error_codes_and_atomicity():
             assert np.array_equal(a, b)
     # device calls on a host-only context are refused, not crashed
     assert nup.nup_commit(ctx, stream=0, raise_on_error=False) == E.NUP_E_STATE
+    import torch
+    assert nup.attn_decode_nonuniform_append(ctx, None, None, None, None, None, 1.0, torch.zeros(1, dtype=torch.uint8),
+                                             stream=0, raise_on_error=False) == E.NUP_E_STATE
+    # graph replays are reported only between commits: arguments first, then state
+    st = nup._lib.nup_note_appends
+    assert st(ctx.handle, 1, 1) == E.NUP_E_ARG          # one layer: -1 and 0 only
+    assert st(ctx.handle, -2, 1) == E.NUP_E_ARG
+    assert st(ctx.handle, 0, -1) == E.NUP_E_ARG
+    assert st(ctx.handle, -1, 1) == E.NUP_E_STATE        # never committed
+    assert np.array_equal(_state(ctx)[0], snap[0])
 
 
 def test_bad_configs_rejected():
