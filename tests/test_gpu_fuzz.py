@@ -1,5 +1,6 @@
 """Randomised parity: shapes, grouping, layers, plan sizes, page orders,
-Reserve / Trim / append sequences and lengths drawn by hypothesis; every
+Reserve / Trim / append sequences and lengths drawn by hypothesis, with the
+append made by kv_append or by the fused append + attention call; every
 example is checked against the oracle at the acceptance bar (attention)
 and bit for bit (pool after appends)."""
 import math
@@ -56,35 +57,49 @@ def test_random_shapes_and_edits(data):
     c.commit()
     qs = [torch.from_numpy(W.normal_bf16("q", (B, H * gqa, D), seed + l).view(np.int16)).to(DEV)
           .view(torch.bfloat16) for l in range(NL)]
-    # one append per layer where every live head has room
+    # one append per layer where every live head has room: kv_append, or
+    # (drawn) the fused append + attention call, checked as it goes
+    fused = data.draw(st.booleans())
     kp, vp = u16(c.kpool).copy(), u16(c.vpool).copy()
     fk, fv = kp.reshape(-1, D), vp.reshape(-1, D)
-    for l in range(NL):
-        sl = slice(l * H, (l + 1) * H)
-        if not (c.spec.lengths[live][:, sl] < c.spec.caps[live][:, sl]).all():
-            continue
-        nup.set_layer(c.ctx, l)
-        kn = W.normal_bf16("k", (B, H, D), seed + 100 + l)
-        vn = W.normal_bf16("v", (B, H, D), seed + 100 + l)
-        nup.kv_append(c.ctx, torch.from_numpy(kn.view(np.int16)).to(DEV),
-                      torch.from_numpy(vn.view(np.int16)).to(DEV))
-        for s in np.nonzero(live)[0]:
-            for h in range(H):
-                v = l * H + h
-                row = c.spec.physical_row(s, v, int(c.spec.lengths[s, v]))
-                fk[row], fv[row] = kn[s, h], vn[s, h]
-                c.spec.lengths[s, v] += 1
-    torch.cuda.synchronize()
-    assert np.array_equal(nup.get_lengths(c.ctx), c.spec.lengths)
-    assert np.array_equal(u16(c.kpool), kp) and np.array_equal(u16(c.vpool), vp)
-    for l in range(NL):
-        nup.set_layer(c.ctx, l)
-        rows, ws_, hrs = nup.get_plan(c.ctx)
-        nup.attn_decode_nonuniform(c.ctx, qs[l], c.out, c.lse, c.scale, c.ws)
+    tag = f"seed {seed} D{D} gqa{gqa} H{H} NL{NL} ng{ng} B{B} W{workers} fused {fused}"
+
+    def check(l):
         torch.cuda.synchronize()
         sl = slice(l * H, (l + 1) * H)
         ref, ref_lse = oracle.decode(u16(qs[l]), kp, vp, c.spec.page_table, c.spec.lengths[:, sl],
                                      c.spec.group_of_head[sl], c.spec.slot_of_head[sl], c.scale)
         assert_attention_close(c.out.cpu().numpy().astype(np.float64),
-                               c.lse.cpu().numpy().astype(np.float64), ref, ref_lse,
-                               f"seed {seed} layer {l} D{D} gqa{gqa} H{H} NL{NL} ng{ng} B{B} W{workers}")
+                               c.lse.cpu().numpy().astype(np.float64), ref, ref_lse, f"{tag} layer {l}")
+
+    for l in range(NL):
+        sl = slice(l * H, (l + 1) * H)
+        room = (c.spec.lengths[live][:, sl] < c.spec.caps[live][:, sl]).all()
+        nup.set_layer(c.ctx, l)
+        if room:
+            kn = W.normal_bf16("k", (B, H, D), seed + 100 + l)
+            vn = W.normal_bf16("v", (B, H, D), seed + 100 + l)
+            kd, vd = torch.from_numpy(kn.view(np.int16)).to(DEV), torch.from_numpy(vn.view(np.int16)).to(DEV)
+            if fused:
+                nup.attn_decode_nonuniform_append(c.ctx, kd, vd, qs[l], c.out, c.lse, c.scale, c.ws)
+            else:
+                nup.kv_append(c.ctx, kd, vd)
+            for s in np.nonzero(live)[0]:
+                for h in range(H):
+                    v = l * H + h
+                    row = c.spec.physical_row(s, v, int(c.spec.lengths[s, v]))
+                    fk[row], fv[row] = kn[s, h], vn[s, h]
+                    c.spec.lengths[s, v] += 1
+        if fused:
+            if not room:
+                nup.attn_decode_nonuniform(c.ctx, qs[l], c.out, c.lse, c.scale, c.ws)
+            check(l)
+    torch.cuda.synchronize()
+    assert np.array_equal(nup.get_lengths(c.ctx), c.spec.lengths)
+    assert np.array_equal(u16(c.kpool), kp) and np.array_equal(u16(c.vpool), vp)
+    assert nup.device_errors(c.ctx) == nup.NUP_OK
+    if not fused:
+        for l in range(NL):
+            nup.set_layer(c.ctx, l)
+            nup.attn_decode_nonuniform(c.ctx, qs[l], c.out, c.lse, c.scale, c.ws)
+            check(l)
