@@ -603,14 +603,16 @@ def _check_selection(got, spec, q, pool_k, K, window, heads, eps=1e-3):
         assert gs.sum() == ws_.sum()
 
 
-def test_select_topk_exact_ties():
+@pytest.mark.parametrize("plan_mode", [nup.PLAN_BALANCED, nup.PLAN_UNIFORM])
+def test_select_topk_exact_ties(plan_mode):
     """Exactly representable scores with many ties: the GPU selection equals
-    the oracle's bit for bit (ties to the lower position)."""
+    the oracle's bit for bit (ties to the lower position), whichever plan the
+    score kernel walks."""
     B, H, gqa, D = 2, 4, 2, 128
     L = np.array([[300, 257, 64, 129], [512, 96, 400, 33]], np.int32)
     max_pages = 33
     c = Case(H=H, Hq=H * gqa, D=D, ng=2, B=B, num_pages=B * 2 * max_pages, max_pages=max_pages,
-             num_workers=13, salt=40)
+             num_workers=13, salt=40, plan_mode=plan_mode, uniform_splits=3)
     c.alloc([0, 1], L, L)
     c.commit()
     # keys: dims 3 and 5 carry small integers (many repeats), all else zero
