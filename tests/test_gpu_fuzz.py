@@ -4,6 +4,7 @@ append made by kv_append or by the fused append + attention call; every
 example is checked against the oracle at the acceptance bar (attention)
 and bit for bit (pool after appends)."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -19,7 +20,9 @@ from tests.gpu_common import DEV, Case, assert_attention_close, u16
 pytestmark = pytest.mark.gpu
 
 
-@settings(max_examples=60, deadline=None, derandomize=True, suppress_health_check=list(HealthCheck))
+# NUP_FUZZ_EXAMPLES raises the count for a longer soak of passing code
+@settings(max_examples=int(os.environ.get("NUP_FUZZ_EXAMPLES", "60")), deadline=None, derandomize=True,
+          suppress_health_check=list(HealthCheck))
 @given(st.data())
 def test_random_shapes_and_edits(data):
     D = data.draw(st.sampled_from([64, 128]))
