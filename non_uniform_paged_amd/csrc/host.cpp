@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -173,6 +174,7 @@ struct nup_ctx {
         std::vector<int32_t> head_row_start; // [B*H+1]
     };
     std::vector<Plan> plan;                  // [NL]
+    std::vector<long long> plan_base, plan_bound;   // the balanced planner's scratch
 
     // active descriptor on the device (offsets into the inbox, in bytes)
     bool committed = false;
@@ -262,13 +264,21 @@ void plan_balanced(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
     const int32_t *capl = c->cap.data() + (size_t)layer * H;   // row s at capl + s*V
     const int NH = B * H;
     static_assert(nup::kPage == 16, "page arithmetic below uses shifts");
-    std::vector<long long> base((size_t)NH + 1, 0);  // first page of each head
-    for (int s = 0, sh = 0; s < B; ++s)
-        for (int h = 0; h < H; ++h, ++sh)
-            base[sh + 1] = base[sh] + (c->active[s] ? ((long long)capl[(size_t)s * c->V + h] + 15) >> 4 : 0);
+    // 64-bit page positions: with Alias the summed head pages are not
+    // bounded by the pool
+    std::vector<long long> &base = c->plan_base;    // first page of each head
+    std::vector<long long> &bound = c->plan_bound;  // first page of each worker's share
+    base.resize((size_t)NH + 1);
+    base[0] = 0;
+    for (int s = 0, sh = 0; s < B; ++s) {
+        const int32_t *cr = capl + (size_t)s * c->V;
+        const bool act = c->active[s] != 0;
+        for (int h = 0; h < H; ++h, ++sh) base[sh + 1] = base[sh] + (act ? (cr[h] + 15) >> 4 : 0);
+    }
     const long long T = base[NH];
-    // share boundaries floor(T*w/W), built without divisions in the loop
-    std::vector<long long> bound((size_t)W + 1);
+    // share boundaries floor(T*w/W), built without divisions in the loop; a
+    // sentinel past the last one ends every forward scan
+    bound.resize((size_t)W + 2);
     {
         const long long q = T / W, r = T % W;
         long long acc = 0, b = 0;
@@ -281,58 +291,64 @@ void plan_balanced(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
                 ++b;
             }
         }
+        bound[(size_t)W + 1] = LLONG_MAX;
     }
     const size_t max_rows = (size_t)W + 2 * (size_t)NH;
-    pl.rows.resize(4 * max_rows);
+    if (pl.rows.size() < 4 * max_rows) pl.rows.resize(4 * max_rows);
     pl.head_row_start.resize((size_t)NH + 1);
     pl.worker_start.resize((size_t)W + 1);
     int32_t *rw = pl.rows.data();
     int32_t *wst = pl.worker_start.data();
-    size_t n = 0;
+    int32_t *hrs = pl.head_row_start.data();
+    const long long *bd = bound.data();
+    int32_t n = 0;
     int w = 0;      // worker holding the current page; only moves forward
     int next = 0;   // first worker whose start row is not set yet
     // the row about to be written belongs to worker `o`: it starts every
     // worker up to o that has no row yet (owners never decrease)
     auto own = [&](int o) {
-        while (next <= o) wst[next++] = (int32_t)n;
+        while (next <= o) wst[next++] = n;
     };
     for (int sh = 0, s = 0, h = 0; sh < NH; ++sh, (++h == H ? (h = 0, ++s) : 0)) {
-        pl.head_row_start[sh] = (int32_t)n;
+        hrs[sh] = n;
         const long long lo = base[sh], hi = base[sh + 1];
+        const int32_t li = s * c->V + h;
+        int32_t *r = rw + 4 * (size_t)n;
         if (lo == hi) {
             int ow;
             if (T > 0) {
                 const long long pos = std::min(lo, T - 1);
-                while (bound[w + 1] <= pos) ++w;
+                while (bd[w + 1] <= pos) ++w;
                 ow = w;
             } else {
                 ow = (int)((long long)sh * W / NH);
             }
             own(ow);
-            rw[4 * n + 0] = sh;
-            rw[4 * n + 1] = 0;
-            rw[4 * n + 2] = 0;
-            rw[4 * n + 3] = s * c->V + h;
+            r[0] = sh;
+            r[1] = 0;
+            r[2] = 0;
+            r[3] = li;
             ++n;
             continue;
         }
         const long long cap = capl[(size_t)s * c->V + h];
         long long p = lo;
         while (p < hi) {
-            while (bound[w + 1] <= p) ++w;
-            const long long end = std::min(hi, bound[w + 1]);
+            while (bd[w + 1] <= p) ++w;
+            const long long end = std::min(hi, bd[w + 1]);
             own(w);
-            rw[4 * n + 0] = sh;
-            rw[4 * n + 1] = (int32_t)((p - lo) << 4);
-            rw[4 * n + 2] = (int32_t)std::min<long long>((end - lo) << 4, cap);
-            rw[4 * n + 3] = s * c->V + h;
+            r[0] = sh;
+            r[1] = (int32_t)((p - lo) << 4);
+            r[2] = (int32_t)std::min((end - lo) << 4, cap);
+            r[3] = li;
+            r += 4;
             ++n;
             p = end;
         }
     }
-    pl.head_row_start[NH] = (int32_t)n;
-    pl.rows.resize(4 * n);
-    while (next <= W) wst[next++] = (int32_t)n;
+    hrs[NH] = n;
+    pl.rows.resize(4 * (size_t)n);
+    while (next <= W) wst[next++] = n;
 }
 
 // The uniform split (the control): every head is cut into the same number of

@@ -239,6 +239,8 @@ void partial_attn_kernel(PartialArgs a) {
                 uint4 *dst = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(isv ? a.vbase : a.kbase) + off) + c;
                 *dst = *src;
             }
+            // every counter to zero: the stores have completed before this
+            // wave issues the loads of the page that holds them
             __builtin_amdgcn_s_waitcnt(0);
         }
 
