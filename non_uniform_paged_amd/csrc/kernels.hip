@@ -390,14 +390,25 @@ void partial_attn_kernel(PartialArgs a) {
 
 #if NUP_PREFETCH == 2
         // Two page buffers: page p+1 is in flight while page p is computed.
+        // The steady-state loads are unconditional, so the wait before each
+        // page's compute leaves the next page's eight loads outstanding
+        // (a conditional load there made the compiler wait for everything);
+        // the last one or two pages are a separate tail.
         uint4 kA[TPL], vA[TPL], kB[TPL], vB[TPL];
         load(p0, page_base(p0), kA, vA);
-        for (int p = p0; p <= p1; p += 2) {
-            if (p + 1 <= p1) load(p + 1, page_base(p + 1), kB, vB);
+        int p = p0;
+        for (; p + 2 <= p1; p += 2) {
+            load(p + 1, page_base(p + 1), kB, vB);
             compute(p, kA, vA);
-            if (p + 1 > p1) break;
-            if (p + 2 <= p1) load(p + 2, page_base(p + 2), kA, vA);
+            load(p + 2, page_base(p + 2), kA, vA);
             compute(p + 1, kB, vB);
+        }
+        if (p + 1 <= p1) {
+            load(p + 1, page_base(p + 1), kB, vB);
+            compute(p, kA, vA);
+            compute(p + 1, kB, vB);
+        } else {
+            compute(p, kA, vA);
         }
 #else
         // Ring of kDepth page buffers: pages p+1 .. p+kDepth-1 are in flight
