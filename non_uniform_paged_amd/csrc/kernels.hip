@@ -647,11 +647,22 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         };
         // only K is read: a ring of kScoreDepth pages keeps as many bytes in
         // flight as the attention kernel's K+V double buffer
+        // Steady-state trips issue every prefetch unconditionally, so the
+        // wait before a page leaves the later pages in flight; the last
+        // pages go through the guarded tail.
         uint4 kb[kScoreDepth][TPL];
 #pragma unroll
         for (int j = 0; j + 1 < kScoreDepth; ++j)
             if (p0 + j <= p1) load(p0 + j, kb[j]);
-        for (int pb = p0; pb <= p1; pb += kScoreDepth) {
+        int pb = p0;
+        for (; pb + 2 * kScoreDepth - 2 <= p1; pb += kScoreDepth) {
+#pragma unroll
+            for (int j = 0; j < kScoreDepth; ++j) {
+                load(pb + j + kScoreDepth - 1, kb[(j + kScoreDepth - 1) % kScoreDepth]);
+                score(pb + j, kb[j]);
+            }
+        }
+        for (; pb <= p1; pb += kScoreDepth) {
 #pragma unroll
             for (int j = 0; j < kScoreDepth; ++j) {
                 const int p = pb + j;
