@@ -441,10 +441,11 @@ nup_status nup_device_errors(nup_ctx *ctx, void *stream, int32_t *code);
  * achievable-bandwidth ceiling.  Errors: NUP_E_ARG, NUP_E_HIP. */
 nup_status nup_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 
-/* Plain streaming read of `bytes` (a multiple of 16) from src with 16-byte
- * loads; `sink` is a device word the kernel may write (it keeps the loads
- * alive).  The achievable read-bandwidth ceiling the decode kernel is
- * compared with.  Errors: NUP_E_ARG, NUP_E_HIP. */
+/* Plain streaming read of `bytes` (a multiple of 16) from src: 2048 waves,
+ * each reading its own contiguous share with 16-byte nontemporal loads, four
+ * per lane in flight.  `sink` is a device word the kernel may write (it keeps
+ * the loads alive).  The achievable read-bandwidth ceiling the decode kernel
+ * is compared with.  Errors: NUP_E_ARG, NUP_E_HIP. */
 nup_status nup_probe_read(const void *src, size_t bytes, void *sink, void *stream);
 
 #ifdef __cplusplus
