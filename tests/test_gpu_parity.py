@@ -86,6 +86,40 @@ def test_long_skewed_head():
     assert_attention_close(out, lse, ref, ref_lse, "long head")
 
 
+def test_two_million_token_head():
+    """One head of 2,097,152 tokens (131072 pages, page ids past 2^17, the
+    head split over every worker and merged from about 2000 rows) next to
+    short and empty heads, with a fused append at the end of the long head."""
+    H, gqa, D, B = 4, 2, 64, 2
+    L = np.array([[2 * 1024 * 1024 - 1, 40, 0, 17], [3, 1, 900, 64]], np.int32)
+    caps = L + 1
+    max_pages = 2 * 1024 * 1024 // 16
+    num_pages = max_pages + 200
+    c = Case(H=H, Hq=H * gqa, D=D, ng=H, B=B, num_pages=num_pages, max_pages=max_pages,
+             num_workers=2048, salt=19)
+    assert c.alloc([0, 1], caps, L) == pg.OK
+    c.commit()
+    kp, vp = u16(c.kpool).copy(), u16(c.vpool).copy()
+    kn = W.normal_bf16("k", (B, H, D), 191)
+    vn = W.normal_bf16("v", (B, H, D), 191)
+    nup.attn_decode_nonuniform_append(c.ctx, torch.from_numpy(kn.view(np.int16)).to(DEV),
+                                      torch.from_numpy(vn.view(np.int16)).to(DEV), c.q, c.out, c.lse,
+                                      c.scale, c.ws)
+    torch.cuda.synchronize()
+    fk, fv = kp.reshape(-1, D), vp.reshape(-1, D)
+    for s_ in range(B):
+        for h in range(H):
+            row = c.spec.physical_row(s_, h, int(c.spec.lengths[s_, h]))
+            fk[row], fv[row] = kn[s_, h], vn[s_, h]
+            c.spec.lengths[s_, h] += 1
+    assert np.array_equal(nup.get_lengths(c.ctx), c.spec.lengths)
+    assert np.array_equal(u16(c.kpool), kp) and np.array_equal(u16(c.vpool), vp)
+    ref, ref_lse = oracle.decode(u16(c.q), kp, vp, c.spec.page_table, c.spec.lengths, c.spec.group_of_head,
+                                 c.spec.slot_of_head, c.scale)
+    assert_attention_close(c.out.cpu().numpy().astype(np.float64), c.lse.cpu().numpy().astype(np.float64),
+                           ref, ref_lse, "2M-token head")
+
+
 def test_length_one_returns_v_bit_exact():
     H, gqa, D, B = 8, 5, 128, 3
     L = np.ones((B, H), np.int32)
