@@ -825,8 +825,8 @@ def main():
                          "calibration and achievable-bandwidth ceiling), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the path shards by sequence "
-                                   "or head group with no exchange, but no multi-GPU run is provided",
+        print(json.dumps({"error": "one GPU only: the path would shard by sequence or head group "
+                                   "with no exchange between GPUs, but no multi-GPU run is provided",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
