@@ -112,7 +112,8 @@ typedef struct nup_config {
 } nup_config;
 
 /* Bytes of the device descriptor arena a configuration needs (active
- * descriptor, page tables, error word).  Host only; no device call. */
+ * descriptor with every layer's plan at a fixed place, page tables, error
+ * word).  Host only; no device call. */
 nup_status nup_desc_bytes(const nup_config *cfg, size_t *bytes);
 
 /* Create a context over caller-owned pools and arena.  The arena is not
@@ -185,8 +186,8 @@ nup_status kv_free_seqs(nup_ctx *ctx, int32_t n, const int32_t *slots);
 
 /* nup_commit -- seal the step (KV-RM, Fig 3: one Frame commit through a
  * shadow-to-active descriptor swap).  One host-to-device copy of the packed
- * shadow (activity, lengths, and when they changed: the split-K plan, the
- * trains and page-table row patches) into the arena, then, if rows changed,
+ * shadow (activity, lengths, and when they changed: the budgets, the
+ * split-K plan, the trains and page-table row patches) into the arena, then, if rows changed,
  * one small kernel that applies the patches.  Kernels enqueued earlier on
  * the stream see the previous descriptor.  Every kernel argument the
  * library derives from the descriptor (plan, lengths and page-table
