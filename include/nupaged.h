@@ -356,7 +356,9 @@ nup_status attn_decode_topk_paged(nup_ctx *ctx, const void *q, const int32_t *id
  *   workspace  device, >= nup_select_workspace_bytes() bytes, 256-byte aligned
  *              (fp32 scores, then the selection's histograms and counts)
  * Requires a committed descriptor and L >= K for every active head (checked
- * on the host).  Errors: NUP_E_ARG, NUP_E_STATE, NUP_E_HIP. */
+ * on the host; for a captured call the check covers the lengths at capture,
+ * and the caller keeps L >= K through the replays).  Errors: NUP_E_ARG,
+ * NUP_E_STATE, NUP_E_HIP. */
 nup_status kv_select_topk(nup_ctx *ctx, const void *q, int32_t K, int32_t window, int32_t *idx_out,
                           void *workspace, size_t ws_bytes, void *stream);
 /* Workspace bytes for kv_select_topk: B_max * H_kv * max_pages * P fp32

@@ -222,3 +222,69 @@ def test_graph_append_stops_at_budget(fused):
                                      sp.slot_of_head[sl], c.scale)
         assert_attention_close(c.out.cpu().numpy().astype(np.float64), c.lse.cpu().numpy().astype(np.float64),
                                ref, ref_lse, f"after replays, layer {l}")
+
+
+def test_graph_select_then_attend_in_place():
+    """The sparse decode step (KVDrive, Fig 1: choose critical entries, then
+    attend to them) in a graph: append, exact top-K selection and in-place
+    top-K attention, replayed across Trim / Reserve commits and compared bit
+    for bit with the same calls made eagerly on a twin context."""
+    rs = np.random.default_rng(77)
+    H1, gqa, D1, B1, K, window, replays = 4, 4, 128, 3, 32, 8, 5
+    max_pages = 40
+    kw = dict(H=H1, Hq=H1 * gqa, D=D1, ng=2, B=B1, num_pages=B1 * 2 * max_pages + 3, max_pages=max_pages,
+              free_list_init=rs.permutation(B1 * 2 * max_pages + 3), num_workers=50, salt=77)
+    G, E = Case(**kw), Case(**kw)
+
+    def lengths(n):
+        return rs.integers(K + 1, 600, size=(n, H1)).astype(np.int32)
+
+    L = lengths(2)
+    for c in (G, E):
+        assert c.alloc([0, 2], L + replays + 2, L) == pg.OK
+        c.commit()
+    kn = torch.empty((B1, H1, D1), dtype=torch.bfloat16, device=DEV)
+    vn = torch.empty_like(kn)
+    q = torch.empty((B1, H1 * gqa, D1), dtype=torch.bfloat16, device=DEV)
+    bufs = {}
+    for name, c in (("G", G), ("E", E)):
+        bufs[name] = dict(idx=torch.full((B1, H1, K), -3, dtype=torch.int32, device=DEV),
+                          out=torch.empty((B1, H1 * gqa, D1), dtype=torch.float32, device=DEV),
+                          lse=torch.empty((B1, H1 * gqa), dtype=torch.float32, device=DEV),
+                          sws=torch.empty(nup.select_workspace_bytes(c.ctx), dtype=torch.uint8, device=DEV),
+                          aws=torch.empty(nup.workspace_bytes(c.ctx, K), dtype=torch.uint8, device=DEV))
+
+    def step(c, b):
+        nup.kv_append(c.ctx, kn, vn)
+        nup.kv_select_topk(c.ctx, q, K, window, b["idx"], b["sws"])
+        nup.attn_decode_topk_paged(c.ctx, q, b["idx"], K, b["out"], b["lse"], c.scale, b["aws"])
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(G, bufs["G"])
+    live = {0, 2}
+    for i in range(replays):
+        if i == 2:
+            for c in (G, E):
+                c.free([0])
+            live.discard(0)
+        if i == 3:
+            L = lengths(2)
+            for c in (G, E):
+                assert c.alloc([0, 1], L + replays, L) == pg.OK
+            live |= {0, 1}
+        for c in (G, E):
+            c.commit()
+        kn.copy_(_dev_bf16("k", (B1, H1, D1), 3000 + i))
+        vn.copy_(_dev_bf16("v", (B1, H1, D1), 3000 + i))
+        q.copy_(_dev_bf16("q", (B1, H1 * gqa, D1), 3000 + i))
+        g.replay()
+        nup.note_appends(G.ctx, 1)
+        step(E, bufs["E"])
+        torch.cuda.synchronize()
+        act = sorted(live)
+        for key in ("idx", "out", "lse"):
+            assert torch.equal(bufs["G"][key][act], bufs["E"][key][act]), (i, key)
+        assert np.array_equal(nup.get_lengths(G.ctx), nup.get_lengths(E.ctx)), i
+    assert torch.equal(G.kpool, E.kpool) and torch.equal(G.vpool, E.vpool)
+    assert nup.device_errors(G.ctx) == nup.NUP_OK and nup.device_errors(E.ctx) == nup.NUP_OK
