@@ -11,11 +11,11 @@
 //  * Frame commit (KV-RM, Fig 3 shadow-to-active swap): the host shadow is
 //    packed into a pinned buffer and reaches the device in one copy; page
 //    table rows that changed travel as patches applied by one small kernel.
-//    Every section sits at a fixed place in the arena, so the kernels'
-//    arguments never change for a context and a decode step captured into a
-//    HIP graph once replays correctly across commits (KV-RM's static-graph
-//    decoder); calls made under capture leave the host shadow to
-//    nup_note_appends.
+//    What the decode kernels read (lengths, budgets, every layer's plan, the
+//    page tables) sits at fixed places in the arena, so their arguments never
+//    change for a context and a decode step captured into a HIP graph once
+//    replays correctly across commits (KV-RM's static-graph decoder); calls
+//    made under capture leave the host shadow to nup_note_appends.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
