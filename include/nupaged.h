@@ -186,16 +186,19 @@ nup_status kv_free_seqs(nup_ctx *ctx, int32_t n, const int32_t *slots);
 
 /* nup_commit -- seal the step (KV-RM, Fig 3: one Frame commit through a
  * shadow-to-active descriptor swap).  One host-to-device copy of the packed
- * shadow (activity, lengths, and when they changed: the budgets, the
- * split-K plan, the trains and page-table row patches) into the arena, then, if rows changed,
- * one small kernel that applies the patches.  Kernels enqueued earlier on
- * the stream see the previous descriptor.  Every kernel argument the
- * library derives from the descriptor (plan, lengths and page-table
- * addresses, worker counts) is the same after every commit of a context, so
- * a decode step captured into a HIP graph once stays valid while commits
- * between its replays change the mapping (KV-RM, abstract and Fig 2: a
- * fixed-shape decoder over a per-step descriptor).  Always eager: refused
- * with NUP_E_STATE on a capturing stream.  Errors: NUP_E_STATE, NUP_E_HIP. */
+ * shadow (activity and lengths; when they changed, also the budgets, the
+ * split-K plans, the trains and page-table row patches) into the arena,
+ * then, if rows changed, one small kernel that applies the patches.  Kernels
+ * enqueued earlier on the stream see the previous descriptor.
+ * Every argument that the decode calls (kv_append, the attention calls,
+ * kv_select_topk) derive from the descriptor -- plan, lengths and
+ * page-table addresses, worker counts -- is the same after every commit of
+ * a context.  So a decode step captured into a HIP graph once stays valid
+ * while commits between its replays change the mapping (KV-RM, abstract and
+ * Fig 2: a fixed-shape decoder over a per-step descriptor).  The trains
+ * gathers size their launches from the current trains and are not for
+ * capture.  The commit itself always runs eagerly: NUP_E_STATE on a
+ * capturing stream.  Errors: NUP_E_STATE, NUP_E_HIP. */
 nup_status nup_commit(nup_ctx *ctx, void *stream);
 
 /*
