@@ -196,8 +196,8 @@ nup_status kv_free_seqs(nup_ctx *ctx, int32_t n, const int32_t *slots);
  * a context.  So a decode step captured into a HIP graph once stays valid
  * while commits between its replays change the mapping (KV-RM, abstract and
  * Fig 2: a fixed-shape decoder over a per-step descriptor).  The trains
- * gathers size their launches from the current trains and are not for
- * capture.  The commit itself always runs eagerly: NUP_E_STATE on a
+ * gathers size their launches from the current trains and refuse capture
+ * (NUP_E_STATE).  The commit itself always runs eagerly: NUP_E_STATE on a
  * capturing stream.  Errors: NUP_E_STATE, NUP_E_HIP. */
 nup_status nup_commit(nup_ctx *ctx, void *stream);
 

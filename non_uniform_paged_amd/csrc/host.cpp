@@ -954,6 +954,8 @@ nup_status kv_gather_compact(nup_ctx *c, int32_t mode, const int32_t *idx, int32
         e = nup::launch_gather_index(a, c->D, st);
     } else if (mode == 0) {
         if (!row_off) return fail(c, NUP_E_ARG, "train mode needs row_off");
+        // the launch is sized by the current trains, which the next commit changes
+        if (capturing(st)) return fail(c, NUP_E_STATE, "the trains gather cannot be captured into a graph");
         nup::GatherRunsArgs a{};
         a.k_pool = c->kpool;
         a.v_pool = c->vpool;
@@ -987,6 +989,7 @@ nup_status kv_gather_trains_dma(nup_ctx *c, void *k_out, void *v_out, const int6
     if (!c->committed || c->pending) return fail(c, NUP_E_STATE, "needs a committed descriptor and no pending edits");
     if (!k_out || !v_out || !row_off) return fail(c, NUP_E_ARG, "k_out, v_out and row_off are required");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (capturing(st)) return fail(c, NUP_E_STATE, "copies of the current trains cannot be captured into a graph");
     const size_t row_bytes = (size_t)c->D * 2, page_rows = (size_t)c->P;
     const size_t page_bytes = page_rows * row_bytes;          // one head's rows of one page
     const size_t src_pitch = (size_t)c->gh * page_bytes;      // next physical page, same head slot

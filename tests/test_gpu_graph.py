@@ -176,6 +176,9 @@ def test_graph_append_stops_at_budget(fused):
                                              raise_on_error=False) == nup.NUP_E_CAPACITY
 
     g = torch.cuda.CUDAGraph()
+    ks = torch.empty((4096, D), dtype=torch.bfloat16, device=DEV)
+    row_off = np.arange(B * H, dtype=np.int64) * 200
+    row_off_dev = torch.from_numpy(row_off).to(DEV)
     with torch.cuda.graph(g):
         for l in range(NL):
             if fused:
@@ -183,6 +186,10 @@ def test_graph_append_stops_at_budget(fused):
             else:
                 nup.set_layer(c.ctx, l)
                 nup.kv_append(c.ctx, kn, vn)
+        # the trains gathers are sized by the current trains: refused under capture
+        assert nup.kv_gather_compact(c.ctx, 0, ks, ks, row_off=row_off_dev,
+                                     raise_on_error=False) == nup.NUP_E_STATE
+        assert nup.kv_gather_trains_dma(c.ctx, ks, ks, row_off, raise_on_error=False) == nup.NUP_E_STATE
     fk, fv = u16(c.kpool).copy().reshape(-1, D), u16(c.vpool).copy().reshape(-1, D)
     sp = c.spec
     for i in range(3):
