@@ -172,6 +172,21 @@ def time_steps(setup, steps, warmup, append=True, fused=True, per_step=None):
     return ms, kms / max(n, 1), mean_L
 
 
+def plan_straggler(ctx, lengths):
+    """Largest over mean per-worker pages of the committed plan, counting
+    each row's pages up to the head's current length: the straggler
+    measure of the split (1.0 = every worker has the same work)."""
+    import non_uniform_paged_amd as nup
+    rows, ws, _ = nup.get_plan(ctx)
+    L = np.asarray(lengths, np.int64).reshape(-1)
+    t1 = np.minimum(rows[:, 2].astype(np.int64), L[rows[:, 0]])
+    t0 = rows[:, 1].astype(np.int64)
+    pages = np.where(t1 > t0, (t1 + 15) // 16 - t0 // 16, 0)
+    cs = np.concatenate([[0], np.cumsum(pages)])
+    per = cs[ws[1:]] - cs[ws[:-1]]
+    return float(per.max() / max(per.mean(), 1e-9)), int(len(ws) - 1)
+
+
 def traffic_from_profiles(kernel_src_sha):
     p = os.path.join(ROOT, "profiles", "traffic_partial_attn_qwen25_32b.json")
     if not os.path.exists(p):
@@ -875,6 +890,8 @@ def main():
              "pct_of_peak_step": round(100 * value / PEAK_HBM_GBS, 2)}
 
     extra["step_launches"] = 3 if args.unfused else 2
+    ratio, nw = plan_straggler(st.ctx, nup.get_lengths(st.ctx))
+    extra["straggler_balanced"] = {"max_over_mean_pages": round(ratio, 3), "workers": nw}
     if not args.no_controls:
         # the distribution of single steps, in a pass of its own (an event
         # between steps keeps them from overlapping, so these run slower)
@@ -908,6 +925,17 @@ def main():
             sc.free()
             del sc
         extra["nonuniform_over_uniform50"] = round(achieved / extra["control_uniform50_kernel_GBs"], 4)
+        # the uniform split Tangram measures against (every head cut into 8
+        # chunks, one per worker) on the same non-uniform batch
+        su = Setup(w, headroom, plan_mode=nup.PLAN_UNIFORM, uniform_splits=8)
+        ums, ukms, uL = time_steps(su, max(10, args.steps // 2), args.warmup)
+        ub = algorithmic_bytes(uL, su.caps, B, Hq, H, ng) - B * Hq * D * 4
+        extra["control_uniform_split_kernel_ms"] = round(ukms, 4)
+        extra["control_uniform_split_kernel_GBs"] = round(ub / (ukms * 1e-3) / 1e9, 1)
+        ratio, nw = plan_straggler(su.ctx, nup.get_lengths(su.ctx))
+        extra["straggler_uniform_split"] = {"max_over_mean_pages": round(ratio, 3), "workers": nw}
+        su.free()
+        del su
 
     # achievable streaming-read ceiling on this device (4 GiB, beyond the caches)
     nbytes = 4 << 30
