@@ -570,7 +570,7 @@ def measure_extras(args, only=None):
         wkms /= max(n, 1)
         res["qwen3_4b"] = {"kv_bytes": kv_bytes(st.lengths0), "attn_call_ms": round(ms, 4),
                            "partial_kernel_ms": round(kms, 4),
-                           "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
+                           "partial_kernel_GBs": round(sum(step_kb) / (kms_total * 1e-3) / 1e9, 1),
                            "warm_attn_call_ms": round(wms, 4), "warm_partial_kernel_ms": round(wkms, 4),
                            "warm_partial_kernel_GBs": round(kb / (wkms * 1e-3) / 1e9, 1),
                            "note": "cold: 1 GiB read between launches; warm: back to back"}
@@ -651,7 +651,7 @@ def measure_extras(args, only=None):
         drv = W.ChurnDriver(w.batch)
         active = np.ones(w.batch, bool)
         freed = np.zeros(0, np.int32)
-        host_us, trains, gpu_ms = [], [], []
+        host_us, trains, gpu_ms, step_kb = [], [], [], []
         nup.kernel_time(st.ctx, reset=True)
         for it in range(steps_warm + steps):
             lib = 0.0   # host time inside the library: Reserve, Trim, frame commit
@@ -681,13 +681,16 @@ def measure_extras(args, only=None):
             if timed:
                 e1.record()
                 nup.set_timing(st.ctx, False)
+                # the call advanced the shadow lengths by the appended token,
+                # which the step also reads: these are the step's K/V bytes
+                step_kb.append(kv_bytes(nup.get_lengths(st.ctx)))
             torch.cuda.synchronize()
             if timed:
                 gpu_ms.append(e0.elapsed_time(e1))
-        kms, n = nup.kernel_time(st.ctx, reset=True)
-        kms /= max(n, 1)
+        kms_total, n = nup.kernel_time(st.ctx, reset=True)
+        assert n == len(step_kb), (n, len(step_kb))
+        kms = kms_total / max(n, 1)
         L_now = nup.get_lengths(st.ctx)
-        kb = kv_bytes(L_now)
         # train-mode gather of the final state
         lens = L_now.astype(np.int64).reshape(-1)
         row_off = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)[:-1]])).cuda()
@@ -699,14 +702,16 @@ def measure_extras(args, only=None):
         g_ms = _timed(gt, 5, flush)
         dma = None if args.no_copy_engine else _dma_trains(st, ksg, vsg, row_off.cpu().numpy(), flush)
         res["mixed_churn"] = {
-            "active_slots": int(active.sum()), "kv_bytes": kb,
+            "active_slots": int(active.sum()),
+            "kv_bytes_per_step_mean": int(np.mean(step_kb)),
+            "kv_bytes_per_step_range": [int(min(step_kb)), int(max(step_kb))],
             "host_trim_reserve_commit_us_mean": round(float(np.mean(host_us)), 1),
             "gpu_append_attn_ms_mean": round(float(np.mean(gpu_ms)), 4),
             "submit_share": round(float(np.mean(host_us)) / (float(np.mean(host_us)) + 1e3 * float(np.mean(gpu_ms))), 4),
             "trains_per_step_mean": round(float(np.mean(trains)), 1),
             "pages_in_use": int(st.num_pages - len(nup.get_free_list(st.ctx))),
             "partial_kernel_ms": round(kms, 4),
-            "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
+            "partial_kernel_GBs": round(sum(step_kb) / (kms_total * 1e-3) / 1e9, 1),
             "gather_trains_ms": round(g_ms, 4),
             "gather_trains_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1),
             "gather_trains_copy_engine": dma}
