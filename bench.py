@@ -570,7 +570,7 @@ def measure_extras(args, only=None):
         wkms /= max(n, 1)
         res["qwen3_4b"] = {"kv_bytes": kv_bytes(st.lengths0), "attn_call_ms": round(ms, 4),
                            "partial_kernel_ms": round(kms, 4),
-                           "partial_kernel_GBs": round(sum(step_kb) / (kms_total * 1e-3) / 1e9, 1),
+                           "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
                            "warm_attn_call_ms": round(wms, 4), "warm_partial_kernel_ms": round(wkms, 4),
                            "warm_partial_kernel_GBs": round(kb / (wkms * 1e-3) / 1e9, 1),
                            "note": "cold: 1 GiB read between launches; warm: back to back"}
