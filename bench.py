@@ -750,14 +750,16 @@ def measure_extras(args, only=None):
     #    unshared batch is timed the same way for comparison
     if want("qwen25_32b_prefix"):
         res["qwen25_32b_prefix"] = {}
-        for tag, w in (("unshared", W.qwen25_32b()), ("forked", W.qwen25_32b_prefix())):
-            st = Setup(w, 0)
+        for tag, w, mode in (("unshared", W.qwen25_32b(), nup.PLAN_BALANCED),
+                             ("forked", W.qwen25_32b_prefix(), nup.PLAN_BALANCED),
+                             ("forked_shared_plan", W.qwen25_32b_prefix(), nup.PLAN_SHARED)):
+            st = Setup(w, 0, plan_mode=mode)
             for _ in range(2):
                 st.step(append=False)
             torch.cuda.synchronize()
             nup.kernel_time(st.ctx, reset=True)
             nup.set_timing(st.ctx, True)
-            _timed(lambda: st.step(append=False), 10, flush)
+            call_ms = _timed(lambda: st.step(append=False), 10, flush)
             nup.set_timing(st.ctx, False)
             kms, n = nup.kernel_time(st.ctx, reset=True)
             kms /= max(n, 1)
@@ -771,6 +773,7 @@ def measure_extras(args, only=None):
                 "pages_in_use": in_use, "page_table_entries": entries,
                 "reserved_saving": round(1 - in_use / entries, 4),
                 "kv_bytes_logical": kb, "kv_bytes_unique": kb - shared_b,
+                "attn_call_ms": round(call_ms, 4),
                 "partial_kernel_ms": round(kms, 4),
                 "partial_kernel_logical_GBs": round(kb / (kms * 1e-3) / 1e9, 1)}
             st.free()

@@ -78,7 +78,16 @@ enum {
     /* The uniform split Tangram measures against (Fig 4c): every head is cut
      * into the same number of chunks regardless of its length, one chunk
      * per worker, scheduled by the hardware. */
-    NUP_PLAN_UNIFORM = 1
+    NUP_PLAN_UNIFORM = 1,
+    /* The balanced plan made aware of Alias (KV-RM, Fig 3): for head-group
+     * pages that several forked sequences map at the same logical positions,
+     * every sharer's copy of a chunk is the first row of its own worker, and
+     * a chunk's workers sit on one XCD, so they read the same blocks together
+     * and all but the first read can be served from that XCD's L2.  Rows are
+     * stored in worker order; nup_get_plan_head_rows() lists each head's rows.
+     * Without shared pages (or with more sharer rows than workers) it equals
+     * NUP_PLAN_BALANCED.  The result is the same attention either way. */
+    NUP_PLAN_SHARED = 2
 };
 
 typedef struct nup_ctx nup_ctx;
@@ -94,7 +103,7 @@ typedef struct nup_config {
     int32_t num_pages;      /* physical pages in each pool */
     int32_t max_pages;      /* logical pages per (slot, group): page-table row length */
     int32_t num_workers;    /* split-K workers (waves); 0 = chosen from the device */
-    int32_t plan_mode;      /* NUP_PLAN_BALANCED or NUP_PLAN_UNIFORM */
+    int32_t plan_mode;      /* NUP_PLAN_BALANCED, NUP_PLAN_UNIFORM or NUP_PLAN_SHARED */
     int32_t uniform_splits; /* chunks per head for NUP_PLAN_UNIFORM (0 = 8) */
     int32_t num_layers;     /* layers sharing the pager (0 or 1: a single layer).
                                The pager's heads are the V = num_layers * H_kv
@@ -426,6 +435,12 @@ nup_status nup_get_runs(const nup_ctx *ctx, int32_t *out, int32_t max_runs, int3
  *   head_row_start int32 [B_max*H_kv + 1] */
 nup_status nup_get_plan(const nup_ctx *ctx, int32_t *n_rows, int32_t *n_workers,
                         int32_t *rows, int32_t *worker_start, int32_t *head_row_start);
+/* Row ids of each head in the current layer's plan, int32 [n_rows]: head
+ * sh's rows are head_rows[head_row_start[sh] .. head_row_start[sh+1]), in
+ * token order.  Under NUP_PLAN_SHARED the rows table is in worker order and
+ * this is the index the merge uses; under the other modes a head's rows are
+ * contiguous and this is 0, 1, ..., n_rows - 1.  Errors: NUP_E_ARG. */
+nup_status nup_get_plan_head_rows(const nup_ctx *ctx, int32_t *head_rows);
 
 /* ---- measurement helpers ------------------------------------------------ */
 

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libnupaged.so")
 NUP_OK, NUP_E_ARG, NUP_E_NOPAGES, NUP_E_CAPACITY, NUP_E_STATE, NUP_E_HIP, NUP_E_INDEX = range(7)
 STATUS_NAMES = {0: "NUP_OK", 1: "NUP_E_ARG", 2: "NUP_E_NOPAGES", 3: "NUP_E_CAPACITY",
                 4: "NUP_E_STATE", 5: "NUP_E_HIP", 6: "NUP_E_INDEX"}
-PLAN_BALANCED, PLAN_UNIFORM = 0, 1
+PLAN_BALANCED, PLAN_UNIFORM, PLAN_SHARED = 0, 1, 2
 PAGE = 16
 
 
@@ -79,6 +79,7 @@ _sigs = {
     "nup_note_appends": [_P, _I, _I],
     "nup_get_runs": [_P, _P, _I, _P],
     "nup_get_plan": [_P, _P, _P, _P, _P, _P],
+    "nup_get_plan_head_rows": [_P, _P],
     "nup_set_timing": [_P, _I],
     "nup_kernel_time": [_P, _P, _P, _I],
     "nup_device_errors": [_P, _P, _P],
@@ -371,6 +372,14 @@ def get_plan(ctx: Context):
     ctx.check(_lib.nup_get_plan(ctx.handle, None, None, rows.ctypes.data, ws.ctypes.data,
                                 hrs.ctypes.data))
     return rows[: nr.value], ws, hrs
+
+
+def get_plan_head_rows(ctx: Context) -> np.ndarray:
+    nr = ctypes.c_int32()
+    ctx.check(_lib.nup_get_plan(ctx.handle, ctypes.byref(nr), None, None, None, None))
+    out = np.zeros(max(nr.value, 1), np.int32)
+    ctx.check(_lib.nup_get_plan_head_rows(ctx.handle, out.ctypes.data))
+    return out[: nr.value]
 
 
 def set_timing(ctx: Context, enable: bool = True):

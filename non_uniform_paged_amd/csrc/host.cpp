@@ -77,7 +77,8 @@ nup_status validate(const nup_config *c, std::string *why) {
         return bad("pool too large for 32-bit row ids");
     if ((long long)c->max_pages * nup::kPage > 0x7fffffffLL) return bad("max_pages too large");
     if (c->num_workers < 0) return bad("num_workers must be >= 0");
-    if (c->plan_mode != NUP_PLAN_BALANCED && c->plan_mode != NUP_PLAN_UNIFORM) return bad("unknown plan_mode");
+    if (c->plan_mode != NUP_PLAN_BALANCED && c->plan_mode != NUP_PLAN_UNIFORM && c->plan_mode != NUP_PLAN_SHARED)
+        return bad("unknown plan_mode");
     if (c->uniform_splits < 0) return bad("uniform_splits must be >= 0");
     return NUP_OK;
 }
@@ -90,6 +91,10 @@ Sizes compute_sizes(const nup_config &c, int workers) {
     if (c.plan_mode == NUP_PLAN_UNIFORM) {
         z.max_rows = (int)(B * H * splits);
         z.max_workers = z.max_rows;
+    } else if (c.plan_mode == NUP_PLAN_SHARED) {
+        // at most one gang row per worker, plus the balanced bound
+        z.max_rows = 2 * workers + 2 * (int)(B * H);
+        z.max_workers = workers;
     } else {
         z.max_rows = workers + 2 * (int)(B * H);
         z.max_workers = workers;
@@ -98,6 +103,9 @@ Sizes compute_sizes(const nup_config &c, int workers) {
     z.caps = align_up(4 * B * V);
     z.plan_layer = align_up(4 * ((size_t)z.max_workers + 1)) + align_up(4 * (B * H + 1)) +
                    align_up(16 * (size_t)z.max_rows);
+    // the shared plan's rows are in worker order; head_rows lists each
+    // head's rows for the merge
+    if (c.plan_mode == NUP_PLAN_SHARED) z.plan_layer += align_up(4 * (size_t)z.max_rows);
     z.plan_max = NL * z.plan_layer;
     // every train covers at least one live page-table entry; with Alias the
     // entries (not the physical pages) are what bounds their number
@@ -177,13 +185,14 @@ struct nup_ctx {
         std::vector<int32_t> rows;           // [n][4] (s*H + h, t0, t1, 0)
         std::vector<int32_t> worker_start;   // [W+1]
         std::vector<int32_t> head_row_start; // [B*H+1]
+        std::vector<int32_t> head_rows;      // shared plan: row ids by head (empty: identity)
     };
     std::vector<Plan> plan;                  // [NL]
     std::vector<long long> plan_base, plan_bound;   // the balanced planner's scratch
 
     // active descriptor on the device (offsets into the inbox, in bytes)
     bool committed = false;
-    std::vector<size_t> off_ws, off_hrs, off_rows;   // [NL]
+    std::vector<size_t> off_ws, off_hrs, off_rows, off_hr;   // [NL]
     std::vector<int> dev_workers, dev_rows;          // [NL]
     size_t off_runs = 0, off_runpre = 0;
     int dev_runs = 0, dev_run_pages = 0;
@@ -385,9 +394,250 @@ void plan_uniform(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
     std::iota(pl.worker_start.begin(), pl.worker_start.end(), 0);
 }
 
+// Share-aware plan (KV-RM, Fig 3: Alias).  Sequences forked from one source
+// map the same physical pages at the same logical positions, so those
+// tokens hold the same K/V for every sharer.  The balanced plan reads them
+// once per sharer at unrelated points of the pass, far too far apart for any
+// cache to keep them.  Here every sharer's copy of a shared chunk is the
+// first row of its own worker, and the workers of one chunk ("a gang") sit
+// on one XCD: they start together and read the same blocks within a short
+// window, so after the first read the others can hit in that XCD's L2.
+//  * Sharing sets: per head group, active slots whose page-table rows begin
+//    with the same page, provided that page has more than one reference.
+//    The set's shared range is the pages all its rows have in common,
+//    capped at every member head's capacity.
+//  * Gangs: every (set, head of this layer in the group) range is cut into
+//    near-equal chunks of at most c pages, c the smallest size for which
+//    all chunks' rows (one per sharer) fit one per worker.
+//  * The rest of every head (everything, for heads in no set) is cut like
+//    the balanced plan, with each worker's share reduced by its gang row.
+// Rows are stored in worker order; head_rows lists each head's rows for the
+// merge.  No sharing, or sharing too wide for the workers, gives exactly the
+// balanced plan.  Correctness never depends on the sharing: every head's
+// [0, cap) is still covered exactly once.
+void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
+    const int B = c->B, H = c->H, W = c->workers;
+    const int NH = B * H;
+    const int32_t *capl = c->cap.data() + (size_t)layer * H;
+    auto pages_of = [&](int s, int h) -> long long {
+        return c->active[s] ? ((long long)capl[(size_t)s * c->V + h] + 15) >> 4 : 0;
+    };
+    // -- sharing sets and their shared page counts
+    struct Gang { int g, h; long long len; int first, n; };   // members: mem[first .. first+n)
+    std::vector<int32_t> mem;
+    std::vector<Gang> gangs;
+    std::vector<long long> shared0((size_t)NH, 0);   // first unshared page of each head
+    {
+        std::vector<std::pair<int32_t, int32_t>> keys;   // (first page, slot)
+        for (int g = 0; g < c->ng; ++g) {
+            std::vector<int> heads;
+            for (int h = 0; h < H; ++h)
+                if (c->goh[(size_t)layer * H + h] == g) heads.push_back(h);
+            if (heads.empty()) continue;
+            keys.clear();
+            for (int s = 0; s < B; ++s) {
+                const size_t ri = (size_t)g * B + s;
+                if (!c->active[s] || c->npages[ri] == 0) continue;
+                const int32_t p0 = c->pt[ri * c->max_pages];
+                if (p0 >= 0 && c->ref[p0] > 1) keys.emplace_back(p0, s);
+            }
+            std::sort(keys.begin(), keys.end());
+            for (size_t i = 0; i < keys.size();) {
+                size_t j = i;
+                while (j < keys.size() && keys[j].first == keys[i].first) ++j;
+                if (j - i >= 2) {
+                    const int32_t *r0 = &c->pt[((size_t)g * B + keys[i].second) * c->max_pages];
+                    long long len = c->npages[(size_t)g * B + keys[i].second];
+                    for (size_t k = i + 1; k < j; ++k) {
+                        const size_t rk = (size_t)g * B + keys[k].second;
+                        const int32_t *r = &c->pt[rk * c->max_pages];
+                        long long m = 0;
+                        const long long lim = std::min<long long>(len, c->npages[rk]);
+                        while (m < lim && r[m] == r0[m]) ++m;
+                        len = m;
+                    }
+                    for (int h : heads)
+                        for (size_t k = i; k < j; ++k)
+                            len = std::min(len, (long long)capl[(size_t)keys[k].second * c->V + h] >> 4);
+                    if (len > 0) {
+                        for (int h : heads) {
+                            gangs.push_back({g, h, len, (int)mem.size(), (int)(j - i)});
+                            for (size_t k = i; k < j; ++k) shared0[(size_t)keys[k].second * H + h] = len;
+                        }
+                        for (size_t k = i; k < j; ++k) mem.push_back(keys[k].second);
+                    }
+                }
+                i = j;
+            }
+        }
+    }
+    long long T = 0;
+    for (int s = 0; s < B; ++s)
+        for (int h = 0; h < H; ++h) T += pages_of(s, h);
+    const long long Aq = W > 0 ? (T + W - 1) / W : 0;
+    long long maxlen = 0, nsum = 0;
+    for (const Gang &gg : gangs) {
+        maxlen = std::max(maxlen, gg.len);
+        nsum += gg.n;
+    }
+    auto gang_rows = [&](long long cc) {
+        long long r = 0;
+        for (const Gang &gg : gangs) r += (long long)gg.n * ((gg.len + cc - 1) / cc);
+        return r;
+    };
+    long long chunk = 0;
+    if (!gangs.empty() && nsum <= W && T > 0) {
+        long long lo = 1, hi = maxlen;   // gang_rows(maxlen) = nsum <= W
+        while (lo < hi) {
+            const long long mid = (lo + hi) / 2;
+            if (gang_rows(mid) <= W) hi = mid;
+            else lo = mid + 1;
+        }
+        chunk = lo;
+        if (chunk > Aq) chunk = 0;   // a chunk longer than a worker's share would straggle
+    }
+    if (chunk == 0) {
+        pl.head_rows.clear();
+        plan_balanced(c, layer, pl);
+        return;
+    }
+    // -- gang rows: virtual worker v, XCD-major, so that consecutive v share
+    //    an XCD (workgroups go to the XCDs round robin, kWavesPerBlock waves each)
+    constexpr int kXcd = 8;
+    const int per_xcd = W / kXcd;
+    const bool xcd_map = W % (kXcd * nup::kWavesPerBlock) == 0;
+    auto phys = [&](int v) -> int {
+        if (!xcd_map) return v;
+        const int x = v / per_xcd, j = v % per_xcd;
+        return ((j / nup::kWavesPerBlock) * kXcd + x) * nup::kWavesPerBlock + j % nup::kWavesPerBlock;
+    };
+    std::vector<int32_t> grow((size_t)W * 4, -1);   // the gang row of each physical worker
+    std::vector<long long> gload((size_t)W, 0);
+    {
+        int v = 0;
+        for (const Gang &gg : gangs) {
+            const long long k = (gg.len + chunk - 1) / chunk;
+            for (long long i = 0; i < k; ++i) {
+                const long long p0 = gg.len * i / k, p1 = gg.len * (i + 1) / k;
+                for (int m = 0; m < gg.n; ++m, ++v) {
+                    const int s = mem[(size_t)gg.first + m];
+                    const int w = phys(v);
+                    int32_t *r = &grow[(size_t)w * 4];
+                    r[0] = s * H + gg.h;
+                    r[1] = (int32_t)(p0 << 4);
+                    r[2] = (int32_t)(p1 << 4);
+                    r[3] = s * c->V + gg.h;
+                    gload[w] = p1 - p0;
+                }
+            }
+        }
+    }
+    // -- the rest, cut into shares proportional to each worker's room
+    std::vector<long long> ubase((size_t)NH + 1, 0);
+    for (int sh = 0; sh < NH; ++sh) {
+        const long long hp = pages_of(sh / H, sh % H);
+        ubase[sh + 1] = ubase[sh] + std::max(0LL, hp - shared0[sh]);
+    }
+    const long long U = ubase[NH];
+    std::vector<long long> bound((size_t)W + 2);
+    {
+        long long room_total = 0;
+        for (int w = 0; w < W; ++w) room_total += std::max(0LL, Aq - gload[w]);
+        long long acc = 0;
+        for (int w = 0; w <= W; ++w) {
+            bound[w] = room_total ? (long long)((__int128)U * acc / room_total) : (w ? U : 0);
+            if (w < W) acc += std::max(0LL, Aq - gload[w]);
+        }
+        bound[W] = U;
+        bound[(size_t)W + 1] = LLONG_MAX;
+    }
+    // rest rows in head order; owners never decrease
+    std::vector<int32_t> rest;     // [n][4]
+    std::vector<int32_t> owner;    // [n]
+    {
+        int w = 0;
+        for (int sh = 0; sh < NH; ++sh) {
+            const int s = sh / H, h = sh % H;
+            const long long lo = ubase[sh], hi = ubase[sh + 1];
+            const int32_t li = s * c->V + h;
+            if (lo == hi) {
+                if (shared0[sh] > 0) continue;   // covered by its gang rows
+                int ow;
+                if (U > 0) {
+                    const long long pos = std::min(lo, U - 1);
+                    while (bound[w + 1] <= pos) ++w;
+                    ow = w;
+                } else {
+                    ow = std::max(w, (int)((long long)sh * W / NH));
+                }
+                rest.insert(rest.end(), {sh, 0, 0, li});
+                owner.push_back(ow);
+                continue;
+            }
+            const long long cap = capl[(size_t)s * c->V + h];
+            const long long off = shared0[sh];
+            long long p = lo;
+            while (p < hi) {
+                while (bound[w + 1] <= p) ++w;
+                const long long end = std::min(hi, bound[w + 1]);
+                rest.insert(rest.end(), {sh, (int32_t)((p - lo + off) << 4),
+                                         (int32_t)std::min((end - lo + off) << 4, cap), li});
+                owner.push_back(w);
+                p = end;
+            }
+        }
+    }
+    // -- the table in worker order: each worker's gang row, then its rest
+    const size_t nrest = owner.size();
+    size_t ngang = 0;
+    for (int w = 0; w < W; ++w) ngang += grow[(size_t)w * 4] >= 0;
+    const size_t n = nrest + ngang;
+    if (n > (size_t)c->sz.max_rows) {   // not expected (bounded above); stay valid
+        pl.head_rows.clear();
+        plan_balanced(c, layer, pl);
+        return;
+    }
+    pl.rows.resize(4 * n);
+    pl.worker_start.resize((size_t)W + 1);
+    {
+        size_t k = 0, ri = 0;
+        for (int w = 0; w < W; ++w) {
+            pl.worker_start[w] = (int32_t)k;
+            if (grow[(size_t)w * 4] >= 0) {
+                std::copy(&grow[(size_t)w * 4], &grow[(size_t)w * 4] + 4, &pl.rows[4 * k]);
+                ++k;
+            }
+            while (ri < nrest && owner[ri] == w) {
+                std::copy(&rest[4 * ri], &rest[4 * ri] + 4, &pl.rows[4 * k]);
+                ++k;
+                ++ri;
+            }
+        }
+        pl.worker_start[W] = (int32_t)k;
+        if (ri != nrest || k != n) {   // owners out of order: not expected; stay valid
+            pl.head_rows.clear();
+            plan_balanced(c, layer, pl);
+            return;
+        }
+    }
+    // -- each head's rows, in token order
+    pl.head_row_start.assign((size_t)NH + 1, 0);
+    for (size_t k = 0; k < n; ++k) pl.head_row_start[pl.rows[4 * k] + 1]++;
+    for (int sh = 0; sh < NH; ++sh) pl.head_row_start[sh + 1] += pl.head_row_start[sh];
+    pl.head_rows.resize(n);
+    {
+        std::vector<int32_t> fill(pl.head_row_start.begin(), pl.head_row_start.end() - 1);
+        for (size_t k = 0; k < n; ++k) pl.head_rows[fill[pl.rows[4 * k]]++] = (int32_t)k;
+        for (int sh = 0; sh < NH; ++sh)
+            std::sort(pl.head_rows.begin() + pl.head_row_start[sh], pl.head_rows.begin() + pl.head_row_start[sh + 1],
+                      [&](int32_t a, int32_t b) { return pl.rows[4 * (size_t)a + 1] < pl.rows[4 * (size_t)b + 1]; });
+    }
+}
+
 void replan(nup_ctx *c) {
     for (int l = 0; l < c->NL; ++l) {
         if (c->cfg.plan_mode == NUP_PLAN_UNIFORM) plan_uniform(c, l, c->plan[l]);
+        else if (c->cfg.plan_mode == NUP_PLAN_SHARED) plan_shared(c, l, c->plan[l]);
         else plan_balanced(c, l, c->plan[l]);
     }
 }
@@ -562,10 +812,12 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
     c->off_ws.assign(c->NL, 0);
     c->off_hrs.assign(c->NL, 0);
     c->off_rows.assign(c->NL, 0);
+    c->off_hr.assign(c->NL, 0);
     for (int l = 0; l < c->NL; ++l) {
         c->off_ws[l] = c->sz.fixed + c->sz.caps + (size_t)l * c->sz.plan_layer;
         c->off_hrs[l] = c->off_ws[l] + align_up(4 * ((size_t)c->sz.max_workers + 1));
         c->off_rows[l] = c->off_hrs[l] + align_up(4 * ((size_t)c->B * c->H + 1));
+        c->off_hr[l] = c->off_rows[l] + align_up(16 * (size_t)c->sz.max_rows);
     }
     c->dev_workers.assign(c->NL, 0);
     c->dev_rows.assign(c->NL, 0);
@@ -806,6 +1058,11 @@ nup_status nup_commit(nup_ctx *c, void *stream) {
             for (size_t w = pl.worker_start.size(); w <= (size_t)c->sz.max_workers; ++w) wsd[w] = nr;
             std::memcpy(blob + c->off_hrs[l], pl.head_row_start.data(), 4 * pl.head_row_start.size());
             if (nr) std::memcpy(blob + c->off_rows[l], pl.rows.data(), 16 * (size_t)nr);
+            if (c->cfg.plan_mode == NUP_PLAN_SHARED) {
+                int32_t *hr = reinterpret_cast<int32_t *>(blob + c->off_hr[l]);
+                if (pl.head_rows.empty()) std::iota(hr, hr + nr, 0);
+                else std::memcpy(hr, pl.head_rows.data(), 4 * (size_t)nr);
+            }
             c->dev_workers[l] = c->sz.max_workers;
             c->dev_rows[l] = nr;
         }
@@ -1154,6 +1411,7 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
     m.ws_o = wso;
     m.ws_ml = wsml;
     m.head_row_start = a.head_row_start;
+    m.head_rows = (!topk && c->cfg.plan_mode == NUP_PLAN_SHARED) ? c->inbox_i32(c->off_hr[c->layer]) : nullptr;
     m.uniform_splits = splits;
     m.out = out;
     m.lse = lse;
@@ -1407,6 +1665,16 @@ nup_status nup_get_plan(const nup_ctx *c, int32_t *n_rows, int32_t *n_workers, i
     if (rows) std::copy(pl.rows.begin(), pl.rows.end(), rows);
     if (worker_start) std::copy(pl.worker_start.begin(), pl.worker_start.end(), worker_start);
     if (head_row_start) std::copy(pl.head_row_start.begin(), pl.head_row_start.end(), head_row_start);
+    return NUP_OK;
+}
+
+nup_status nup_get_plan_head_rows(const nup_ctx *c, int32_t *head_rows) {
+    if (!c || !head_rows) return NUP_E_ARG;
+    if (c->plan_dirty) replan(const_cast<nup_ctx *>(c));
+    const nup_ctx::Plan &pl = c->plan[c->layer];
+    const int32_t n = (int32_t)(pl.rows.size() / 4);
+    if (pl.head_rows.empty()) std::iota(head_rows, head_rows + n, 0);
+    else std::copy(pl.head_rows.begin(), pl.head_rows.end(), head_rows);
     return NUP_OK;
 }
 

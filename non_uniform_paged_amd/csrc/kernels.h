@@ -58,6 +58,7 @@ struct MergeArgs {
     const float *ws_o;
     const float *ws_ml;
     const int32_t *head_row_start; // [Bmax*Hkv+1] (table mode) or NULL
+    const int32_t *head_rows;      // partial slot of each head's rows, by head (NULL: the row index itself)
     int32_t uniform_splits;        // rows of head sh are sh*splits.. (when table NULL)
     float *out;                    // fp32 [Bmax][Hq][D]
     float *lse;                    // fp32 [Bmax][Hq] or NULL

@@ -522,10 +522,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         for (int u = 0; u < kBatch; ++u) {
             const int i = b + u;
             const bool ok = i < re;
-            const size_t mo = ((size_t)(ok ? i : rb) * GQA + r) * 2;
+            const int slot = a.head_rows ? a.head_rows[ok ? i : rb] : (ok ? i : rb);
+            const size_t mo = ((size_t)slot * GQA + r) * 2;
             mi[u] = ok ? a.ws_ml[mo] : -INFINITY;
             li[u] = a.ws_ml[mo + 1];
-            const float *oi = a.ws_o + ((size_t)(ok ? i : rb) * GQA + r) * D;
+            const float *oi = a.ws_o + ((size_t)slot * GQA + r) * D;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) ov[u][j] = oi[lane + 64 * j];
         }

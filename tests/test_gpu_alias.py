@@ -47,14 +47,20 @@ def _append_steps(c, steps, salt):
     return kp, vp
 
 
-def test_alias_decode_append_gather_trim():
+# (plan mode, workers): the share-aware plan with room for its gangs, and
+# with too few workers for them (it then plans like the balanced one)
+PLANS = [(nup.PLAN_BALANCED, 37), (nup.PLAN_SHARED, 64), (nup.PLAN_SHARED, 37)]
+
+
+@pytest.mark.parametrize("plan_mode,workers", PLANS)
+def test_alias_decode_append_gather_trim(plan_mode, workers):
     H, gqa, D, B, ng = 8, 4, 128, 6, 2
     rs = np.random.default_rng(31)
     L0 = rs.integers(200, 700, size=H)
     max_pages = 64
     num_pages = 300
     c = Case(H=H, Hq=H * gqa, D=D, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages,
-             free_list_init=rs.permutation(num_pages), num_workers=37, salt=31)
+             free_list_init=rs.permutation(num_pages), num_workers=workers, plan_mode=plan_mode, salt=31)
     assert c.alloc([0], (L0 + 20)[None], L0[None]) == pg.OK
     goh = c.spec.group_of_head
     forks = [1, 2, 3, 4]
@@ -74,12 +80,41 @@ def test_alias_decode_append_gather_trim():
     ref, ref_lse = c.oracle()
     assert_attention_close(out, lse, ref, ref_lse, "forks over shared pages")
 
+    if plan_mode == nup.PLAN_SHARED and workers == 64:
+        # the forks' common prefix is planned as gangs: rows in worker order
+        hr = nup.get_plan_head_rows(c.ctx)
+        assert not np.array_equal(hr, np.arange(len(hr)))
+
     # decode steps after the fork: every write lands on an unshared page
     kp, vp = _append_steps(c, 6, 3100)
     assert np.array_equal(u16(c.kpool), kp) and np.array_equal(u16(c.vpool), vp)
     out, lse = c.attend()
     ref, ref_lse = c.oracle()
     assert_attention_close(out, lse, ref, ref_lse, "after appends")
+
+    # one fused step (append inside the split-K kernel, lengths advanced by
+    # the merge); the oracle's pools get the rows by its own pager
+    kn = W.normal_bf16("k", (c.B, c.H, c.D), 3199)
+    vn = W.normal_bf16("v", (c.B, c.H, c.D), 3199)
+    nup.attn_decode_nonuniform_append(c.ctx, torch.from_numpy(kn.view(np.int16)).to(DEV),
+                                      torch.from_numpy(vn.view(np.int16)).to(DEV),
+                                      c.q, c.out, c.lse, c.scale, c.ws)
+    torch.cuda.synchronize()
+    st, pos = c.spec.append_positions()
+    assert st == pg.OK
+    fk, fv = kp.reshape(-1, D), vp.reshape(-1, D)
+    for s in range(B):
+        if c.spec.active[s]:
+            for h in range(H):
+                row = c.spec.physical_row(s, h, int(pos[s, h]))
+                fk[row], fv[row] = kn[s, h], vn[s, h]
+    assert np.array_equal(u16(c.kpool), kp) and np.array_equal(u16(c.vpool), vp)
+    assert np.array_equal(nup.get_lengths(c.ctx), c.spec.lengths)
+    ref, ref_lse = oracle.decode(u16(c.q), kp, vp, c.spec.page_table, c.spec.lengths,
+                                 c.spec.group_of_head, c.spec.slot_of_head, c.scale)
+    assert_attention_close(c.out.cpu().numpy().astype(np.float64), c.lse.cpu().numpy().astype(np.float64),
+                           ref, ref_lse, "fused step over shared pages")
+    c.commit()
 
     # trains of the forked rows: bit-exact rows, shared prefix included
     lens_now = c.spec.lengths.astype(np.int64)
@@ -109,15 +144,18 @@ def test_alias_decode_append_gather_trim():
     assert np.array_equal(nup.get_refcounts(c.ctx), c.spec.ref)
 
 
-def test_alias_full_size_prefix_batch():
+@pytest.mark.parametrize("plan_mode", [nup.PLAN_BALANCED, nup.PLAN_SHARED])
+def test_alias_full_size_prefix_batch(plan_mode):
     """Qwen2.5-32B-shaped batch where 60 of 64 sessions fork from 4 sources
-    (a shared 8192-token prompt); checked on sampled sessions."""
+    (a shared 8192-token prompt); checked on sampled sessions, under the
+    balanced plan and under the share-aware one (the bench's launch: 2048
+    workers)."""
     w = W.qwen25_32b_prefix()
     src = w.extra["alias_src"]
     pre = w.extra["prefix_tokens"]
     max_pages = int(math.ceil(w.caps.max() / 16))
     c = Case(H=w.num_kv_heads, Hq=w.num_q_heads, D=w.head_dim, ng=w.num_groups, B=w.batch,
-             num_pages=w.num_pages, max_pages=max_pages, salt=32)
+             num_pages=w.num_pages, max_pages=max_pages, plan_mode=plan_mode, salt=32)
     roots = [s for s in range(w.batch) if src[s] < 0]
     forks = [s for s in range(w.batch) if src[s] >= 0]
     assert c.alloc(roots, w.caps[roots], w.lengths[roots]) == pg.OK

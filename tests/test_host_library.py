@@ -267,3 +267,124 @@ def test_product_does_not_touch_the_oracle():
                 src = open(os.path.join(root, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
                 assert "_liboracle" not in src, f
+
+
+def _forked_ctx(w, plan_mode, num_workers=2048):
+    """The forked-prefix batch on a host-only context: Reserve the sources,
+    then Alias each fork onto the whole pages of its shared prefix."""
+    ctx = _host_ctx(H=w.num_kv_heads, Hq=w.num_q_heads, D=w.head_dim, ng=w.num_groups,
+                    B=w.batch, num_pages=w.num_pages, max_pages=int(w.caps.max() // 16 + 1),
+                    num_workers=num_workers, plan_mode=plan_mode)
+    src = w.extra["alias_src"]
+    roots, forks = np.nonzero(src < 0)[0], np.nonzero(src >= 0)[0]
+    goh = nup.kv_alloc_groups(ctx, roots, w.caps[roots], w.lengths[roots])
+    share = np.zeros((len(forks), w.num_groups), np.int32)
+    for g in range(w.num_groups):
+        share[:, g] = w.extra["prefix_tokens"][forks][:, goh == g].min(axis=1) // 16
+    nup.kv_alias(ctx, forks, src[forks], share, w.caps[forks], w.lengths[forks])
+    return ctx, goh, forks, share
+
+
+def test_shared_plan_equals_balanced_without_sharing():
+    import workloads as W
+    w = W.qwen25_32b()
+    plans = []
+    for mode in (nup.PLAN_BALANCED, nup.PLAN_SHARED):
+        ctx = _host_ctx(H=w.num_kv_heads, Hq=w.num_q_heads, D=w.head_dim, ng=w.num_groups,
+                        B=w.batch, num_pages=w.num_pages, max_pages=int(w.caps.max() // 16 + 1),
+                        num_workers=2048, plan_mode=mode)
+        nup.kv_alloc_groups(ctx, np.arange(w.batch), w.caps, w.lengths)
+        plans.append(nup.get_plan(ctx) + (nup.get_plan_head_rows(ctx),))
+    for a, b in zip(plans[0], plans[1]):
+        assert np.array_equal(a, b)
+    assert np.array_equal(plans[1][3], np.arange(len(plans[1][0])))
+
+
+def test_shared_plan_on_forked_batch():
+    """Every head's capacity is covered exactly once (read through
+    head_rows), workers stay within one page of the balance bound, and each
+    set of sharers reads its common prefix as gangs: the chunk is the first
+    row of each sharer's worker, and a chunk's workers sit on one XCD
+    (workgroups of 4 waves dealt to 8 XCDs in turn)."""
+    import workloads as W
+    w = W.qwen25_32b_prefix()
+    ctx, goh, forks, share = _forked_ctx(w, nup.PLAN_SHARED)
+    rows, ws, hrs = nup.get_plan(ctx)
+    hr = nup.get_plan_head_rows(ctx)
+    B, H = w.batch, w.num_kv_heads
+    loads = wt.check(rows, ws, hrs, w.caps, np.ones(B, bool), head_rows=hr, slack=1)
+    bctx, *_ = _forked_ctx(w, nup.PLAN_BALANCED)
+    brows, bws, bhrs = nup.get_plan(bctx)
+    bloads = wt.check(brows, bws, bhrs, w.caps, np.ones(B, bool))
+    assert sum(loads) == sum(bloads)
+    first = np.zeros(len(rows), bool)
+    first[ws[:-1][ws[:-1] < ws[1:]]] = True
+    worker_of = np.repeat(np.arange(len(ws) - 1), np.diff(ws))
+    xcd = (worker_of // 4) % 8
+    src = w.extra["alias_src"]
+    n_gang_rows = 0
+    for s0 in np.nonzero(src < 0)[0]:
+        for h in range(H):
+            g = goh[h]
+            members = [s0] + [f for i, f in enumerate(forks) if src[f] == s0 and share[i, g] > 0]
+            if len(members) < 2:
+                continue
+            common = min(int(share[i, g]) for i, f in enumerate(forks) if src[f] == s0 and share[i, g] > 0)
+            common = min(common, min(int(w.caps[m, hh]) // 16 for m in members
+                                     for hh in range(H) if goh[hh] == g))
+            chunks = None
+            for m in members:
+                sh = m * H + h
+                mine = [int(r) for r in hr[hrs[sh]:hrs[sh + 1]] if rows[r, 2] <= common * 16]
+                assert sum(rows[r, 2] - rows[r, 1] for r in mine) == common * 16
+                assert all(first[r] for r in mine)
+                spans = [(int(rows[r, 1]), int(rows[r, 2])) for r in mine]
+                if chunks is None:
+                    chunks = {sp: [] for sp in spans}
+                assert set(spans) == set(chunks)
+                for r in mine:
+                    chunks[(int(rows[r, 1]), int(rows[r, 2]))].append(xcd[r])
+                n_gang_rows += len(mine)
+            for span, xs in chunks.items():
+                assert len(set(xs)) == 1, (s0, h, span, xs)
+    assert n_gang_rows > len(forks)
+
+
+@settings(max_examples=30, deadline=None)
+@given(st.data())
+def test_shared_plan_random_forks(data):
+    """Random forks (some of forks), groups and worker counts: the shared
+    plan always covers every head exactly once, within one page of balance."""
+    H = 4
+    ng = data.draw(st.sampled_from([1, 2, 4]))
+    B, num_pages, max_pages = 8, 400, 12
+    W_ = data.draw(st.sampled_from([3, 7, 16, 37, 64]))
+    ctx = _host_ctx(H=H, Hq=2 * H, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages,
+                    num_workers=W_, plan_mode=nup.PLAN_SHARED)
+    spec = pg.PagerSpec(H, ng, B, num_pages, max_pages, 16, None)
+    n_src = data.draw(st.integers(1, 3))
+    lens = np.array([[data.draw(st.integers(16, 150)) for _ in range(H)] for _ in range(n_src)])
+    caps = lens + 16
+    assert spec.alloc(list(range(n_src)), caps, lens) == nup.kv_alloc_groups(ctx, list(range(n_src)), caps, lens,
+                                                                              raise_on_error=False)
+    slot = n_src
+    for _ in range(data.draw(st.integers(0, B - n_src))):
+        s0 = data.draw(st.integers(0, slot - 1))
+        if not spec.active[s0]:
+            continue
+        goh = spec.group_of_head
+        most = [min(int(spec.lengths[s0, h]) for h in range(H) if goh[h] == g) // 16 for g in range(ng)]
+        sh = [data.draw(st.integers(0, m)) for m in most]
+        fl = np.array([[sh[goh[h]] * 16 + data.draw(st.integers(0, 40)) for h in range(H)]])
+        fc = fl + data.draw(st.integers(0, 20))
+        a = spec.alias([slot], [s0], [sh], fc, fl)
+        b = nup.kv_alias(ctx, [slot], [s0], [sh], fc, fl, raise_on_error=False)
+        assert a == b
+        slot += 1
+    if data.draw(st.booleans()):
+        victim = data.draw(st.integers(0, slot - 1))
+        if spec.active[victim]:
+            assert spec.free_seqs([victim]) == nup.kv_free_seqs(ctx, [victim], raise_on_error=False)
+    rows, ws, hrs = nup.get_plan(ctx)
+    hr = nup.get_plan_head_rows(ctx)
+    wt.check(rows, ws, hrs, spec.caps, spec.active, head_rows=hr, slack=1)

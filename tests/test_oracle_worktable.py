@@ -47,3 +47,40 @@ def test_rejects_invalid(mutate):
         hrs = np.array([0, 2, 3, 3, 5])
     with pytest.raises(AssertionError):
         wt.check(rows, ws, hrs, CAPS, ACTIVE)
+
+
+def _worker_ordered():
+    # the valid table above, stored in worker order with the rows of head 3
+    # split across the two workers: worker 0 runs (3, 16..48) first, then
+    # head 0; worker 1 runs heads 1, 2 and (3, 0..16)
+    rows = [(3, 16, 48, 0), (0, 0, 32, 0), (0, 32, 48, 0),
+            (0, 48, 64, 0), (1, 0, 16, 0), (2, 0, 0, 0), (3, 0, 16, 0)]
+    head_rows = [1, 2, 3, 4, 5, 6, 0]      # by head, in token order
+    return np.array(rows), np.array([0, 3, 7]), np.array([0, 3, 4, 5, 7]), np.array(head_rows)
+
+
+def test_accepts_worker_ordered_table_through_head_rows():
+    rows, ws, hrs, hr = _worker_ordered()
+    loads = wt.check(rows, ws, hrs, CAPS, ACTIVE, head_rows=hr, balanced=False)
+    assert loads == [5, 3]
+    # worker 0 holds one page above the ceiling of the mean (4): accepted
+    # only with the slack
+    with pytest.raises(AssertionError):
+        wt.check(rows, ws, hrs, CAPS, ACTIVE, head_rows=hr, slack=0)
+    wt.check(rows, ws, hrs, CAPS, ACTIVE, head_rows=hr, slack=1)
+
+
+@pytest.mark.parametrize("mutate", ["no_index", "not_permutation", "token_order", "wrong_head"])
+def test_rejects_bad_head_rows(mutate):
+    rows, ws, hrs, hr = _worker_ordered()
+    hr = hr.copy()
+    if mutate == "no_index":
+        hr = None                          # the table is not head-contiguous
+    elif mutate == "not_permutation":
+        hr[0] = 2
+    elif mutate == "token_order":
+        hr[5], hr[6] = hr[6], hr[5]        # head 3's rows out of token order
+    elif mutate == "wrong_head":
+        hr[3], hr[4] = hr[4], hr[3]        # a row of head 2 listed under head 1
+    with pytest.raises(AssertionError):
+        wt.check(rows, ws, hrs, CAPS, ACTIVE, head_rows=hr, slack=1)
