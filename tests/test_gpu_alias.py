@@ -3,10 +3,12 @@ physical pages of a live source.  Decode over shared pages, appends after
 the fork, trains gathers and Trim of the source are checked against the
 oracle's own pager and fp64 attention."""
 import math
+import os
 
 import numpy as np
 import pytest
 import torch
+from hypothesis import HealthCheck, given, settings, strategies as st
 
 import non_uniform_paged_amd as nup
 import oracle
@@ -173,3 +175,75 @@ def test_alias_full_size_prefix_batch(plan_mode):
     out = c.out.cpu().numpy().astype(np.float64)[sample]
     lse = c.lse.cpu().numpy().astype(np.float64)[sample]
     assert_attention_close(out, lse, ref, ref_lse, "qwen25_32b_prefix sampled")
+
+
+@settings(max_examples=int(os.environ.get("NUP_FUZZ_EXAMPLES", "30")), deadline=None, derandomize=True,
+          suppress_health_check=list(HealthCheck))
+@given(st.data())
+def test_shared_plan_random_forks(data):
+    """Random shapes, layers, groups and worker counts; sources with forks
+    of random shares (and sometimes a Trim of a source), attended under the
+    share-aware plan, every layer against the oracle; then one fused step."""
+    D = data.draw(st.sampled_from([64, 128]))
+    gqa = data.draw(st.sampled_from([1, 2, 4, 5, 8]))
+    H = data.draw(st.sampled_from([1, 2, 4, 8]))
+    NL = data.draw(st.sampled_from([1, 1, 2]))
+    V = NL * H
+    ng = data.draw(st.sampled_from([g for g in range(1, V + 1) if V % g == 0]))
+    B = data.draw(st.integers(2, 8))
+    workers = data.draw(st.sampled_from([5, 16, 64, 0]))
+    seed = data.draw(st.integers(0, 2 ** 16))
+    rs = np.random.default_rng(seed)
+    maxL = 400
+    max_pages = (maxL + 100) // 16 + 1     # room for a fork's share + 59 + headroom
+    num_pages = B * ng * max_pages + 7
+    c = Case(H=H, Hq=H * gqa, D=D, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages,
+             free_list_init=rs.permutation(num_pages), num_workers=workers, plan_mode=nup.PLAN_SHARED,
+             salt=seed % 83 + 1, num_layers=NL)
+    n_src = int(rs.integers(1, min(3, B - 1) + 1))
+    L0 = rs.integers(16, maxL + 1, size=(n_src, V)).astype(np.int32)
+    assert c.alloc(list(range(n_src)), L0 + rs.integers(1, 40, size=L0.shape), L0) == pg.OK
+    goh = c.spec.group_of_head
+    for f in range(n_src, B):
+        s0 = int(rs.integers(0, n_src))
+        most = _group_share(goh, c.spec.lengths[s0], ng)
+        share = rs.integers(0, most + 1)
+        if rs.random() < 0.5:                  # one group shared in full
+            g = int(rs.integers(0, ng))
+            share[g] = most[g]
+        L = (share[goh] * 16 + rs.integers(0, 60, size=V)).astype(np.int32)
+        assert c.alias([f], [s0], share[None], (L + rs.integers(1, 30, size=V))[None], L[None]) == pg.OK
+    if rs.random() < 0.3:
+        c.free([0])
+    c.commit()
+    tag = f"seed {seed} D{D} gqa{gqa} H{H} NL{NL} ng{ng} B{B} W{workers}"
+    for l in range(NL):
+        nup.set_layer(c.ctx, l)
+        out, lse = c.attend()
+        sl = slice(l * H, (l + 1) * H)
+        ref, ref_lse = oracle.decode(u16(c.q), u16(c.kpool), u16(c.vpool), c.spec.page_table,
+                                     c.spec.lengths[:, sl], goh[sl], c.spec.slot_of_head[sl], c.scale)
+        assert_attention_close(out, lse, ref, ref_lse, f"{tag} layer {l}")
+    # one fused step on layer 0; the oracle's pools get the rows by its pager
+    nup.set_layer(c.ctx, 0)
+    kp, vp = u16(c.kpool).copy(), u16(c.vpool).copy()
+    kn = W.normal_bf16("k", (B, H, D), seed + 1)
+    vn = W.normal_bf16("v", (B, H, D), seed + 1)
+    nup.attn_decode_nonuniform_append(c.ctx, torch.from_numpy(kn.view(np.int16)).to(DEV),
+                                      torch.from_numpy(vn.view(np.int16)).to(DEV),
+                                      c.q, c.out, c.lse, c.scale, c.ws)
+    torch.cuda.synchronize()
+    fk, fv = kp.reshape(-1, D), vp.reshape(-1, D)
+    for s in range(B):
+        if c.spec.active[s]:
+            for h in range(H):
+                row = c.spec.physical_row(s, h, int(c.spec.lengths[s, h]))
+                fk[row], fv[row] = kn[s, h], vn[s, h]
+                c.spec.lengths[s, h] += 1
+    assert np.array_equal(u16(c.kpool), kp) and np.array_equal(u16(c.vpool), vp), tag
+    assert np.array_equal(nup.get_lengths(c.ctx), c.spec.lengths), tag
+    ref, ref_lse = oracle.decode(u16(c.q), kp, vp, c.spec.page_table, c.spec.lengths[:, :H],
+                                 goh[:H], c.spec.slot_of_head[:H], c.scale)
+    assert_attention_close(c.out.cpu().numpy().astype(np.float64), c.lse.cpu().numpy().astype(np.float64),
+                           ref, ref_lse, f"{tag} fused")
+    assert nup.device_errors(c.ctx) == nup.NUP_OK

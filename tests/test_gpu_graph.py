@@ -58,7 +58,8 @@ def _step(c, layer, kn, vn, q, out, lse, fused):
 
 
 @pytest.mark.parametrize("plan_mode,fused", [(nup.PLAN_BALANCED, False), (nup.PLAN_UNIFORM, False),
-                                             (nup.PLAN_BALANCED, True), (nup.PLAN_UNIFORM, True)])
+                                             (nup.PLAN_SHARED, False), (nup.PLAN_BALANCED, True),
+                                             (nup.PLAN_UNIFORM, True), (nup.PLAN_SHARED, True)])
 def test_graph_replay_across_commits(plan_mode, fused):
     rs = np.random.default_rng(70 + plan_mode)
     steps = 8
@@ -113,6 +114,12 @@ def test_graph_replay_across_commits(plan_mode, fused):
             cp = caps_for(L)
             for c in (G, E):
                 assert c.alias([4], [0], np.array([share], np.int32), cp, L) == pg.OK
+            if plan_mode == nup.PLAN_SHARED:
+                # the shared prefix is planned as gangs: a worker-ordered table
+                for l in range(NL):
+                    nup.set_layer(G.ctx, l)
+                    hr = nup.get_plan_head_rows(G.ctx)
+                    assert not np.array_equal(hr, np.arange(len(hr))), l
         if i == 6:
             for c in (G, E):
                 c.free([0, 3])

@@ -29,7 +29,7 @@ def test_random_graph_replays(data):
     V = NL * H
     ng = data.draw(st.sampled_from([g for g in range(1, V + 1) if V % g == 0]))
     B = data.draw(st.integers(1, 5))
-    plan_mode = data.draw(st.sampled_from([nup.PLAN_BALANCED, nup.PLAN_UNIFORM]))
+    plan_mode = data.draw(st.sampled_from([nup.PLAN_BALANCED, nup.PLAN_UNIFORM, nup.PLAN_SHARED]))
     workers = data.draw(st.sampled_from([1, 7, 64, 0]))
     fused = data.draw(st.booleans())
     replays = data.draw(st.integers(1, 5))
