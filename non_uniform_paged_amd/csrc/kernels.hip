@@ -510,6 +510,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         re = rb + a.uniform_splits;
     }
     if (re - rb <= 1) return;   // a head of one row was written by the partial kernel
+    // the partial slots of the head's first 64 rows, one per lane, loaded in
+    // one round trip (worker-ordered plans index them through head_rows)
+    const int slot_lane = a.head_rows ? a.head_rows[min(rb + lane, re - 1)] : 0;
     // One online pass over the head's rows, eight at a time: all loads of a
     // batch are issued before any is used, so a batch costs one round trip.
     constexpr int kBatch = 8;
@@ -522,7 +525,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         for (int u = 0; u < kBatch; ++u) {
             const int i = b + u;
             const bool ok = i < re;
-            const int slot = a.head_rows ? a.head_rows[ok ? i : rb] : (ok ? i : rb);
+            const int j = ok ? i : rb;
+            int slot = j;
+            if (a.head_rows)
+                slot = j - rb < 64 ? __builtin_amdgcn_readlane(slot_lane, j - rb) : a.head_rows[j];
             const size_t mo = ((size_t)slot * GQA + r) * 2;
             mi[u] = ok ? a.ws_ml[mo] : -INFINITY;
             li[u] = a.ws_ml[mo + 1];
