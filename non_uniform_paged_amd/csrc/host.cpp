@@ -512,6 +512,8 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
         return ((j / nup::kWavesPerBlock) * kXcd + x) * nup::kWavesPerBlock + j % nup::kWavesPerBlock;
     };
     std::vector<int32_t> grow((size_t)W * 4, -1);   // the gang row of each physical worker
+    std::vector<int32_t> gpiece((size_t)W, 0);      // its chunk's index within the head's range
+    std::vector<int32_t> gcount((size_t)NH, 0);     // gang rows of each head
     std::vector<long long> gload((size_t)W, 0);
     {
         int v = 0;
@@ -528,6 +530,8 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
                     r[2] = (int32_t)(p1 << 4);
                     r[3] = s * c->V + gg.h;
                     gload[w] = p1 - p0;
+                    gpiece[w] = (int32_t)i;
+                    gcount[(size_t)s * H + gg.h]++;
                 }
             }
         }
@@ -539,14 +543,38 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
         ubase[sh + 1] = ubase[sh] + std::max(0LL, hp - shared0[sh]);
     }
     const long long U = ubase[NH];
+    // share boundaries floor(U * room_before(w) / room_total), carried as a
+    // quotient and remainder: a room value's own quotient and remainder are
+    // computed once (rooms take few distinct values), not one 128-bit
+    // division per worker
     std::vector<long long> bound((size_t)W + 2);
     {
-        long long room_total = 0;
-        for (int w = 0; w < W; ++w) room_total += std::max(0LL, Aq - gload[w]);
-        long long acc = 0;
+        long long R = 0;
+        for (int w = 0; w < W; ++w) R += std::max(0LL, Aq - gload[w]);
+        std::vector<std::pair<long long, long long>> per_room((size_t)std::min<long long>(Aq + 1, 1 << 16), {-1, 0});
+        auto step_of = [&](long long d) -> std::pair<long long, long long> {
+            auto calc = [&]() {
+                const __int128 x = (__int128)U * d;
+                return std::make_pair((long long)(x / R), (long long)(x % R));
+            };
+            if (d < (long long)per_room.size()) {
+                if (per_room[d].first < 0) per_room[d] = calc();
+                return per_room[d];
+            }
+            return calc();
+        };
+        long long q = 0, r = 0;   // U * room_before(w) = q * R + r
         for (int w = 0; w <= W; ++w) {
-            bound[w] = room_total ? (long long)((__int128)U * acc / room_total) : (w ? U : 0);
-            if (w < W) acc += std::max(0LL, Aq - gload[w]);
+            bound[w] = R ? q : (w ? U : 0);
+            if (w < W && R) {
+                const auto st = step_of(std::max(0LL, Aq - gload[w]));
+                q += st.first;
+                r += st.second;
+                if (r >= R) {
+                    r -= R;
+                    ++q;
+                }
+            }
         }
         bound[W] = U;
         bound[(size_t)W + 1] = LLONG_MAX;
@@ -554,6 +582,14 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
     // rest rows in head order; owners never decrease
     std::vector<int32_t> rest;     // [n][4]
     std::vector<int32_t> owner;    // [n]
+    rest.reserve(4 * ((size_t)NH + W + 1));
+    owner.reserve((size_t)NH + W + 1);
+    auto push_row = [&](int32_t a0, int32_t a1, int32_t a2, int32_t a3) {
+        rest.push_back(a0);
+        rest.push_back(a1);
+        rest.push_back(a2);
+        rest.push_back(a3);
+    };
     {
         int w = 0;
         for (int sh = 0; sh < NH; ++sh) {
@@ -570,7 +606,7 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
                 } else {
                     ow = std::max(w, (int)((long long)sh * W / NH));
                 }
-                rest.insert(rest.end(), {sh, 0, 0, li});
+                push_row(sh, 0, 0, li);
                 owner.push_back(ow);
                 continue;
             }
@@ -580,8 +616,7 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
             while (p < hi) {
                 while (bound[w + 1] <= p) ++w;
                 const long long end = std::min(hi, bound[w + 1]);
-                rest.insert(rest.end(), {sh, (int32_t)((p - lo + off) << 4),
-                                         (int32_t)std::min((end - lo + off) << 4, cap), li});
+                push_row(sh, (int32_t)((p - lo + off) << 4), (int32_t)std::min((end - lo + off) << 4, cap), li);
                 owner.push_back(w);
                 p = end;
             }
@@ -620,17 +655,24 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
             return;
         }
     }
-    // -- each head's rows, in token order
+    // -- each head's rows, in token order: its gang rows by chunk index, then
+    //    its rest rows, which were made in token order and all start later
     pl.head_row_start.assign((size_t)NH + 1, 0);
     for (size_t k = 0; k < n; ++k) pl.head_row_start[pl.rows[4 * k] + 1]++;
     for (int sh = 0; sh < NH; ++sh) pl.head_row_start[sh + 1] += pl.head_row_start[sh];
     pl.head_rows.resize(n);
     {
-        std::vector<int32_t> fill(pl.head_row_start.begin(), pl.head_row_start.end() - 1);
-        for (size_t k = 0; k < n; ++k) pl.head_rows[fill[pl.rows[4 * k]]++] = (int32_t)k;
-        for (int sh = 0; sh < NH; ++sh)
-            std::sort(pl.head_rows.begin() + pl.head_row_start[sh], pl.head_rows.begin() + pl.head_row_start[sh + 1],
-                      [&](int32_t a, int32_t b) { return pl.rows[4 * (size_t)a + 1] < pl.rows[4 * (size_t)b + 1]; });
+        std::vector<int32_t> next_rest((size_t)NH);
+        for (int sh = 0; sh < NH; ++sh) next_rest[sh] = pl.head_row_start[sh] + gcount[sh];
+        for (int w = 0; w < W; ++w) {
+            int32_t k = pl.worker_start[w];
+            const int32_t ke = pl.worker_start[w + 1];
+            if (k < ke && grow[(size_t)w * 4] >= 0) {   // the worker's gang row
+                pl.head_rows[pl.head_row_start[grow[(size_t)w * 4]] + gpiece[w]] = k;
+                ++k;
+            }
+            for (; k < ke; ++k) pl.head_rows[next_rest[pl.rows[4 * (size_t)k]]++] = k;
+        }
     }
 }
 
