@@ -353,17 +353,20 @@ def test_shared_plan_on_forked_batch():
 @settings(max_examples=30, deadline=None)
 @given(st.data())
 def test_shared_plan_random_forks(data):
-    """Random forks (some of forks), groups and worker counts: the shared
-    plan always covers every head exactly once, within one page of balance."""
+    """Random forks (some of forks), layers, groups (spanning layers) and
+    worker counts: every layer's shared plan covers each of its heads exactly
+    once, within one page of balance."""
     H = 4
-    ng = data.draw(st.sampled_from([1, 2, 4]))
-    B, num_pages, max_pages = 8, 400, 12
+    NL = data.draw(st.sampled_from([1, 2, 3]))
+    V = NL * H
+    ng = data.draw(st.sampled_from([g for g in (1, 2, 3, 4, 6, 8, 12) if V % g == 0]))
+    B, num_pages, max_pages = 8, 400 * NL, 12
     W_ = data.draw(st.sampled_from([3, 7, 16, 37, 64]))
     ctx = _host_ctx(H=H, Hq=2 * H, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages,
-                    num_workers=W_, plan_mode=nup.PLAN_SHARED)
-    spec = pg.PagerSpec(H, ng, B, num_pages, max_pages, 16, None)
+                    num_workers=W_, plan_mode=nup.PLAN_SHARED, num_layers=NL)
+    spec = pg.PagerSpec(V, ng, B, num_pages, max_pages, 16, None)
     n_src = data.draw(st.integers(1, 3))
-    lens = np.array([[data.draw(st.integers(16, 150)) for _ in range(H)] for _ in range(n_src)])
+    lens = np.array([[data.draw(st.integers(16, 150)) for _ in range(V)] for _ in range(n_src)])
     caps = lens + 16
     assert spec.alloc(list(range(n_src)), caps, lens) == nup.kv_alloc_groups(ctx, list(range(n_src)), caps, lens,
                                                                               raise_on_error=False)
@@ -373,9 +376,9 @@ def test_shared_plan_random_forks(data):
         if not spec.active[s0]:
             continue
         goh = spec.group_of_head
-        most = [min(int(spec.lengths[s0, h]) for h in range(H) if goh[h] == g) // 16 for g in range(ng)]
+        most = [min(int(spec.lengths[s0, h]) for h in range(V) if goh[h] == g) // 16 for g in range(ng)]
         sh = [data.draw(st.integers(0, m)) for m in most]
-        fl = np.array([[sh[goh[h]] * 16 + data.draw(st.integers(0, 40)) for h in range(H)]])
+        fl = np.array([[sh[goh[h]] * 16 + data.draw(st.integers(0, 40)) for h in range(V)]])
         fc = fl + data.draw(st.integers(0, 20))
         a = spec.alias([slot], [s0], [sh], fc, fl)
         b = nup.kv_alias(ctx, [slot], [s0], [sh], fc, fl, raise_on_error=False)
@@ -385,6 +388,8 @@ def test_shared_plan_random_forks(data):
         victim = data.draw(st.integers(0, slot - 1))
         if spec.active[victim]:
             assert spec.free_seqs([victim]) == nup.kv_free_seqs(ctx, [victim], raise_on_error=False)
-    rows, ws, hrs = nup.get_plan(ctx)
-    hr = nup.get_plan_head_rows(ctx)
-    wt.check(rows, ws, hrs, spec.caps, spec.active, head_rows=hr, slack=1)
+    for layer in range(NL):
+        nup.set_layer(ctx, layer)
+        rows, ws, hrs = nup.get_plan(ctx)
+        hr = nup.get_plan_head_rows(ctx)
+        wt.check(rows, ws, hrs, spec.caps[:, layer * H:(layer + 1) * H], spec.active, head_rows=hr, slack=1)
