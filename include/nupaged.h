@@ -431,8 +431,11 @@ nup_status nup_get_runs(const nup_ctx *ctx, int32_t *out, int32_t max_runs, int3
  *   rows           int32 [n_rows][4] = (slot*H_kv + head, t0, t1, slot*V + head);
  *                  the last word indexes the head's length from the current
  *                  layer's first head, length rows being V apart
- *   worker_start   int32 [n_workers + 1]
- *   head_row_start int32 [B_max*H_kv + 1] */
+ *   worker_start   int32 [n_workers + 1]: worker w runs rows worker_start[w] ..
+ *                  worker_start[w+1] - 1, in that order
+ *   head_row_start int32 [B_max*H_kv + 1]: head sh has head_row_start[sh+1] -
+ *                  head_row_start[sh] rows; they are those rows of the table
+ *                  except under NUP_PLAN_SHARED (see nup_get_plan_head_rows) */
 nup_status nup_get_plan(const nup_ctx *ctx, int32_t *n_rows, int32_t *n_workers,
                         int32_t *rows, int32_t *worker_start, int32_t *head_row_start);
 /* Row ids of each head in the current layer's plan, int32 [n_rows]: head

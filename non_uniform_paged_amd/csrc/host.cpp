@@ -412,8 +412,8 @@ void plan_uniform(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
 //  * The rest of every head (everything, for heads in no set) is cut like
 //    the balanced plan, with each worker's share reduced by its gang row.
 // Rows are stored in worker order; head_rows lists each head's rows for the
-// merge.  No sharing, or sharing too wide for the workers, gives exactly the
-// balanced plan.  Correctness never depends on the sharing: every head's
+// merge.  No sharing, more sharer rows than workers, or a chunk longer than
+// a worker's share gives exactly the balanced plan.  Correctness never depends on the sharing: every head's
 // [0, cap) is still covered exactly once.
 void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
     const int B = c->B, H = c->H, W = c->workers;
