@@ -444,6 +444,15 @@ nup_status nup_get_plan(const nup_ctx *ctx, int32_t *n_rows, int32_t *n_workers,
  * this is the index the merge uses; under the other modes a head's rows are
  * contiguous and this is 0, 1, ..., n_rows - 1.  Errors: NUP_E_ARG. */
 nup_status nup_get_plan_head_rows(const nup_ctx *ctx, int32_t *head_rows);
+/* The gang launch of the current layer's NUP_PLAN_SHARED plan (head_dim 128):
+ * *n_blocks workgroups whose four waves hold one chunk of shared pages for
+ * four sharers; gang_rows int32 [4 * n_blocks] are their plan rows (the first
+ * row of each of those workers), run by the split-K kernel's gang mode, where
+ * the four waves load each page once between them through LDS; worker_skip
+ * int32 [n_workers] is 1 for the workers whose first row is run there (the
+ * main launch skips it).  Any pointer may be NULL; zero blocks under the
+ * other modes.  Errors: NUP_E_ARG. */
+nup_status nup_get_plan_gangs(const nup_ctx *ctx, int32_t *n_blocks, int32_t *gang_rows, int32_t *worker_skip);
 
 /* ---- measurement helpers ------------------------------------------------ */
 

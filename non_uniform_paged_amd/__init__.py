@@ -80,6 +80,7 @@ _sigs = {
     "nup_get_runs": [_P, _P, _I, _P],
     "nup_get_plan": [_P, _P, _P, _P, _P, _P],
     "nup_get_plan_head_rows": [_P, _P],
+    "nup_get_plan_gangs": [_P, _P, _P, _P],
     "nup_set_timing": [_P, _I],
     "nup_kernel_time": [_P, _P, _P, _I],
     "nup_device_errors": [_P, _P, _P],
@@ -380,6 +381,18 @@ def get_plan_head_rows(ctx: Context) -> np.ndarray:
     out = np.zeros(max(nr.value, 1), np.int32)
     ctx.check(_lib.nup_get_plan_head_rows(ctx.handle, out.ctypes.data))
     return out[: nr.value]
+
+
+def get_plan_gangs(ctx: Context):
+    """(gang_rows [n_blocks][4], worker_skip [n_workers]) of the current layer's plan."""
+    nb = ctypes.c_int32()
+    ctx.check(_lib.nup_get_plan_gangs(ctx.handle, ctypes.byref(nb), None, None))
+    nw = ctypes.c_int32()
+    ctx.check(_lib.nup_get_plan(ctx.handle, None, ctypes.byref(nw), None, None, None))
+    gr = np.zeros((max(nb.value, 1), 4), np.int32)
+    sk = np.zeros(max(nw.value, 1), np.int32)
+    ctx.check(_lib.nup_get_plan_gangs(ctx.handle, None, gr.ctypes.data, sk.ctypes.data))
+    return gr[: nb.value], sk[: nw.value]
 
 
 def set_timing(ctx: Context, enable: bool = True):

@@ -105,7 +105,10 @@ Sizes compute_sizes(const nup_config &c, int workers) {
                    align_up(16 * (size_t)z.max_rows);
     // the shared plan's rows are in worker order; head_rows lists each
     // head's rows for the merge
-    if (c.plan_mode == NUP_PLAN_SHARED) z.plan_layer += align_up(4 * (size_t)z.max_rows);
+    // and the gang launch's rows (four per workgroup), its workgroup count and
+    // which workers skip their first row
+    if (c.plan_mode == NUP_PLAN_SHARED)
+        z.plan_layer += align_up(4 * (size_t)z.max_rows) + 2 * align_up(4 * (size_t)z.max_workers) + kAlign;
     z.plan_max = NL * z.plan_layer;
     // every train covers at least one live page-table entry; with Alias the
     // entries (not the physical pages) are what bounds their number
@@ -186,13 +189,15 @@ struct nup_ctx {
         std::vector<int32_t> worker_start;   // [W+1]
         std::vector<int32_t> head_row_start; // [B*H+1]
         std::vector<int32_t> head_rows;      // shared plan: row ids by head (empty: identity)
+        std::vector<int32_t> gang_rows;      // shared plan: rows of the gang launch, four per workgroup
+        std::vector<int32_t> worker_skip;    // shared plan: [W] 1 if the worker's first row is in gang_rows
     };
     std::vector<Plan> plan;                  // [NL]
     std::vector<long long> plan_base, plan_bound;   // the balanced planner's scratch
 
     // active descriptor on the device (offsets into the inbox, in bytes)
     bool committed = false;
-    std::vector<size_t> off_ws, off_hrs, off_rows, off_hr;   // [NL]
+    std::vector<size_t> off_ws, off_hrs, off_rows, off_hr, off_skip, off_gang, off_gn;   // [NL]
     std::vector<int> dev_workers, dev_rows;          // [NL]
     size_t off_runs = 0, off_runpre = 0;
     int dev_runs = 0, dev_run_pages = 0;
@@ -496,6 +501,8 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
         chunk = lo;
         if (chunk > Aq) chunk = 0;   // a chunk longer than a worker's share would straggle
     }
+    pl.gang_rows.clear();
+    pl.worker_skip.clear();
     if (chunk == 0) {
         pl.head_rows.clear();
         plan_balanced(c, layer, pl);
@@ -513,13 +520,15 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
     };
     std::vector<int32_t> grow((size_t)W * 4, -1);   // the gang row of each physical worker
     std::vector<int32_t> gpiece((size_t)W, 0);      // its chunk's index within the head's range
+    std::vector<long long> gchunk((size_t)W, -1);   // which chunk (numbered over all gangs)
     std::vector<int32_t> gcount((size_t)NH, 0);     // gang rows of each head
     std::vector<long long> gload((size_t)W, 0);
     {
         int v = 0;
+        long long chunk_id = 0;
         for (const Gang &gg : gangs) {
             const long long k = (gg.len + chunk - 1) / chunk;
-            for (long long i = 0; i < k; ++i) {
+            for (long long i = 0; i < k; ++i, ++chunk_id) {
                 const long long p0 = gg.len * i / k, p1 = gg.len * (i + 1) / k;
                 for (int m = 0; m < gg.n; ++m, ++v) {
                     const int s = mem[(size_t)gg.first + m];
@@ -531,8 +540,26 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
                     r[3] = s * c->V + gg.h;
                     gload[w] = p1 - p0;
                     gpiece[w] = (int32_t)i;
+                    gchunk[w] = chunk_id;
                     gcount[(size_t)s * H + gg.h]++;
                 }
+            }
+        }
+    }
+    // -- workgroups whose four waves hold one chunk run it in the gang launch
+    //    (the split-K kernel's gang mode: the four waves load each page once
+    //    between them, through LDS); their workers skip that row in the main
+    //    launch, so it takes no room there
+    constexpr int kG = nup::kWavesPerBlock;
+    std::vector<uint8_t> coop((size_t)W / kG, 0);
+    if (xcd_map && c->D == 128) {
+        for (int b = 0; b < W / kG; ++b) {
+            const long long id = gchunk[(size_t)b * kG];
+            bool same = id >= 0;
+            for (int j = 1; j < kG && same; ++j) same = gchunk[(size_t)b * kG + j] == id;
+            if (same) {
+                coop[b] = 1;
+                for (int j = 0; j < kG; ++j) gload[(size_t)b * kG + j] = 0;
             }
         }
     }
@@ -672,6 +699,17 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
                 ++k;
             }
             for (; k < ke; ++k) pl.head_rows[next_rest[pl.rows[4 * (size_t)k]]++] = k;
+        }
+    }
+    // -- the gang launch: each cooperating workgroup's four gang rows (the
+    //    first row of each of its workers)
+    pl.worker_skip.assign((size_t)W, 0);
+    for (int b = 0; b < W / kG; ++b) {
+        if (!coop[b]) continue;
+        for (int j = 0; j < kG; ++j) {
+            const int w = b * kG + j;
+            pl.gang_rows.push_back(pl.worker_start[w]);
+            pl.worker_skip[w] = 1;
         }
     }
 }
@@ -855,11 +893,17 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
     c->off_hrs.assign(c->NL, 0);
     c->off_rows.assign(c->NL, 0);
     c->off_hr.assign(c->NL, 0);
+    c->off_skip.assign(c->NL, 0);
+    c->off_gang.assign(c->NL, 0);
+    c->off_gn.assign(c->NL, 0);
     for (int l = 0; l < c->NL; ++l) {
         c->off_ws[l] = c->sz.fixed + c->sz.caps + (size_t)l * c->sz.plan_layer;
         c->off_hrs[l] = c->off_ws[l] + align_up(4 * ((size_t)c->sz.max_workers + 1));
         c->off_rows[l] = c->off_hrs[l] + align_up(4 * ((size_t)c->B * c->H + 1));
         c->off_hr[l] = c->off_rows[l] + align_up(16 * (size_t)c->sz.max_rows);
+        c->off_skip[l] = c->off_hr[l] + align_up(4 * (size_t)c->sz.max_rows);
+        c->off_gang[l] = c->off_skip[l] + align_up(4 * (size_t)c->sz.max_workers);
+        c->off_gn[l] = c->off_gang[l] + align_up(4 * (size_t)c->sz.max_workers);
     }
     c->dev_workers.assign(c->NL, 0);
     c->dev_rows.assign(c->NL, 0);
@@ -1104,6 +1148,12 @@ nup_status nup_commit(nup_ctx *c, void *stream) {
                 int32_t *hr = reinterpret_cast<int32_t *>(blob + c->off_hr[l]);
                 if (pl.head_rows.empty()) std::iota(hr, hr + nr, 0);
                 else std::memcpy(hr, pl.head_rows.data(), 4 * (size_t)nr);
+                int32_t *sk = reinterpret_cast<int32_t *>(blob + c->off_skip[l]);
+                std::fill(sk, sk + c->sz.max_workers, 0);
+                if (!pl.worker_skip.empty()) std::memcpy(sk, pl.worker_skip.data(), 4 * pl.worker_skip.size());
+                if (!pl.gang_rows.empty())
+                    std::memcpy(blob + c->off_gang[l], pl.gang_rows.data(), 4 * pl.gang_rows.size());
+                *reinterpret_cast<int32_t *>(blob + c->off_gn[l]) = (int32_t)(pl.gang_rows.size() / nup::kWavesPerBlock);
             }
             c->dev_workers[l] = c->sz.max_workers;
             c->dev_rows[l] = nr;
@@ -1443,6 +1493,21 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
             return hip_fail(c, e, "hipEventCreate");
         if ((e = hipEventRecord(e0, st)) != hipSuccess) return hip_fail(c, e, "hipEventRecord");
     }
+    const bool gang = !topk && c->cfg.plan_mode == NUP_PLAN_SHARED && c->D == 128 &&
+                      c->sz.max_workers % nup::kWavesPerBlock == 0;
+    if (gang) {
+        // the share-aware plan's gang launch first: workgroups of four
+        // sharers of one chunk (the count is read on the device, so a
+        // captured launch follows the plan); no appends there
+        nup::PartialArgs g = a;
+        g.k_new = nullptr;
+        g.v_new = nullptr;
+        g.gang_rows = c->inbox_i32(c->off_gang[c->layer]);
+        g.gang_blocks = c->inbox_i32(c->off_gn[c->layer]);
+        e = nup::launch_partial(g, c->D, c->gqa, nup::kModeGang, st);
+        if (e != hipSuccess) return hip_fail(c, e, "gang attention launch");
+        a.worker_skip = c->inbox_i32(c->off_skip[c->layer]);
+    }
     e = nup::launch_partial(a, c->D, c->gqa, mode, st);
     if (e != hipSuccess) return hip_fail(c, e, "partial attention launch");
     if (timed) {
@@ -1717,6 +1782,20 @@ nup_status nup_get_plan_head_rows(const nup_ctx *c, int32_t *head_rows) {
     const int32_t n = (int32_t)(pl.rows.size() / 4);
     if (pl.head_rows.empty()) std::iota(head_rows, head_rows + n, 0);
     else std::copy(pl.head_rows.begin(), pl.head_rows.end(), head_rows);
+    return NUP_OK;
+}
+
+nup_status nup_get_plan_gangs(const nup_ctx *c, int32_t *n_blocks, int32_t *gang_rows, int32_t *worker_skip) {
+    if (!c) return NUP_E_ARG;
+    if (c->plan_dirty) replan(const_cast<nup_ctx *>(c));
+    const nup_ctx::Plan &pl = c->plan[c->layer];
+    if (n_blocks) *n_blocks = (int32_t)(pl.gang_rows.size() / nup::kWavesPerBlock);
+    if (gang_rows) std::copy(pl.gang_rows.begin(), pl.gang_rows.end(), gang_rows);
+    if (worker_skip) {
+        const size_t W = pl.worker_start.empty() ? 0 : pl.worker_start.size() - 1;
+        std::fill(worker_skip, worker_skip + W, 0);
+        std::copy(pl.worker_skip.begin(), pl.worker_skip.end(), worker_skip);
+    }
     return NUP_OK;
 }
 

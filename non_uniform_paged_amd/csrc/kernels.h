@@ -17,6 +17,8 @@ constexpr int kWavesPerBlock = 4;   // split-K workers per 256-thread workgroup
 constexpr int kModePaged = 0;     // pool through the page tables, plan rows
 constexpr int kModeStaged = 1;    // contiguous staging [Bmax*Hkv][K][D], equal split
 constexpr int kModeIndexed = 2;   // pool rows named by top-K indices, equal split
+constexpr int kModeGang = 3;      // shared pages, one plan row per wave, four sharers per workgroup (D = 128)
+constexpr int kGangDepth = 8;     // pages in flight per workgroup in gang mode
 constexpr int kMaxTopkChunk = 2048;  // entries per top-K worker (LDS row ids)
 
 // Split-K decode attention.  One wave is one worker.  In table mode a
@@ -52,6 +54,10 @@ struct PartialArgs {
     // the merge kernel then advances L
     const uint16_t *k_new, *v_new;
     const int32_t *caps;        // this layer's budgets, indexed like lengths
+    // share-aware plans (paged and gang modes; NULL otherwise)
+    const int32_t *worker_skip; // [W]: 1 if the worker's first row runs in gang mode instead
+    const int32_t *gang_rows;   // [4 * blocks]: the plan rows of workgroup b's four waves
+    const int32_t *gang_blocks; // workgroups that have a chunk (device, read at run time)
 };
 
 struct MergeArgs {

@@ -107,7 +107,9 @@ __device__ __forceinline__ void write_final(const PartialArgs &a, size_t qh0, in
 template <int D, int GQA, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NUP_WAVES_PER_EU, 8)))
 void partial_attn_kernel(PartialArgs a) {
-    constexpr bool TOPK = MODE != kModePaged;   // equal split of K entries per head
+    constexpr bool TOPK = MODE == kModeStaged || MODE == kModeIndexed;   // equal split of K entries per head
+    constexpr bool GANG = MODE == kModeGang;
+    static_assert(!GANG || D == 128, "gang mode: two 16-byte pieces of a page per thread");
     constexpr int NJ = D / 32;     // MFMA steps over the head dim
     constexpr int LPR = D / 8;     // lanes per V row (16-byte pieces)
     constexpr int TPL = LPR / 4;   // tokens per lane for V
@@ -125,7 +127,7 @@ void partial_attn_kernel(PartialArgs a) {
     // through an LDS tile, rows padded by one 16-byte piece.  The counters
     // still show about 16 bank-conflict cycles per 16-token page, well under
     // one percent of a page's time.
-    constexpr bool kRowK = MODE != kModePaged;
+    constexpr bool kRowK = TOPK;
     static_assert(NJ == TPL, "one K register per MFMA step either way");
     __shared__ uint4 k_lds[kWavesPerBlock][kRowK ? kPage : 1][LPR + 1];
     // indexed top-K: the pool row of every entry of the worker's chunk (-1: not readable)
@@ -147,17 +149,35 @@ void partial_attn_kernel(PartialArgs a) {
     const int tg = lane / LPR, ve = lane % LPR;
 
     int rb, re;
+    int lead = 0;   // gang mode: the plan row of the workgroup's first wave
     if (TOPK) {
         rb = w;
         re = w + 1;
+    } else if (GANG) {
+        // a workgroup without a chunk leaves as a whole
+        if ((int)blockIdx.x >= ld_uniform(a.gang_blocks)) return;
+        rb = ld_uniform(a.gang_rows + w);
+        re = rb + 1;
+        lead = ld_uniform(a.gang_rows + (int)blockIdx.x * kWavesPerBlock);
     } else {
         rb = ld_uniform(a.worker_start + w);
         re = ld_uniform(a.worker_start + w + 1);
+        if (a.worker_skip) rb += ld_uniform(a.worker_skip + w);
     }
     for (int row = rb; row < re; ++row) {
         int sh, t0, t1;
         int app_at = -1;   // fused append: the position this row stores and reads the new token at
-        if (TOPK) {
+        int t1g = 0;       // gang mode: the workgroup's planned end, shared by its four waves
+        if (GANG) {
+            // The workgroup's four rows hold one chunk of pages that their
+            // sequences share.  Pages and the page count come from the first
+            // wave's row, so every wave meets the same barriers; each wave
+            // masks its own tokens at its own length.
+            sh = ld_uniform(a.rows + row * 4 + 0);
+            t0 = ld_uniform(a.rows + lead * 4 + 1);
+            t1g = ld_uniform(a.rows + lead * 4 + 2);
+            t1 = min(t1g, ld_uniform(a.lengths + ld_uniform(a.rows + row * 4 + 3)));
+        } else if (TOPK) {
             sh = row / a.topk_splits;
             t0 = (row - sh * a.topk_splits) * a.topk_chunk;
             const int n = ld_uniform(a.active + sh / a.hkv) ? a.topk_k : 0;
@@ -190,7 +210,7 @@ void partial_attn_kernel(PartialArgs a) {
             nrows = ld_uniform(a.head_row_start + sh + 1) - hr0;
         }
         const size_t qh0 = (size_t)s * a.hkv * GQA + (size_t)h * GQA;   // first query head
-        if (t0 >= t1) {
+        if (GANG ? t0 >= t1g : t0 >= t1) {
             if (nrows == 1) {
                 write_final<D, GQA>(a, qh0, lane, nullptr);
             } else {
@@ -223,11 +243,13 @@ void partial_attn_kernel(PartialArgs a) {
         const int32_t *ptrow = nullptr;
         size_t slot_off = 0;
         if (MODE != kModeStaged) {
-            ptrow = a.page_table + ((size_t)ld_uniform(a.group_of_head + h) * a.bmax + s) * (size_t)a.max_pages;
+            // gang mode reads the first wave's pages (the same physical pages)
+            const int ps = GANG ? ld_uniform(a.rows + lead * 4 + 0) / a.hkv : s;
+            ptrow = a.page_table + ((size_t)ld_uniform(a.group_of_head + h) * a.bmax + ps) * (size_t)a.max_pages;
             slot_off = (size_t)ld_uniform(a.slot_of_head + h) * kPage * D;
         }
         const size_t head_base = MODE == kModeStaged ? (size_t)sh * a.topk_k * D : 0;
-        const int p0 = t0 / kPage, p1 = (t1 - 1) / kPage;  // inclusive page range
+        const int p0 = t0 / kPage, p1 = ((GANG ? t1g : t1) - 1) / kPage;  // inclusive page range
 
         if (MODE == kModePaged && app_at >= 0) {
             // store the new K and V rows before any page of the row is read
@@ -390,6 +412,66 @@ void partial_attn_kernel(PartialArgs a) {
             __builtin_amdgcn_wave_barrier();
         };
 
+        if constexpr (GANG) {
+            // Gang mode.  Thread j of the workgroup loads 16-byte piece j of
+            // the page's K block and of its V block, kGangDepth pages ahead;
+            // the pieces meet in a double-buffered LDS tile (rows padded by
+            // one piece), and every wave reads the whole page from there for
+            // its own query rows.  One workgroup barrier per page, fenced on
+            // LDS only, so the loads in flight stay in flight.
+            __shared__ uint4 g_lds[2][2 * kPage][LPR + 1];
+            const int gj = (int)threadIdx.x;
+            const int g_row = gj / LPR, g_col = gj % LPR;
+            const uint32_t g_off = (uint32_t)g_row * LPR + g_col;
+            constexpr int PF = kGangDepth;
+            uint4 gk[PF], gv[PF];
+            auto gload = [&](int pi, uint4 &kr, uint4 &vr) {
+                const size_t base = page_base(pi);
+                kr = ld_stream(reinterpret_cast<const uint4 *>(a.kbase + base) + g_off);
+                vr = ld_stream(reinterpret_cast<const uint4 *>(a.vbase + base) + g_off);
+            };
+            auto gpage = [&](int pi, const uint4 &kr, const uint4 &vr, bool more) {
+                const int st = (pi - p0) & 1;
+                g_lds[st][g_row][g_col] = kr;
+                g_lds[st][kPage + g_row][g_col] = vr;
+                return st;
+            };
+            auto gcompute = [&](int pi, int st) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+                uint4 k[TPL], v[TPL];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) k[j] = g_lds[st][qn][4 * j + qg];
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) v[i] = g_lds[st][kPage + tg * TPL + i][ve];
+                compute(pi, k, v);
+            };
+#pragma unroll
+            for (int j = 0; j < PF; ++j)
+                if (p0 + j <= p1) gload(p0 + j, gk[j], gv[j]);
+            int pb = p0;
+            // steady state: every prefetch unconditional
+            for (; pb + 2 * PF - 1 <= p1; pb += PF) {
+#pragma unroll
+                for (int j = 0; j < PF; ++j) {
+                    const int st = gpage(pb + j, gk[j], gv[j], true);
+                    gload(pb + j + PF, gk[j], gv[j]);
+                    gcompute(pb + j, st);
+                }
+            }
+            for (; pb <= p1; pb += PF) {
+#pragma unroll
+                for (int j = 0; j < PF; ++j) {
+                    const int p = pb + j;
+                    if (p <= p1) {
+                        const int st = gpage(p, gk[j], gv[j], true);
+                        if (p + PF <= p1) gload(p + PF, gk[j], gv[j]);
+                        gcompute(p, st);
+                    }
+                }
+            }
+        } else {
 #if NUP_PREFETCH == 2
         // Two page buffers: page p+1 is in flight while page p is computed.
         // The steady-state loads are unconditional, so the wait before each
@@ -431,6 +513,7 @@ void partial_attn_kernel(PartialArgs a) {
             }
         }
 #endif
+        }
 
         // Combine: the row sums over the four token quads, the outputs over
         // the token groups of V.
@@ -446,6 +529,15 @@ void partial_attn_kernel(PartialArgs a) {
                 for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
                 o[r][c] = x;
             }
+        if (GANG && lt == 0.f) {   // no token of its own (not planned): nothing to add
+            if (nrows == 1) {
+                write_final<D, GQA>(a, qh0, lane, nullptr);
+            } else if (lane < GQA) {
+                ml[lane * 2 + 0] = -INFINITY;
+                ml[lane * 2 + 1] = 0.f;
+            }
+            continue;
+        }
         if (nrows == 1) {
             // the head is this row: normalise and write the output
             if (lane < GQA) {
@@ -1506,6 +1598,7 @@ void *partial_fn_mode(int gqa, int mode) {
         case kModePaged: return partial_fn_gqa<D, kModePaged>(gqa);
         case kModeStaged: return partial_fn_gqa<D, kModeStaged>(gqa);
         case kModeIndexed: return partial_fn_gqa<D, kModeIndexed>(gqa);
+        case kModeGang: return D == 128 ? partial_fn_gqa<128, kModeGang>(gqa) : nullptr;
         default: return nullptr;
     }
 }
@@ -1555,6 +1648,10 @@ hipError_t launch_partial(const PartialArgs &a, int head_dim, int gqa, int mode,
     if (!a.q || !a.kbase || !a.vbase || !a.active || !a.ws_o || !a.ws_ml || !a.out) return hipErrorInvalidValue;
     if (mode == kModePaged && (!a.page_table || !a.lengths || !a.group_of_head || !a.slot_of_head || !a.rows ||
                                !a.worker_start || !a.head_row_start))
+        return hipErrorInvalidValue;
+    if (mode == kModeGang && (head_dim != 128 || !a.page_table || !a.lengths || !a.group_of_head ||
+                              !a.slot_of_head || !a.rows || !a.head_row_start || !a.gang_rows || !a.gang_blocks ||
+                              a.k_new || a.n_workers % kWavesPerBlock))
         return hipErrorInvalidValue;
     if (mode == kModeIndexed && (!a.page_table || !a.lengths || !a.group_of_head || !a.slot_of_head || !a.idx ||
                                  !a.err))

@@ -21,7 +21,9 @@ the table is judged by properties rather than bit-exactly:
     each head's rows, and the coverage checks apply to the table read
     through it; head_rows must be a permutation of the rows.  Shares there
     follow each worker's room after its first row, so the balance bound
-    takes a slack of one page.
+    takes a slack of one page.  Workers whose first row runs in a launch of
+    its own (skip[w] = 1: the share-aware plan's gang launch) are balanced
+    without that row.
 
 Parity: the checker is pinned by tests that feed it hand-made valid and
 invalid tables (tests/test_oracle_worktable.py).
@@ -34,7 +36,7 @@ import numpy as np
 
 
 def check(rows, worker_start, head_row_start, caps, active, page=16,
-          balanced=True, head_rows=None, slack=0):
+          balanced=True, head_rows=None, slack=0, skip=None):
     """rows: int [n][4] = (s*Hkv + h, t0, t1, _); worker_start: [W+1];
     head_row_start: [B*Hkv + 1]; head_rows: [n] row ids by head, or None
     when each head's rows are contiguous in the table.  Raises
@@ -73,7 +75,11 @@ def check(rows, worker_start, head_row_start, caps, active, page=16,
     loads = []
     for w in range(len(worker_start) - 1):
         pages = 0
-        for i in range(int(worker_start[w]), int(worker_start[w + 1])):
+        first = int(worker_start[w])
+        if skip is not None and skip[w]:
+            assert first < int(worker_start[w + 1]), f"worker {w} skips a row it does not have"
+            first += 1
+        for i in range(first, int(worker_start[w + 1])):
             pages += math.ceil(rows[i, 2] / page) - rows[i, 1] // page
         loads.append(pages)
     if balanced and loads:

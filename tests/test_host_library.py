@@ -311,12 +311,25 @@ def test_shared_plan_on_forked_batch():
     ctx, goh, forks, share = _forked_ctx(w, nup.PLAN_SHARED)
     rows, ws, hrs = nup.get_plan(ctx)
     hr = nup.get_plan_head_rows(ctx)
+    gangs, skip = nup.get_plan_gangs(ctx)
     B, H = w.batch, w.num_kv_heads
-    loads = wt.check(rows, ws, hrs, w.caps, np.ones(B, bool), head_rows=hr, slack=1)
+    # the main launch, without the rows the gang launch runs, is balanced
+    loads = wt.check(rows, ws, hrs, w.caps, np.ones(B, bool), head_rows=hr, slack=1, skip=skip)
     bctx, *_ = _forked_ctx(w, nup.PLAN_BALANCED)
     brows, bws, bhrs = nup.get_plan(bctx)
     bloads = wt.check(brows, bws, bhrs, w.caps, np.ones(B, bool))
-    assert sum(loads) == sum(bloads)
+    gang_pages = sum(int(rows[r, 2] - rows[r, 1]) // 16 for r in gangs.reshape(-1))
+    assert sum(loads) + gang_pages == sum(bloads)
+    # gang workgroups: four consecutive workers (one workgroup), each running
+    # its first row there, all four rows one chunk of one head's shared pages
+    assert len(gangs) > 0 and int(skip.sum()) == 4 * len(gangs)
+    for blk in gangs:
+        wk = [int(np.searchsorted(ws, r, side="right") - 1) for r in blk]
+        assert wk[0] % 4 == 0 and wk == list(range(wk[0], wk[0] + 4))
+        assert all(ws[x] == r and skip[x] == 1 for x, r in zip(wk, blk))
+        assert len({tuple(rows[r, 1:3]) for r in blk}) == 1
+        assert len({int(rows[r, 0]) % H for r in blk}) == 1
+        assert len({int(rows[r, 0]) // H for r in blk}) == 4
     first = np.zeros(len(rows), bool)
     first[ws[:-1][ws[:-1] < ws[1:]]] = True
     worker_of = np.repeat(np.arange(len(ws) - 1), np.diff(ws))
@@ -362,7 +375,8 @@ def test_shared_plan_random_forks(data):
     ng = data.draw(st.sampled_from([g for g in (1, 2, 3, 4, 6, 8, 12) if V % g == 0]))
     B, num_pages, max_pages = 8, 400 * NL, 12
     W_ = data.draw(st.sampled_from([3, 7, 16, 37, 64]))
-    ctx = _host_ctx(H=H, Hq=2 * H, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages,
+    D = data.draw(st.sampled_from([64, 128]))       # head_dim 128 may add gang workgroups
+    ctx = _host_ctx(H=H, Hq=2 * H, D=D, ng=ng, B=B, num_pages=num_pages, max_pages=max_pages,
                     num_workers=W_, plan_mode=nup.PLAN_SHARED, num_layers=NL)
     spec = pg.PagerSpec(V, ng, B, num_pages, max_pages, 16, None)
     n_src = data.draw(st.integers(1, 3))
@@ -392,4 +406,6 @@ def test_shared_plan_random_forks(data):
         nup.set_layer(ctx, layer)
         rows, ws, hrs = nup.get_plan(ctx)
         hr = nup.get_plan_head_rows(ctx)
-        wt.check(rows, ws, hrs, spec.caps[:, layer * H:(layer + 1) * H], spec.active, head_rows=hr, slack=1)
+        gangs, skip = nup.get_plan_gangs(ctx)
+        wt.check(rows, ws, hrs, spec.caps[:, layer * H:(layer + 1) * H], spec.active, head_rows=hr, slack=1,
+                 skip=skip)

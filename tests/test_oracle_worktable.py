@@ -84,3 +84,13 @@ def test_rejects_bad_head_rows(mutate):
         hr[3], hr[4] = hr[4], hr[3]        # a row of head 2 listed under head 1
     with pytest.raises(AssertionError):
         wt.check(rows, ws, hrs, CAPS, ACTIVE, head_rows=hr, slack=1)
+
+
+def test_skip_balances_without_the_skipped_rows():
+    # worker 0's first row (head 3, 16..48) runs in a launch of its own: the
+    # remaining loads are 3 and 3, within the ceiling of their mean
+    rows, ws, hrs, hr = _worker_ordered()
+    loads = wt.check(rows, ws, hrs, CAPS, ACTIVE, head_rows=hr, skip=[1, 0])
+    assert loads == [3, 3]
+    with pytest.raises(AssertionError):            # a worker with no row cannot skip one
+        wt.check(rows, np.array([0, 0, 7]), hrs, CAPS, ACTIVE, head_rows=hr, skip=[1, 0], balanced=False)
