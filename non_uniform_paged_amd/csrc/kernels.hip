@@ -430,12 +430,15 @@ void partial_attn_kernel(PartialArgs a) {
                 kr = ld_stream(reinterpret_cast<const uint4 *>(a.kbase + base) + g_off);
                 vr = ld_stream(reinterpret_cast<const uint4 *>(a.vbase + base) + g_off);
             };
-            auto gpage = [&](int pi, const uint4 &kr, const uint4 &vr, bool more) {
+            // the pieces of page pi into its LDS stage; returns the stage
+            auto gstore = [&](int pi, const uint4 &kr, const uint4 &vr) {
                 const int st = (pi - p0) & 1;
                 g_lds[st][g_row][g_col] = kr;
                 g_lds[st][kPage + g_row][g_col] = vr;
                 return st;
             };
+            // after the workgroup barrier, the whole page from LDS in the
+            // operand layouts, then this wave's rows
             auto gcompute = [&](int pi, int st) {
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
                 __builtin_amdgcn_s_barrier();
@@ -455,7 +458,7 @@ void partial_attn_kernel(PartialArgs a) {
             for (; pb + 2 * PF - 1 <= p1; pb += PF) {
 #pragma unroll
                 for (int j = 0; j < PF; ++j) {
-                    const int st = gpage(pb + j, gk[j], gv[j], true);
+                    const int st = gstore(pb + j, gk[j], gv[j]);
                     gload(pb + j + PF, gk[j], gv[j]);
                     gcompute(pb + j, st);
                 }
@@ -465,7 +468,7 @@ void partial_attn_kernel(PartialArgs a) {
                 for (int j = 0; j < PF; ++j) {
                     const int p = pb + j;
                     if (p <= p1) {
-                        const int st = gpage(p, gk[j], gv[j], true);
+                        const int st = gstore(p, gk[j], gv[j]);
                         if (p + PF <= p1) gload(p + PF, gk[j], gv[j]);
                         gcompute(p, st);
                     }
