@@ -247,3 +247,43 @@ def test_shared_plan_random_forks(data):
     assert_attention_close(c.out.cpu().numpy().astype(np.float64), c.lse.cpu().numpy().astype(np.float64),
                            ref, ref_lse, f"{tag} fused")
     assert nup.device_errors(c.ctx) == nup.NUP_OK
+
+
+def test_select_topk_under_shared_plan_equals_balanced():
+    """Exact top-K selection walks every row of the plan, the gang rows of
+    the share-aware plan included (only the attention's main launch skips
+    them): on forked sequences its choices are bit-identical to the
+    balanced plan's on a twin context, and so is the attention."""
+    H, gqa, D, B, ng = 8, 4, 128, 6, 2
+    rs = np.random.default_rng(33)
+    L0 = rs.integers(300, 700, size=H)
+    twins = [Case(H=H, Hq=H * gqa, D=D, ng=ng, B=B, num_pages=300, max_pages=64,
+                  free_list_init=np.random.default_rng(33).permutation(300), num_workers=64,
+                  plan_mode=mode, salt=33) for mode in (nup.PLAN_BALANCED, nup.PLAN_SHARED)]
+    for c in twins:
+        assert c.alloc([0], (L0 + 20)[None], L0[None]) == pg.OK
+    goh = twins[0].spec.group_of_head
+    most = _group_share(goh, L0, ng)
+    forks = [1, 2, 3, 4]
+    share = np.tile(most, (len(forks), 1))
+    lens = share[:, goh] * 16 + 64 + rs.integers(0, 200, size=(len(forks), H))
+    caps = lens + 16
+    for c in twins:
+        assert c.alias(forks, [0] * len(forks), share, caps, lens) == pg.OK
+        c.commit()
+    gangs, _ = nup.get_plan_gangs(twins[1].ctx)
+    assert len(gangs) > 0                           # the shared plan has a gang launch
+    K, window = 48, 8
+    picks = []
+    for c in twins:
+        out = torch.full((B, H, K), -5, dtype=torch.int32, device=DEV)
+        ws = torch.empty(nup.select_workspace_bytes(c.ctx), dtype=torch.uint8, device=DEV)
+        nup.kv_select_topk(c.ctx, c.q, K, window, out, ws)
+        torch.cuda.synchronize()
+        picks.append(out.cpu().numpy())
+    assert np.array_equal(picks[0], picks[1])
+    assert (picks[0][:5] >= 0).all() and (picks[0][5] == -5).all()
+    outs = [c.attend() for c in twins]
+    ref, ref_lse = twins[1].oracle()
+    for out, lse in outs:
+        assert_attention_close(out, lse, ref, ref_lse, "twins")
