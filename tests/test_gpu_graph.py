@@ -302,3 +302,73 @@ def test_graph_select_then_attend_in_place():
         assert np.array_equal(nup.get_lengths(G.ctx), nup.get_lengths(E.ctx)), i
     assert torch.equal(G.kpool, E.kpool) and torch.equal(G.vpool, E.vpool)
     assert nup.device_errors(G.ctx) == nup.NUP_OK and nup.device_errors(E.ctx) == nup.NUP_OK
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_gang_launch_follows_commits(fused):
+    """The share-aware plan's gang launch inside a captured graph: forks of
+    one source are added (Alias) and removed (Trim) between replays, so the
+    number of gang workgroups changes from commit to commit (the kernel
+    reads it on the device).  Every replay equals the same calls made eagerly
+    on a twin, bit for bit; the last one is checked against the oracle."""
+    Hh, gq, Dd, Bb = 4, 4, 128, 8
+    rs = np.random.default_rng(91)
+    kw = dict(H=Hh, Hq=Hh * gq, D=Dd, ng=1, B=Bb, num_pages=Bb * 40 + 8, max_pages=40,
+              free_list_init=np.random.default_rng(91).permutation(Bb * 40 + 8), num_workers=64,
+              plan_mode=nup.PLAN_SHARED, salt=91)
+    G, E = Case(**kw), Case(**kw)
+    L0 = rs.integers(300, 500, size=(1, Hh)).astype(np.int32)
+    for c in (G, E):
+        assert c.alloc([0], L0 + 40, L0) == pg.OK
+        c.commit()
+    kn = torch.empty((Bb, Hh, Dd), dtype=torch.bfloat16, device=DEV)
+    vn = torch.empty_like(kn)
+    q = torch.empty((Bb, Hh * gq, Dd), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((Bb, Hh * gq, Dd), dtype=torch.float32, device=DEV)
+    lse = torch.empty((Bb, Hh * gq), dtype=torch.float32, device=DEV)
+    e_out, e_lse = torch.empty_like(out), torch.empty_like(lse)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _step(G, 0, kn, vn, q, out, lse, fused)
+    counts = []
+    fk, fv = u16(G.kpool).copy().reshape(-1, Dd), u16(G.vpool).copy().reshape(-1, Dd)
+    for i in range(6):
+        share = int(E.spec.lengths[0].min()) // 16 // 2
+        if i in (1, 2):                      # four more sharers each time
+            new = [1, 2, 3, 4] if i == 1 else [5, 6, 7]
+            L = np.full((len(new), Hh), 16 * share + 20, np.int32)
+            for c in (G, E):
+                assert c.alias(new, [0] * len(new), np.full((len(new), 1), share, np.int32), L + 40, L) == pg.OK
+        if i == 4:
+            for c in (G, E):
+                c.free([2, 5])
+        for c in (G, E):
+            c.commit()
+        counts.append(len(nup.get_plan_gangs(G.ctx)[0]))
+        fk, fv = u16(G.kpool).copy().reshape(-1, Dd), u16(G.vpool).copy().reshape(-1, Dd)
+        kn.copy_(_dev_bf16("k", (Bb, Hh, Dd), 500 + i))
+        vn.copy_(_dev_bf16("v", (Bb, Hh, Dd), 500 + i))
+        q.copy_(_dev_bf16("q", (Bb, Hh * gq, Dd), 500 + i))
+        g.replay()
+        nup.note_appends(G.ctx, 1)
+        nup.kv_append(E.ctx, kn, vn)
+        nup.attn_decode_nonuniform(E.ctx, q, e_out, e_lse, E.scale, E.ws)
+        sp = E.spec
+        for s in range(Bb):
+            if sp.active[s]:
+                for h in range(Hh):
+                    row = sp.physical_row(s, h, int(sp.lengths[s, h]))
+                    fk[row], fv[row] = u16(kn)[s, h], u16(vn)[s, h]
+                    sp.lengths[s, h] += 1
+        G.spec.lengths[:] = sp.lengths
+        torch.cuda.synchronize()
+        assert torch.equal(out, e_out) and torch.equal(lse, e_lse), i
+        assert torch.equal(G.kpool, E.kpool) and torch.equal(G.vpool, E.vpool), i
+        assert np.array_equal(nup.get_lengths(G.ctx), sp.lengths), i
+    assert counts[0] == 0 and max(counts) > 0 and len(set(counts)) > 2, counts
+    assert nup.device_errors(G.ctx) == nup.NUP_OK
+    kp, vp = fk.reshape(u16(G.kpool).shape), fv.reshape(u16(G.vpool).shape)
+    ref, ref_lse = oracle.decode(u16(q), kp, vp, E.spec.page_table, E.spec.lengths,
+                                 E.spec.group_of_head, E.spec.slot_of_head, G.scale)
+    assert_attention_close(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                           ref, ref_lse, "gang graph, last replay")
