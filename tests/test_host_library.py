@@ -409,3 +409,30 @@ def test_shared_plan_random_forks(data):
         gangs, skip = nup.get_plan_gangs(ctx)
         wt.check(rows, ws, hrs, spec.caps[:, layer * H:(layer + 1) * H], spec.active, head_rows=hr, slack=1,
                  skip=skip)
+
+
+def test_plan_gangs_only_for_shared_plan_at_head_dim_128():
+    """The gang launch exists only under the share-aware plan with head_dim
+    128 and whole workgroups of workers; otherwise no workgroup is listed and
+    no worker skips a row (the forked batch at 2048 workers has both)."""
+    import workloads as W
+    w = W.qwen25_32b_prefix()
+    for mode, expect in ((nup.PLAN_BALANCED, False), (nup.PLAN_SHARED, True)):
+        ctx, *_ = _forked_ctx(w, mode)
+        gangs, skip = nup.get_plan_gangs(ctx)
+        assert (len(gangs) > 0) == expect and (int(skip.sum()) > 0) == expect
+    for D, workers in ((64, 2048), (128, 2044)):
+        ctx = _host_ctx(H=w.num_kv_heads, Hq=w.num_q_heads, D=D, ng=w.num_groups, B=w.batch,
+                        num_pages=w.num_pages, max_pages=int(w.caps.max() // 16 + 1),
+                        num_workers=workers, plan_mode=nup.PLAN_SHARED)
+        src = w.extra["alias_src"]
+        roots, forks = np.nonzero(src < 0)[0], np.nonzero(src >= 0)[0]
+        goh = nup.kv_alloc_groups(ctx, roots, w.caps[roots], w.lengths[roots])
+        share = np.zeros((len(forks), w.num_groups), np.int32)
+        for g in range(w.num_groups):
+            share[:, g] = w.extra["prefix_tokens"][forks][:, goh == g].min(axis=1) // 16
+        nup.kv_alias(ctx, forks, src[forks], share, w.caps[forks], w.lengths[forks])
+        gangs, skip = nup.get_plan_gangs(ctx)
+        assert len(gangs) == 0 and not skip.any(), (D, workers)
+        rows, ws, hrs = nup.get_plan(ctx)
+        wt.check(rows, ws, hrs, w.caps, np.ones(w.batch, bool), head_rows=nup.get_plan_head_rows(ctx), slack=1)
