@@ -125,11 +125,29 @@ typedef struct nup_config {
  * word).  Host only; no device call. */
 nup_status nup_desc_bytes(const nup_config *cfg, size_t *bytes);
 
-/* Create a context over caller-owned pools and arena.  The arena is not
- * touched until the first nup_commit().  cfg->k_pool / v_pool / desc may be
- * NULL for host-only use (pager, planner and coalescer queries); device
- * calls on such a context fail with NUP_E_STATE.  Errors: NUP_E_ARG. */
+/*
+ * nup_create -- set up the block pager over caller-owned physical storage
+ * (KV-RM, abstract: logical KV histories decoupled from physical storage
+ * and tracked by a block pager; Fig 2: the KV pager of the control plane).
+ * The K and V pools are the physical pages, the FIFO free list starts as
+ * cfg->free_list_init (or 0..num_pages-1), every slot is inactive and no
+ * head is grouped yet.
+ *   cfg   host; read, not kept (free_list_init is copied)
+ *   out   host; receives the new context (NULL on failure)
+ * The arena is not touched until the first nup_commit().  cfg->k_pool /
+ * v_pool / desc may be NULL for host-only use (pager, planner and
+ * coalescer queries); device calls on such a context fail with
+ * NUP_E_STATE.  The library keeps the device pointers but never frees
+ * them.  Errors: NUP_E_ARG (a shape the kernels do not support, sizes out
+ * of range, an arena not 256-byte aligned, a free_list_init that is not a
+ * permutation), NUP_E_HIP (device buffers given but no HIP device); the
+ * reason goes to stderr, and nothing is kept on failure. */
 nup_status nup_create(const nup_config *cfg, nup_ctx **out);
+/* nup_destroy -- release the context's host state and pinned staging
+ * buffers (the end of the pager of nup_create; KV-RM, abstract), after
+ * waiting for the commits that still read those buffers.  The caller's
+ * device buffers are left alone; kernels still queued that read the arena
+ * or pools must finish before the caller frees them.  NULL is a no-op. */
 void nup_destroy(nup_ctx *ctx);
 const char *nup_last_error(const nup_ctx *ctx);
 
@@ -211,7 +229,10 @@ nup_status kv_free_seqs(nup_ctx *ctx, int32_t n, const int32_t *slots);
 nup_status nup_commit(nup_ctx *ctx, void *stream);
 
 /*
- * kv_append -- the decode step's write: for every active (slot, KV head),
+ * kv_append -- the decode step's write (KV-RM, Fig 3: one decode step
+ * under the pager's contract, whose new token lands in the mapping sealed
+ * by the frame commit; Tangram, abstract: the head's footprint is fixed, so
+ * the write must fit its budget): for every active (slot, KV head),
  * store the new token's K and V rows at logical position L (page table
  * entry L / P of the head's group, row L % P of the head's slot) and
  * advance L by one, on the device and in the shadow.

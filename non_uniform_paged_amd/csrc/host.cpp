@@ -461,9 +461,19 @@ void plan_shared(nup_ctx *c, int layer, nup_ctx::Plan &pl) {
                         while (m < lim && r[m] == r0[m]) ++m;
                         len = m;
                     }
+                    // Only whole pages below every member head's current
+                    // length: shared pages are full (kv_alias checks it) and
+                    // lengths only grow, so this cap changes nothing today,
+                    // but it states at the point of use what the gang launch
+                    // relies on: a gang chunk never holds a head's append
+                    // position, whose token only the main launch stores.
+                    const int32_t *lenl = c->len.data() + (size_t)layer * H;
                     for (int h : heads)
-                        for (size_t k = i; k < j; ++k)
-                            len = std::min(len, (long long)capl[(size_t)keys[k].second * c->V + h] >> 4);
+                        for (size_t k = i; k < j; ++k) {
+                            const size_t sk = (size_t)keys[k].second * c->V + h;
+                            len = std::min(len, (long long)capl[sk] >> 4);
+                            len = std::min(len, (long long)lenl[sk] >> 4);
+                        }
                     if (len > 0) {
                         for (int h : heads) {
                             gangs.push_back({g, h, len, (int)mem.size(), (int)(j - i)});

@@ -172,7 +172,10 @@ void partial_attn_kernel(PartialArgs a) {
             // The workgroup's four rows hold one chunk of pages that their
             // sequences share.  Pages and the page count come from the first
             // wave's row, so every wave meets the same barriers; each wave
-            // masks its own tokens at its own length.
+            // masks its own tokens at its own length.  The planner keeps
+            // gang chunks below every member's length (whole shared pages),
+            // so no gang row holds an append position: the fused append
+            // happens only in the main launch.
             sh = ld_uniform(a.rows + row * 4 + 0);
             t0 = ld_uniform(a.rows + lead * 4 + 1);
             t1g = ld_uniform(a.rows + lead * 4 + 2);

@@ -501,7 +501,7 @@ def test_full_size_mixed_churn():
 
 
 def test_repeated_launches_bit_identical():
-    """Split-K arrival counters return to zero after every launch: repeated
+    """No device state carries over from one launch to the next: repeated
     launches, interleaved paged and top-K calls, give identical results."""
     c, L, caps = _gather_case(21, B=3, H=8, gqa=5, ng=4)
     c.alloc([0, 1, 2], caps, L)

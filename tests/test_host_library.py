@@ -54,6 +54,24 @@ def test_tiny_fixture_identity():
     assert nup.get_runs(ctx).tolist() == g["after_realloc_seq0"]["runs"]
 
 
+def test_grouping_ties_fixture_through_the_library():
+    """The tied-budget grouping fixture through the C ABI: same groups, slots,
+    page tables and trains, and the grouping stays fixed on a later Reserve."""
+    T = json.load(open(os.path.join(ROOT, "tests", "golden", "tiny_grouping_ties.json")))
+    ctx = _host_ctx(num_pages=T["num_pages"], max_pages=T["max_pages"])
+    caps = np.array(T["caps"])
+    goh = nup.kv_alloc_groups(ctx, [0, 1], caps, caps)
+    assert goh.tolist() == T["group_of_head"]
+    assert nup.get_groups(ctx)[1].tolist() == T["slot_of_head"]
+    assert nup.get_page_table(ctx).tolist() == T["page_table"]
+    assert nup.get_runs(ctx).tolist() == T["runs"]
+    R = T["after_free_seq0_realloc"]
+    nup.kv_free_seqs(ctx, [0])
+    nup.kv_alloc_groups(ctx, [0], np.array([R["caps_seq0"]]))
+    assert nup.get_groups(ctx)[0].tolist() == R["group_of_head"]
+    assert nup.get_page_table(ctx)[:, 0].tolist() == R["page_table_seq0"]
+
+
 def test_tiny_fixture_scrambled():
     sc = GOLD["scrambled"]
     ctx = _host_ctx(fl=sc["free_list_init"])

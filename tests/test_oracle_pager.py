@@ -11,6 +11,7 @@ from oracle import pager as pg
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_pager.json")))
 ALIAS = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_alias.json")))
+TIES = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_grouping_ties.json")))
 
 
 def _tiny(free_list_init=None):
@@ -37,6 +38,75 @@ def test_tiny_identity_fixture():
     assert p.page_table[:, 0].tolist() == g["after_realloc_seq0"]["page_table_seq0"]
     runs = pg.coalesce(p.page_table, p.n_pages, p.active)
     assert [list(r) for r in runs] == g["after_realloc_seq0"]["runs"]
+
+
+def test_grouping_ties_fixture():
+    """Tied budgets and capacities that differ between sequences: the
+    grouping key (sum over the first Reserve) and its tie-break (lower head
+    index) against hand-worked groups, pages, trains and rows."""
+    T = TIES
+    caps = np.array(T["caps"])
+    assert caps.sum(axis=0).tolist() == T["budget_sum"]
+    goh, soh, members = pg.group_heads(caps, T["num_groups"])
+    assert goh.tolist() == T["group_of_head"]
+    assert soh.tolist() == T["slot_of_head"]
+    p = pg.PagerSpec(T["num_kv_heads"], T["num_groups"], 2, T["num_pages"], T["max_pages"], 16)
+    assert p.alloc([0, 1], caps, caps) == pg.OK
+    assert p.group_of_head.tolist() == T["group_of_head"]
+    assert p.slot_of_head.tolist() == T["slot_of_head"]
+    assert p.n_pages.T.tolist() == T["pages_per_seq_group"]
+    assert p.page_table.tolist() == T["page_table"]
+    fl = p.free_list().tolist()
+    assert len(fl) == T["free_list_after_len"] and fl[:3] == T["free_list_after_front"]
+    runs = pg.coalesce(p.page_table, p.n_pages, p.active)
+    assert [list(r) for r in runs] == T["runs"]
+    assert p.physical_row(0, 2, 37) == T["physical_row_s0_h2_t37"]
+    assert p.physical_row(1, 3, 17) == T["physical_row_s1_h3_t17"]
+    # the grouping stays fixed through a later Reserve
+    R = T["after_free_seq0_realloc"]
+    assert p.free_seqs([0]) == pg.OK
+    assert p.free_list().tolist()[-len(R["free_list_after_free_tail"]):] == R["free_list_after_free_tail"]
+    assert p.alloc([0], np.array([R["caps_seq0"]])) == pg.OK
+    assert p.group_of_head.tolist() == R["group_of_head"]
+    assert p.page_table[:, 0].tolist() == R["page_table_seq0"]
+
+
+def _grouping_with(key_of, reverse_ties=False):
+    """A deliberately wrong grouping rule (planted here, on the CPU) that
+    differs from the oracle's only in its key or its tie-break."""
+    def rule(caps, ng):
+        caps = np.asarray(caps, dtype=np.int64)
+        hkv = caps.shape[1]
+        key = key_of(caps)
+        tie = (lambda h: -h) if reverse_ties else (lambda h: h)
+        order = sorted(range(hkv), key=lambda h: (int(key[h]), tie(h)))
+        goh = np.zeros(hkv, dtype=np.int32)
+        soh = np.zeros(hkv, dtype=np.int32)
+        for rank, h in enumerate(order):
+            goh[h], soh[h] = rank // (hkv // ng), rank % (hkv // ng)
+        return goh, soh
+    return rule
+
+
+@pytest.mark.parametrize("name,rule", [
+    ("reversed_tie_break", _grouping_with(lambda c: c.sum(axis=0), reverse_ties=True)),
+    ("max_capacity_key", _grouping_with(lambda c: c.max(axis=0))),
+    ("first_sequence_key", _grouping_with(lambda c: c[0])),
+    ("last_sequence_key", _grouping_with(lambda c: c[-1])),
+])
+def test_grouping_fixture_rejects_wrong_rules(name, rule, monkeypatch):
+    """Each plausible mistake in the grouping rule yields the groups the
+    fixture works out for it, and so fails the fixture: planted into the
+    oracle, it breaks test_grouping_ties_fixture."""
+    T = TIES
+    goh, soh = rule(np.array(T["caps"]), T["num_groups"])
+    assert goh.tolist() == T["wrong_rules"][name]["group_of_head"]
+    assert soh.tolist() == T["wrong_rules"][name]["slot_of_head"]
+    assert (goh.tolist(), soh.tolist()) != (T["group_of_head"], T["slot_of_head"])
+    planted = lambda caps, ng: (*rule(caps, ng), None)
+    monkeypatch.setattr(pg, "group_heads", planted)
+    with pytest.raises(AssertionError):
+        test_grouping_ties_fixture()
 
 
 def test_tiny_scrambled_fixture():
