@@ -78,25 +78,6 @@ class Case:
                              self.scale, tokens=tokens)
 
 
-def sub_oracle(spec, q_dev, kpool, vpool, seqs, scale, tokens=None):
-    """Oracle over a subset of sequences: only their pages are copied to the
-    host (torch indexing), renumbered, and handed to the oracle."""
-    seqs = list(seqs)
-    ng = spec.page_table.shape[0]
-    sub_pt = spec.page_table[:, seqs, :]
-    used = np.unique(sub_pt[sub_pt >= 0])
-    remap = np.full(spec.num_pages, -1, np.int64)
-    remap[used] = np.arange(len(used))
-    pt = np.where(sub_pt >= 0, remap[np.maximum(sub_pt, 0)], -1).astype(np.int32)
-    idx = torch.from_numpy(used.astype(np.int64)).to(kpool.device)
-    pk = u16(kpool.index_select(0, idx))
-    pv = u16(vpool.index_select(0, idx))
-    q = u16(q_dev)[seqs]
-    tok = None if tokens is None else tokens[seqs]
-    return oracle.decode(q, pk, pv, pt, spec.lengths[seqs], spec.group_of_head, spec.slot_of_head,
-                         scale, tokens=tok)
-
-
 def assert_attention_close(out, lse, ref_out, ref_lse, what=""):
     assert np.isfinite(out).all(), f"{what}: non-finite output"
     diff = np.abs(out - ref_out)

@@ -15,7 +15,7 @@ import non_uniform_paged_amd as nup
 import oracle
 import workloads as W
 from oracle import pager as pg
-from tests.gpu_common import (DEV, Case, assert_attention_close, sub_oracle, u16)
+from tests.gpu_common import (DEV, Case, assert_attention_close, u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -420,7 +420,7 @@ def test_gather_trains_bit_exact():
                                                              c.spec.active)
 
 
-# ---- full-size configurations, checked on sampled sequences -----------------
+# ---- full-size configurations, every output value checked ------------------
 
 def _full_case(w, num_workers=0, max_pages=None):
     max_pages = max_pages or int(math.ceil(w.caps.max() / 16))
@@ -429,8 +429,20 @@ def _full_case(w, num_workers=0, max_pages=None):
                 num_workers=num_workers)
 
 
+def _physical_rows(spec, idx):
+    """Physical row id of every entry of idx [B][H][K] (logical positions),
+    from the oracle pager's page table: page * G_h * P + slot * P + t % P."""
+    B, H, K = idx.shape
+    g = spec.group_of_head[np.arange(H)][None, :, None]
+    s = np.arange(B)[:, None, None]
+    page = spec.page_table[g, s, idx // 16].astype(np.int64)
+    return (page * spec.g_h + spec.slot_of_head[np.arange(H)][None, :, None]) * 16 + idx % 16
+
+
 @pytest.mark.parametrize("name", ["qwen3_4b", "qwen25_32b", "qwen25_32b_uniform50"])
-def test_full_size_sampled(name):
+def test_full_size_whole_output(name):
+    """The bench's launch configuration at full size; every sequence and
+    every query head is compared with the oracle."""
     if name == "qwen25_32b_uniform50":
         w = W.qwen25_32b(control="uniform50")
     else:
@@ -439,13 +451,13 @@ def test_full_size_sampled(name):
     c.alloc(list(range(w.batch)), w.caps, w.lengths)
     c.commit()
     out, lse = c.attend()
-    seqs = [0, 1, w.batch // 2, w.batch - 1]
-    ref, ref_lse = sub_oracle(c.spec, c.q, c.kpool, c.vpool, seqs, c.scale)
-    assert_attention_close(out[seqs], lse[seqs], ref, ref_lse, name)
-    assert np.isfinite(out).all()
+    ref, ref_lse = c.oracle()
+    assert_attention_close(out, lse, ref, ref_lse, name)
 
 
 def test_full_size_llama_topk():
+    """Llama-3-8B shape: index gather (every row and physical id) and the
+    attention over the staging, every output value against the oracle."""
     w = W.llama3_8b_topk()
     c = _full_case(w)
     c.alloc(list(range(w.batch)), w.caps, w.lengths)
@@ -460,19 +472,16 @@ def test_full_size_llama_topk():
     nup.attn_decode_topk(c.ctx, c.q, ks, vs, K, c.out, c.lse, c.scale, ws)
     torch.cuda.synchronize()
     assert nup.device_errors(c.ctx) == nup.NUP_OK
-    seqs = [0, 5]
-    gp = phys.cpu().numpy()
-    flat_k = c.kpool.view(-1, 128)
-    for s in seqs:
-        for h in range(8):
-            want = np.array([c.spec.physical_row(s, h, int(t)) for t in idx[s, h]], np.int64)
-            assert np.array_equal(gp[s, h], want)
-            rows = flat_k.index_select(0, torch.from_numpy(want).to(DEV))
-            assert torch.equal(rows.view(torch.int16), ks[s, h].view(torch.int16))
-    ref, ref_lse = sub_oracle(c.spec, c.q, c.kpool, c.vpool, seqs, c.scale, tokens=idx)
+    want = _physical_rows(c.spec, idx)
+    assert np.array_equal(phys.cpu().numpy(), want)
+    wt = torch.from_numpy(want.reshape(-1)).to(DEV)
+    for pool, st in ((c.kpool, ks), (c.vpool, vs)):
+        rows = pool.view(-1, 128).index_select(0, wt)
+        assert torch.equal(rows.view(torch.int16), st.reshape(-1, 128).view(torch.int16))
+    ref, ref_lse = c.oracle(tokens=idx)
     out = c.out.cpu().numpy().astype(np.float64)
     lse = c.lse.cpu().numpy().astype(np.float64)
-    assert_attention_close(out[seqs], lse[seqs], ref, ref_lse, "llama top-K")
+    assert_attention_close(out, lse, ref, ref_lse, "llama top-K")
 
 
 def test_full_size_mixed_churn():
@@ -492,10 +501,8 @@ def test_full_size_mixed_churn():
         c.free(freed)
         c.commit()
     out, lse = c.attend()
-    act = np.nonzero(c.spec.active)[0]
-    seqs = [int(act[0]), int(act[len(act) // 2]), int(act[-1])]
-    ref, ref_lse = sub_oracle(c.spec, c.q, c.kpool, c.vpool, seqs, c.scale)
-    assert_attention_close(out[seqs], lse[seqs], ref, ref_lse, "mixed churn")
+    ref, ref_lse = c.oracle()
+    assert_attention_close(out, lse, ref, ref_lse, "mixed churn")
     for s in freed:
         assert np.all(out[s] == 0) and np.all(np.isneginf(lse[s]))
 
@@ -582,7 +589,7 @@ def test_topk_paged_masks_bad_entries():
 
 def test_full_size_llama_topk_paged_equals_staged():
     """Llama-3-8B shape: the in-place top-K attention equals the oracle on
-    sampled sequences and the staged path (gather, then attend) bit for bit."""
+    every output value and the staged path (gather, then attend) bit for bit."""
     w = W.llama3_8b_topk()
     c = _full_case(w)
     c.alloc(list(range(w.batch)), w.caps, w.lengths)
@@ -602,9 +609,8 @@ def test_full_size_llama_topk_paged_equals_staged():
     torch.cuda.synchronize()
     assert nup.device_errors(c.ctx) == nup.NUP_OK
     assert np.array_equal(out_p, c.out.cpu().numpy()) and np.array_equal(lse_p, c.lse.cpu().numpy())
-    seqs = [1, 6]
-    ref, ref_lse = sub_oracle(c.spec, c.q, c.kpool, c.vpool, seqs, c.scale, tokens=idx_h)
-    assert_attention_close(out_p[seqs].astype(np.float64), lse_p[seqs].astype(np.float64), ref, ref_lse,
+    ref, ref_lse = c.oracle(tokens=idx_h)
+    assert_attention_close(out_p.astype(np.float64), lse_p.astype(np.float64), ref, ref_lse,
                            "llama top-K in place")
 
 
@@ -723,8 +729,11 @@ def test_select_topk_threshold_bin_beyond_lds():
 
 def test_full_size_llama_select_then_attend():
     """Llama-3-8B shape: select 2048 entries (1024 recent) per KV head from
-    122880, then attend in place.  Checked on sampled heads against the
-    oracle's own selection and attention."""
+    122880, then attend in place.  Every head's selection is checked against
+    the oracle's outside a margin around its threshold (fp32 and fp64 scores
+    may order near-ties differently, so several selections are correct);
+    every head's attention is then compared with the oracle's attention over
+    the GPU's own (valid) index list."""
     w = W.llama3_8b_topk()
     c = _full_case(w)
     c.alloc(list(range(w.batch)), w.caps, w.lengths)
@@ -740,36 +749,12 @@ def test_full_size_llama_select_then_attend():
     got = idx.cpu().numpy()
     out = c.out.cpu().numpy().astype(np.float64)
     lse = c.lse.cpu().numpy().astype(np.float64)
-    seqs = [2, 7]
-    # the oracle sees only the sampled sequences' pages (renumbered)
-    sub = c.spec.page_table[:, seqs, :]
-    used = np.unique(sub[sub >= 0])
-    remap = np.full(c.spec.num_pages, -1, np.int64)
-    remap[used] = np.arange(len(used))
-    spec2 = pg.PagerSpec(8, 1, len(seqs), len(used), c.spec.max_pages, 16)
-    spec2.page_table = np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(np.int32)
-    spec2.lengths = c.spec.lengths[seqs].copy()
-    spec2.caps = c.spec.caps[seqs].copy()
-    spec2.active[:] = True
-    spec2.n_pages = c.spec.n_pages[:, seqs].copy()
-    spec2.group_of_head, spec2.slot_of_head = c.spec.group_of_head, c.spec.slot_of_head
-    tsel = torch.from_numpy(used.astype(np.int64)).to(DEV)
-    pk = u16(c.kpool.index_select(0, tsel))
-    pv = u16(c.vpool.index_select(0, tsel))
-    q2 = u16(c.q)[seqs]
-    heads = [(0, 0), (0, 5), (1, 3)]
-    _check_selection(got[seqs], spec2, q2, pk, K, window, heads)
-    want = np.stack([np.stack([osel.select(osel.scores(q2, pk, spec2, i, h), K, window)
-                               for h in range(8)]) for i in range(len(seqs))])
-    same = [(i, h) for i in range(len(seqs)) for h in range(8) if np.array_equal(want[i, h], got[seqs][i, h])]
-    assert len(same) >= 12          # near-ties flip only occasionally
-    ref, ref_lse = oracle.decode(q2, pk, pv, spec2.page_table, spec2.lengths, spec2.group_of_head,
-                                 spec2.slot_of_head, c.scale, tokens=want)
-    gqa = 4
-    for (i, h) in same:
-        rows = slice(h * gqa, (h + 1) * gqa)
-        assert_attention_close(out[seqs[i], rows], lse[seqs[i], rows], ref[i, rows], ref_lse[i, rows],
-                               f"select+attend {seqs[i]},{h}")
+    q = u16(c.q)
+    pk = u16(c.kpool)
+    heads = [(s, h) for s in range(w.batch) for h in range(8)]
+    _check_selection(got, c.spec, q, pk, K, window, heads)
+    ref, ref_lse = c.oracle(tokens=got)
+    assert_attention_close(out, lse, ref, ref_lse, "select + attend, every head")
 
 
 def test_graph_replays_match_eager():
