@@ -327,6 +327,29 @@ nup_status attn_decode_nonuniform(nup_ctx *ctx, const void *q, float *out, float
                                   void *stream);
 
 /*
+ * attn_decode_nonuniform_noalloc -- attn_decode_nonuniform without a
+ * workspace argument and without any allocation, for callers that cannot
+ * allocate device memory around the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same kernels, same
+ * results, bit for bit.  The split-K partials go to a scratch array of
+ * NUP_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds per GPU for the
+ * life of the process; its address is looked up at nup_create.  The call
+ * makes no hipMalloc / hipFree and creates no events (nup_set_timing does
+ * not time it).
+ *   q, out, lse, scale, stream   as for attn_decode_nonuniform
+ * Every call on one GPU shares that GPU's scratch, from every context:
+ * calls that may overlap on one GPU (several streams, several threads)
+ * race and must be ordered by the caller.  Nothing in the scratch needs to
+ * start at zero; each launch writes what it reads.
+ * Errors: NUP_E_ARG if this context's partials exceed the scratch (the
+ * message gives both sizes; nothing is launched), NUP_E_STATE (no device
+ * buffers, no committed descriptor, or a current device other than the
+ * one the context was created on), NUP_E_HIP. */
+#define NUP_NOALLOC_SCRATCH_BYTES (32u << 20)
+nup_status attn_decode_nonuniform_noalloc(nup_ctx *ctx, const void *q, float *out, float *lse,
+                                          float scale, void *stream);
+
+/*
  * attn_decode_nonuniform_append -- kv_append followed by
  * attn_decode_nonuniform for the current layer, in two launches instead of
  * three (the decode step of KV-RM, abstract: the step's write and the

@@ -64,6 +64,7 @@ _sigs = {
     "nup_workspace_bytes": [_P, _I, _P],
     "attn_decode_nonuniform": [_P, _P, _P, _P, ctypes.c_float, _P, _S, _P],
     "attn_decode_nonuniform_append": [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _S, _P],
+    "attn_decode_nonuniform_noalloc": [_P, _P, _P, _P, ctypes.c_float, _P],
     "attn_decode_topk": [_P, _P, _P, _P, _I, _P, _P, ctypes.c_float, _P, _S, _P],
     "attn_decode_topk_paged": [_P, _P, _P, _I, _P, _P, ctypes.c_float, _P, _S, _P],
     "kv_select_topk": [_P, _P, _I, _I, _P, _P, _S, _P],
@@ -255,6 +256,16 @@ def attn_decode_nonuniform(ctx: Context, q, out, lse, scale: float, workspace, s
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib.attn_decode_nonuniform(ctx.handle, _ptr(q), _ptr(out), _ptr(lse), float(scale),
                                      _ptr(workspace), nbytes, _stream(stream))
+    return ctx.check(st) if raise_on_error else st
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # NUP_NOALLOC_SCRATCH_BYTES in nupaged.h
+
+
+def attn_decode_nonuniform_noalloc(ctx: Context, q, out, lse, scale: float, stream=None,
+                                   raise_on_error=True):
+    st = _lib.attn_decode_nonuniform_noalloc(ctx.handle, _ptr(q), _ptr(out), _ptr(lse), float(scale),
+                                             _stream(stream))
     return ctx.check(st) if raise_on_error else st
 
 

@@ -163,6 +163,7 @@ struct nup_ctx {
     Sizes sz{};
     std::string err;
     bool has_device = false;
+    int device = -1;              // the HIP device current at nup_create (device contexts)
 
     // pager shadow
     PageRing free_list;
@@ -869,6 +870,18 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
         const int nb = nup::partial_blocks_per_cu(c->D, c->gqa, nup::kModePaged);
         c->workers = prop.multiProcessorCount * std::max(1, nb) * nup::kWavesPerBlock;
     }
+    if (c->has_device) {
+        // set-up of the allocation-free entry point: look up this device's
+        // scratch address now, with the device current (a failure is kept
+        // and reported by that entry point)
+        if (hipGetDevice(&c->device) != hipSuccess) {
+            delete c;
+            fprintf(stderr, "nup_create: no HIP device for a device context\n");
+            return NUP_E_HIP;
+        }
+        void *scratch = nullptr;
+        (void)nup::scratch_buffer(c->device, &scratch);
+    }
     c->sz = compute_sizes(c->cfg, c->workers);
     c->free_list.init((size_t)c->num_pages);
     if (cfg->free_list_init) {
@@ -1431,7 +1444,7 @@ nup_status nup_workspace_bytes(const nup_ctx *c, int32_t K, size_t *bytes) {
 static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse, float scale, void *ws,
                               size_t ws_bytes, void *stream, int mode, const void *ks, const void *vs,
                               const int32_t *idx, int K, const void *k_new = nullptr,
-                              const void *v_new = nullptr) {
+                              const void *v_new = nullptr, bool may_time = true) {
     const bool topk = mode != nup::kModePaged;
     if (!c) return NUP_E_ARG;
     if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
@@ -1497,7 +1510,9 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
     a.head_row_start = topk ? nullptr : c->inbox_i32(c->off_hrs[c->layer]);
     hipError_t e;
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    const bool timed = c->timing && !capturing(st);   // a graph's launches are not timed
+    // a graph's launches are not timed, nor the allocation-free call's
+    // (creating events is an allocation)
+    const bool timed = may_time && c->timing && !capturing(st);
     if (timed) {
         if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess)
             return hip_fail(c, e, "hipEventCreate");
@@ -1549,6 +1564,29 @@ nup_status attn_decode_nonuniform(nup_ctx *c, const void *q, float *out, float *
                                   void *workspace, size_t ws_bytes, void *stream) {
     return attn_common(c, q, out, lse, scale, workspace, ws_bytes, stream, nup::kModePaged, nullptr,
                        nullptr, nullptr, 0);
+}
+
+static_assert(nup::kScratchBytes == (size_t)NUP_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
+
+nup_status attn_decode_nonuniform_noalloc(nup_ctx *c, const void *q, float *out, float *lse, float scale,
+                                          void *stream) {
+    if (!c) return NUP_E_ARG;
+    if (!c->has_device) return fail(c, NUP_E_STATE, "context has no device buffers");
+    size_t need = 0;
+    nup_workspace_bytes(c, 0, &need);
+    if (need > nup::kScratchBytes)
+        return fail(c, NUP_E_ARG,
+                    "split-K partials of this context need %zu bytes; the allocation-free call holds at most "
+                    "%zu (use attn_decode_nonuniform with a workspace)",
+                    need, nup::kScratchBytes);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != c->device)
+        return fail(c, NUP_E_STATE, "current device %d is not the context's device %d", dev, c->device);
+    void *ws = nullptr;
+    const hipError_t e = nup::scratch_buffer(c->device, &ws);
+    if (e != hipSuccess || !ws) return hip_fail(c, e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch lookup");
+    return attn_common(c, q, out, lse, scale, ws, nup::kScratchBytes, stream, nup::kModePaged, nullptr, nullptr,
+                       nullptr, 0, nullptr, nullptr, /*may_time=*/false);
 }
 
 nup_status attn_decode_nonuniform_append(nup_ctx *c, const void *k_new, const void *v_new, const void *q,

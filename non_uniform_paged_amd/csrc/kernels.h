@@ -162,6 +162,14 @@ struct GatherRunsArgs {
     int32_t layer_base;            // first head of this layer in head_of_gslot numbering
 };
 
+// Split-K scratch of the allocation-free entry point: a device array of
+// this many bytes in kernels.hip, one copy per GPU for the life of the
+// process.  scratch_buffer() gives the calling thread's current device's
+// copy; `device` must be that current device (checked).  The address is
+// looked up once per device and kept.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+hipError_t scratch_buffer(int device, void **ptr);
+
 bool supported_shape(int head_dim, int gqa);
 int partial_blocks_per_cu(int head_dim, int gqa, int mode);
 

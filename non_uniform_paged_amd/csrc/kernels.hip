@@ -15,6 +15,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace nup {
@@ -1635,6 +1637,37 @@ hipError_t launch_raw(void *fn, dim3 grid, dim3 block, void *arg, size_t arg_siz
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: room for the split-K partials
+// that the workspace argument holds otherwise.  In host code `scratch` names
+// a host-side stand-in, not device memory, so it is never passed to a kernel
+// or a copy: each device's address is looked up once, with that device
+// current, and that address is what the launches take.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void *scratch_addr[kMaxDevices];
+hipError_t scratch_status[kMaxDevices];
+}  // namespace
+
+hipError_t scratch_buffer(int device, void **ptr) {
+    *ptr = nullptr;
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device || device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(scratch_once[device], [device] {
+        void *p = nullptr;
+        scratch_status[device] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        scratch_addr[device] = scratch_status[device] == hipSuccess ? p : nullptr;
+    });
+    *ptr = scratch_addr[device];
+    return scratch_status[device];
+}
 
 bool supported_shape(int head_dim, int gqa) { return partial_ptr(head_dim, gqa, kModePaged) != nullptr; }
 

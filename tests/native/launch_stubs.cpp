@@ -20,5 +20,9 @@ hipError_t launch_apply_patches(int32_t *, const int32_t *, const int32_t *, int
     return hipSuccess;
 }
 hipError_t launch_probe_copy(const void *, void *, size_t, hipStream_t) { return hipSuccess; }
+hipError_t scratch_buffer(int, void **ptr) {
+    *ptr = nullptr;
+    return hipErrorNoDevice;
+}
 hipError_t launch_probe_read(const void *, size_t, uint32_t *, hipStream_t) { return hipSuccess; }
 }  // namespace nup
