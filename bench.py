@@ -49,6 +49,10 @@ def algorithmic_bytes(lengths, caps, B, Hq, Hkv, ng, D=128, page=16, gqa_rows=Tr
     return kv + q + out + pages * 4 + B * Hkv * 4
 
 
+# where split heads are merged (nupaged.h NUP_MERGE_*): set by --merge
+MERGE_MODE = 0
+
+
 class Setup:
     """Pools, context and step buffers for one workload on the GPU."""
 
@@ -81,7 +85,7 @@ class Setup:
         W.fill_normal_bf16_torch(self.vpool, "v")
         cfg = dict(num_kv_heads=H, num_q_heads=Hq, head_dim=D, num_groups=ng, max_batch=B,
                    num_pages=num_pages, max_pages=max_pages, num_workers=num_workers,
-                   plan_mode=plan_mode, uniform_splits=uniform_splits)
+                   plan_mode=plan_mode, uniform_splits=uniform_splits, merge_mode=MERGE_MODE)
         self.desc = torch.empty(nup.desc_bytes(**cfg), dtype=torch.uint8, device="cuda")
         self.ctx = nup.Context(**cfg, k_pool=self.kpool, v_pool=self.vpool, desc=self.desc,
                                free_list_init=free_list)
@@ -381,7 +385,7 @@ def _layer_group_sweep(flush):
     for G in (1, 2, 4, 8, 16, 32):
         ng = V // G
         cfg = dict(num_kv_heads=H, num_q_heads=w.num_q_heads, head_dim=D, num_groups=ng, max_batch=B,
-                   max_pages=max_pages, num_layers=NL)
+                   max_pages=max_pages, num_layers=NL, merge_mode=MERGE_MODE)
         # exact page need from a host-only pager, then pools of that size
         probe = nup.Context(**cfg, num_pages=B * ng * max_pages)
         nup.kv_alloc_groups(probe, np.arange(B), caps, lens)
@@ -435,7 +439,7 @@ def _graph_decode(flush, context, steps=10, warmup=2):
     caps, lens = w.caps.astype(np.int32), w.lengths.astype(np.int32)
     max_pages = int(math.ceil(caps.max() / 16))
     cfg = dict(num_kv_heads=H, num_q_heads=Hq, head_dim=D, num_groups=ng, max_batch=B,
-               max_pages=max_pages, num_layers=NL)
+               max_pages=max_pages, num_layers=NL, merge_mode=MERGE_MODE)
     probe = nup.Context(**cfg, num_pages=B * ng * max_pages)
     nup.kv_alloc_groups(probe, np.arange(B), caps, lens)
     pages = B * ng * max_pages - len(nup.get_free_list(probe))
@@ -846,7 +850,12 @@ def main():
     ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
                     help="only run the plain streaming copy kernel over BYTES (counter "
                          "calibration and achievable-bandwidth ceiling), then exit")
+    ap.add_argument("--merge", choices=["auto", "launch", "split"], default="auto",
+                    help="where split heads' partials are merged: the library's choice, a merge "
+                         "launch, or inside the split-K launch")
     args = ap.parse_args()
+    global MERGE_MODE
+    MERGE_MODE = {"auto": 0, "launch": 1, "split": 2}[args.merge]
     if args.gpus != 1:
         print(json.dumps({"error": "one GPU only: the path would shard by sequence or head group "
                                    "with no exchange between GPUs, but no multi-GPU run is provided",

@@ -90,6 +90,21 @@ enum {
     NUP_PLAN_SHARED = 2
 };
 
+/* Where the partial results of a head split over several work rows are
+ * merged (the log-sum-exp merge of split-K decoding).  Both give the same
+ * bits. */
+enum {
+    NUP_MERGE_AUTO = 0,     /* the library's choice: the merge launch, which
+                               measured faster on MI355X everywhere */
+    NUP_MERGE_LAUNCH = 1,   /* a merge launch after the split-K launch */
+    NUP_MERGE_IN_SPLIT = 2  /* inside the split-K launch: partials are written
+                               at device scope and counted per head, and the
+                               row of a head that counts last merges it; with
+                               the fused append it also advances the length.
+                               Not under NUP_PLAN_SHARED, which keeps the
+                               merge launch. */
+};
+
 typedef struct nup_ctx nup_ctx;
 
 typedef struct nup_config {
@@ -112,6 +127,7 @@ typedef struct nup_config {
                                (Tangram, Fig 11: group sizes beyond one layer's
                                heads).  Per-layer calls act on the layer chosen
                                by nup_set_layer(). */
+    int32_t merge_mode;     /* NUP_MERGE_AUTO, NUP_MERGE_LAUNCH or NUP_MERGE_IN_SPLIT */
     void *k_pool;           /* device, bf16 pool for K (caller-owned) */
     void *v_pool;           /* device, bf16 pool for V (caller-owned) */
     void *desc;             /* device, descriptor arena of nup_desc_bytes() bytes,

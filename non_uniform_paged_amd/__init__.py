@@ -24,6 +24,7 @@ NUP_OK, NUP_E_ARG, NUP_E_NOPAGES, NUP_E_CAPACITY, NUP_E_STATE, NUP_E_HIP, NUP_E_
 STATUS_NAMES = {0: "NUP_OK", 1: "NUP_E_ARG", 2: "NUP_E_NOPAGES", 3: "NUP_E_CAPACITY",
                 4: "NUP_E_STATE", 5: "NUP_E_HIP", 6: "NUP_E_INDEX"}
 PLAN_BALANCED, PLAN_UNIFORM, PLAN_SHARED = 0, 1, 2
+MERGE_AUTO, MERGE_LAUNCH, MERGE_IN_SPLIT = 0, 1, 2
 PAGE = 16
 
 
@@ -40,6 +41,7 @@ class NupConfig(ctypes.Structure):
                 ("num_pages", ctypes.c_int32), ("max_pages", ctypes.c_int32),
                 ("num_workers", ctypes.c_int32), ("plan_mode", ctypes.c_int32),
                 ("uniform_splits", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+                ("merge_mode", ctypes.c_int32),
                 ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("desc", ctypes.c_void_p), ("free_list_init", ctypes.c_void_p)]
 
@@ -132,10 +134,10 @@ class Context:
     def __init__(self, *, num_kv_heads, num_q_heads, head_dim, num_groups, max_batch,
                  num_pages, max_pages, k_pool=None, v_pool=None, desc=None,
                  free_list_init=None, num_workers=0, plan_mode=PLAN_BALANCED,
-                 uniform_splits=0, num_layers=1):
+                 uniform_splits=0, num_layers=1, merge_mode=0):
         cfg = NupConfig(num_kv_heads, num_q_heads, head_dim, PAGE, num_groups, max_batch,
                         num_pages, max_pages, num_workers, plan_mode, uniform_splits, num_layers,
-                        _ptr(k_pool), _ptr(v_pool), _ptr(desc), None)
+                        merge_mode, _ptr(k_pool), _ptr(v_pool), _ptr(desc), None)
         self._fl = None
         if free_list_init is not None:
             self._fl = _i32(free_list_init)
@@ -168,7 +170,8 @@ def desc_bytes(**cfg) -> int:
     c = NupConfig(cfg["num_kv_heads"], cfg["num_q_heads"], cfg["head_dim"], PAGE,
                   cfg["num_groups"], cfg["max_batch"], cfg["num_pages"], cfg["max_pages"],
                   cfg.get("num_workers", 0), cfg.get("plan_mode", 0),
-                  cfg.get("uniform_splits", 0), cfg.get("num_layers", 1), None, None, None, None)
+                  cfg.get("uniform_splits", 0), cfg.get("num_layers", 1), cfg.get("merge_mode", 0),
+                  None, None, None, None)
     n = ctypes.c_size_t()
     st = _lib.nup_desc_bytes(ctypes.byref(c), ctypes.byref(n))
     if st != NUP_OK:

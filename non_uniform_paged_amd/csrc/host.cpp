@@ -50,7 +50,8 @@ struct Sizes {
     size_t inbox;        // fixed + plan_max + runs_max + patches_max (aligned)
     size_t pt;           // page table bytes
     size_t err;          // error word (padded)
-    size_t total;        // inbox + pt + error word
+    size_t arrive;       // in-launch merge: arrival counts [NL][B*H], zero between launches
+    size_t total;        // inbox + pt + error word + arrival counts
     int max_rows;
     int max_workers;
 };
@@ -80,6 +81,8 @@ nup_status validate(const nup_config *c, std::string *why) {
     if (c->plan_mode != NUP_PLAN_BALANCED && c->plan_mode != NUP_PLAN_UNIFORM && c->plan_mode != NUP_PLAN_SHARED)
         return bad("unknown plan_mode");
     if (c->uniform_splits < 0) return bad("uniform_splits must be >= 0");
+    if (c->merge_mode != NUP_MERGE_AUTO && c->merge_mode != NUP_MERGE_LAUNCH && c->merge_mode != NUP_MERGE_IN_SPLIT)
+        return bad("unknown merge_mode");
     return NUP_OK;
 }
 
@@ -118,7 +121,8 @@ Sizes compute_sizes(const nup_config &c, int workers) {
     z.inbox = z.fixed + z.caps + z.plan_max + z.runs_max + z.patches_max;
     z.pt = align_up(4 * ng * B * (size_t)c.max_pages);
     z.err = kAlign;
-    z.total = z.inbox + z.pt + z.err;
+    z.arrive = align_up(4 * NL * B * H);
+    z.total = z.inbox + z.pt + z.err + z.arrive;
     return z;
 }
 
@@ -230,6 +234,7 @@ struct nup_ctx {
     size_t lbase() const { return (size_t)layer * H; }
     int32_t *d_pt() { return reinterpret_cast<int32_t *>(desc + sz.inbox); }
     int32_t *d_err() { return reinterpret_cast<int32_t *>(desc + sz.inbox + sz.pt); }
+    int32_t *d_arrive() { return reinterpret_cast<int32_t *>(desc + sz.inbox + sz.pt + sz.err); }
 };
 
 namespace {
@@ -1228,9 +1233,11 @@ nup_status nup_commit(nup_ctx *c, void *stream) {
         c->dev_run_pages = pre[nruns];
     }
     hipError_t e;
-    if (!c->committed) {  // the latched device error word starts clear
+    if (!c->committed) {  // the latched device error word and the arrival counts start clear
         e = nup::launch_fill(c->d_err(), 1, 0, st);
         if (e != hipSuccess) return hip_fail(c, e, "clear device error word");
+        e = nup::launch_fill(c->d_arrive(), c->NL * c->B * c->H, 0, st);
+        if (e != hipSuccess) return hip_fail(c, e, "clear arrival counts");
     }
     e = hipMemcpyAsync(c->desc, blob, used, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync (commit)");
@@ -1520,6 +1527,24 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
     }
     const bool gang = !topk && c->cfg.plan_mode == NUP_PLAN_SHARED && c->D == 128 &&
                       c->sz.max_workers % nup::kWavesPerBlock == 0;
+    // The merge inside the split-K launch, when asked for: it needs each
+    // head's rows contiguous in the table (the share-aware plan keeps its
+    // merge launch) and partial areas that 32-bit buffer offsets reach.  The
+    // default is the merge launch: on MI355X the device-scope round trips of
+    // the in-launch merge (store, count, reload) cost more than the launch.
+    const size_t o_bytes = align_up((size_t)rows_max * c->gqa * c->D * 4);
+    const size_t ml_bytes = (size_t)rows_max * c->gqa * 2 * 4;
+    const bool in_split = c->cfg.merge_mode == NUP_MERGE_IN_SPLIT && (topk || c->cfg.plan_mode != NUP_PLAN_SHARED) &&
+                          o_bytes < 0x80000000ull;
+    if (in_split) {
+        a.arrive = c->d_arrive() + (size_t)c->layer * c->B * c->H;
+        a.ws_o_bytes = (uint32_t)o_bytes;
+        a.ws_ml_bytes = (uint32_t)ml_bytes;
+        if (k_new) {
+            a.lengths_w = c->d_len() + c->lbase();
+            a.active = c->d_active();
+        }
+    }
     if (gang) {
         // the share-aware plan's gang launch first: workgroups of four
         // sharers of one chunk (the count is read on the device, so a
@@ -1539,6 +1564,7 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
         if ((e = hipEventRecord(e1, st)) != hipSuccess) return hip_fail(c, e, "hipEventRecord");
         c->tev.emplace_back(e0, e1);
     }
+    if (in_split) return NUP_OK;
     nup::MergeArgs m{};
     m.ws_o = wso;
     m.ws_ml = wsml;

@@ -58,6 +58,15 @@ struct PartialArgs {
     const int32_t *worker_skip; // [W]: 1 if the worker's first row runs in gang mode instead
     const int32_t *gang_rows;   // [4 * blocks]: the plan rows of workgroup b's four waves
     const int32_t *gang_blocks; // workgroups that have a chunk (device, read at run time)
+    // In-launch merge (arrive non-NULL; plans whose head rows are contiguous,
+    // i.e. not the share-aware plan): partials are written at device scope,
+    // every row of a split head then counts itself in arrive[head], and the
+    // row that counts last merges the head's partials itself.  With the fused
+    // append, the wave that finishes a head (that last row, or an unsplit
+    // head's only row) advances its length.  NULL: a merge launch follows.
+    int32_t *arrive;            // [Bmax*Hkv] this layer's counts; zero between launches
+    int32_t *lengths_w;         // fused append + in-launch merge: lengths to advance (as lengths)
+    uint32_t ws_o_bytes, ws_ml_bytes;   // sizes of the partial areas (buffer range checks)
 };
 
 struct MergeArgs {

@@ -106,7 +106,110 @@ __device__ __forceinline__ void write_final(const PartialArgs &a, size_t qh0, in
     if (!acc && a.lse && lane < GQA) a.lse[qh0 + lane] = -INFINITY;
 }
 
-template <int D, int GQA, int MODE>
+// ---------------------------------------------------------------------------
+// In-launch merge.  The rows of a split head run on waves of different CUs,
+// possibly on different XCDs, whose L2 caches are not kept coherent with each
+// other.  So the partials go through buffer instructions at device scope
+// (cache policy sc1): such a store has completed only once the whole device
+// can see it, and such a load is served coherently.  A row counts itself
+// with a device atomic only after its stores have completed, so the row that
+// counts last sees every partial of its head.  No wave ever waits for
+// another: the last arriver merges, the others just go on.
+// ---------------------------------------------------------------------------
+constexpr int kBufWord3 = 0x00020000;   // gfx9 buffer resource, word 3: raw 32-bit data
+constexpr int kScopeDevice = 16;        // buffer cache policy bits: sc1, device scope
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufWord3);
+}
+
+// Merge the partials of one head (rows hr0 .. hr0+nrows-1 of the workspace)
+// and write its GQA output rows.  Lane l takes float4 pieces l, l+64, ... of
+// the head's GQA*D outputs.  The (m, l) pairs of up to 64 / GQA rows come in
+// one load per lane and meet in the wave's LDS tile `pl`; the o pieces of
+// eight rows are in flight together.  The arithmetic and the row order are
+// those of merge_kernel, so both give the same bits.
+template <int D, int GQA>
+__device__ __forceinline__ void merge_head(const PartialArgs &a, int hr0, int nrows, size_t qh0, int lane,
+                                           float *pl) {
+    constexpr int NQ = D / 4;              // float4 pieces per query row
+    constexpr int NF = GQA * NQ;           // of the head
+    constexpr int KF = (NF + 63) / 64;     // per lane
+    constexpr int RC = 64 / GQA;           // rows whose (m, l) pairs one round of loads brings
+    constexpr int kBatch = 8;              // rows whose o pieces are in flight together
+    const __amdgpu_buffer_rsrc_t ro = raw_rsrc(a.ws_o, a.ws_o_bytes);
+    const __amdgpu_buffer_rsrc_t rml = raw_rsrc(a.ws_ml, a.ws_ml_bytes);
+    int rr[KF], cc[KF];
+    float M[KF], L[KF];
+    f32x4_t acc[KF];
+#pragma unroll
+    for (int k = 0; k < KF; ++k) {
+        const int f = lane + 64 * k;
+        rr[k] = f < NF ? f / NQ : 0;
+        cc[k] = f % NQ;
+        M[k] = -INFINITY;
+        L[k] = 0.f;
+        acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int c0 = 0; c0 < nrows; c0 += RC) {
+        const int nr = min(RC, nrows - c0);
+        // lane j < nr*GQA: (m, l) of query row j % GQA of row c0 + j / GQA
+        u32x2_t m2 = {0u, 0u};
+        if (lane < nr * GQA)
+            m2 = __builtin_amdgcn_raw_buffer_load_b64(
+                rml, (int)(((uint32_t)(hr0 + c0 + lane / GQA) * GQA + (uint32_t)(lane % GQA)) * 8u), 0, kScopeDevice);
+        for (int b = 0; b < nr; b += kBatch) {
+            u32x4_t ov[kBatch][KF];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const uint32_t slot = (uint32_t)(hr0 + c0 + min(b + u, nr - 1));
+#pragma unroll
+                for (int k = 0; k < KF; ++k)
+                    ov[u][k] = __builtin_amdgcn_raw_buffer_load_b128(
+                        ro, (int)(((slot * GQA + (uint32_t)rr[k]) * D + 4u * (uint32_t)cc[k]) * 4u), 0, kScopeDevice);
+            }
+            if (b == 0) {
+                if (lane < nr * GQA) {
+                    pl[2 * lane] = __uint_as_float(m2.x);
+                    pl[2 * lane + 1] = __uint_as_float(m2.y);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (b + u >= nr) break;
+#pragma unroll
+                for (int k = 0; k < KF; ++k) {
+                    const int j = (b + u) * GQA + rr[k];
+                    const float mi = pl[2 * j], li = pl[2 * j + 1];
+                    if (mi == -INFINITY) continue;   // no tokens
+                    const float Mn = fmaxf(M[k], mi);
+                    const float sc = exp2f(M[k] - Mn);    // 0 while M is -inf
+                    const float wg = exp2f(mi - Mn);
+                    L[k] = fmaf(L[k], sc, wg * li);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[k][e] = fmaf(acc[k][e], sc, wg * __uint_as_float(ov[u][k][e]));
+                    M[k] = Mn;
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();   // reads of pl done before the next round's writes
+    }
+#pragma unroll
+    for (int k = 0; k < KF; ++k) {
+        if (lane + 64 * k >= NF) continue;
+        const size_t qr = qh0 + rr[k];
+        const float inv = (M[k] != -INFINITY) ? 1.0f / L[k] : 0.f;
+        reinterpret_cast<float4 *>(a.out + qr * D)[cc[k]] =
+            make_float4(acc[k][0] * inv, acc[k][1] * inv, acc[k][2] * inv, acc[k][3] * inv);
+        if (a.lse && cc[k] == 0) a.lse[qr] = (M[k] != -INFINITY) ? (M[k] + log2f(L[k])) * kLn2 : -INFINITY;
+    }
+}
+
+template <int D, int GQA, int MODE, bool INM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NUP_WAVES_PER_EU, 8)))
 void partial_attn_kernel(PartialArgs a) {
     constexpr bool TOPK = MODE == kModeStaged || MODE == kModeIndexed;   // equal split of K entries per head
@@ -168,6 +271,7 @@ void partial_attn_kernel(PartialArgs a) {
     }
     for (int row = rb; row < re; ++row) {
         int sh, t0, t1;
+        int li = 0;        // paged and gang modes: the head's index into lengths
         int app_at = -1;   // fused append: the position this row stores and reads the new token at
         int t1g = 0;       // gang mode: the workgroup's planned end, shared by its four waves
         if (GANG) {
@@ -181,7 +285,8 @@ void partial_attn_kernel(PartialArgs a) {
             sh = ld_uniform(a.rows + row * 4 + 0);
             t0 = ld_uniform(a.rows + lead * 4 + 1);
             t1g = ld_uniform(a.rows + lead * 4 + 2);
-            t1 = min(t1g, ld_uniform(a.lengths + ld_uniform(a.rows + row * 4 + 3)));
+            li = ld_uniform(a.rows + row * 4 + 3);
+            t1 = min(t1g, ld_uniform(a.lengths + li));
         } else if (TOPK) {
             sh = row / a.topk_splits;
             t0 = (row - sh * a.topk_splits) * a.topk_chunk;
@@ -191,11 +296,12 @@ void partial_attn_kernel(PartialArgs a) {
             sh = ld_uniform(a.rows + row * 4 + 0);
             t0 = ld_uniform(a.rows + row * 4 + 1);
             // the row's fourth word is its head's index into lengths
-            t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + ld_uniform(a.rows + row * 4 + 3)));
+            li = ld_uniform(a.rows + row * 4 + 3);
+            t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + li));
         } else {
             sh = ld_uniform(a.rows + row * 4 + 0);
             t0 = ld_uniform(a.rows + row * 4 + 1);
-            const int li = ld_uniform(a.rows + row * 4 + 3);
+            li = ld_uniform(a.rows + row * 4 + 3);
             const int r2 = ld_uniform(a.rows + row * 4 + 2);
             const int L = ld_uniform(a.lengths + li);
             // a head below its budget takes the token at L: the one row whose
@@ -215,14 +321,46 @@ void partial_attn_kernel(PartialArgs a) {
             nrows = ld_uniform(a.head_row_start + sh + 1) - hr0;
         }
         const size_t qh0 = (size_t)s * a.hkv * GQA + (size_t)h * GQA;   // first query head
+        // In-launch merge with the fused append: the wave that finishes a
+        // head advances its length (every row of the head has read it).
+        auto finish_head = [&]() {
+            if (!INM || !a.k_new || lane != 0 || !ld_uniform(a.active + s)) return;
+            const int L = a.lengths_w[li];
+            if (L < ld_uniform(a.caps + li)) a.lengths_w[li] = L + 1;
+            else atomicOr(a.err, 2);
+        };
+        // A split head's row leaves (m, l) per query row: at device scope for
+        // the in-launch merge, which then counts the row in.
+        auto write_ml = [&](float m, float l) {
+            if (lane >= GQA) return;
+            if constexpr (INM) {
+                const u32x2_t v = {__float_as_uint(m), __float_as_uint(l)};
+                __builtin_amdgcn_raw_buffer_store_b64(v, raw_rsrc(a.ws_ml, a.ws_ml_bytes),
+                                                      (int)(((uint32_t)row * GQA + lane) * 8u), 0, kScopeDevice);
+            } else {
+                ml[lane * 2 + 0] = m;
+                ml[lane * 2 + 1] = l;
+            }
+        };
+        auto arrive_split = [&]() {
+            if constexpr (!INM) return;
+            __builtin_amdgcn_s_waitcnt(0);   // this row's partial is visible device-wide
+            int old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(a.arrive + sh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __builtin_amdgcn_readfirstlane(old);
+            if (old == nrows - 1) {
+                merge_head<D, GQA>(a, hr0, nrows, qh0, lane, pl);
+                if (lane == 0) __hip_atomic_store(a.arrive + sh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                finish_head();
+            }
+        };
         if (GANG ? t0 >= t1g : t0 >= t1) {
             if (nrows == 1) {
                 write_final<D, GQA>(a, qh0, lane, nullptr);
+                finish_head();
             } else {
-                if (lane < GQA) {
-                    ml[lane * 2 + 0] = -INFINITY;
-                    ml[lane * 2 + 1] = 0.f;
-                }
+                write_ml(-INFINITY, 0.f);
+                arrive_split();
             }
             continue;
         }
@@ -540,9 +678,10 @@ void partial_attn_kernel(PartialArgs a) {
         if (GANG && lt == 0.f) {   // no token of its own (not planned): nothing to add
             if (nrows == 1) {
                 write_final<D, GQA>(a, qh0, lane, nullptr);
-            } else if (lane < GQA) {
-                ml[lane * 2 + 0] = -INFINITY;
-                ml[lane * 2 + 1] = 0.f;
+                finish_head();
+            } else {
+                write_ml(-INFINITY, 0.f);
+                arrive_split();
             }
             continue;
         }
@@ -564,21 +703,36 @@ void partial_attn_kernel(PartialArgs a) {
             }
             if (a.lse && lane < GQA) a.lse[qh0 + lane] = al[8 + lane];
             __builtin_amdgcn_wave_barrier();
+            finish_head();
             continue;
         }
-        float *wo = a.ws_o + (size_t)row * GQA * D;
+        if constexpr (INM) {
+            const __amdgpu_buffer_rsrc_t ro = raw_rsrc(a.ws_o, a.ws_o_bytes);
 #pragma unroll
-        for (int r = 0; r < GQA; ++r) {
-            if (tg == r % NTG) {
-                float4 *dst = reinterpret_cast<float4 *>(wo + (size_t)r * D + 8 * ve);
-                dst[0] = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
-                dst[1] = make_float4(o[r][4], o[r][5], o[r][6], o[r][7]);
+            for (int r = 0; r < GQA; ++r) {
+                if (tg == r % NTG) {
+                    const int off = (int)((((uint32_t)row * GQA + r) * D + 8u * ve) * 4u);
+                    const u32x4_t v0 = {__float_as_uint(o[r][0]), __float_as_uint(o[r][1]),
+                                        __float_as_uint(o[r][2]), __float_as_uint(o[r][3])};
+                    const u32x4_t v1 = {__float_as_uint(o[r][4]), __float_as_uint(o[r][5]),
+                                        __float_as_uint(o[r][6]), __float_as_uint(o[r][7])};
+                    __builtin_amdgcn_raw_buffer_store_b128(v0, ro, off, 0, kScopeDevice);
+                    __builtin_amdgcn_raw_buffer_store_b128(v1, ro, off + 16, 0, kScopeDevice);
+                }
+            }
+        } else {
+            float *wo = a.ws_o + (size_t)row * GQA * D;
+#pragma unroll
+            for (int r = 0; r < GQA; ++r) {
+                if (tg == r % NTG) {
+                    float4 *dst = reinterpret_cast<float4 *>(wo + (size_t)r * D + 8 * ve);
+                    dst[0] = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
+                    dst[1] = make_float4(o[r][4], o[r][5], o[r][6], o[r][7]);
+                }
             }
         }
-        if (lane < GQA) {
-            ml[lane * 2 + 0] = m_run;
-            ml[lane * 2 + 1] = lt;
-        }
+        write_ml(m_run, lt);
+        arrive_split();
     }
 }
 
@@ -1585,35 +1739,37 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const uint4 *src, uint3
     if (x == 0x9e3779b9u) sink[0] = x;  // keeps the loads; practically never stores
 }
 
-template <int D, int GQA, int MODE>
-void *partial_fn() { return reinterpret_cast<void *>(&partial_attn_kernel<D, GQA, MODE>); }
+template <int D, int GQA, int MODE, bool INM>
+void *partial_fn() { return reinterpret_cast<void *>(&partial_attn_kernel<D, GQA, MODE, INM>); }
 
-template <int D, int MODE>
+template <int D, int MODE, bool INM>
 void *partial_fn_gqa(int gqa) {
     switch (gqa) {
-        case 1: return partial_fn<D, 1, MODE>();
-        case 2: return partial_fn<D, 2, MODE>();
-        case 4: return partial_fn<D, 4, MODE>();
-        case 5: return partial_fn<D, 5, MODE>();
-        case 8: return partial_fn<D, 8, MODE>();
+        case 1: return partial_fn<D, 1, MODE, INM>();
+        case 2: return partial_fn<D, 2, MODE, INM>();
+        case 4: return partial_fn<D, 4, MODE, INM>();
+        case 5: return partial_fn<D, 5, MODE, INM>();
+        case 8: return partial_fn<D, 8, MODE, INM>();
         default: return nullptr;
     }
 }
 
-template <int D>
+template <int D, bool INM>
 void *partial_fn_mode(int gqa, int mode) {
     switch (mode) {
-        case kModePaged: return partial_fn_gqa<D, kModePaged>(gqa);
-        case kModeStaged: return partial_fn_gqa<D, kModeStaged>(gqa);
-        case kModeIndexed: return partial_fn_gqa<D, kModeIndexed>(gqa);
-        case kModeGang: return D == 128 ? partial_fn_gqa<128, kModeGang>(gqa) : nullptr;
+        case kModePaged: return partial_fn_gqa<D, kModePaged, INM>(gqa);
+        case kModeStaged: return partial_fn_gqa<D, kModeStaged, INM>(gqa);
+        case kModeIndexed: return partial_fn_gqa<D, kModeIndexed, INM>(gqa);
+        case kModeGang: return D == 128 && !INM ? partial_fn_gqa<128, kModeGang, false>(gqa) : nullptr;
         default: return nullptr;
     }
 }
 
-void *partial_ptr(int d, int gqa, int mode) {
-    if (d == 64) return partial_fn_mode<64>(gqa, mode);
-    if (d == 128) return partial_fn_mode<128>(gqa, mode);
+// The split-K kernel for a head dim, GQA and mode; inm: the variant that
+// merges split heads itself.
+void *partial_ptr(int d, int gqa, int mode, bool inm = false) {
+    if (d == 64) return inm ? partial_fn_mode<64, true>(gqa, mode) : partial_fn_mode<64, false>(gqa, mode);
+    if (d == 128) return inm ? partial_fn_mode<128, true>(gqa, mode) : partial_fn_mode<128, false>(gqa, mode);
     return nullptr;
 }
 
@@ -1680,7 +1836,7 @@ int partial_blocks_per_cu(int head_dim, int gqa, int mode) {
 }
 
 hipError_t launch_partial(const PartialArgs &a, int head_dim, int gqa, int mode, hipStream_t st) {
-    void *fn = partial_ptr(head_dim, gqa, mode);
+    void *fn = partial_ptr(head_dim, gqa, mode, a.arrive != nullptr);
     if (!fn) return hipErrorInvalidValue;
     if (a.n_workers <= 0) return hipSuccess;
     // every pointer the chosen paths dereference must be set
@@ -1696,6 +1852,12 @@ hipError_t launch_partial(const PartialArgs &a, int head_dim, int gqa, int mode,
                                  !a.err))
         return hipErrorInvalidValue;
     if (a.k_new && (mode != kModePaged || !a.v_new || !a.caps)) return hipErrorInvalidValue;
+    // in-launch merge: counts, partial sizes, and for the fused append the
+    // lengths it advances; never with the gang launch (its heads' rows are
+    // not contiguous)
+    if (a.arrive && (mode == kModeGang || !a.ws_o_bytes || !a.ws_ml_bytes ||
+                     (a.k_new && (!a.lengths_w || !a.err || !a.active))))
+        return hipErrorInvalidValue;
     const unsigned blocks = (unsigned)((a.n_workers + kWavesPerBlock - 1) / kWavesPerBlock);
     PartialArgs copy = a;
     return launch_raw(fn, dim3(blocks), dim3(256), &copy, sizeof(copy), st);

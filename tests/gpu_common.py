@@ -23,7 +23,7 @@ def u16(t: torch.Tensor) -> np.ndarray:
 
 class Case:
     def __init__(self, *, H, Hq, D, ng, B, num_pages, max_pages, free_list_init=None,
-                 num_workers=0, plan_mode=0, uniform_splits=0, salt=0, num_layers=1):
+                 num_workers=0, plan_mode=0, uniform_splits=0, salt=0, num_layers=1, merge_mode=0):
         self.H, self.Hq, self.D, self.ng, self.B = H, Hq, D, ng, B
         self.NL, self.V = num_layers, num_layers * H      # the pager's (layer, head) pairs
         self.gh = self.V // ng
@@ -34,7 +34,8 @@ class Case:
         fill_normal_bf16_torch(self.vpool, "v", salt)
         cfg = dict(num_kv_heads=H, num_q_heads=Hq, head_dim=D, num_groups=ng, max_batch=B,
                    num_pages=num_pages, max_pages=max_pages, num_workers=num_workers,
-                   plan_mode=plan_mode, uniform_splits=uniform_splits, num_layers=num_layers)
+                   plan_mode=plan_mode, uniform_splits=uniform_splits, num_layers=num_layers,
+                   merge_mode=merge_mode)
         self.desc = torch.empty(nup.desc_bytes(**cfg), dtype=torch.uint8, device=DEV)
         self.ctx = nup.Context(**cfg, k_pool=self.kpool, v_pool=self.vpool, desc=self.desc,
                                free_list_init=free_list_init)

@@ -26,11 +26,11 @@ def _dev_bf16(name, shape, salt):
     return torch.from_numpy(W.normal_bf16(name, shape, salt).view(np.int16)).to(DEV).view(torch.bfloat16)
 
 
-def _twins(plan_mode, max_pages, num_pages, salt):
+def _twins(plan_mode, max_pages, num_pages, salt, merge_mode=0):
     perm = np.random.default_rng(salt).permutation(num_pages)
     kw = dict(H=H, Hq=H * GQA, D=D, ng=NG, B=B, num_pages=num_pages, max_pages=max_pages,
               free_list_init=perm, num_workers=37, plan_mode=plan_mode, uniform_splits=3, salt=salt,
-              num_layers=NL)
+              num_layers=NL, merge_mode=merge_mode)
     return Case(**kw), Case(**kw)
 
 
@@ -159,15 +159,18 @@ def test_graph_replay_across_commits(plan_mode, fused):
                                lses[l].cpu().numpy().astype(np.float64), ref, ref_lse, f"graph layer {l}")
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_graph_append_stops_at_budget(fused):
+@pytest.mark.parametrize("fused,merge_mode", [(False, nup.MERGE_LAUNCH), (True, nup.MERGE_LAUNCH),
+                                              (True, nup.MERGE_IN_SPLIT)])
+def test_graph_append_stops_at_budget(fused, merge_mode):
     """A replayed append cannot be refused on the host: the kernel drops the
     token of a head at its budget, latches NUP_E_CAPACITY, and
-    nup_note_appends mirrors exactly that."""
+    nup_note_appends mirrors exactly that (with the fused step, the length
+    advance is the merge launch's or, merged in the split-K launch, the
+    finishing wave's)."""
     rs = np.random.default_rng(75)
     max_pages = 12
     num_pages = B * NG * max_pages + 5
-    c, _ = _twins(nup.PLAN_BALANCED, max_pages, num_pages, 75)
+    c, _ = _twins(nup.PLAN_BALANCED, max_pages, num_pages, 75, merge_mode)
     L = rs.integers(20, 150, size=(2, V)).astype(np.int32)
     caps = (L + 5).astype(np.int32)
     caps[0, 1] = L[0, 1] + 1          # one append left
