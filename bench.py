@@ -204,21 +204,38 @@ def traffic_from_profiles(kernel_src_sha):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(setup, budget_s=12.0):
-    """The fp64 oracle on the first n sessions of the same workload, n chosen so
-    that the run takes roughly budget_s seconds of CPU time."""
-    import torch
-    import oracle
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        return ""
+
+
+def oracle_spec(setup):
+    """The oracle's own pager state for a Setup's first Reserve (the same
+    capacities, lengths and free list as the library's)."""
     from oracle import pager as pg
     w = setup.w
     spec = pg.PagerSpec(w.num_kv_heads, w.num_groups, w.batch, setup.num_pages,
                         setup.max_pages, 16, setup.free_list)
     assert spec.alloc(np.arange(w.batch), setup.caps, setup.lengths0) == pg.OK
-    # the threads the oracle actually runs on: the OpenMP setting of this host
-    # (the GPU hosts pin it to the CPU share of one GPU), else the affinity mask
+    return spec
+
+
+def oracle_timing(setup, spec, tokens=None, budget_all_s=1.5, budget_one_s=1.0, runs_all=5, runs_one=3):
+    """The fp64 oracle (test infrastructure, timed here as the CPU baseline)
+    on this host's cores and on one thread: the median of `runs` calls over
+    the first n sessions of the same inputs, n sized so that one call takes
+    about budget seconds.  Rates are the calls' algorithmic bytes per second
+    (K/V of every retained token or listed entry, q, out, page-table
+    entries, lengths)."""
+    import torch
+    import oracle
+    w = setup.w
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
 
-    def run(seqs):
+    def sample(seqs):
         sub = spec.page_table[:, seqs, :]
         used = np.unique(sub[sub >= 0])
         remap = np.full(spec.num_pages, -1, np.int64)
@@ -229,42 +246,48 @@ def cpu_baseline(setup, budget_s=12.0):
         pv = setup.vpool.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
         q = setup.q.view(torch.int16).cpu().numpy().view(np.uint16)[seqs]
         L = spec.lengths[seqs]
+        tok = None if tokens is None else np.ascontiguousarray(tokens[seqs])
+        if tokens is None:
+            nb = algorithmic_bytes(L, setup.caps[seqs], len(seqs), w.num_q_heads, w.num_kv_heads,
+                                   w.num_groups)
+        else:
+            n_ent = len(seqs) * w.num_kv_heads * tokens.shape[-1]
+            nb = n_ent * (2 * w.head_dim * 2 + 4) + len(seqs) * w.num_q_heads * w.head_dim * (2 + 4)
+        return (q, pk, pv, pt, L, tok), nb
+
+    def call(smp, nt):
+        q, pk, pv, pt, L, tok = smp
         t0 = time.perf_counter()
         oracle.decode(q, pk, pv, pt, L, spec.group_of_head, spec.slot_of_head, setup.scale,
-                      num_threads=threads)
-        dt = time.perf_counter() - t0
-        b = algorithmic_bytes(L, setup.caps[seqs], len(seqs), w.num_q_heads, w.num_kv_heads,
-                              w.num_groups)
-        return dt, b
+                      tokens=tok, num_threads=nt)
+        return time.perf_counter() - t0
 
-    dt, b = run([0])
-    n = int(max(1, min(w.batch, math.floor(budget_s / max(dt, 1e-3)))))
-    if n > 1:
-        dt, b = run(list(range(n)))
-    reps, total_t, total_b = 1, dt, b
-    while total_t < budget_s and reps < 50:   # whole batch is quick: repeat it
-        dt, b = run(list(range(n)))
-        reps, total_t, total_b = reps + 1, total_t + dt, total_b + b
-    # the same oracle on one thread, over a few sessions (about 3 s)
-    threads_all, threads = threads, 1
-    d1, b1 = run([0])
-    n1 = int(max(1, min(w.batch, math.floor(3.0 / max(d1, 1e-3)))))
-    if n1 > 1:
-        d1, b1 = run(list(range(n1)))
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
-    return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": threads_all,
-            "kind": "oracle",
-            "sample": f"first {n} of {w.batch} sessions of the same batch (all their KV heads), "
-                      f"one decode step of attention, x{reps} runs, {total_t:.1f} s wall; fp64 C "
-                      f"oracle with OpenMP",
-            "one_thread_value": round(b1 / d1 / 1e9, 4),
-            "one_thread_sample": f"first {n1} sessions, {d1:.1f} s",
-            "cpu_model": model}
+    def size(budget, nt):
+        smp, nb = sample([0])
+        dt = call(smp, nt)
+        n = int(max(1, min(w.batch, math.floor(budget / max(dt, 1e-4)))))
+        if n > 1:
+            smp, nb = sample(list(range(n)))
+        return (smp, nb), n
+
+    (smp, nb), n = size(budget_all_s, threads)
+    t_all = float(np.median([call(smp, threads) for _ in range(runs_all)]))
+    del smp
+    (smp1, nb1), n1 = size(budget_one_s, 1)
+    t_one = float(np.median([call(smp1, 1) for _ in range(runs_one)]))
+    del smp1
+    what = "listed entries" if tokens is not None else "retained tokens"
+    return {"value": round(nb / t_all / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.batch} sessions (all KV heads, their {what}), one decode step of "
+                      f"attention; median of {runs_all} calls of {t_all:.2f} s; fp64 C oracle with OpenMP",
+            "one_thread_value": round(nb1 / t_one / 1e9, 4),
+            "one_thread_sample": f"first {n1} sessions, median of {runs_one} calls of {t_one:.2f} s",
+            "cpu_model": _cpu_model()}
+
+
+def cpu_baseline(setup):
+    """The CPU baseline of the headline line: the oracle on the same batch."""
+    return oracle_timing(setup, oracle_spec(setup), budget_all_s=2.5, budget_one_s=1.5)
 
 
 def _timed(fn, iters, flush=None):
@@ -309,12 +332,17 @@ def _dma_trains(st, ks, vs, row_off, flush):
             "host_enqueue_ms": round(1e3 * float(np.mean(enq)), 3), "rows_equal_kernel": same}
 
 
-def _centroid_sweep(flush):
-    """For C clusters per KV head on the Llama-3-8B shape: keys are the
-    cluster centre plus noise (bf16), positions assigned to clusters at
-    random.  Reports the centroid selection's time and the share of the
-    exact selection's older entries it finds (the recent window, kept by
-    both, is left out)."""
+def _centroid_sweep(flush, T=8192):
+    """Centroid selection against the exact one on the Llama-3-8B shape, for
+    2048, 4096 and 8192 centroids per KV head.  The keys have a structure of
+    their own: every position belongs to one of T = 8192 true clusters and
+    its key is that cluster's centre plus noise (bf16).  The clustering
+    handed to the selection merges true clusters (ids equal mod C), and each
+    centroid is the mean of its members' keys, so fewer centroids describe
+    the keys more coarsely (KVDrive, Fig 18 / Fig 19: the number of
+    centroids trades selection time against accuracy).  Reports the
+    selection's time and the share of the exact selection's older entries
+    it finds (the recent window, kept by both, is left out)."""
     import torch
     import non_uniform_paged_amd as nup
     import workloads as W
@@ -330,24 +358,35 @@ def _centroid_sweep(flush):
     exact = torch.empty((B, H, K), dtype=torch.int32, device="cuda")
     approx = torch.empty_like(exact)
     ws_sel = torch.empty(nup.select_workspace_bytes(st.ctx), dtype=torch.uint8, device="cuda")
-    out = []
     g = torch.Generator(device="cuda")
+    g.manual_seed(W.torch_seed("k", T))
+    centre = torch.randn((B, H, T, D), generator=g, device="cuda")
+    # keys: the true centre of each position plus noise, written through the page table
+    true_of_pos, _, _ = W.nested_cluster_lists(w.lengths, T, T, salt=T)
+    kflat = st.kpool.view(-1, D)
+    keys_f = torch.empty((B, H, L, D), dtype=torch.float32, device="cuda")
+    for s in range(B):
+        for h in range(H):
+            rows = (pt[goh[h], s, t // 16].astype(np.int64) * gh + soh[h]) * 16 + t % 16
+            k = centre[s, h][torch.from_numpy(true_of_pos[s, h, :L].astype(np.int64)).cuda()]
+            k += 0.5 * torch.randn(k.shape, generator=g, device="cuda")
+            kb = k.to(torch.bfloat16)
+            kflat[torch.from_numpy(rows).cuda()] = kb
+            keys_f[s, h] = kb.float()
+    torch.cuda.synchronize()
+    nup.kv_select_topk(st.ctx, st.q, K, window, exact, ws_sel)
+    e = exact.cpu().numpy()[..., :K - window]
+    out = []
     for C in (2048, 4096, 8192):
-        start, pos = W.cluster_lists(w.lengths, C, salt=C)
-        g.manual_seed(W.torch_seed("k", C))
-        cent = torch.randn((B, H, C, D), generator=g, device="cuda").to(torch.bfloat16)
-        kflat = st.kpool.view(-1, D)
-        for s in range(B):
-            for h in range(H):
-                counts = np.diff(start[s, h])
-                assign = np.empty(L, np.int64)
-                assign[pos[s, h, :L]] = np.repeat(np.arange(C), counts)
-                rows = (pt[goh[h], s, t // 16].astype(np.int64) * gh + soh[h]) * 16 + t % 16
-                keys = cent[s, h][torch.from_numpy(assign).cuda()].float()
-                keys += 0.5 * torch.randn(keys.shape, generator=g, device="cuda")
-                kflat[torch.from_numpy(rows).cuda()] = keys.to(torch.bfloat16)
-        torch.cuda.synchronize()
-        nup.kv_select_topk(st.ctx, st.q, K, window, exact, ws_sel)
+        _, start, pos = W.nested_cluster_lists(w.lengths, T, C, salt=T)
+        # each centroid: the mean of its members' keys (bf16)
+        assign = torch.from_numpy((true_of_pos[..., :L] % C).astype(np.int64)).cuda()   # [B][H][L]
+        sums = torch.zeros((B, H, C, D), dtype=torch.float32, device="cuda")
+        sums.scatter_add_(2, assign[..., None].expand(B, H, L, D), keys_f)
+        cnt = torch.bincount((assign + C * torch.arange(B * H, device="cuda").view(B, H, 1)).view(-1),
+                             minlength=B * H * C).view(B, H, C, 1).clamp_(min=1)
+        cent = (sums / cnt).to(torch.bfloat16)
+        del sums, cnt, assign
         ws_c = torch.empty(nup.centroid_workspace_bytes(st.ctx, C), dtype=torch.uint8, device="cuda")
         cs, ps = torch.from_numpy(start).cuda(), torch.from_numpy(pos).cuda()
         sel = lambda: nup.kv_select_topk_centroids(st.ctx, st.q, cent, C, cs, ps, pos.shape[2], K, window,
@@ -355,12 +394,14 @@ def _centroid_sweep(flush):
         sel()
         torch.cuda.synchronize()
         ms = _timed(sel, 10, flush)
-        e, a = exact.cpu().numpy()[..., :K - window], approx.cpu().numpy()[..., :K - window]
+        a = approx.cpu().numpy()[..., :K - window]
         recall = np.mean([len(np.intersect1d(e[s, h], a[s, h])) / (K - window)
                           for s in range(B) for h in range(H)])
         assert nup.device_errors(st.ctx) == nup.NUP_OK
-        out.append({"centroids": C, "select_ms": round(ms, 4), "recall_of_exact_topk": round(float(recall), 4)})
+        out.append({"centroids": C, "true_clusters": T, "select_ms": round(ms, 4),
+                    "recall_of_exact_topk": round(float(recall), 4)})
         del cent, ws_c, cs, ps
+    del keys_f, centre
     st.free()
     return out
 
@@ -542,11 +583,16 @@ def measure_extras(args, only=None):
     import workloads as W
 
     res = {}
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(5)
-    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    flush_w = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+    flush_r = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
 
     def flush():
-        nup.probe_read(flush_buf, flush_buf.numel(), sink)
+        # a cached 1 GiB write, then a cached 1 GiB read of other memory
+        # (each four times the 256 MB MALL, and far beyond the L2s): what a
+        # timed call reads next comes from HBM, and the write's dirty lines
+        # have been written back during the read, before the timed call
+        flush_w.fill_(1)
+        flush_r.sum()
 
     def want(name):
         return only is None or only == name
@@ -573,11 +619,16 @@ def measure_extras(args, only=None):
         wkms, n = nup.kernel_time(st.ctx, reset=True)
         wkms /= max(n, 1)
         res["qwen3_4b"] = {"kv_bytes": kv_bytes(st.lengths0), "attn_call_ms": round(ms, 4),
+                           "tokens_per_s_per_step": round(w.batch / (ms * 1e-3), 1),
                            "partial_kernel_ms": round(kms, 4),
                            "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
+                           "frac": round(kb / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                            "warm_attn_call_ms": round(wms, 4), "warm_partial_kernel_ms": round(wkms, 4),
                            "warm_partial_kernel_GBs": round(kb / (wkms * 1e-3) / 1e9, 1),
-                           "note": "cold: 1 GiB read between launches; warm: back to back"}
+                           "note": "cold: 1 GiB read and written through the caches before each call; "
+                                   "warm: back to back"}
+        if not args.no_cpu_baseline:
+            res["qwen3_4b"]["cpu_baseline"] = oracle_timing(st, oracle_spec(st))
         st.free()
         del st
 
@@ -600,7 +651,12 @@ def measure_extras(args, only=None):
         rows = w.batch * 8 * K
         g_ms = _timed(gather, 20, flush)
         t_ms = _timed(topk, 20, flush)
+        nup.kernel_time(st.ctx, reset=True)
+        nup.set_timing(st.ctx, True)
         f_ms = _timed(fused, 20, flush)
+        nup.set_timing(st.ctx, False)
+        fk_ms, n = nup.kernel_time(st.ctx, reset=True)
+        fk_ms /= max(n, 1)
         both32 = _timed(lambda: [f() for _ in range(32) for f in (gather, topk)], 3) / 32
         fused32 = _timed(lambda: [fused() for _ in range(32)], 3) / 32
         # the same 32-layer stack captured in one HIP graph (launch cost amortised)
@@ -625,17 +681,24 @@ def measure_extras(args, only=None):
         k_bytes = int(w.lengths.sum()) * 256
         gb = rows * 512 * 2 + rows * 4
         tb = rows * 512 + w.batch * 32 * 128 * (2 + 4)
+        fb = rows * (512 + 4) + w.batch * 32 * 128 * 6
         res["llama3_8b_topk"] = {
             "gather_ms": round(g_ms, 4), "gather_GBs": round(gb / (g_ms * 1e-3) / 1e9, 1),
             "topk_attn_ms": round(t_ms, 4), "topk_attn_GBs": round(tb / (t_ms * 1e-3) / 1e9, 1),
             "gather_plus_attn_ms_32_back_to_back": round(both32, 4),
             "topk_in_place_ms": round(f_ms, 4),
-            "topk_in_place_GBs": round((rows * (512 + 4) + w.batch * 32 * 128 * 6) / (f_ms * 1e-3) / 1e9, 1),
+            "topk_in_place_GBs": round(fb / (f_ms * 1e-3) / 1e9, 1),
+            "tokens_per_s_per_step": round(w.batch / (f_ms * 1e-3), 1),
+            "topk_in_place_partial_kernel_ms": round(fk_ms, 4),
+            "frac": round(fb / (fk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "topk_in_place_ms_32_back_to_back": round(fused32, 4),
             "topk_in_place_ms_32_layer_graph": round(graph32, 4),
             "select_ms": round(s_ms, 4),
             "select_score_GBs": round(k_bytes / (s_ms * 1e-3) / 1e9, 1),
-            "note": "per call cold (1 GiB read before each); 32 back-to-back pairs for a 32-layer stack"}
+            "note": "per call cold (1 GiB read and written through the caches before each); 32 "
+                    "back-to-back pairs for a 32-layer stack; frac: the in-place call's split-K kernel"}
+        if not args.no_cpu_baseline:
+            res["llama3_8b_topk"]["cpu_baseline"] = oracle_timing(st, oracle_spec(st), tokens=idx.cpu().numpy())
         assert nup.device_errors(st.ctx) == nup.NUP_OK
         del graph
         st.free()
@@ -652,10 +715,12 @@ def measure_extras(args, only=None):
         steps_warm, steps = 20, 20
         pad_steps = steps_warm + steps + 4
         st = Setup(w, pad_steps, max_pages=int(math.ceil((131072 + 16 * math.ceil((pad_steps + 1) / 16)) / 16)))
+        # the oracle on the batch as first reserved (before any churn step)
+        cpu = None if args.no_cpu_baseline else oracle_timing(st, oracle_spec(st))
         drv = W.ChurnDriver(w.batch)
         active = np.ones(w.batch, bool)
         freed = np.zeros(0, np.int32)
-        host_us, trains, gpu_ms, step_kb = [], [], [], []
+        host_us, trains, gpu_ms, step_kb, n_active = [], [], [], [], []
         nup.kernel_time(st.ctx, reset=True)
         for it in range(steps_warm + steps):
             lib = 0.0   # host time inside the library: Reserve, Trim, frame commit
@@ -677,6 +742,7 @@ def measure_extras(args, only=None):
             if timed:
                 host_us.append(lib * 1e6)
                 trains.append(len(nup.get_runs(st.ctx)))
+                n_active.append(int(active.sum()))
                 nup.set_timing(st.ctx, True)
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -714,8 +780,11 @@ def measure_extras(args, only=None):
             "submit_share": round(float(np.mean(host_us)) / (float(np.mean(host_us)) + 1e3 * float(np.mean(gpu_ms))), 4),
             "trains_per_step_mean": round(float(np.mean(trains)), 1),
             "pages_in_use": int(st.num_pages - len(nup.get_free_list(st.ctx))),
+            "tokens_per_s_per_step": round(float(np.mean(n_active)) / (float(np.mean(gpu_ms)) * 1e-3), 1),
             "partial_kernel_ms": round(kms, 4),
             "partial_kernel_GBs": round(sum(step_kb) / (kms_total * 1e-3) / 1e9, 1),
+            "frac": round(sum(step_kb) / (kms_total * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "cpu_baseline": cpu,
             "gather_trains_ms": round(g_ms, 4),
             "gather_trains_GBs": round(2 * total * 512 / (g_ms * 1e-3) / 1e9, 1),
             "gather_trains_copy_engine": dma}
@@ -826,7 +895,7 @@ def measure_extras(args, only=None):
             del st
             torch.cuda.empty_cache()
         res["qwen25_32b_heads_per_group"] = sweep
-    del flush_buf
+    del flush_w, flush_r
     torch.cuda.empty_cache()
     return res
 

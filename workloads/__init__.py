@@ -293,6 +293,32 @@ def cluster_lists(lengths: np.ndarray, C: int, salt: int = 5):
     return start, pos
 
 
+def nested_cluster_lists(lengths: np.ndarray, T: int, C: int, salt: int = 6):
+    """Clustered positions for the centroid sweep.  Every position 0..L-1 of
+    (s, h) draws one of T true clusters uniformly at random (the same draws
+    whatever C is); the C clusters handed to the selection merge the true
+    clusters whose ids are equal mod C (C divides T), so fewer centroids
+    stand for coarser groups.  Returns true_of_pos int32 [B][H][P] (-1 past
+    L), cl_start int32 [B][H][C+1] and cl_pos int32 [B][H][P] (each list
+    ascending), P = max L."""
+    assert T % C == 0
+    g = rng("indices", salt)
+    b, h = lengths.shape
+    P = int(lengths.max())
+    true_of_pos = np.full((b, h, P), -1, np.int32)
+    start = np.zeros((b, h, C + 1), np.int32)
+    pos = np.full((b, h, P), -1, np.int32)
+    for s in range(b):
+        for j in range(h):
+            L = int(lengths[s, j])
+            t = g.integers(0, T, size=L)
+            true_of_pos[s, j, :L] = t
+            assign = t % C
+            pos[s, j, :L] = np.argsort(assign, kind="stable")
+            start[s, j, 1:] = np.cumsum(np.bincount(assign, minlength=C))
+    return true_of_pos, start, pos
+
+
 def lognormal_lengths(n: int, g: np.random.Generator, median: float = 2048.0,
                       sigma: float = 1.0, lo: int = 16, hi: int = 131072) -> np.ndarray:
     """Mixed request lengths: lognormal with the given median, clipped."""
