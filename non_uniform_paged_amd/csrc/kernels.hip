@@ -269,7 +269,27 @@ void partial_attn_kernel(PartialArgs a) {
         re = ld_uniform(a.worker_start + w + 1);
         if (a.worker_skip) rb += ld_uniform(a.worker_skip + w);
     }
+    // Paged mode: the worker's first 64 rows and what each row needs of its
+    // head (length, budget, row range, group, slot), one vector load per
+    // lane and level, so that a row after the first starts without scalar
+    // round trips (workers of short heads hold many rows, an inactive
+    // slot's heads one empty row each).
+    constexpr bool PAGED = MODE == kModePaged;
+    int4 vrow = make_int4(0, 0, 0, 0);
+    int vlen = 0, vcap = 0, vhr0 = 0, vhr1 = 0, vgrp = 0, vslot = 0;
+    if (PAGED && lane < re - rb) {
+        vrow = reinterpret_cast<const int4 *>(a.rows)[rb + lane];
+        vlen = a.lengths[vrow.w];
+        if (a.k_new) vcap = a.caps[vrow.w];
+        vhr0 = a.head_row_start[vrow.x];
+        vhr1 = a.head_row_start[vrow.x + 1];
+        const int hh = vrow.x % a.hkv;
+        vgrp = a.group_of_head[hh];
+        vslot = a.slot_of_head[hh];
+    }
     for (int row = rb; row < re; ++row) {
+        const int rj = row - rb;            // paged mode: the row's lane in the prefetched rows
+        const bool pre = PAGED && rj < 64;
         int sh, t0, t1;
         int li = 0;        // paged and gang modes: the head's index into lengths
         int app_at = -1;   // fused append: the position this row stores and reads the new token at
@@ -292,23 +312,33 @@ void partial_attn_kernel(PartialArgs a) {
             t0 = (row - sh * a.topk_splits) * a.topk_chunk;
             const int n = ld_uniform(a.active + sh / a.hkv) ? a.topk_k : 0;
             t1 = min(t0 + a.topk_chunk, n);
-        } else if (!a.k_new) {
-            sh = ld_uniform(a.rows + row * 4 + 0);
-            t0 = ld_uniform(a.rows + row * 4 + 1);
-            // the row's fourth word is its head's index into lengths
-            li = ld_uniform(a.rows + row * 4 + 3);
-            t1 = min(ld_uniform(a.rows + row * 4 + 2), ld_uniform(a.lengths + li));
         } else {
-            sh = ld_uniform(a.rows + row * 4 + 0);
-            t0 = ld_uniform(a.rows + row * 4 + 1);
-            li = ld_uniform(a.rows + row * 4 + 3);
-            const int r2 = ld_uniform(a.rows + row * 4 + 2);
-            const int L = ld_uniform(a.lengths + li);
-            // a head below its budget takes the token at L: the one row whose
-            // range holds L stores it; every row of the head reads up to L
-            const int app = L < ld_uniform(a.caps + li) ? 1 : 0;
-            t1 = min(r2, L + app);
-            if (app && t0 <= L && L < r2) app_at = L;
+            // the row's fourth word is its head's index into lengths
+            int r2, L;
+            if (pre) {
+                sh = __builtin_amdgcn_readlane(vrow.x, rj);
+                t0 = __builtin_amdgcn_readlane(vrow.y, rj);
+                r2 = __builtin_amdgcn_readlane(vrow.z, rj);
+                li = __builtin_amdgcn_readlane(vrow.w, rj);
+                L = __builtin_amdgcn_readlane(vlen, rj);
+            } else {
+                sh = ld_uniform(a.rows + row * 4 + 0);
+                t0 = ld_uniform(a.rows + row * 4 + 1);
+                r2 = ld_uniform(a.rows + row * 4 + 2);
+                li = ld_uniform(a.rows + row * 4 + 3);
+                L = ld_uniform(a.lengths + li);
+            }
+            if (!a.k_new) {
+                t1 = min(r2, L);
+            } else {
+                // a head below its budget takes the token at L: the one row
+                // whose range holds L stores it; every row of the head reads
+                // up to L
+                const int cp = pre ? __builtin_amdgcn_readlane(vcap, rj) : ld_uniform(a.caps + li);
+                const int app = L < cp ? 1 : 0;
+                t1 = min(r2, L + app);
+                if (app && t0 <= L && L < r2) app_at = L;
+            }
         }
         const int s = sh / a.hkv, h = sh - s * a.hkv;
         float *ml = a.ws_ml + (size_t)row * GQA * 2;
@@ -316,6 +346,9 @@ void partial_attn_kernel(PartialArgs a) {
         if (TOPK) {
             hr0 = sh * a.topk_splits;
             nrows = a.topk_splits;
+        } else if (pre) {
+            hr0 = __builtin_amdgcn_readlane(vhr0, rj);
+            nrows = __builtin_amdgcn_readlane(vhr1, rj) - hr0;
         } else {
             hr0 = ld_uniform(a.head_row_start + sh);
             nrows = ld_uniform(a.head_row_start + sh + 1) - hr0;
@@ -388,8 +421,10 @@ void partial_attn_kernel(PartialArgs a) {
         if (MODE != kModeStaged) {
             // gang mode reads the first wave's pages (the same physical pages)
             const int ps = GANG ? ld_uniform(a.rows + lead * 4 + 0) / a.hkv : s;
-            ptrow = a.page_table + ((size_t)ld_uniform(a.group_of_head + h) * a.bmax + ps) * (size_t)a.max_pages;
-            slot_off = (size_t)ld_uniform(a.slot_of_head + h) * kPage * D;
+            const int grp = pre ? __builtin_amdgcn_readlane(vgrp, rj) : ld_uniform(a.group_of_head + h);
+            const int slot = pre ? __builtin_amdgcn_readlane(vslot, rj) : ld_uniform(a.slot_of_head + h);
+            ptrow = a.page_table + ((size_t)grp * a.bmax + ps) * (size_t)a.max_pages;
+            slot_off = (size_t)slot * kPage * D;
         }
         const size_t head_base = MODE == kModeStaged ? (size_t)sh * a.topk_k * D : 0;
         const int p0 = t0 / kPage, p1 = ((GANG ? t1g : t1) - 1) / kPage;  // inclusive page range
