@@ -721,6 +721,7 @@ def measure_extras(args, only=None):
         active = np.ones(w.batch, bool)
         freed = np.zeros(0, np.int32)
         host_us, trains, gpu_ms, step_kb, n_active = [], [], [], [], []
+        all_kb = []   # every launch's K/V bytes, warm-up included (what a profiler averages over)
         nup.kernel_time(st.ctx, reset=True)
         for it in range(steps_warm + steps):
             lib = 0.0   # host time inside the library: Reserve, Trim, frame commit
@@ -748,12 +749,13 @@ def measure_extras(args, only=None):
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
             nup.attn_decode_nonuniform_append(st.ctx, st.k_new, st.v_new, st.q, st.out, st.lse, st.scale, st.ws)
+            # the call advanced the shadow lengths by the appended token,
+            # which the step also reads: these are the step's K/V bytes
+            all_kb.append(kv_bytes(nup.get_lengths(st.ctx)))
             if timed:
                 e1.record()
                 nup.set_timing(st.ctx, False)
-                # the call advanced the shadow lengths by the appended token,
-                # which the step also reads: these are the step's K/V bytes
-                step_kb.append(kv_bytes(nup.get_lengths(st.ctx)))
+                step_kb.append(all_kb[-1])
             torch.cuda.synchronize()
             if timed:
                 gpu_ms.append(e0.elapsed_time(e1))
@@ -775,6 +777,7 @@ def measure_extras(args, only=None):
             "active_slots": int(active.sum()),
             "kv_bytes_per_step_mean": int(np.mean(step_kb)),
             "kv_bytes_per_step_range": [int(min(step_kb)), int(max(step_kb))],
+            "kv_bytes_all_launches_mean": int(np.mean(all_kb)),
             "host_trim_reserve_commit_us_mean": round(float(np.mean(host_us)), 1),
             "gpu_append_attn_ms_mean": round(float(np.mean(gpu_ms)), 4),
             "submit_share": round(float(np.mean(host_us)) / (float(np.mean(host_us)) + 1e3 * float(np.mean(gpu_ms))), 4),

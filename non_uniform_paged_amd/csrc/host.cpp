@@ -882,7 +882,10 @@ nup_status nup_create(const nup_config *cfg, nup_ctx **out) {
             fprintf(stderr, "nup_create: the split-K kernel does not fit a compute unit\n");
             return NUP_E_HIP;
         }
-        c->workers = prop.multiProcessorCount * nup::kWavesPerBlock;
+        // The share-aware plan keeps two waves per SIMD: its gang launch
+        // wants the larger worker count (forked batch: 46 + 375 us against
+        // 77 + 382 us with one wave per SIMD).
+        c->workers = prop.multiProcessorCount * nup::kWavesPerBlock * (c->cfg.plan_mode == NUP_PLAN_SHARED ? 2 : 1);
     }
     if (c->has_device) {
         // set-up of the allocation-free entry point: look up this device's
