@@ -625,8 +625,8 @@ def measure_extras(args, only=None):
                            "frac": round(kb / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                            "warm_attn_call_ms": round(wms, 4), "warm_partial_kernel_ms": round(wkms, 4),
                            "warm_partial_kernel_GBs": round(kb / (wkms * 1e-3) / 1e9, 1),
-                           "note": "cold: 1 GiB read and written through the caches before each call; "
-                                   "warm: back to back"}
+                           "note": "cold: 1 GiB written, then 1 GiB read, through the caches before each "
+                                   "call; warm: back to back"}
         if not args.no_cpu_baseline:
             res["qwen3_4b"]["cpu_baseline"] = oracle_timing(st, oracle_spec(st))
         st.free()
@@ -695,7 +695,7 @@ def measure_extras(args, only=None):
             "topk_in_place_ms_32_layer_graph": round(graph32, 4),
             "select_ms": round(s_ms, 4),
             "select_score_GBs": round(k_bytes / (s_ms * 1e-3) / 1e9, 1),
-            "note": "per call cold (1 GiB read and written through the caches before each); 32 "
+            "note": "per call cold (1 GiB written, then 1 GiB read, through the caches before each); 32 "
                     "back-to-back pairs for a 32-layer stack; frac: the in-place call's split-K kernel"}
         if not args.no_cpu_baseline:
             res["llama3_8b_topk"]["cpu_baseline"] = oracle_timing(st, oracle_spec(st), tokens=idx.cpu().numpy())
@@ -855,8 +855,8 @@ def measure_extras(args, only=None):
             st.free()
             del st
             torch.cuda.empty_cache()
-        res["qwen25_32b_prefix"]["note"] = ("prefix 8192 tokens, 4 sources; cold (1 GiB read before each "
-                                            "step); logical bytes count every session's reads")
+        res["qwen25_32b_prefix"]["note"] = ("prefix 8192 tokens, 4 sources; cold (1 GiB written, then 1 GiB "
+                                            "read, before each step); logical bytes count every session's reads")
 
     # -- head groups across layers (Tangram, Fig 11): the 36-layer Qwen3-4B
     #    shape in one pager, heads per group 1 .. 32 (groups beyond 8 span layers)
@@ -1071,7 +1071,7 @@ def main():
                             "nup_commit + attn_decode_nonuniform_append (partial with the append, merge)")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": "partial_attn_kernel<128,5,0>"},
+                     "traffic": traffic, "kernel": "partial_attn_kernel<128,5,0,false>"},
         "cpu_baseline": cpu,
         "extra": extra,
     }
