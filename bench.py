@@ -141,39 +141,49 @@ class Setup:
         torch.cuda.empty_cache()
 
 
-def time_steps(setup, steps, warmup, append=True, fused=True, per_step=None):
-    """Returns (ms per step, partial-kernel ms per launch, mean lengths).
+def time_steps(setup, steps, warmup, append=True, fused=True, per_step=None, kernel=True):
+    """Returns (ms per step, mean lengths of those steps, split-K kernel ms per
+    launch, mean lengths of the kernel pass).  The step time comes from a pass
+    without the library's kernel events, since every timing event adds a few
+    microseconds of GPU time between the launches it brackets; the kernel
+    time (when `kernel`) from a second pass of as many steps with them.
     per_step: a list that receives each timed step's milliseconds (an event
     between consecutive steps on the launch stream)."""
     import torch
     import non_uniform_paged_amd as nup
+
+    def one_pass(per):
+        L_before = setup.lengths0 + setup.steps_done
+        torch.cuda.synchronize()
+        # per-step events only when asked: each one is a barrier between steps
+        n_ev = steps + 1 if per is not None else 2
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        ev[0].record()
+        for i in range(steps):
+            setup.step(append, fused)
+            if per is not None:
+                ev[i + 1].record()
+        if per is None:
+            ev[1].record()
+        torch.cuda.synchronize()
+        if per is not None:
+            per.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        L_after = setup.lengths0 + setup.steps_done
+        # lengths seen by the attention of each timed step: L_before+1 .. L_after
+        mean_L = (L_before + L_after + 1) / 2.0 if append else L_before
+        return ev[0].elapsed_time(ev[-1]) / steps, mean_L
+
     for _ in range(warmup):
         setup.step(append, fused)
-    torch.cuda.synchronize()
+    ms, mean_L = one_pass(per_step)
+    if not kernel:
+        return ms, mean_L, None, None
     nup.kernel_time(setup.ctx, reset=True)
     nup.set_timing(setup.ctx, True)
-    L_before = setup.lengths0 + setup.steps_done
-    torch.cuda.synchronize()
-    # per-step events only when asked: each one is a barrier between steps
-    n_ev = steps + 1 if per_step is not None else 2
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ev[0].record()
-    for i in range(steps):
-        setup.step(append, fused)
-        if per_step is not None:
-            ev[i + 1].record()
-    if per_step is None:
-        ev[1].record()
-    torch.cuda.synchronize()
+    _, kmean_L = one_pass(None)
     nup.set_timing(setup.ctx, False)
-    ms = ev[0].elapsed_time(ev[-1]) / steps
-    if per_step is not None:
-        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     kms, n = nup.kernel_time(setup.ctx, reset=True)
-    L_after = setup.lengths0 + setup.steps_done
-    # lengths seen by the attention of each timed step: L_before+1 .. L_after
-    mean_L = (L_before + L_after + (1 if append else 0)) / 2.0 if append else L_before
-    return ms, kms / max(n, 1), mean_L
+    return ms, mean_L, kms / max(n, 1), kmean_L
 
 
 def plan_straggler(ctx, lengths):
@@ -306,6 +316,21 @@ def _timed(fn, iters, flush=None):
         torch.cuda.synchronize()
         total += e0.elapsed_time(e1)
     return total / iters
+
+
+def _timed_call_and_kernel(ctx, fn, iters, flush=None):
+    """(ms per call, ms per split-K launch).  The call time comes from a pass
+    without the library's own kernel events, since every timing event adds
+    a few microseconds of GPU time between the launches it brackets; the
+    kernel time from a second pass with them."""
+    import non_uniform_paged_amd as nup
+    ms = _timed(fn, iters, flush)
+    nup.kernel_time(ctx, reset=True)
+    nup.set_timing(ctx, True)
+    _timed(fn, iters, flush)
+    nup.set_timing(ctx, False)
+    kms, n = nup.kernel_time(ctx, reset=True)
+    return ms, kms / max(n, 1)
 
 
 def _dma_trains(st, ks, vs, row_off, flush):
@@ -604,20 +629,11 @@ def measure_extras(args, only=None):
         for _ in range(3):
             st.step(append=False)
         torch.cuda.synchronize()
-        nup.kernel_time(st.ctx, reset=True)
-        nup.set_timing(st.ctx, True)
-        ms = _timed(lambda: st.step(append=False), 20, flush)
-        nup.set_timing(st.ctx, False)
-        kms, n = nup.kernel_time(st.ctx, reset=True)
-        kms /= max(n, 1)
+        ms, kms = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 20, flush)
         kb = algorithmic_bytes(st.lengths0, st.caps, w.batch, w.num_q_heads, w.num_kv_heads,
                                w.num_groups) - w.batch * w.num_q_heads * w.head_dim * 4
         # warm: back to back, part of the 512 MiB still in the 256 MB MALL
-        nup.set_timing(st.ctx, True)
-        wms = _timed(lambda: st.step(append=False), 20)
-        nup.set_timing(st.ctx, False)
-        wkms, n = nup.kernel_time(st.ctx, reset=True)
-        wkms /= max(n, 1)
+        wms, wkms = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 20)
         res["qwen3_4b"] = {"kv_bytes": kv_bytes(st.lengths0), "attn_call_ms": round(ms, 4),
                            "tokens_per_s_per_step": round(w.batch / (ms * 1e-3), 1),
                            "partial_kernel_ms": round(kms, 4),
@@ -651,12 +667,7 @@ def measure_extras(args, only=None):
         rows = w.batch * 8 * K
         g_ms = _timed(gather, 20, flush)
         t_ms = _timed(topk, 20, flush)
-        nup.kernel_time(st.ctx, reset=True)
-        nup.set_timing(st.ctx, True)
-        f_ms = _timed(fused, 20, flush)
-        nup.set_timing(st.ctx, False)
-        fk_ms, n = nup.kernel_time(st.ctx, reset=True)
-        fk_ms /= max(n, 1)
+        f_ms, fk_ms = _timed_call_and_kernel(st.ctx, fused, 20, flush)
         both32 = _timed(lambda: [f() for _ in range(32) for f in (gather, topk)], 3) / 32
         fused32 = _timed(lambda: [fused() for _ in range(32)], 3) / 32
         # the same 32-layer stack captured in one HIP graph (launch cost amortised)
@@ -712,8 +723,11 @@ def measure_extras(args, only=None):
     # -- mixed-length churn: 10% EOS per step, freed slots refilled next step
     if want("mixed_churn"):
         w = W.mixed_churn()
+        # 20 warm-up steps, 20 with the library's kernel events (kernel time
+        # and each step's bytes), then 20 without them (the step's GPU time:
+        # every timing event adds GPU time between the launches it brackets)
         steps_warm, steps = 20, 20
-        pad_steps = steps_warm + steps + 4
+        pad_steps = steps_warm + 2 * steps + 4
         st = Setup(w, pad_steps, max_pages=int(math.ceil((131072 + 16 * math.ceil((pad_steps + 1) / 16)) / 16)))
         # the oracle on the batch as first reserved (before any churn step)
         cpu = None if args.no_cpu_baseline else oracle_timing(st, oracle_spec(st))
@@ -722,8 +736,9 @@ def measure_extras(args, only=None):
         freed = np.zeros(0, np.int32)
         host_us, trains, gpu_ms, step_kb, n_active = [], [], [], [], []
         all_kb = []   # every launch's K/V bytes, warm-up included (what a profiler averages over)
+        timed_kb = []  # the step-timed steps' K/V bytes
         nup.kernel_time(st.ctx, reset=True)
-        for it in range(steps_warm + steps):
+        for it in range(steps_warm + 2 * steps):
             lib = 0.0   # host time inside the library: Reserve, Trim, frame commit
             if len(freed):
                 L = drv.refill_lengths(len(freed))
@@ -739,12 +754,15 @@ def measure_extras(args, only=None):
             lib += time.perf_counter() - t0
             active[eos] = False
             freed = eos
-            timed = it >= steps_warm
-            if timed:
+            kern = steps_warm <= it < steps_warm + steps       # kernel-timed steps
+            timed = it >= steps_warm + steps                    # step-timed steps
+            if kern or timed:
                 host_us.append(lib * 1e6)
                 trains.append(len(nup.get_runs(st.ctx)))
-                n_active.append(int(active.sum()))
+            if kern:
                 nup.set_timing(st.ctx, True)
+            if timed:
+                n_active.append(int(active.sum()))
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
@@ -752,10 +770,12 @@ def measure_extras(args, only=None):
             # the call advanced the shadow lengths by the appended token,
             # which the step also reads: these are the step's K/V bytes
             all_kb.append(kv_bytes(nup.get_lengths(st.ctx)))
-            if timed:
-                e1.record()
+            if kern:
                 nup.set_timing(st.ctx, False)
                 step_kb.append(all_kb[-1])
+            if timed:
+                e1.record()
+                timed_kb.append(all_kb[-1])
             torch.cuda.synchronize()
             if timed:
                 gpu_ms.append(e0.elapsed_time(e1))
@@ -780,6 +800,8 @@ def measure_extras(args, only=None):
             "kv_bytes_all_launches_mean": int(np.mean(all_kb)),
             "host_trim_reserve_commit_us_mean": round(float(np.mean(host_us)), 1),
             "gpu_append_attn_ms_mean": round(float(np.mean(gpu_ms)), 4),
+            "step_kv_bytes_mean": int(np.mean(timed_kb)),
+            "step_GBs": round(float(np.mean(timed_kb)) / (float(np.mean(gpu_ms)) * 1e-3) / 1e9, 1),
             "submit_share": round(float(np.mean(host_us)) / (float(np.mean(host_us)) + 1e3 * float(np.mean(gpu_ms))), 4),
             "trains_per_step_mean": round(float(np.mean(trains)), 1),
             "pages_in_use": int(st.num_pages - len(nup.get_free_list(st.ctx))),
@@ -833,12 +855,7 @@ def measure_extras(args, only=None):
             for _ in range(2):
                 st.step(append=False)
             torch.cuda.synchronize()
-            nup.kernel_time(st.ctx, reset=True)
-            nup.set_timing(st.ctx, True)
-            call_ms = _timed(lambda: st.step(append=False), 10, flush)
-            nup.set_timing(st.ctx, False)
-            kms, n = nup.kernel_time(st.ctx, reset=True)
-            kms /= max(n, 1)
+            call_ms, kms = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 10, flush)
             in_use = int(st.num_pages - len(nup.get_free_list(st.ctx)))
             entries = int(np.count_nonzero(nup.get_page_table(st.ctx) >= 0))
             kb = kv_bytes(st.lengths0)
@@ -967,12 +984,12 @@ def main():
     sha = hashlib.sha256(src).hexdigest()
 
     w = W.qwen25_32b()
-    headroom = 2 * args.warmup + 3 * args.steps + 8
+    headroom = 2 * args.warmup + 4 * args.steps + 8
     st = Setup(w, headroom, num_workers=args.workers)
-    ms, kms, mean_L = time_steps(st, args.steps, args.warmup, fused=not args.unfused)
+    ms, mean_L, kms, kmean_L = time_steps(st, args.steps, args.warmup, fused=not args.unfused)
     B, Hq, H, D, ng = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_groups
     step_bytes = algorithmic_bytes(mean_L, st.caps, B, Hq, H, ng) + B * H * D * 2 * 2 * 2
-    kern_bytes = algorithmic_bytes(mean_L, st.caps, B, Hq, H, ng) - B * Hq * D * 4
+    kern_bytes = algorithmic_bytes(kmean_L, st.caps, B, Hq, H, ng) - B * Hq * D * 4
     value = step_bytes / (ms * 1e-3) / 1e9
     achieved = kern_bytes / (kms * 1e-3) / 1e9
     extra = {"kv_bytes_per_step": kv_bytes(mean_L), "partial_kernel_ms": round(kms, 4),
@@ -985,11 +1002,11 @@ def main():
         # the distribution of single steps, in a pass of its own (an event
         # between steps keeps them from overlapping, so these run slower)
         step_ms = []
-        time_steps(st, args.steps, 0, fused=not args.unfused, per_step=step_ms)
+        time_steps(st, args.steps, 0, fused=not args.unfused, per_step=step_ms, kernel=False)
         extra["single_step_ms_median"] = round(float(np.median(step_ms)), 4)
         extra["single_step_ms_p90"] = round(float(np.percentile(step_ms, 90)), 4)
         # the other form of the same step on the same batch (a few tokens longer)
-        oms, _, oL = time_steps(st, args.steps, args.warmup, fused=args.unfused)
+        oms, oL, _, _ = time_steps(st, args.steps, args.warmup, fused=args.unfused, kernel=False)
         ob = algorithmic_bytes(oL, st.caps, B, Hq, H, ng) + B * H * D * 2 * 2 * 2
         tag = "fused" if args.unfused else "unfused_3_launches"
         extra[f"{tag}_ms_per_step"] = round(oms, 4)
@@ -1007,7 +1024,7 @@ def main():
         for tag, ctl in (("uniform50", "uniform50"), ("uniform_mean", "uniform_mean")):
             wc = W.qwen25_32b(control=ctl)
             sc = Setup(wc, headroom, num_workers=args.workers)
-            cms, ckms, cL = time_steps(sc, max(10, args.steps // 2), args.warmup)
+            _, _, ckms, cL = time_steps(sc, max(10, args.steps // 2), args.warmup)
             cb = algorithmic_bytes(cL, sc.caps, B, Hq, H, ng) - B * Hq * D * 4
             extra[f"control_{tag}_kernel_GBs"] = round(cb / (ckms * 1e-3) / 1e9, 1)
             extra[f"control_{tag}_kernel_ms"] = round(ckms, 4)
@@ -1017,7 +1034,7 @@ def main():
         # the uniform split Tangram measures against (every head cut into 8
         # chunks, one per worker) on the same non-uniform batch
         su = Setup(w, headroom, plan_mode=nup.PLAN_UNIFORM, uniform_splits=8)
-        ums, ukms, uL = time_steps(su, max(10, args.steps // 2), args.warmup)
+        _, _, ukms, uL = time_steps(su, max(10, args.steps // 2), args.warmup)
         ub = algorithmic_bytes(uL, su.caps, B, Hq, H, ng) - B * Hq * D * 4
         extra["control_uniform_split_kernel_ms"] = round(ukms, 4)
         extra["control_uniform_split_kernel_GBs"] = round(ub / (ukms * 1e-3) / 1e9, 1)

@@ -455,13 +455,32 @@ void partial_attn_kernel(PartialArgs a) {
             const int L = ld_uniform(a.lengths + s * a.lstride + h);
             const int slot = ld_uniform(a.slot_of_head + h);
             bool bad = false;
-            for (int e = t0 + lane; e < t1; e += 64) {
-                const int t = il[e];
-                const bool in_range = t >= 0 && t < L;
-                int rid = -1;
-                if (in_range) rid = (ptrow[t / kPage] * a.gh + slot) * kPage + t % kPage;
-                bad |= !in_range || (e > 0 && il[e - 1] >= t);
-                rl[e - t0] = rid;
+            // Four entries per lane at a time, each level's loads issued
+            // together: one round trip for the indices (and each entry's
+            // predecessor, for the order check), one for the page-table
+            // entries, instead of three dependent loads per entry.
+            constexpr int RB = 4;
+            for (int e0 = t0 + lane; e0 < t1; e0 += 64 * RB) {
+                int t[RB], tp[RB], pg[RB];
+#pragma unroll
+                for (int k = 0; k < RB; ++k) {
+                    const int e = e0 + 64 * k;
+                    t[k] = e < t1 ? il[e] : 0;
+                    tp[k] = (e < t1 && e > 0) ? il[e - 1] : -1;
+                }
+#pragma unroll
+                for (int k = 0; k < RB; ++k) {
+                    const bool in_range = e0 + 64 * k < t1 && t[k] >= 0 && t[k] < L;
+                    pg[k] = in_range ? ptrow[t[k] / kPage] : 0;
+                }
+#pragma unroll
+                for (int k = 0; k < RB; ++k) {
+                    const int e = e0 + 64 * k;
+                    if (e >= t1) continue;
+                    const bool in_range = t[k] >= 0 && t[k] < L;
+                    bad |= !in_range || (e > 0 && tp[k] >= t[k]);
+                    rl[e - t0] = in_range ? (pg[k] * a.gh + slot) * kPage + t[k] % kPage : -1;
+                }
             }
             if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(a.err, 1);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
