@@ -1437,7 +1437,9 @@ nup_status kv_gather_trains_dma(nup_ctx *c, void *k_out, void *v_out, const int6
 static void topk_split(const nup_ctx *c, int K, int *splits, int *chunk) {
     const int heads = c->B * c->H;
     const int pages = (K + nup::kPage - 1) / nup::kPage;
-    const int target = std::max(1, c->workers);
+    // one per SIMD: the context's worker count, which the share-aware plan doubles
+    const int target = std::max(1, c->cfg.plan_mode == NUP_PLAN_SHARED && c->cfg.num_workers <= 0 ? c->workers / 2
+                                                                                                  : c->workers);
     int S = std::max(1, (target + heads - 1) / heads);
     S = std::max(S, (K + nup::kMaxTopkChunk - 1) / nup::kMaxTopkChunk);  // chunk <= LDS row-id room
     S = std::min(S, pages);
