@@ -696,12 +696,23 @@ void partial_attn_kernel(PartialArgs a) {
         }
 #else
         // Ring of kDepth page buffers: pages p+1 .. p+kDepth-1 are in flight
-        // while page p is computed.
+        // while page p is computed.  As for the two-buffer ring, the steady
+        // state issues every prefetch unconditionally; the last pages go
+        // through a guarded tail.
         uint4 kb[kDepth][TPL], vb[kDepth][TPL];
 #pragma unroll
         for (int k = 0; k + 1 < kDepth; ++k)
             if (p0 + k <= p1) load(p0 + k, page_base(p0 + k), kb[k], vb[k]);
-        for (int pb = p0; pb <= p1; pb += kDepth) {
+        int pb = p0;
+        for (; pb + 2 * kDepth - 2 <= p1; pb += kDepth) {
+#pragma unroll
+            for (int k = 0; k < kDepth; ++k) {
+                const int pf = pb + k + kDepth - 1;
+                load(pf, page_base(pf), kb[(k + kDepth - 1) % kDepth], vb[(k + kDepth - 1) % kDepth]);
+                compute(pb + k, kb[k], vb[k]);
+            }
+        }
+        for (; pb <= p1; pb += kDepth) {
 #pragma unroll
             for (int k = 0; k < kDepth; ++k) {
                 const int p = pb + k;
