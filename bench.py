@@ -720,7 +720,8 @@ def measure_extras(args, only=None):
         del st, ks, vs, ws, sel_idx, ws_sel
 
     # -- centroid selection (KVDrive, Fig 18 / Fig 19): time and recall of the
-    #    exact top-K on keys drawn around 2048, 4096 or 8192 cluster centres
+    #    exact top-K with 2048, 4096 or 8192 centroids over keys drawn around
+    #    8192 true cluster centres
     if want("llama3_8b_centroids"):
         res["llama3_8b_centroids"] = _centroid_sweep(flush)
 
