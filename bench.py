@@ -300,11 +300,12 @@ def cpu_baseline(setup):
     return oracle_timing(setup, oracle_spec(setup), budget_all_s=2.5, budget_one_s=1.5)
 
 
-def _timed(fn, iters, flush=None):
-    """Average ms of fn() over iters calls, each preceded (outside the timed
-    window) by flush() when given; events on the current stream."""
+def _timed_stats(fn, iters, flush=None):
+    """(mean, median, p90) ms of fn() over iters calls, each preceded
+    (outside the timed window) by flush() when given; events on the current
+    stream."""
     import torch
-    total = 0.0
+    times = []
     for _ in range(iters):
         if flush is not None:
             flush()
@@ -314,23 +315,33 @@ def _timed(fn, iters, flush=None):
         fn()
         e1.record()
         torch.cuda.synchronize()
-        total += e0.elapsed_time(e1)
-    return total / iters
+        times.append(e0.elapsed_time(e1))
+    return float(np.mean(times)), float(np.median(times)), float(np.percentile(times, 90))
+
+
+def _timed(fn, iters, flush=None):
+    """Average ms of fn() over iters calls (see _timed_stats)."""
+    return _timed_stats(fn, iters, flush)[0]
+
+
+def _med_p90(stats, key):
+    """{key_median, key_p90} from a _timed_stats triple, rounded."""
+    return {key + "_median": round(stats[1], 4), key + "_p90": round(stats[2], 4)}
 
 
 def _timed_call_and_kernel(ctx, fn, iters, flush=None):
-    """(ms per call, ms per split-K launch).  The call time comes from a pass
-    without the library's own kernel events, since every timing event adds
-    a few microseconds of GPU time between the launches it brackets; the
-    kernel time from a second pass with them."""
+    """(ms per call, ms per split-K launch, the call's _timed_stats).  The
+    call time comes from a pass without the library's own kernel events,
+    since every timing event adds a few microseconds of GPU time between the
+    launches it brackets; the kernel time from a second pass with them."""
     import non_uniform_paged_amd as nup
-    ms = _timed(fn, iters, flush)
+    stats = _timed_stats(fn, iters, flush)
     nup.kernel_time(ctx, reset=True)
     nup.set_timing(ctx, True)
     _timed(fn, iters, flush)
     nup.set_timing(ctx, False)
     kms, n = nup.kernel_time(ctx, reset=True)
-    return ms, kms / max(n, 1)
+    return stats[0], kms / max(n, 1), stats
 
 
 def _dma_trains(st, ks, vs, row_off, flush):
@@ -609,7 +620,9 @@ def measure_extras(args, only=None):
 
     res = {}
     flush_w = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
-    flush_r = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    # float32, so that the sum is one reduction over the buffer itself (an
+    # int32 sum would first copy it out as int64)
+    flush_r = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 
     def flush():
         # a cached 1 GiB write, then a cached 1 GiB read of other memory
@@ -629,13 +642,15 @@ def measure_extras(args, only=None):
         for _ in range(3):
             st.step(append=False)
         torch.cuda.synchronize()
-        ms, kms = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 20, flush)
+        # cold calls: 100 timed after the warm-up above
+        ms, kms, cst = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 100, flush)
         kb = algorithmic_bytes(st.lengths0, st.caps, w.batch, w.num_q_heads, w.num_kv_heads,
                                w.num_groups) - w.batch * w.num_q_heads * w.head_dim * 4
         # warm: back to back, part of the 512 MiB still in the 256 MB MALL
-        wms, wkms = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 20)
+        wms, wkms, _ = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 100)
         res["qwen3_4b"] = {"kv_bytes": kv_bytes(st.lengths0), "attn_call_ms": round(ms, 4),
-                           "tokens_per_s_per_step": round(w.batch / (ms * 1e-3), 1),
+                           **_med_p90(cst, "attn_call_ms"),
+                           "tokens_per_s_per_step": round(w.batch / (cst[1] * 1e-3), 1),   # median call
                            "partial_kernel_ms": round(kms, 4),
                            "partial_kernel_GBs": round(kb / (kms * 1e-3) / 1e9, 1),
                            "frac": round(kb / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -667,9 +682,11 @@ def measure_extras(args, only=None):
             topk()
             fused()
         rows = w.batch * 8 * K
-        g_ms = _timed(gather, 20, flush)
-        t_ms = _timed(topk, 20, flush)
-        f_ms, fk_ms = _timed_call_and_kernel(st.ctx, fused, 20, flush)
+        # cold calls: 100 timed of each
+        gst = _timed_stats(gather, 100, flush)
+        tst = _timed_stats(topk, 100, flush)
+        g_ms, t_ms = gst[0], tst[0]
+        f_ms, fk_ms, fst = _timed_call_and_kernel(st.ctx, fused, 100, flush)
         both32 = _timed(lambda: [f() for _ in range(32) for f in (gather, topk)], 3) / 32
         fused32 = _timed(lambda: [fused() for _ in range(32)], 3) / 32
         # the same 32-layer stack captured in one HIP graph (launch cost amortised)
@@ -696,12 +713,14 @@ def measure_extras(args, only=None):
         tb = rows * 512 + w.batch * 32 * 128 * (2 + 4)
         fb = rows * (512 + 4) + w.batch * 32 * 128 * 6
         res["llama3_8b_topk"] = {
-            "gather_ms": round(g_ms, 4), "gather_GBs": round(gb / (g_ms * 1e-3) / 1e9, 1),
-            "topk_attn_ms": round(t_ms, 4), "topk_attn_GBs": round(tb / (t_ms * 1e-3) / 1e9, 1),
+            "gather_ms": round(g_ms, 4), **_med_p90(gst, "gather_ms"),
+            "gather_GBs": round(gb / (g_ms * 1e-3) / 1e9, 1),
+            "topk_attn_ms": round(t_ms, 4), **_med_p90(tst, "topk_attn_ms"),
+            "topk_attn_GBs": round(tb / (t_ms * 1e-3) / 1e9, 1),
             "gather_plus_attn_ms_32_back_to_back": round(both32, 4),
-            "topk_in_place_ms": round(f_ms, 4),
+            "topk_in_place_ms": round(f_ms, 4), **_med_p90(fst, "topk_in_place_ms"),
             "topk_in_place_GBs": round(fb / (f_ms * 1e-3) / 1e9, 1),
-            "tokens_per_s_per_step": round(w.batch / (f_ms * 1e-3), 1),
+            "tokens_per_s_per_step": round(w.batch / (fst[1] * 1e-3), 1),   # over the median call
             "topk_in_place_partial_kernel_ms": round(fk_ms, 4),
             "frac": round(fb / (fk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "topk_in_place_ms_32_back_to_back": round(fused32, 4),
@@ -861,7 +880,7 @@ def measure_extras(args, only=None):
             for _ in range(2):
                 st.step(append=False)
             torch.cuda.synchronize()
-            call_ms, kms = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 10, flush)
+            call_ms, kms, _ = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 10, flush)
             in_use = int(st.num_pages - len(nup.get_free_list(st.ctx)))
             entries = int(np.count_nonzero(nup.get_page_table(st.ctx) >= 0))
             kb = kv_bytes(st.lengths0)
