@@ -635,7 +635,7 @@ def measure_extras(args, only=None):
     def want(name):
         return only is None or only == name
 
-    # -- Qwen3-4B-shaped layer: attention only, caches flushed between launches
+    # -- Qwen3-4B-shaped layer: attention only, cold (caches flushed before each call) and warm
     if want("qwen3_4b"):
         w = W.qwen3_4b()
         st = Setup(w, 8)
