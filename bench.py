@@ -642,12 +642,12 @@ def measure_extras(args, only=None):
         for _ in range(3):
             st.step(append=False)
         torch.cuda.synchronize()
-        # cold calls: 100 timed after the warm-up above
-        ms, kms, cst = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 100, flush)
+        # cold calls (100 by default) timed after the warm-up above
+        ms, kms, cst = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), args.cold_calls, flush)
         kb = algorithmic_bytes(st.lengths0, st.caps, w.batch, w.num_q_heads, w.num_kv_heads,
                                w.num_groups) - w.batch * w.num_q_heads * w.head_dim * 4
         # warm: back to back, part of the 512 MiB still in the 256 MB MALL
-        wms, wkms, _ = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), 100)
+        wms, wkms, _ = _timed_call_and_kernel(st.ctx, lambda: st.step(append=False), args.cold_calls)
         res["qwen3_4b"] = {"kv_bytes": kv_bytes(st.lengths0), "attn_call_ms": round(ms, 4),
                            **_med_p90(cst, "attn_call_ms"),
                            "tokens_per_s_per_step": round(w.batch / (cst[1] * 1e-3), 1),   # median call
@@ -682,11 +682,11 @@ def measure_extras(args, only=None):
             topk()
             fused()
         rows = w.batch * 8 * K
-        # cold calls: 100 timed of each
-        gst = _timed_stats(gather, 100, flush)
-        tst = _timed_stats(topk, 100, flush)
+        # cold calls (100 by default) of each
+        gst = _timed_stats(gather, args.cold_calls, flush)
+        tst = _timed_stats(topk, args.cold_calls, flush)
         g_ms, t_ms = gst[0], tst[0]
-        f_ms, fk_ms, fst = _timed_call_and_kernel(st.ctx, fused, 100, flush)
+        f_ms, fk_ms, fst = _timed_call_and_kernel(st.ctx, fused, args.cold_calls, flush)
         both32 = _timed(lambda: [f() for _ in range(32) for f in (gather, topk)], 3) / 32
         fused32 = _timed(lambda: [fused() for _ in range(32)], 3) / 32
         # the same 32-layer stack captured in one HIP graph (launch cost amortised)
@@ -951,6 +951,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-calls", type=int, default=100,
+                    help="timed calls per figure of the Qwen3-4B and Llama top-K configurations")
     ap.add_argument("--no-controls", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other configurations (Qwen3-4B, Llama top-K, mixed churn)")
