@@ -1536,7 +1536,10 @@ static nup_status attn_common(nup_ctx *c, const void *q, float *out, float *lse,
     // (creating events is an allocation)
     const bool timed = may_time && c->timing && !capturing(st);
     if (timed) {
-        if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess)
+        // timing-only events: no system-scope fence when recorded, so the
+        // interval holds the launch and not a writeback of the caches
+        if ((e = hipEventCreateWithFlags(&e0, hipEventDisableSystemFence)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&e1, hipEventDisableSystemFence)) != hipSuccess)
             return hip_fail(c, e, "hipEventCreate");
         if ((e = hipEventRecord(e0, st)) != hipSuccess) return hip_fail(c, e, "hipEventRecord");
     }
