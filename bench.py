@@ -141,6 +141,46 @@ class Setup:
         torch.cuda.empty_cache()
 
 
+class _Event:
+    """A timing event on torch's current stream, created without the
+    system-scope fence (hipEventDisableSystemFence): a fenced event adds a
+    writeback of the caches to the interval it closes.  The HIP runtime is
+    the one torch has loaded (same soname)."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if _Event._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            _Event._hip = hip
+        self._ev = ctypes.c_void_p()
+        rc = _Event._hip.hipEventCreateWithFlags(ctypes.byref(self._ev), 0x20000000)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: error {rc}")
+
+    def record(self):
+        import torch
+        rc = _Event._hip.hipEventRecord(self._ev, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord: error {rc}")
+
+    def elapsed_time(self, other):
+        import ctypes
+        ms = ctypes.c_float()
+        rc = _Event._hip.hipEventElapsedTime(ctypes.byref(ms), self._ev, other._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime: error {rc}")
+        return ms.value
+
+    def __del__(self):
+        if _Event._hip is not None and self._ev:
+            _Event._hip.hipEventDestroy(self._ev)
+
+
 def time_steps(setup, steps, warmup, append=True, fused=True, per_step=None, kernel=True):
     """Returns (ms per step, mean lengths of those steps, split-K kernel ms per
     launch, mean lengths of the kernel pass).  The step time comes from a pass
@@ -157,7 +197,7 @@ def time_steps(setup, steps, warmup, append=True, fused=True, per_step=None, ker
         torch.cuda.synchronize()
         # per-step events only when asked: each one is a barrier between steps
         n_ev = steps + 1 if per is not None else 2
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        ev = [_Event() for _ in range(n_ev)]
         ev[0].record()
         for i in range(steps):
             setup.step(append, fused)
@@ -309,8 +349,7 @@ def _timed_stats(fn, iters, flush=None):
     for _ in range(iters):
         if flush is not None:
             flush()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        e0, e1 = _Event(), _Event()
         e0.record()
         fn()
         e1.record()
@@ -572,8 +611,8 @@ def _graph_decode(flush, context, steps=10, warmup=2):
             fn()
         torch.cuda.synchronize()
         flush()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        e0 = _Event()
+        e1 = _Event()
         host = 0.0
         e0.record()
         for _ in range(steps):
@@ -799,8 +838,8 @@ def measure_extras(args, only=None):
                 nup.set_timing(st.ctx, True)
             if timed:
                 n_active.append(int(active.sum()))
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0 = _Event()
+                e1 = _Event()
                 e0.record()
             nup.attn_decode_nonuniform_append(st.ctx, st.k_new, st.v_new, st.q, st.out, st.lse, st.scale, st.ws)
             # the call advanced the shadow lengths by the appended token,
@@ -1001,8 +1040,8 @@ def main():
         for _ in range(2):
             nup.probe_copy(a, b, n)
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        e0 = _Event()
+        e1 = _Event()
         reps = 5
         e0.record()
         for _ in range(reps):
@@ -1088,8 +1127,8 @@ def main():
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     nup.probe_read(buf, nbytes, sink)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    e0 = _Event()
+    e1 = _Event()
     e0.record()
     for _ in range(5):
         nup.probe_read(buf, nbytes, sink)
