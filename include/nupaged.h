@@ -517,9 +517,11 @@ nup_status nup_get_plan_gangs(const nup_ctx *ctx, int32_t *n_blocks, int32_t *ga
 /* ---- measurement helpers ------------------------------------------------ */
 
 /* When enabled, the library brackets each split-K partial-attention launch
- * with HIP events on the caller's stream; nup_kernel_time() returns the
- * summed milliseconds and launch count since the last reset (synchronises
- * on the recorded events).  Launches recorded into a graph are not timed. */
+ * with HIP events on the caller's stream, created without the system-scope
+ * fence (hipEventDisableSystemFence: timing only, so the interval holds the
+ * launch and no cache writeback); nup_kernel_time() returns the summed
+ * milliseconds and launch count since the last reset (synchronises on the
+ * recorded events).  Launches recorded into a graph are not timed. */
 nup_status nup_set_timing(nup_ctx *ctx, int32_t enable);
 nup_status nup_kernel_time(nup_ctx *ctx, double *partial_ms, int32_t *launches, int32_t reset);
 
