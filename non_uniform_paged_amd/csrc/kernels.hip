@@ -1574,19 +1574,27 @@ __global__ __launch_bounds__(kClThreads) void cluster_select_kernel(CentroidArgs
     const int words = (n + 31) >> 5;
     for (int i = tid; i < words; i += kClThreads) bits[i] = 0;
     __syncthreads();
-    // 4. mark the chosen positions, one wave per cluster
+    // 4. mark the chosen positions.  A wave reads the counts of 64 clusters
+    //    at once and walks only the clusters that give members, all 64 lanes
+    //    on one cluster's list at a time (a walk over every cluster id, one
+    //    LDS read each, took most of this kernel's time at 8192 clusters).
     if (!short_of && !bad_lds) {
-        for (int c = wid; c < a.C; c += kClThreads / 64) {
-            const int m = take[c];
-            if (m <= 0) continue;
-            const int b = st[c];
-            for (int e = lane; e < m; e += 64) {
-                const int t = ps[b + e];
-                if (t < 0 || t >= n) {
-                    atomicOr(&bad_lds, 1);
-                } else {
-                    const uint32_t bit = 1u << (t & 31);
-                    if (atomicOr(&bits[t >> 5], bit) & bit) atomicOr(&bad_lds, 1);   // repeated
+        for (int c0 = wid * 64; c0 < a.C; c0 += kClThreads) {
+            const int mt = c0 + lane < a.C ? take[c0 + lane] : 0;
+            uint64_t pend = __builtin_amdgcn_ballot_w64(mt > 0);
+            while (pend) {
+                const int j = __builtin_ctzll(pend);
+                pend &= pend - 1;
+                const int m = __builtin_amdgcn_readlane(mt, j);
+                const int b = st[c0 + j];
+                for (int e = lane; e < m; e += 64) {
+                    const int t = ps[b + e];
+                    if (t < 0 || t >= n) {
+                        atomicOr(&bad_lds, 1);
+                    } else {
+                        const uint32_t bit = 1u << (t & 31);
+                        if (atomicOr(&bits[t >> 5], bit) & bit) atomicOr(&bad_lds, 1);   // repeated
+                    }
                 }
             }
         }
