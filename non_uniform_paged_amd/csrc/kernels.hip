@@ -1498,33 +1498,57 @@ __global__ __launch_bounds__(kClThreads) void cluster_select_kernel(CentroidArgs
         cut_info[0] = -1;
         cut_info[1] = 0;
     }
-    // 1. keys; members below n (member offsets must lie in [0, P], in order)
+    // 1. keys; members below n (member offsets must lie in [0, P], in order).
+    //    A thread's clusters c = tid + u*kClThreads take their loads in two
+    //    batches, all clusters at once and without branches: the scores and
+    //    offsets, then each list's last member.  Most lists end below n and
+    //    are done; a list that ends in the window (members at or past n sit
+    //    at its end, ascending) steps back a few members and then searches.
     int mine = 0;
-    for (int c = tid; c < a.C; c += kClThreads) {
-        ckey[c] = order_key(cs[c]);
-        const int b = st[c], e = st[c + 1];
-        int m = 0;
-        if (b < 0 || e < b || e > a.P) {
-            atomicOr(&bad_lds, 1);
-        } else {
-            // members at or past n are the window's, at the end of the
-            // ascending list: step back a few, then search what is left
-            int hi = e;
-            for (int k = 0; k < 4 && hi > b && ps[hi - 1] >= n; ++k) --hi;
-            int lo = b;
-            if (hi > b && ps[hi - 1] >= n) {
-                while (lo < hi) {    // first member >= n
-                    const int mid = (lo + hi) >> 1;
-                    if (ps[mid] < n) lo = mid + 1; else hi = mid;
-                }
-            } else {
-                lo = hi;
-            }
-            m = lo - b;
+    {
+        float sc[kPer];
+        int sb[kPer], se[kPer], last[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int c = min(tid + u * kClThreads, a.C - 1);
+            sc[u] = cs[c];
+            sb[u] = st[c];
+            se[u] = st[c + 1];
         }
-        cnt[c] = m;
-        take[c] = 0;
-        mine += m;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const bool ok = sb[u] >= 0 && se[u] > sb[u] && se[u] <= a.P;
+            last[u] = a.P > 0 ? ps[ok ? se[u] - 1 : 0] : -1;   // P > 0 whenever a list is not empty
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int c = tid + u * kClThreads;
+            if (c >= a.C) continue;
+            ckey[c] = order_key(sc[u]);
+            take[c] = 0;
+            const int b = sb[u], e = se[u];
+            int m = 0;
+            if (b < 0 || e < b || e > a.P) {
+                atomicOr(&bad_lds, 1);
+            } else if (e == b || last[u] < n) {
+                m = e - b;
+            } else {
+                int hi = e - 1;   // ps[e - 1] >= n
+                for (int k = 1; k < 4 && hi > b && ps[hi - 1] >= n; ++k) --hi;
+                int lo = b;
+                if (hi > b && ps[hi - 1] >= n) {
+                    while (lo < hi) {    // first member >= n
+                        const int mid = (lo + hi) >> 1;
+                        if (ps[mid] < n) lo = mid + 1; else hi = mid;
+                    }
+                } else {
+                    lo = hi;
+                }
+                m = lo - b;
+            }
+            cnt[c] = m;
+            mine += m;
+        }
     }
     int total = 0;
     block_exclusive_scan<kClThreads>(mine, scan_lds, &total);
@@ -1538,9 +1562,22 @@ __global__ __launch_bounds__(kClThreads) void cluster_select_kernel(CentroidArgs
         for (int shift = 24; shift >= 0; shift -= 8) {
             for (int i = tid; i < 256 + 8; i += kClThreads) hist[i] = 0;
             __syncthreads();
+            // a thread adds up its clusters' weights while their digit stays
+            // the same: the high digits of scores of one head mostly agree,
+            // and one atomic per run instead of per cluster keeps them from
+            // queueing on one LDS address
+            uint32_t dig = 0xffffffffu, acc = 0;
             for (int c = tid; c < a.C; c += kClThreads)
-                if ((ckey[c] & mask) == prefix && cnt[c] > 0)
-                    atomicAdd(&hist[padb((ckey[c] >> shift) & 255u)], (uint32_t)cnt[c]);
+                if ((ckey[c] & mask) == prefix && cnt[c] > 0) {
+                    const uint32_t d = (ckey[c] >> shift) & 255u;
+                    if (d != dig) {
+                        if (acc) atomicAdd(&hist[padb(dig)], acc);
+                        dig = d;
+                        acc = 0;
+                    }
+                    acc += (uint32_t)cnt[c];
+                }
+            if (acc) atomicAdd(&hist[padb(dig)], acc);
             __syncthreads();
             if (tid < 64) find_digit<256>(hist, remaining, pick);
             __syncthreads();
