@@ -890,6 +890,10 @@ __device__ __forceinline__ float dpp_f(float x) {
 }
 
 constexpr int kScoreDepth = 4;
+// Scores wait in LDS and go out as one burst per segment of a row: written
+// page by page, 64 bytes at a time, they broke up the K read stream.
+constexpr int kScoreSegPages = 512;                       // pages per staged segment
+constexpr int kScoreStage = kScoreSegPages * kPage;       // floats per wave
 
 template <int D, int GQA>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
@@ -900,11 +904,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     // K tile staged row-major, rows padded by one piece, read back in the
     // MFMA operand layout (about 16 bank-conflict cycles per page counted)
     __shared__ uint4 k_lds[kWavesPerBlock][kPage][LPR + 1];
+    __shared__ float4 s_stage[kWavesPerBlock][kScoreStage / 4];
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = blockIdx.x * kWavesPerBlock + wid;
     if (w >= a.n_workers) return;
     uint4 (*kt)[LPR + 1] = k_lds[wid];
+    float *sst = reinterpret_cast<float *>(s_stage[wid]);
     const int qn = lane & 15, qg = lane >> 4;
     const int tg = lane / LPR, ve = lane % LPR;
     const int rb = ld_uniform(a.worker_start + w), re = ld_uniform(a.worker_start + w + 1);
@@ -928,7 +934,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
             a.page_table + ((size_t)ld_uniform(a.group_of_head + h) * a.bmax + s) * (size_t)a.max_pages;
         const size_t slot_off = (size_t)ld_uniform(a.slot_of_head + h) * kPage * D;
         float *out = a.scores + (size_t)sh * a.stride;
-        const int p0 = t0 / kPage, p1 = (t1 - 1) / kPage;
+        const int rp0 = t0 / kPage, rp1 = (t1 - 1) / kPage;
+        int sbase = 0;   // first position of the staged segment
         // row-major, fully coalesced: an instruction reads RPI whole rows
         auto load = [&](int pi, uint4 (&k)[TPL]) {
             const uint4 *kp = reinterpret_cast<const uint4 *>(
@@ -959,47 +966,56 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
                 x = fmaxf(x, dpp_f<kRowRor1>(x));
                 m[i] = x;
             }
-            // 16 bytes of scores per lane of the first row; the 31 MB these
-            // writes add to a 2 GB read stream cost the kernel about a sixth
-            // of its time, however they are batched
+            // 16 bytes of scores per lane of the first row, into the stage
             const int tb = pi * kPage + 4 * qg;
-            if (qn == 0) {
-                if (tb + 3 < t1) {
-                    *reinterpret_cast<float4 *>(out + tb) = make_float4(m[0], m[1], m[2], m[3]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (tb + i < t1) out[tb + i] = m[i];
-                }
-            }
+            if (qn == 0) reinterpret_cast<float4 *>(sst)[(tb - sbase) >> 2] = make_float4(m[0], m[1], m[2], m[3]);
+        };
+        // the staged scores of positions [sbase, te) to the head's row, in
+        // 16-byte stores (sbase is a page start, the row 16-float aligned)
+        auto flush = [&](int te) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int nv = te - sbase;
+            for (int i = 4 * lane; i + 3 < nv; i += 256)
+                *reinterpret_cast<float4 *>(out + sbase + i) = reinterpret_cast<const float4 *>(sst)[i >> 2];
+            for (int i = (nv & ~3) + lane; i < nv; i += 64) out[sbase + i] = sst[i];
+            __builtin_amdgcn_wave_barrier();   // reads of the stage done before it is written again
         };
         // only K is read: a ring of kScoreDepth pages keeps as many bytes in
         // flight as the attention kernel's K+V double buffer
         // Steady-state trips issue every prefetch unconditionally, so the
         // wait before a page leaves the later pages in flight; the last
         // pages go through the guarded tail.
-        uint4 kb[kScoreDepth][TPL];
+        // The row in segments of kScoreSegPages pages, each streamed through
+        // the ring and then written out from the stage in one burst.
+        for (int p0 = rp0; p0 <= rp1; p0 += kScoreSegPages) {
+            const int p1 = min(rp1, p0 + kScoreSegPages - 1);
+            sbase = p0 * kPage;
+            uint4 kb[kScoreDepth][TPL];
 #pragma unroll
-        for (int j = 0; j + 1 < kScoreDepth; ++j)
-            if (p0 + j <= p1) load(p0 + j, kb[j]);
-        int pb = p0;
-        for (; pb + 2 * kScoreDepth - 2 <= p1; pb += kScoreDepth) {
+            for (int j = 0; j + 1 < kScoreDepth; ++j)
+                if (p0 + j <= p1) load(p0 + j, kb[j]);
+            int pb = p0;
+            for (; pb + 2 * kScoreDepth - 2 <= p1; pb += kScoreDepth) {
 #pragma unroll
-            for (int j = 0; j < kScoreDepth; ++j) {
-                load(pb + j + kScoreDepth - 1, kb[(j + kScoreDepth - 1) % kScoreDepth]);
-                score(pb + j, kb[j]);
-            }
-        }
-        for (; pb <= p1; pb += kScoreDepth) {
-#pragma unroll
-            for (int j = 0; j < kScoreDepth; ++j) {
-                const int p = pb + j;
-                if (p <= p1) {
-                    const int pf = p + kScoreDepth - 1;
-                    if (pf <= p1) load(pf, kb[(j + kScoreDepth - 1) % kScoreDepth]);
-                    score(p, kb[j]);
+                for (int j = 0; j < kScoreDepth; ++j) {
+                    load(pb + j + kScoreDepth - 1, kb[(j + kScoreDepth - 1) % kScoreDepth]);
+                    score(pb + j, kb[j]);
                 }
             }
+            for (; pb <= p1; pb += kScoreDepth) {
+#pragma unroll
+                for (int j = 0; j < kScoreDepth; ++j) {
+                    const int p = pb + j;
+                    if (p <= p1) {
+                        const int pf = p + kScoreDepth - 1;
+                        if (pf <= p1) load(pf, kb[(j + kScoreDepth - 1) % kScoreDepth]);
+                        score(p, kb[j]);
+                    }
+                }
+            }
+            flush(min(t1, (p1 + 1) * kPage));
         }
     }
 }
