@@ -1171,11 +1171,16 @@ __global__ __launch_bounds__(256) void sel_hist_kernel(SelectArgs a) {
 
 // kSelSplit workgroups per head: each finds the threshold's top bin d1 from
 // the finished histogram, counts its slice's entries above d1 and appends the
-// slice's entries in d1 to the head's candidate list (one atomic per wave).
+// slice's entries in d1 to the head's candidate list.  The entries gather in
+// LDS and reach the list with one global atomic per workgroup: one per wave
+// and step made every wave wait on a device round trip per step.
+constexpr int kCollectCap = 1024;   // entries a workgroup gathers in LDS (the rest go straight out)
 __global__ __launch_bounds__(256) void sel_collect_kernel(SelectArgs a) {
     __shared__ uint32_t bins[kSelBins + kSelBins / 32];
     __shared__ uint32_t pick[2];
-    __shared__ int gt_lds;
+    __shared__ int gt_lds, ln_lds, lbase_lds;
+    __shared__ uint32_t lkey[kCollectCap];
+    __shared__ int32_t lpos[kCollectCap];
     const int sh = blockIdx.y, j = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     int n, k, cs;
     if (!sel_head(a, sh, n, k, cs) || k <= 0) return;
@@ -1187,7 +1192,10 @@ __global__ __launch_bounds__(256) void sel_collect_kernel(SelectArgs a) {
     }
     const uint32_t *row = a.hist + (size_t)sh * kSelHistStride;
     for (int i = tid; i < kSelBins; i += 256) bins[padb(i)] = row[i];
-    if (tid == 0) gt_lds = 0;
+    if (tid == 0) {
+        gt_lds = 0;
+        ln_lds = 0;
+    }
     __syncthreads();
     if (tid < 64) find_digit<kSelBins>(bins, k, pick);
     __syncthreads();
@@ -1229,7 +1237,7 @@ __global__ __launch_bounds__(256) void sel_collect_kernel(SelectArgs a) {
             }
             if (tot) {
                 int base = 0;
-                if (lane == 0) base = (int)atomicAdd(ncand, (uint32_t)tot);
+                if (lane == 0) base = atomicAdd(&ln_lds, tot);
                 base = __shfl(base, 0);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -1237,9 +1245,15 @@ __global__ __launch_bounds__(256) void sel_collect_kernel(SelectArgs a) {
                     const int p = base + before[q] +
                                   (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[q] >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m[q], 0u));
-                    if (p < kSelCap) {
-                        ck[p] = key[q];
-                        cp[p] = t + q;
+                    if (p < kCollectCap) {
+                        lkey[p] = key[q];
+                        lpos[p] = t + q;
+                    } else {   // past the LDS room: straight to the list
+                        const int g = (int)atomicAdd(ncand, 1u);
+                        if (g < kSelCap) {
+                            ck[g] = key[q];
+                            cp[g] = t + q;
+                        }
                     }
                 }
             }
@@ -1260,7 +1274,20 @@ __global__ __launch_bounds__(256) void sel_collect_kernel(SelectArgs a) {
     gt = wave_sum(gt);
     if (lane == 0 && gt) atomicAdd(&gt_lds, gt);
     __syncthreads();
-    if (tid == 0) *sgt = gt_lds;
+    // the gathered entries to the head's list in one piece
+    const int nl = min(ln_lds, kCollectCap);
+    if (tid == 0) {
+        lbase_lds = nl ? (int)atomicAdd(ncand, (uint32_t)nl) : 0;
+        *sgt = gt_lds;
+    }
+    __syncthreads();
+    for (int i = tid; i < nl; i += 256) {
+        const int g = lbase_lds + i;
+        if (g < kSelCap) {
+            ck[g] = lkey[i];
+            cp[g] = lpos[i];
+        }
+    }
 }
 
 __global__ __launch_bounds__(kSelThreads) void sel_thresh_kernel(SelectArgs a) {
