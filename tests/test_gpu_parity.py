@@ -676,6 +676,38 @@ def test_select_topk_exact_ties(plan_mode):
         assert np.array_equal(out.cpu().numpy(), want), (K, window)
 
 
+def test_select_topk_long_rows():
+    """Few workers and long heads, so that a score-kernel row spans several
+    staged segments of 512 pages (and ends in a partial one); exactly
+    representable scores with ties, so the selection equals the oracle's
+    bit for bit."""
+    B, H, gqa, D = 1, 2, 2, 128
+    L = np.array([[20000, 13001]], np.int32)
+    max_pages = int(math.ceil(L.max() / 16)) + 1
+    c = Case(H=H, Hq=H * gqa, D=D, ng=1, B=B, num_pages=B * max_pages + 7, max_pages=max_pages,
+             num_workers=2, salt=42)
+    c.alloc([0], L, L)
+    c.commit()
+    rs = np.random.default_rng(42)
+    kp = torch.zeros_like(c.kpool, dtype=torch.float32)
+    kp[:, :, :, 3] = torch.from_numpy(rs.integers(-8, 9, size=kp.shape[:3]).astype(np.float32)).to(DEV)
+    kp[:, :, :, 5] = torch.from_numpy(rs.integers(-8, 9, size=kp.shape[:3]).astype(np.float32)).to(DEV)
+    c.kpool.copy_(kp.to(torch.bfloat16))
+    qf = torch.zeros((B, H * gqa, D), dtype=torch.float32)
+    qf[:, 0::2, 3], qf[:, 0::2, 5] = 1.0, 0.5
+    qf[:, 1::2, 3], qf[:, 1::2, 5] = -0.25, 2.0
+    c.q.copy_(qf.to(torch.bfloat16).to(DEV))
+    rows, ws_, _ = nup.get_plan(c.ctx)
+    assert (rows[:, 2] - rows[:, 1]).max() > 2 * 512 * 16   # a row of three segments
+    for K, window in ((64, 16), (1500, 100)):
+        out = torch.full((B, H, K), -5, dtype=torch.int32, device=DEV)
+        ws = torch.empty(nup.select_workspace_bytes(c.ctx), dtype=torch.uint8, device=DEV)
+        nup.kv_select_topk(c.ctx, c.q, K, window, out, ws)
+        torch.cuda.synchronize()
+        want, _ = osel.select_all(u16(c.q), u16(c.kpool), c.spec, K, window)
+        assert np.array_equal(out.cpu().numpy(), want), (K, window)
+
+
 def test_select_topk_random_and_refused_cases():
     c, L, caps = _gather_case(41, B=3, H=8, gqa=5, ng=4)
     c.alloc([0, 2], caps[[0, 2]], L[[0, 2]])
