@@ -53,7 +53,7 @@ def test_centroid_select_exact_inputs():
     qf[:, 0::2, 3], qf[:, 0::2, 5] = 1.0, 0.5
     qf[:, 1::2, 3], qf[:, 1::2, 5] = -0.25, 2.0
     c.q.copy_(_dev(f32_to_bf16_bits(qf).view(np.int16)).view(torch.bfloat16))
-    for C in (1, 7, 64):
+    for C in (1, 7, 64, 5000, 8192):      # up to the largest C: most lists empty
         cf = np.zeros((B, H, C, D), np.float32)
         cf[..., 3] = rs.integers(-4, 5, size=(B, H, C))
         cf[..., 5] = rs.integers(-4, 5, size=(B, H, C))
